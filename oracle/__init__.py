@@ -1,0 +1,104 @@
+"""fp64 CPU oracle for one decode step of paged attention.
+
+TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import this package.  The product library
+(paged_kv_cache_64_amd) never imports it, and it never imports the product.
+
+The arithmetic lives in pa_oracle.c; this module only marshals numpy arrays
+into it and builds the oracle's own slot-indexed host cache from the seeded
+generator's block contents (no device layout is involved).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        lib.pa_oracle_f16_to_f64.restype = ctypes.c_double
+        lib.pa_oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.pa_oracle_slot.restype = ctypes.c_int64
+        lib.pa_oracle_slot.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]
+        lib.pa_oracle_kv_bytes_per_token.restype = ctypes.c_int64
+        lib.pa_oracle_kv_bytes_per_token.argtypes = [ctypes.c_int32] * 4
+        lib.pa_oracle_page_bytes.restype = ctypes.c_int64
+        lib.pa_oracle_page_bytes.argtypes = [ctypes.c_int32] * 5
+        lib.pa_oracle_decode.restype = ctypes.c_int
+        lib.pa_oracle_decode.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_double, ctypes.c_void_p, ctypes.c_int32]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def f16_to_f64(bits: int) -> float:
+    """binary16 bit pattern -> exact double (the oracle's own decoder)."""
+    return _load().pa_oracle_f16_to_f64(int(bits) & 0xFFFF)
+
+
+def slot(table_row, block_size: int, pos: int) -> int:
+    row = np.ascontiguousarray(table_row, dtype=np.int32)
+    return int(_load().pa_oracle_slot(_ptr(row), block_size, pos))
+
+
+def kv_bytes_per_token(layers, kv_heads, head_dim, bytes_per_value) -> int:
+    return int(_load().pa_oracle_kv_bytes_per_token(layers, kv_heads, head_dim, bytes_per_value))
+
+
+def page_bytes(block_size, kv_heads, key_dim, value_dim, bytes_per_value) -> int:
+    return int(_load().pa_oracle_page_bytes(block_size, kv_heads, key_dim, value_dim,
+                                            bytes_per_value))
+
+
+def host_cache(num_blocks, block_size, block_ids, blocks, fill=np.nan):
+    """Slot-indexed host cache [num_blocks*block_size, kv_heads, head_dim] (F16).
+
+    `blocks` holds the contents of the physical blocks named by `block_ids`,
+    shaped [n, block_size, kv_heads, head_dim]; every other slot gets `fill`.
+    """
+    blocks = np.asarray(blocks, dtype=np.float16)
+    n, b, hkv, d = blocks.shape
+    assert b == block_size
+    cache = np.full((num_blocks, block_size, hkv, d), fill, dtype=np.float16)
+    cache[np.asarray(block_ids, dtype=np.int64)] = blocks
+    return cache.reshape(num_blocks * block_size, hkv, d)
+
+
+def decode(q, k_slots, v_slots, block_tables, ctx_lens, scale, block_size, threads=0):
+    """fp64 attention output [batch, num_q_heads, head_dim] for one layer.
+
+    q: F16 [batch, Hq, d]; k_slots/v_slots: F16 [num_slots, Hkv, d];
+    block_tables: int32 [batch, max_blocks]; ctx_lens: int32 [batch].
+    """
+    q = np.ascontiguousarray(q, dtype=np.float16)
+    k_slots = np.ascontiguousarray(k_slots, dtype=np.float16)
+    v_slots = np.ascontiguousarray(v_slots, dtype=np.float16)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    batch, hq, d = q.shape
+    num_slots, hkv, d2 = k_slots.shape
+    assert d2 == d and v_slots.shape == k_slots.shape
+    assert tables.ndim == 2 and tables.shape[0] == batch and lens.shape == (batch,)
+    out = np.empty((batch, hq, d), dtype=np.float64)
+    rc = _load().pa_oracle_decode(
+        _ptr(q.view(np.uint16)), _ptr(k_slots.view(np.uint16)), _ptr(v_slots.view(np.uint16)),
+        num_slots, _ptr(tables), tables.shape[1], _ptr(lens), batch, hq, hkv, d, block_size,
+        float(scale), _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its inputs (code {rc})")
+    return out

@@ -1,0 +1,208 @@
+/*
+ * pa_oracle.c -- TEST INFRASTRUCTURE, not part of the product.
+ *
+ * A plain, slow, fp64 CPU reference for one batched decode step of attention
+ * over a paged KV cache.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  It shares no code,
+ * header, table or constant with the HIP library under paged_kv_cache_64_amd/.
+ *
+ * What it follows (the pages are named by title and section):
+ *  - "vLLM Architecture and Installation", Example 3 (paged KV cache block
+ *    tables): a request's block table lists the physical blocks holding its
+ *    tokens in order; the slot of logical position p is
+ *    table[p / block_size] * block_size + p % block_size, and the attention
+ *    kernel reads a request's history through that table.
+ *  - "Reading Inference Engine Codebases", Example 2: the attention scale is
+ *    1/sqrt(head dimension) unless the model overrides it, so the scale is an
+ *    argument; KV heads may be shared by several query heads (grouped-query
+ *    attention).
+ *  - "Reading Inference Engine Codebases", Example 6: softmax is computed in
+ *    its max-shifted form exp(x - max) / sum.
+ *  - "vLLM Architecture and Installation", Example 6 and "Batching and
+ *    Scheduling", Example 1: page size = block size x KV heads x (key dim +
+ *    value dim) x bytes per value; 128 KiB of F16 KV per token for the 8B
+ *    shape.
+ *
+ * Readings where the pages are silent (each is a stated choice):
+ *  - query head h uses KV head h / (num_q_heads / num_kv_heads) (contiguous
+ *    groups);
+ *  - the context of sequence s is exactly its positions [0, ctx_s); the
+ *    newest token is already stored, so no causal mask is needed;
+ *  - table entries at or past ceil(ctx_s / block_size) and slots past ctx_s in
+ *    the last block are never read;
+ *  - ctx_s == 0 gives an all-zero output row;
+ *  - the same physical block may appear in several tables (and twice in one
+ *    table); each occurrence is simply read.
+ *
+ * Parity pins (tests/test_oracle_pins.py): brute force over a contiguous
+ * cache, torch's scaled_dot_product_attention in fp64, permutation of block
+ * ids, ctx = 1, identical keys, the two-token sigmoid form, V scaling, the
+ * pages' slot example and sizing figures.  No function here is
+ * "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* IEEE 754 binary16 -> double, written from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ *   e == 0      : subnormal, value = frac * 2^-24
+ *   e == 31     : infinity (frac == 0) or NaN
+ *   otherwise   : value = (1024 + frac) * 2^(e - 25)
+ * Every binary16 value is exactly representable as a double. */
+double pa_oracle_f16_to_f64(uint16_t bits)
+{
+    const int sign = (bits >> 15) & 1;
+    const int e = (bits >> 10) & 0x1f;
+    const int frac = bits & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)frac, -24);
+    else if (e == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), e - 25);
+    return sign ? -v : v;
+}
+
+/* Slot of logical position `pos` for one request ("vLLM Architecture and
+ * Installation", Example 3): the table entry at pos / block_size names the
+ * physical block, pos % block_size is the offset inside it. */
+int64_t pa_oracle_slot(const int32_t *table_row, int32_t block_size, int64_t pos)
+{
+    return (int64_t)table_row[pos / block_size] * block_size + pos % block_size;
+}
+
+/* Bytes of K plus V for one token over all layers ("Batching and Scheduling",
+ * Example 1: 128 KiB per token for 32 layers x 8 KV heads x 128 dims in F16). */
+int64_t pa_oracle_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                                     int32_t bytes_per_value)
+{
+    return (int64_t)layers * kv_heads * head_dim * 2 /* K and V */ * bytes_per_value;
+}
+
+/* Page size of one block in one layer ("vLLM Architecture and Installation",
+ * Example 6): block size x KV heads x (key dim + value dim) x bytes. */
+int64_t pa_oracle_page_bytes(int32_t block_size, int32_t kv_heads, int32_t key_dim,
+                             int32_t value_dim, int32_t bytes_per_value)
+{
+    return (int64_t)block_size * kv_heads * (key_dim + value_dim) * bytes_per_value;
+}
+
+/*
+ * One decode step of attention, one layer.
+ *
+ *   q            F16 bits [batch][num_q_heads][head_dim]
+ *   k_slots      F16 bits [num_slots][num_kv_heads][head_dim]  (slot-indexed cache)
+ *   v_slots      F16 bits [num_slots][num_kv_heads][head_dim]
+ *   block_tables int32    [batch][max_blocks]
+ *   ctx_lens     int32    [batch]
+ *   out          double   [batch][num_q_heads][head_dim]
+ *
+ * For each sequence s and query head h (g = h / (num_q_heads/num_kv_heads)):
+ *   z[t]  = scale * sum_i q[s][h][i] * K[slot(s,t)][g][i]      t = 0 .. ctx_s-1
+ *   M     = max_t z[t]
+ *   w[t]  = exp(z[t] - M),  L = sum_t w[t]
+ *   out[s][h][i] = sum_t w[t] * V[slot(s,t)][g][i] / L
+ * all in double, sums taken in increasing t.
+ *
+ * Returns 0 on success, 1 on a bad geometry, 2 when a table entry or a
+ * context length points outside the given arrays, 3 on allocation failure.
+ */
+int pa_oracle_decode(const uint16_t *q, const uint16_t *k_slots, const uint16_t *v_slots,
+                     int64_t num_slots, const int32_t *block_tables, int32_t max_blocks,
+                     const int32_t *ctx_lens, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, double scale,
+                     double *out, int32_t num_threads)
+{
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks < 0 || num_q_heads % num_kv_heads != 0)
+        return 1;
+
+    /* Every table entry that will be read must name a slot inside the arrays. */
+    for (int32_t s = 0; s < batch; ++s) {
+        const int64_t ctx = ctx_lens[s];
+        if (ctx < 0 || ctx > (int64_t)max_blocks * block_size)
+            return 2;
+        const int32_t *row = block_tables + (int64_t)s * max_blocks;
+        for (int64_t t = 0; t < ctx; ++t) {
+            const int64_t slot = pa_oracle_slot(row, block_size, t);
+            if (slot < 0 || slot >= num_slots)
+                return 2;
+        }
+    }
+
+    const int32_t group = num_q_heads / num_kv_heads;
+    const int64_t rows = (int64_t)batch * num_q_heads;
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (num_threads <= 0)
+        num_threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads) reduction(| : failed)
+#endif
+    for (int64_t r = 0; r < rows; ++r) {
+        const int32_t s = (int32_t)(r / num_q_heads);
+        const int32_t h = (int32_t)(r % num_q_heads);
+        const int32_t g = h / group;
+        const int64_t ctx = ctx_lens[s];
+        const int32_t *row = block_tables + (int64_t)s * max_blocks;
+        const uint16_t *qh = q + r * head_dim;
+        double *o = out + r * head_dim;
+
+        for (int32_t i = 0; i < head_dim; ++i)
+            o[i] = 0.0;
+        if (ctx == 0)
+            continue;
+
+        double *z = (double *)malloc(sizeof(double) * (size_t)ctx);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)head_dim);
+        if (!z || !qd) {
+            free(z);
+            free(qd);
+            failed |= 1;
+            continue;
+        }
+        for (int32_t i = 0; i < head_dim; ++i)
+            qd[i] = pa_oracle_f16_to_f64(qh[i]);
+
+        /* scores, gathered through the block table */
+        double m = -INFINITY;
+        for (int64_t t = 0; t < ctx; ++t) {
+            const int64_t slot = pa_oracle_slot(row, block_size, t);
+            const uint16_t *kr = k_slots + (slot * num_kv_heads + g) * head_dim;
+            double dot = 0.0;
+            for (int32_t i = 0; i < head_dim; ++i)
+                dot += qd[i] * pa_oracle_f16_to_f64(kr[i]);
+            z[t] = scale * dot;
+            if (z[t] > m)
+                m = z[t];
+        }
+
+        /* max-shifted softmax weights and their sum */
+        double l = 0.0;
+        for (int64_t t = 0; t < ctx; ++t) {
+            z[t] = exp(z[t] - m);
+            l += z[t];
+        }
+
+        /* weighted sum of values */
+        for (int64_t t = 0; t < ctx; ++t) {
+            const int64_t slot = pa_oracle_slot(row, block_size, t);
+            const uint16_t *vr = v_slots + (slot * num_kv_heads + g) * head_dim;
+            for (int32_t i = 0; i < head_dim; ++i)
+                o[i] += z[t] * pa_oracle_f16_to_f64(vr[i]);
+        }
+        for (int32_t i = 0; i < head_dim; ++i)
+            o[i] /= l;
+
+        free(z);
+        free(qd);
+    }
+    return failed ? 3 : 0;
+}
