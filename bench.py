@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of paged attention on one MI355X.
+
+Default workload: the full 32-layer decode step of the 8B geometry -- batch 32,
+every context 4096 tokens, 32 query heads / 8 KV heads, head_dim 128,
+block_size 16, F16 K/V ~ N(0, 1), a fresh random block table per layer in a
+pool of twice the needed blocks.  One step = for each of the 32 layers:
+pa_write_kv of the newest token's K/V, pa_decode_partial, pa_decode_merge.
+
+Prints one JSON line: achieved KV GB/s (value), decode tokens/s, the fraction
+of HBM peak, a roofline record for the dominant kernel (decode_partial), and
+the fp64 CPU oracle timed on this host as a baseline.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved KV GB/s (% HBM peak) and decode tokens/s"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_64_amd", "csrc", "pa_kernels.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partial_c3_counters.txt")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_counters():
+    """HBM traffic per decode_partial launch from the committed rocprofv3 summary,
+    or None when it is missing or was taken on other kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if ":" in line:
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_launch"])) + int(float(kv["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not "
+              f"supported: this library has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_64_amd as pa
+    import workloads
+    from paged_kv_cache_64_amd import roofline
+
+    lib = pa.load_library()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w = workloads.config(args.config, args.seed)
+    B, HQ, HKV, D = w.block_size, w.num_q_heads, w.num_kv_heads, w.head_dim
+    log(f"workload: {w.name}; pool {w.layers} layers x {w.pool_blocks} blocks")
+
+    # ---- stage the pool through pa_write_kv, layer by layer ----
+    t_stage = time.time()
+    pool = pa.Pool(w.layers, w.pool_blocks, HKV, D, B, device=dev, fill=0.0)
+    lens_dev = torch.from_numpy(w.ctx_lens.copy()).to(dev)
+    q_dev, tables_dev, knew, vnew, slots = [], [], [], [], []
+    host0 = None
+    ctx = w.ctx_lens.astype(np.int64)
+    for layer in range(w.layers):
+        ids, k, v = w.kv_blocks(layer)
+        pool.write_blocks(layer, torch.from_numpy(ids).to(dev), torch.from_numpy(k).to(dev),
+                          torch.from_numpy(v).to(dev))
+        q = w.q(layer)
+        tables = w.tables(layer)
+        q_dev.append(torch.from_numpy(q).to(dev))
+        tables_dev.append(torch.from_numpy(tables).to(dev))
+        # the step's newest token (position ctx-1) is rewritten with its own values
+        live = ctx > 0
+        pos = np.maximum(ctx - 1, 0)
+        blk = tables[np.arange(w.batch), pos // B]
+        rank = np.searchsorted(ids, blk)
+        rank = np.minimum(rank, len(ids) - 1) if len(ids) else rank
+        kn = k[rank, pos % B] if len(ids) else np.zeros((w.batch, HKV, D), np.float16)
+        vn = v[rank, pos % B] if len(ids) else np.zeros((w.batch, HKV, D), np.float16)
+        sl = np.where(live, blk.astype(np.int64) * B + pos % B, -1).astype(np.int32)
+        knew.append(torch.from_numpy(np.ascontiguousarray(kn)).to(dev))
+        vnew.append(torch.from_numpy(np.ascontiguousarray(vn)).to(dev))
+        slots.append(torch.from_numpy(sl).to(dev))
+        if layer == 0 and not args.no_cpu_baseline:
+            host0 = (q, tables, ids, k, v)
+        del ids, k, v
+        if layer % 8 == 7:
+            log(f"staged {layer + 1}/{w.layers} layers")
+    torch.cuda.synchronize()
+    log(f"staging took {time.time() - t_stage:.1f} s")
+
+    mcl = w.max_context_len
+    width = w.max_blocks
+    split = pool.split_tokens(w.batch, HQ, mcl)
+    ws_bytes = pool.workspace_bytes(w.batch, HQ, mcl)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(q) for q in q_dev]
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    h = pool.handle
+    scale = ctypes.c_float(w.scale)
+
+    # pre-marshalled argument tuples: the launch loop only calls into the library
+    write_args = [(h, L, knew[L].data_ptr(), vnew[L].data_ptr(), slots[L].data_ptr(), w.batch, sptr)
+                  for L in range(w.layers)]
+    part_args = [(h, L, q_dev[L].data_ptr(), outs[L].data_ptr(), tables_dev[L].data_ptr(), width,
+                  lens_dev.data_ptr(), w.batch, HQ, mcl, scale, ws.data_ptr(), ws_bytes, sptr)
+                 for L in range(w.layers)]
+    merge_args = [(h, outs[L].data_ptr(), lens_dev.data_ptr(), w.batch, HQ, mcl, ws.data_ptr(),
+                   ws_bytes, sptr) for L in range(w.layers)]
+    f_write, f_part, f_merge = lib.pa_write_kv, lib.pa_decode_partial, lib.pa_decode_merge
+
+    def step(events=None):
+        for L in range(w.layers):
+            rc = f_write(*write_args[L])
+            if events is not None:
+                events[L][0].record(stream)
+            rc |= f_part(*part_args[L])
+            if events is not None:
+                events[L][1].record(stream)
+            rc |= f_merge(*merge_args[L])
+            if rc != 0:
+                raise RuntimeError(f"library call failed in layer {L}: {rc}")
+
+    kv_bytes_step = w.kv_bytes()
+    cold_flush = kv_bytes_step < (4 << 30)   # small steps would run from the 256 MB cache
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if cold_flush else None
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); split={split} tokens, workspace={ws_bytes} B, "
+        f"cold flush between steps: {cold_flush}")
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(w.layers)] for _ in range(args.steps)]
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        step_ev[i][0].record(stream)
+        step(ev[i])
+        step_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
+    part_us = [1e3 * a.elapsed_time(b) for e in ev for a, b in e]
+    ms_per_step = float(np.mean(step_ms))
+    log(f"timed {args.steps} steps: mean {ms_per_step:.4f} ms, min {min(step_ms):.4f} ms, "
+        f"wall {1e3 * wall / args.steps:.4f} ms/step; decode_partial mean {np.mean(part_us):.2f} us")
+
+    kv_gbps = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = w.batch / (ms_per_step * 1e-3)
+    kb = roofline.split_kernel_bytes(w.ctx_lens, HQ, HKV, D, B)
+    part_mean_s = float(np.mean(part_us)) * 1e-6
+    achieved = kb["total"] / part_mean_s / 1e9
+    traffic = read_counters()
+
+    # ---- HBM read probe: the bandwidth this GPU reaches on a plain stream ----
+    probe = None
+    if not args.no_probe:
+        plib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_64_amd", "libpa_probe.so"))
+        plib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        plib.pa_probe_read.restype = ctypes.c_int32
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        buf.fill_(1)
+        sink = torch.empty(plib.pa_probe_read_groups(), dtype=torch.int32, device=dev)
+        for _ in range(2):
+            plib.pa_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), sptr)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        a.record(stream)
+        for _ in range(reps):
+            plib.pa_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), sptr)
+        b.record(stream)
+        torch.cuda.synchronize()
+        probe = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+        del buf
+        log(f"HBM read probe: {probe:.0f} GB/s")
+
+    # ---- oracle on the host: baseline timing and a parity sample ----
+    cpu = None
+    parity = None
+    if host0 is not None:
+        import oracle
+
+        q, tables, ids, k, v = host0
+        kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, w.ctx_lens, B)
+        threads = len(os.sched_getaffinity(0))
+        # one decode of layer 0 for the parity sample
+        lib.pa_decode(h, 0, q_dev[0].data_ptr(), outs[0].data_ptr(), tables_dev[0].data_ptr(), width,
+                      lens_dev.data_ptr(), w.batch, HQ, mcl, scale, ws.data_ptr(), ws_bytes, sptr)
+        torch.cuda.synchronize()
+        gpu0 = outs[0].cpu().numpy().astype(np.float64)
+        done, done_bytes, errs, refs, diffs = 0, 0, [], [], []
+        t_cpu = time.perf_counter()
+        order = np.random.default_rng(0).permutation(w.batch)
+        chunk = 4
+        while done < w.batch and time.perf_counter() - t_cpu < args.cpu_seconds:
+            seqs = np.sort(order[done:done + chunk])
+            ref = oracle.decode(q[seqs], kc, vc, t2[seqs], w.ctx_lens[seqs], w.scale, B,
+                                threads=threads)
+            errs.append(float(np.abs(gpu0[seqs] - ref).max()))
+            refs.append(float((ref ** 2).sum()))
+            diffs.append(float(((gpu0[seqs] - ref) ** 2).sum()))
+            done += len(seqs)
+            done_bytes += int(w.ctx_lens[seqs].astype(np.int64).sum()) * HKV * D * 4
+        cpu_s = time.perf_counter() - t_cpu
+        cpu = {"value": round(done_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"layer 0, {done} of {w.batch} sequences ({done_bytes} B of K/V), "
+                         f"fp64, {cpu_s:.1f} s",
+               "tokens_per_s_equiv": round(done / cpu_s / w.layers, 4)}
+        parity = {"sequences": done, "max_abs_err": max(errs),
+                  "rel_l2": (sum(diffs) / sum(refs)) ** 0.5}
+        log(f"oracle: {cpu['value']} GB/s on {threads} threads; parity {parity}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(kv_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.batch,
+                   "context": int(w.ctx_lens.max()), "q_heads": HQ, "kv_heads": HKV,
+                   "head_dim": D, "block_size": B, "pool_blocks_per_layer": w.pool_blocks,
+                   "split_tokens": split, "cold_flush_between_steps": cold_flush},
+        "tokens_per_s": round(tokens_per_s, 1),
+        "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
+        "kv_bytes_per_step": kv_bytes_step,
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "decode_partial_kernel",
+                     "bytes_per_launch": kb["total"],
+                     "mean_launch_us": round(part_mean_s * 1e6, 3)},
+        "hbm_read_probe_GBps": round(probe, 1) if probe else None,
+        "pct_of_probe": round(100 * kv_gbps / probe, 2) if probe else None,
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+    }
+    print(json.dumps(line), flush=True)
+    pool.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * pa.h -- paged decode attention for MI355X (gfx950), C ABI.
+ *
+ * One batched decode step of attention over a paged KV cache: each active
+ * sequence contributes one query token; its keys and values live in
+ * fixed-size blocks that a per-sequence block table scatters through a shared
+ * pool ("vLLM Architecture and Installation", Example 3: a block table maps a
+ * request's logical positions to physical blocks; new keys and values are
+ * written to slot table[p / block_size] * block_size + p % block_size, and
+ * attention reads a request's history through its table).
+ *
+ * For sequence s, query head h, with g = h / (num_q_heads / num_kv_heads)
+ * (query heads share KV heads in contiguous groups; "Reading Inference Engine
+ * Codebases", Example 2, and "Batching and Scheduling", Example 10) and
+ * ctx = context_lens[s]:
+ *     z_t = scale * <q[s][h], K[slot(s,t)][g]>            t in [0, ctx)
+ *     out[s][h] = sum_t softmax(z)_t * V[slot(s,t)][g]
+ * with the max-shifted softmax ("Reading Inference Engine Codebases",
+ * Example 6) and scale usually 1/sqrt(head_dim) ("Reading Inference Engine
+ * Codebases", Example 2).  Values are F16; accumulation is fp32; the output
+ * is rounded once to F16 (round to nearest even).  ctx == 0 gives zeros.
+ *
+ * Memory.  Every pointer argument named *_dev is a device pointer owned by
+ * the caller (for example a torch tensor's data_ptr()).  The library never
+ * allocates or frees device memory.  A pa_pool handle lives in host memory
+ * and holds only the geometry and the two pool base pointers; the caller
+ * keeps the pool buffers alive until all stream work using them completes.
+ *
+ * Streams.  Calls that take a hipStream_t only enqueue work on that stream
+ * and return before the GPU finishes.  pa_decode calls may run concurrently
+ * on different streams when they use distinct workspaces and outputs.
+ *
+ * Errors.  Every entry point returns a pa_status and never throws.  Host-side
+ * checks run synchronously before anything is enqueued.  Values that live on
+ * the device (table entries, context lengths, slots) are not validated, since
+ * that would need a synchronisation: table entries must lie in
+ * [0, num_blocks) and context lengths in [0, max_context_len].  The kernels
+ * clamp them so that a bad value cannot make them read or write outside the
+ * pool or the tables; the numbers produced from such a value are unspecified.
+ *
+ * Geometry supported by this build: head_dim 128, block_size 16, F16, and
+ * num_q_heads = 4 * num_kv_heads.  Other values return PA_ERR_UNSUPPORTED.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent geometry */
+    PA_ERR_UNSUPPORTED = -2, /* geometry outside what this build supports */
+    PA_ERR_WORKSPACE = -3,   /* workspace smaller than pa_decode_workspace_bytes() */
+    PA_ERR_HIP = -4          /* a HIP runtime call or a kernel launch failed */
+} pa_status;
+
+typedef enum {
+    PA_F16 = 1 /* IEEE binary16 keys, values, queries and outputs */
+} pa_dtype;
+
+/* Geometry of one KV pool.  The pool holds num_layers independent layers of
+ * num_blocks physical blocks each; one block holds block_size tokens of every
+ * KV head.  Page size per block per layer is block_size x num_kv_heads x
+ * (2 x head_dim) x 2 bytes ("vLLM Architecture and Installation", Example 6):
+ * 65,536 B for block_size 16, 8 KV heads and head_dim 128. */
+typedef struct {
+    int32_t num_layers;
+    int32_t num_blocks;   /* per layer */
+    int32_t block_size;   /* tokens per block; must be 16 */
+    int32_t num_kv_heads;
+    int32_t head_dim;     /* must be 128 */
+    int32_t dtype;        /* a pa_dtype; must be PA_F16 */
+} pa_pool_desc;
+
+/* Opaque host-side handle. */
+typedef struct pa_pool pa_pool;
+
+/* Bytes of ONE of the two pool buffers (K or V):
+ * num_layers * num_blocks * block_size * num_kv_heads * head_dim * 2.
+ * Both buffers have this size; 256-byte alignment is required.  Device layout
+ * of each buffer (row-major, F16):
+ *     [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
+ * so the block_size x head_dim tile of one (block, KV head) is contiguous
+ * (4 KiB for the supported geometry).  Returns 0 for a null or invalid desc. */
+size_t pa_pool_bytes(const pa_pool_desc *desc);
+
+/* Wraps two caller-allocated device buffers of pa_pool_bytes(desc) bytes each
+ * into a handle.  Writes *out only on PA_OK.  Touches no device memory. */
+pa_status pa_pool_create(const pa_pool_desc *desc, void *k_pool_dev, void *v_pool_dev,
+                         pa_pool **out);
+
+/* Frees the handle (host memory only); never frees the device buffers.
+ * A null pool is accepted and ignored. */
+pa_status pa_pool_destroy(pa_pool *pool);
+
+/* Scatters n_tokens new keys and values into the pool of one layer:
+ * token i goes to slot slot_mapping_dev[i], i.e. block slot / block_size,
+ * offset slot % block_size ("vLLM Architecture and Installation", Example 3).
+ *   k_new_dev, v_new_dev: F16 [n_tokens][num_kv_heads][head_dim]
+ *   slot_mapping_dev:     int32 [n_tokens]; a negative slot skips that token,
+ *                         a slot >= num_blocks * block_size is skipped too.
+ * n_tokens == 0 is a no-op.  Two tokens with the same slot race. */
+pa_status pa_write_kv(pa_pool *pool, int32_t layer, const void *k_new_dev, const void *v_new_dev,
+                      const int32_t *slot_mapping_dev, int32_t n_tokens, hipStream_t stream);
+
+/* Length in tokens of one context split of pa_decode for this launch shape
+ * (a multiple of block_size; a sequence of ctx tokens is handled by
+ * ceil(ctx / split) work-groups per KV head).  Returns 0 on invalid input.
+ * Splits never exceed 4096 tokens.  The environment variable
+ * PA_SPLIT_TOKENS, when set to a multiple of 64 in [64, 4096], overrides the
+ * choice (tuning only). */
+int32_t pa_decode_split_tokens(const pa_pool *pool, int32_t batch, int32_t num_q_heads,
+                               int32_t max_context_len);
+
+/* Bytes of device workspace pa_decode needs for this launch shape (0 when a
+ * single split covers max_context_len).  Returns 0 on invalid input too;
+ * pa_decode then reports the error. */
+size_t pa_decode_workspace_bytes(const pa_pool *pool, int32_t batch, int32_t num_q_heads,
+                                 int32_t max_context_len);
+
+/* One decode step of attention for one layer (see the formula at the top).
+ *   q_dev:            F16 [batch][num_q_heads][head_dim]
+ *   out_dev:          F16 [batch][num_q_heads][head_dim]
+ *   block_tables_dev: int32 [batch][max_blocks_per_seq]; only the first
+ *                     ceil(ctx/block_size) entries of a row are read
+ *   context_lens_dev: int32 [batch]
+ *   max_context_len:  host-side upper bound of context_lens (sizes the grid);
+ *                     must be <= max_blocks_per_seq * block_size; tokens past
+ *                     it are ignored
+ *   scale:            logit scale, normally 1/sqrt(head_dim)
+ *   workspace_dev:    >= pa_decode_workspace_bytes(...) bytes, 256-byte
+ *                     aligned; may be null when that size is 0
+ * batch == 0 is a no-op.  Equivalent to pa_decode_partial followed by
+ * pa_decode_merge with the same arguments. */
+pa_status pa_decode(pa_pool *pool, int32_t layer, const void *q_dev, void *out_dev,
+                    const int32_t *block_tables_dev, int32_t max_blocks_per_seq,
+                    const int32_t *context_lens_dev, int32_t batch, int32_t num_q_heads,
+                    int32_t max_context_len, float scale, void *workspace_dev,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* First phase of pa_decode: one work-group per (sequence, KV head, context
+ * split) attends to its split and writes the unnormalised partial output,
+ * running max and running sum (fp32) into the workspace.  When a single split
+ * covers max_context_len it writes the final F16 output instead and
+ * pa_decode_merge has nothing to do. */
+pa_status pa_decode_partial(pa_pool *pool, int32_t layer, const void *q_dev, void *out_dev,
+                            const int32_t *block_tables_dev, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens_dev, int32_t batch, int32_t num_q_heads,
+                            int32_t max_context_len, float scale, void *workspace_dev,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Second phase of pa_decode: merges the per-split partials of every
+ * (sequence, query head) by their log-sum-exp weights, divides by the merged
+ * sum and writes the F16 output.  Takes the same launch shape as the
+ * pa_decode_partial call whose workspace it reads. */
+pa_status pa_decode_merge(pa_pool *pool, void *out_dev, const int32_t *context_lens_dev,
+                          int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                          const void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+
+/* Static English text for a status code. */
+const char *pa_status_string(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

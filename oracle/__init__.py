@@ -102,3 +102,24 @@ def decode(q, k_slots, v_slots, block_tables, ctx_lens, scale, block_size, threa
     if rc != 0:
         raise ValueError(f"oracle rejected its inputs (code {rc})")
     return out
+
+
+def relabelled_cache(ids, k_blocks, v_blocks, tables, ctx_lens, block_size):
+    """Compact slot-indexed caches for the oracle plus tables rewritten to match.
+
+    Block ids[i] becomes block i, so the caches are the block contents
+    themselves ([n*B, Hkv, d], no copy).  Relabelling physical blocks does not
+    change the result (a pinned invariance).  Table entries past a sequence's
+    context are left as 0.
+    """
+    ids = np.asarray(ids)
+    tables = np.asarray(tables)
+    held = -(-np.asarray(ctx_lens, dtype=np.int64) // block_size)
+    out_tables = np.zeros_like(tables, dtype=np.int32)
+    for s in range(tables.shape[0]):
+        row = tables[s, :held[s]]
+        pos = np.searchsorted(ids, row)
+        assert np.all(ids[pos] == row)
+        out_tables[s, :held[s]] = pos
+    n, b, hkv, d = k_blocks.shape
+    return k_blocks.reshape(n * b, hkv, d), v_blocks.reshape(n * b, hkv, d), out_tables

@@ -1,0 +1,270 @@
+"""Python binding for libpa.so, the paged decode-attention library (C ABI in include/pa.h).
+
+The functions below carry the C entry points' names and only marshal
+arguments: torch tensors supply device pointers, and the current torch stream
+supplies the HIP stream.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback.  If libpa.so has not been built, importing
+works but every call raises RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_UNSUPPORTED = -2
+PA_ERR_WORKSPACE = -3
+PA_ERR_HIP = -4
+PA_F16 = 1
+
+EXPORTS = ("pa_pool_bytes", "pa_pool_create", "pa_pool_destroy", "pa_write_kv",
+           "pa_decode_split_tokens", "pa_decode_workspace_bytes", "pa_decode",
+           "pa_decode_partial", "pa_decode_merge", "pa_status_string")
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {pa_status_string(status)} ({status})")
+        self.status = status
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libpa.so (once) and declares every exported signature."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.pa_pool_bytes.restype = ctypes.c_size_t
+    lib.pa_pool_bytes.argtypes = [ctypes.POINTER(PoolDesc)]
+    lib.pa_pool_create.restype = _I
+    lib.pa_pool_create.argtypes = [ctypes.POINTER(PoolDesc), _P, _P, ctypes.POINTER(_P)]
+    lib.pa_pool_destroy.restype = _I
+    lib.pa_pool_destroy.argtypes = [_P]
+    lib.pa_write_kv.restype = _I
+    lib.pa_write_kv.argtypes = [_P, _I, _P, _P, _P, _I, _P]
+    lib.pa_decode_split_tokens.restype = _I
+    lib.pa_decode_split_tokens.argtypes = [_P, _I, _I, _I]
+    lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_decode_workspace_bytes.argtypes = [_P, _I, _I, _I]
+    for name in ("pa_decode", "pa_decode_partial"):
+        fn = getattr(lib, name)
+        fn.restype = _I
+        fn.argtypes = [_P, _I, _P, _P, _P, _I, _P, _I, _I, _I, ctypes.c_float, _P,
+                       ctypes.c_size_t, _P]
+    lib.pa_decode_merge.restype = _I
+    lib.pa_decode_merge.argtypes = [_P, _P, _P, _I, _I, _I, _P, ctypes.c_size_t, _P]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [_I]
+    _lib = lib
+    return lib
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _check(status: int, what: str) -> None:
+    if status != PA_OK:
+        raise PaError(status, what)
+
+
+def _expect(t: torch.Tensor, dtype, shape, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: want contiguous {dtype} {tuple(shape)}, got {t.dtype} "
+                         f"{tuple(t.shape)} contiguous={t.is_contiguous()}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def pa_status_string(status: int) -> str:
+    return load_library().pa_status_string(int(status)).decode()
+
+
+def pa_pool_bytes(desc: PoolDesc) -> int:
+    return int(load_library().pa_pool_bytes(ctypes.byref(desc)))
+
+
+def pa_pool_create(desc: PoolDesc, k_pool, v_pool) -> int:
+    handle = _P()
+    _check(load_library().pa_pool_create(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
+                                         ctypes.byref(handle)), "pa_pool_create")
+    return handle.value
+
+
+def pa_pool_destroy(handle: int) -> None:
+    _check(load_library().pa_pool_destroy(handle), "pa_pool_destroy")
+
+
+def pa_write_kv(handle, layer, k_new, v_new, slot_mapping, n_tokens, stream=None) -> None:
+    _check(load_library().pa_write_kv(handle, layer, _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                                      n_tokens, _stream(stream)), "pa_write_kv")
+
+
+def pa_decode_split_tokens(handle, batch, num_q_heads, max_context_len) -> int:
+    return int(load_library().pa_decode_split_tokens(handle, batch, num_q_heads, max_context_len))
+
+
+def pa_decode_workspace_bytes(handle, batch, num_q_heads, max_context_len) -> int:
+    return int(load_library().pa_decode_workspace_bytes(handle, batch, num_q_heads,
+                                                        max_context_len))
+
+
+def _decode_call(name, handle, layer, q, out, block_tables, max_blocks_per_seq, context_lens,
+                 batch, num_q_heads, max_context_len, scale, workspace, workspace_bytes, stream):
+    fn = getattr(load_library(), name)
+    _check(fn(handle, layer, _ptr(q), _ptr(out), _ptr(block_tables), max_blocks_per_seq,
+              _ptr(context_lens), batch, num_q_heads, max_context_len, float(scale),
+              _ptr(workspace), int(workspace_bytes), _stream(stream)), name)
+
+
+def pa_decode(handle, layer, q, out, block_tables, max_blocks_per_seq, context_lens, batch,
+              num_q_heads, max_context_len, scale, workspace, workspace_bytes, stream=None):
+    _decode_call("pa_decode", handle, layer, q, out, block_tables, max_blocks_per_seq,
+                 context_lens, batch, num_q_heads, max_context_len, scale, workspace,
+                 workspace_bytes, stream)
+
+
+def pa_decode_partial(handle, layer, q, out, block_tables, max_blocks_per_seq, context_lens,
+                      batch, num_q_heads, max_context_len, scale, workspace, workspace_bytes,
+                      stream=None):
+    _decode_call("pa_decode_partial", handle, layer, q, out, block_tables, max_blocks_per_seq,
+                 context_lens, batch, num_q_heads, max_context_len, scale, workspace,
+                 workspace_bytes, stream)
+
+
+def pa_decode_merge(handle, out, context_lens, batch, num_q_heads, max_context_len, workspace,
+                    workspace_bytes, stream=None):
+    _check(load_library().pa_decode_merge(handle, _ptr(out), _ptr(context_lens), batch,
+                                          num_q_heads, max_context_len, _ptr(workspace),
+                                          int(workspace_bytes), _stream(stream)),
+           "pa_decode_merge")
+
+
+# ---------------------------------------------------------------------------
+# a torch-owning convenience wrapper
+# ---------------------------------------------------------------------------
+class Pool:
+    """K and V pools in torch device memory plus the library handle.
+
+    Memory is allocated with torch (uint8 buffers); `fill` initialises it
+    (NaN by default so that any slot that is read without being written
+    shows up in the output).
+    """
+
+    def __init__(self, num_layers, num_blocks, num_kv_heads=8, head_dim=128, block_size=16,
+                 device="cuda", fill=float("nan")):
+        self.desc = PoolDesc(num_layers, num_blocks, block_size, num_kv_heads, head_dim, PA_F16)
+        nbytes = pa_pool_bytes(self.desc)
+        if nbytes == 0:
+            raise ValueError("invalid pool geometry")
+        shape = (num_layers, num_blocks, num_kv_heads, block_size, head_dim)
+        self.k = torch.empty(nbytes // 2, dtype=torch.float16, device=device).view(shape)
+        self.v = torch.empty(nbytes // 2, dtype=torch.float16, device=device).view(shape)
+        if fill is not None:
+            self.k.fill_(fill)
+            self.v.fill_(fill)
+        self.handle = pa_pool_create(self.desc, self.k, self.v)
+        self.num_layers, self.num_blocks = num_layers, num_blocks
+        self.num_kv_heads, self.head_dim, self.block_size = num_kv_heads, head_dim, block_size
+
+    def close(self):
+        if getattr(self, "handle", None):
+            pa_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def write(self, layer, k_new, v_new, slot_mapping, stream=None):
+        n = int(slot_mapping.shape[0])
+        shape = (n, self.num_kv_heads, self.head_dim)
+        _expect(k_new, torch.float16, shape, "k_new")
+        _expect(v_new, torch.float16, shape, "v_new")
+        _expect(slot_mapping, torch.int32, (n,), "slot_mapping")
+        pa_write_kv(self.handle, layer, k_new, v_new, slot_mapping, n, stream)
+
+    def write_blocks(self, layer, block_ids, k_blocks, v_blocks, stream=None):
+        """Writes whole physical blocks: k_blocks[i] ([block_size, Hkv, d]) is
+        stored in block block_ids[i], i.e. slots block_ids[i]*B + 0..B-1."""
+        bs = self.block_size
+        ids = torch.as_tensor(block_ids, dtype=torch.int64, device=k_blocks.device)
+        slots = (ids[:, None] * bs + torch.arange(bs, device=ids.device)[None, :]).reshape(-1)
+        n = slots.shape[0]
+        self.write(layer, k_blocks.reshape(n, self.num_kv_heads, self.head_dim).contiguous(),
+                   v_blocks.reshape(n, self.num_kv_heads, self.head_dim).contiguous(),
+                   slots.to(torch.int32).contiguous(), stream)
+
+    def split_tokens(self, batch, num_q_heads, max_context_len):
+        return pa_decode_split_tokens(self.handle, batch, num_q_heads, max_context_len)
+
+    def workspace_bytes(self, batch, num_q_heads, max_context_len):
+        return pa_decode_workspace_bytes(self.handle, batch, num_q_heads, max_context_len)
+
+    def workspace(self, batch, num_q_heads, max_context_len, device="cuda"):
+        n = self.workspace_bytes(batch, num_q_heads, max_context_len)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
+
+    def _check_decode(self, q, out, block_tables, context_lens, max_context_len):
+        batch, hq, d = q.shape
+        _expect(q, torch.float16, (batch, hq, self.head_dim), "q")
+        _expect(out, torch.float16, (batch, hq, self.head_dim), "out")
+        _expect(block_tables, torch.int32, (batch, block_tables.shape[1]), "block_tables")
+        _expect(context_lens, torch.int32, (batch,), "context_lens")
+        if max_context_len > block_tables.shape[1] * self.block_size:
+            raise ValueError("max_context_len exceeds the table width")
+        return batch, hq, int(block_tables.shape[1])
+
+    def decode(self, layer, q, out, block_tables, context_lens, max_context_len, scale,
+               workspace=None, stream=None, phases=False):
+        batch, hq, width = self._check_decode(q, out, block_tables, context_lens, max_context_len)
+        if workspace is None:
+            workspace = self.workspace(batch, hq, max_context_len, q.device)
+        ws, ws_bytes = workspace
+        if phases:
+            pa_decode_partial(self.handle, layer, q, out, block_tables, width, context_lens, batch,
+                              hq, max_context_len, scale, ws, ws_bytes, stream)
+            pa_decode_merge(self.handle, out, context_lens, batch, hq, max_context_len, ws,
+                            ws_bytes, stream)
+        else:
+            pa_decode(self.handle, layer, q, out, block_tables, width, context_lens, batch, hq,
+                      max_context_len, scale, ws, ws_bytes, stream)
+        return out

@@ -1,0 +1,262 @@
+// pa_api.cpp -- the C ABI declared in include/pa.h: argument checks, the
+// split plan, workspace sizing and kernel launches.  No entry point throws,
+// allocates device memory, or synchronises.
+
+#include "pa.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <new>
+
+#include "pa_internal.h"
+
+struct pa_pool {
+    pa_pool_desc desc;
+    void *k;
+    void *v;
+};
+
+namespace {
+
+using pa::kBlockSize;
+using pa::kGroup;
+using pa::kHeadDim;
+using pa::kMaxSplitTokens;
+using pa::kSplitQuantum;
+
+// Work-groups the split plan aims for: MI355X has 256 compute units and the
+// split kernel keeps two work-groups resident per unit; four rounds of those
+// give the dispatcher room to balance ragged batches.
+constexpr int64_t kTargetWorkGroups = 256 * 2 * 4;
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool desc_ok(const pa_pool_desc *d) {
+    return d && d->num_layers > 0 && d->num_blocks > 0 && d->block_size > 0 && d->num_kv_heads > 0 &&
+           d->head_dim > 0;
+}
+
+bool desc_supported(const pa_pool_desc *d) {
+    return d->block_size == kBlockSize && d->head_dim == kHeadDim && d->dtype == PA_F16;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Split length in tokens for a launch shape (see pa_decode_split_tokens).
+int32_t plan_split(int32_t batch, int32_t num_kv_heads, int32_t max_ctx) {
+    if (const char *env = std::getenv("PA_SPLIT_TOKENS")) {
+        char *end = nullptr;
+        const long v = std::strtol(env, &end, 10);
+        if (end != env && v > 0 && v % kSplitQuantum == 0 && v <= kMaxSplitTokens) return static_cast<int32_t>(v);
+    }
+    if (max_ctx <= 0) return kSplitQuantum;
+    const int64_t pairs = static_cast<int64_t>(batch) * num_kv_heads;
+    const int64_t splits = std::max<int64_t>(1, (kTargetWorkGroups + pairs - 1) / pairs);
+    const int64_t per = (max_ctx + splits - 1) / splits;
+    const int64_t tokens = std::max<int64_t>(kSplitQuantum, round_up(per, kSplitQuantum));
+    return static_cast<int32_t>(std::min<int64_t>(tokens, kMaxSplitTokens));
+}
+
+struct Plan {
+    int32_t split_tokens;
+    int32_t max_splits;
+    size_t workspace;  // bytes; 0 for single-split launches
+    size_t o_bytes;    // offset of the (m, l) array inside the workspace
+};
+
+Plan make_plan(const pa_pool *pool, int32_t batch, int32_t num_q_heads, int32_t max_ctx) {
+    Plan p{};
+    p.split_tokens = plan_split(batch, pool->desc.num_kv_heads, max_ctx);
+    p.max_splits = max_ctx <= 0 ? 1 : static_cast<int32_t>((max_ctx + p.split_tokens - 1) / p.split_tokens);
+    if (p.max_splits > 1) {
+        const size_t rows = static_cast<size_t>(batch) * num_q_heads * p.max_splits;
+        p.o_bytes = round_up(static_cast<int64_t>(rows * kHeadDim * sizeof(float)), 256);
+        p.workspace = p.o_bytes + rows * 2 * sizeof(float);
+    }
+    return p;
+}
+
+// Checks shared by every decode entry point.
+pa_status check_decode_shape(const pa_pool *pool, int32_t batch, int32_t num_q_heads, int32_t max_blocks,
+                             int32_t max_ctx) {
+    if (!pool) return PA_ERR_INVALID_ARG;
+    if (batch < 0 || num_q_heads <= 0 || max_blocks < 0 || max_ctx < 0) return PA_ERR_INVALID_ARG;
+    if (num_q_heads % pool->desc.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(max_ctx) > static_cast<int64_t>(max_blocks) * pool->desc.block_size)
+        return PA_ERR_INVALID_ARG;
+    if (num_q_heads != kGroup * pool->desc.num_kv_heads) return PA_ERR_UNSUPPORTED;
+    if (batch > 65535 || pool->desc.num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+pa_status fill_decode_args(pa_pool *pool, int32_t layer, const void *q, void *out, const int32_t *tables,
+                           int32_t max_blocks, const int32_t *ctx_lens, int32_t batch, int32_t num_q_heads,
+                           int32_t max_ctx, float scale, void *ws, size_t ws_bytes, pa::DecodeArgs *a,
+                           Plan *plan_out) {
+    pa_status st = check_decode_shape(pool, batch, num_q_heads, max_blocks, max_ctx);
+    if (st != PA_OK) return st;
+    if (layer < 0 || layer >= pool->desc.num_layers) return PA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+    if (batch == 0) {
+        *plan_out = Plan{};
+        return PA_OK;
+    }
+    if (!q || !out || !ctx_lens || (max_ctx > 0 && !tables)) return PA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(tables, 4) || !aligned(ctx_lens, 4))
+        return PA_ERR_INVALID_ARG;
+    const Plan plan = make_plan(pool, batch, num_q_heads, max_ctx);
+    if (plan.workspace > 0) {
+        if (!ws || ws_bytes < plan.workspace) return PA_ERR_WORKSPACE;
+        if (!aligned(ws, 256)) return PA_ERR_INVALID_ARG;
+    }
+    const size_t layer_off = static_cast<size_t>(layer) *
+                             pa::layer_elems(pool->desc.num_blocks, pool->desc.num_kv_heads);
+    a->k_layer = static_cast<const uint16_t *>(pool->k) + layer_off;
+    a->v_layer = static_cast<const uint16_t *>(pool->v) + layer_off;
+    a->q = static_cast<const uint16_t *>(q);
+    a->tables = tables;
+    a->ctx_lens = ctx_lens;
+    a->out = static_cast<uint16_t *>(out);
+    a->o_part = plan.workspace ? static_cast<float *>(ws) : nullptr;
+    a->ml_part = plan.workspace ? reinterpret_cast<float *>(static_cast<char *>(ws) + plan.o_bytes) : nullptr;
+    a->batch = batch;
+    a->num_q_heads = num_q_heads;
+    a->num_kv_heads = pool->desc.num_kv_heads;
+    a->num_blocks = pool->desc.num_blocks;
+    a->max_blocks = max_blocks;
+    a->max_ctx = max_ctx;
+    a->split_tokens = plan.split_tokens;
+    a->max_splits = plan.max_splits;
+    a->scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    *plan_out = plan;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_pool_bytes(const pa_pool_desc *desc) {
+    if (!desc_ok(desc)) return 0;
+    const size_t elem = desc->dtype == PA_F16 ? 2 : 0;
+    return static_cast<size_t>(desc->num_layers) * desc->num_blocks * desc->block_size * desc->num_kv_heads *
+           desc->head_dim * elem;
+}
+
+pa_status pa_pool_create(const pa_pool_desc *desc, void *k_pool_dev, void *v_pool_dev, pa_pool **out) {
+    if (!out || !desc_ok(desc) || !k_pool_dev || !v_pool_dev) return PA_ERR_INVALID_ARG;
+    if (!desc_supported(desc)) return PA_ERR_UNSUPPORTED;
+    if (!aligned(k_pool_dev, 256) || !aligned(v_pool_dev, 256)) return PA_ERR_INVALID_ARG;
+    pa_pool *p = new (std::nothrow) pa_pool;
+    if (!p) return PA_ERR_INVALID_ARG;
+    p->desc = *desc;
+    p->k = k_pool_dev;
+    p->v = v_pool_dev;
+    *out = p;
+    return PA_OK;
+}
+
+pa_status pa_pool_destroy(pa_pool *pool) {
+    delete pool;
+    return PA_OK;
+}
+
+pa_status pa_write_kv(pa_pool *pool, int32_t layer, const void *k_new_dev, const void *v_new_dev,
+                      const int32_t *slot_mapping_dev, int32_t n_tokens, hipStream_t stream) {
+    if (!pool || n_tokens < 0 || layer < 0 || layer >= pool->desc.num_layers) return PA_ERR_INVALID_ARG;
+    if (n_tokens == 0) return PA_OK;
+    if (!k_new_dev || !v_new_dev || !slot_mapping_dev) return PA_ERR_INVALID_ARG;
+    if (!aligned(k_new_dev, 16) || !aligned(v_new_dev, 16) || !aligned(slot_mapping_dev, 4))
+        return PA_ERR_INVALID_ARG;
+    const size_t layer_off = static_cast<size_t>(layer) *
+                             pa::layer_elems(pool->desc.num_blocks, pool->desc.num_kv_heads);
+    pa::WriteKvArgs a{};
+    a.k_layer = static_cast<uint16_t *>(pool->k) + layer_off;
+    a.v_layer = static_cast<uint16_t *>(pool->v) + layer_off;
+    a.k_new = static_cast<const uint16_t *>(k_new_dev);
+    a.v_new = static_cast<const uint16_t *>(v_new_dev);
+    a.slot_mapping = slot_mapping_dev;
+    a.n_tokens = n_tokens;
+    a.num_kv_heads = pool->desc.num_kv_heads;
+    a.num_slots = static_cast<int64_t>(pool->desc.num_blocks) * pool->desc.block_size;
+    return pa::launch_write_kv(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int32_t pa_decode_split_tokens(const pa_pool *pool, int32_t batch, int32_t num_q_heads, int32_t max_context_len) {
+    if (!pool || batch < 0 || num_q_heads <= 0 || max_context_len < 0) return 0;
+    return plan_split(batch, pool->desc.num_kv_heads, max_context_len);
+}
+
+size_t pa_decode_workspace_bytes(const pa_pool *pool, int32_t batch, int32_t num_q_heads,
+                                 int32_t max_context_len) {
+    if (!pool || batch <= 0 || num_q_heads <= 0 || max_context_len < 0) return 0;
+    return make_plan(pool, batch, num_q_heads, max_context_len).workspace;
+}
+
+pa_status pa_decode_partial(pa_pool *pool, int32_t layer, const void *q_dev, void *out_dev,
+                            const int32_t *block_tables_dev, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens_dev, int32_t batch, int32_t num_q_heads,
+                            int32_t max_context_len, float scale, void *workspace_dev, size_t workspace_bytes,
+                            hipStream_t stream) {
+    pa::DecodeArgs a{};
+    Plan plan{};
+    pa_status st = fill_decode_args(pool, layer, q_dev, out_dev, block_tables_dev, max_blocks_per_seq,
+                                    context_lens_dev, batch, num_q_heads, max_context_len, scale, workspace_dev,
+                                    workspace_bytes, &a, &plan);
+    if (st != PA_OK || batch == 0) return st;
+    return pa::launch_decode_partial(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_decode_merge(pa_pool *pool, void *out_dev, const int32_t *context_lens_dev, int32_t batch,
+                          int32_t num_q_heads, int32_t max_context_len, const void *workspace_dev,
+                          size_t workspace_bytes, hipStream_t stream) {
+    pa_status st = check_decode_shape(pool, batch, num_q_heads, (max_context_len + kBlockSize - 1) / kBlockSize,
+                                      max_context_len);
+    if (st != PA_OK || batch == 0) return st;
+    if (!out_dev || !context_lens_dev || !aligned(out_dev, 16) || !aligned(context_lens_dev, 4))
+        return PA_ERR_INVALID_ARG;
+    const Plan plan = make_plan(pool, batch, num_q_heads, max_context_len);
+    if (plan.workspace == 0) return PA_OK;  // the partial phase wrote the output
+    if (!workspace_dev || workspace_bytes < plan.workspace) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace_dev, 256)) return PA_ERR_INVALID_ARG;
+    pa::DecodeArgs a{};
+    a.ctx_lens = context_lens_dev;
+    a.out = static_cast<uint16_t *>(out_dev);
+    a.o_part = static_cast<float *>(const_cast<void *>(workspace_dev));
+    a.ml_part = reinterpret_cast<float *>(static_cast<char *>(const_cast<void *>(workspace_dev)) + plan.o_bytes);
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = pool->desc.num_kv_heads;
+    a.max_blocks = (max_context_len + kBlockSize - 1) / kBlockSize;
+    a.max_ctx = max_context_len;
+    a.split_tokens = plan.split_tokens;
+    a.max_splits = plan.max_splits;
+    return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_decode(pa_pool *pool, int32_t layer, const void *q_dev, void *out_dev,
+                    const int32_t *block_tables_dev, int32_t max_blocks_per_seq, const int32_t *context_lens_dev,
+                    int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale,
+                    void *workspace_dev, size_t workspace_bytes, hipStream_t stream) {
+    pa_status st = pa_decode_partial(pool, layer, q_dev, out_dev, block_tables_dev, max_blocks_per_seq,
+                                     context_lens_dev, batch, num_q_heads, max_context_len, scale, workspace_dev,
+                                     workspace_bytes, stream);
+    if (st != PA_OK || batch == 0) return st;
+    return pa_decode_merge(pool, out_dev, context_lens_dev, batch, num_q_heads, max_context_len, workspace_dev,
+                           workspace_bytes, stream);
+}
+
+const char *pa_status_string(pa_status status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_INVALID_ARG: return "invalid argument";
+        case PA_ERR_UNSUPPORTED: return "unsupported geometry";
+        case PA_ERR_WORKSPACE: return "workspace too small";
+        case PA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

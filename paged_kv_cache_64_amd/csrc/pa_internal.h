@@ -1,0 +1,63 @@
+// pa_internal.h -- shared between the C-ABI layer (pa_api.cpp) and the HIP
+// kernels (pa_kernels.hip).  Not installed; callers use include/pa.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace pa {
+
+// Geometry this build's kernels are written for.
+constexpr int kHeadDim = 128;     // elements per head
+constexpr int kBlockSize = 16;    // tokens per block
+constexpr int kGroup = 4;         // query heads per KV head
+constexpr int kWaves = 4;         // waves per work-group of the split kernel
+constexpr int kSplitQuantum = kWaves * kBlockSize;  // split lengths are multiples of this
+constexpr int kMaxSplitTokens = kWaves * 64 * kBlockSize;  // a wave owns at most 64 blocks
+
+// Device layout of one pool buffer (K or V), F16, row-major:
+//   [num_layers][num_blocks][num_kv_heads][kBlockSize][kHeadDim]
+// One (block, KV head) tile of kBlockSize x kHeadDim is contiguous.
+__host__ __device__ inline size_t tile_elems() { return static_cast<size_t>(kBlockSize) * kHeadDim; }
+__host__ __device__ inline size_t layer_elems(int32_t num_blocks, int32_t num_kv_heads) {
+    return static_cast<size_t>(num_blocks) * num_kv_heads * tile_elems();
+}
+
+struct WriteKvArgs {
+    uint16_t *k_layer;            // this layer's K base
+    uint16_t *v_layer;            // this layer's V base
+    const uint16_t *k_new;        // [n_tokens][num_kv_heads][kHeadDim]
+    const uint16_t *v_new;
+    const int32_t *slot_mapping;  // [n_tokens]
+    int32_t n_tokens;
+    int32_t num_kv_heads;
+    int64_t num_slots;            // num_blocks * kBlockSize
+};
+
+struct DecodeArgs {
+    const uint16_t *k_layer;      // this layer's K base
+    const uint16_t *v_layer;      // this layer's V base
+    const uint16_t *q;            // [batch][num_q_heads][kHeadDim]
+    const int32_t *tables;        // [batch][max_blocks]
+    const int32_t *ctx_lens;      // [batch]
+    uint16_t *out;                // [batch][num_q_heads][kHeadDim] (single-split launches)
+    float *o_part;                // [batch][num_q_heads][max_splits][kHeadDim]
+    float *ml_part;               // [batch][num_q_heads][max_splits][2]: running max (log2 units), sum
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t num_blocks;
+    int32_t max_blocks;           // table row length
+    int32_t max_ctx;              // host bound on context lengths
+    int32_t split_tokens;         // multiple of kSplitQuantum
+    int32_t max_splits;           // ceil(max_ctx / split_tokens)
+    float scale_log2e;            // scale * log2(e)
+};
+
+hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream);
+hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,421 @@
+// pa_kernels.hip -- HIP kernels for one decode step of paged attention on
+// gfx950 (CDNA4, wave64).
+//
+//   write_kv_kernel        scatter new K/V rows into pool slots
+//                          ("vLLM Architecture and Installation", Example 3:
+//                          slot = table[p / B] * B + p % B, computed by the
+//                          caller and passed in as slot_mapping)
+//   decode_partial_kernel  one work-group per (sequence, KV head, context
+//                          split): gathers that split's K/V tiles through the
+//                          block table and runs an online, max-shifted softmax
+//                          ("Reading Inference Engine Codebases", Example 6)
+//                          for the four query heads that share the KV head
+//   decode_merge_kernel    merges the per-split partials by their
+//                          log-sum-exp weights and writes F16
+//
+// The step is bound by HBM bandwidth: every sequence reads its own K/V once
+// per step and nothing is shared between sequences ("Batching and
+// Scheduling", Example 1), at about 4 flop per byte.  The kernels are plain
+// VALU code; what matters is keeping 16-byte loads in flight and keeping the
+// per-byte instruction count low.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+struct h2x4 {
+    h2 v[4];
+};
+__device__ __forceinline__ h2x4 pairs(h8 x) { return __builtin_bit_cast(h2x4, x); }
+
+// Online-softmax bookkeeping: the running max m is only raised when a score
+// exceeds it by more than kTau (log2 units), so most blocks skip the
+// cross-lane max and the accumulator rescale.  Every weight is then at most
+// 2^kTau, far from fp32 overflow, and the final division by the sum removes
+// the common factor exactly.
+constexpr float kTau = 8.0f;
+
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+    // quad_perm [1,0,3,2]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+    // quad_perm [2,3,0,1]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_ror4(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_ror8(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+    const int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
+}
+
+// Orders this wave's LDS traffic: stores issued before are visible to loads
+// issued after, for every lane of the wave.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer resource over one 4 KiB tile (gfx9-family dword3).  A resource with
+// zero records turns every load through it into a zero fill that moves no
+// data, which lets the pipelined loop below issue loads unconditionally.
+constexpr int kRsrcDword3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *tile, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), static_cast<short>(0), bytes, kRsrcDword3);
+}
+__device__ __forceinline__ h8 load_tile16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+
+__device__ __forceinline__ int clamp_ctx(int ctx, int max_ctx, int max_blocks) {
+    ctx = ctx < 0 ? 0 : ctx;
+    ctx = ctx > max_ctx ? max_ctx : ctx;
+    const int cap = max_blocks * kBlockSize;
+    return ctx > cap ? cap : ctx;
+}
+
+// ---------------------------------------------------------------------------
+// write_kv: one thread per 16-byte chunk of a (token, KV head) row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
+    constexpr int kChunks = kHeadDim / 8;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(a.n_tokens) * a.num_kv_heads * kChunks;
+    if (idx >= total) return;
+    const int chunk = static_cast<int>(idx % kChunks);
+    const int64_t row = idx / kChunks;  // token * num_kv_heads + head
+    const int head = static_cast<int>(row % a.num_kv_heads);
+    const int64_t token = row / a.num_kv_heads;
+    const int64_t slot = a.slot_mapping[token];
+    if (slot < 0 || slot >= a.num_slots) return;
+    const int64_t blk = slot / kBlockSize;
+    const int64_t off = slot % kBlockSize;
+    const int64_t dst = ((blk * a.num_kv_heads + head) * kBlockSize + off) * kHeadDim + chunk * 8;
+    const int64_t src = row * kHeadDim + chunk * 8;
+    *reinterpret_cast<uint4 *>(a.k_layer + dst) = *reinterpret_cast<const uint4 *>(a.k_new + src);
+    *reinterpret_cast<uint4 *>(a.v_layer + dst) = *reinterpret_cast<const uint4 *>(a.v_new + src);
+}
+
+// ---------------------------------------------------------------------------
+// decode_partial: grid (split, KV head, sequence), 256 threads = 4 waves.
+//
+// Each wave walks its own contiguous run of the split's blocks and keeps its
+// own running max, sum and output accumulator; the four waves are merged
+// through LDS at the end.  Per block (16 tokens x 128 dims, 4 KiB of K and
+// 4 KiB of V for one KV head):
+//
+//   K layout in registers: lane l holds token kt = l/4, dims
+//     {32i + 8(l%4) + e : i < 4, e < 8}  -- four 16-byte loads; each load
+//     instruction covers 64 contiguous bytes of each of 16 token rows.
+//   Scores: 4 heads x 32 dims per lane by v_dot2, then a 4-lane transpose-
+//     reduction leaves lane l with the score of head l%4 for token l/4.
+//   V layout in registers: load c, lane l holds token 4c + l/16, dims
+//     8(l%16) .. +7 -- each load instruction is 1 KiB contiguous.
+//   Weights go from the score lanes to the value lanes through 256 B of LDS.
+// ---------------------------------------------------------------------------
+template <int NBUF>
+__global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
+    const int split = blockIdx.x;
+    const int g = blockIdx.y;
+    const int s = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
+    const int lane = tid & 63;
+    const int kt = lane >> 2, kq = lane & 3;    // score layout
+    const int vt = lane >> 4, vj = lane & 15;   // value layout
+
+    __shared__ float p_lds[kWaves][64];
+    __shared__ float alpha_lds[kWaves][4];
+    __shared__ float m_lds[kWaves][4];
+    __shared__ float l_lds[kWaves][4];
+    __shared__ float o_lds[kWaves][4][kGroup][kHeadDim];
+
+    const int ctx = clamp_ctx(a.ctx_lens[s], a.max_ctx, a.max_blocks);
+    const int t_begin = split * a.split_tokens;
+    const int head0 = g * kGroup;
+    const bool single = a.max_splits == 1;
+
+    if (t_begin >= ctx) {
+        // Nothing to attend to.  With one split this work-group owns the
+        // output row, which is zero for an empty context.
+        if (single && split == 0) {
+            const int h = tid >> 6, d0 = (tid & 63) * 2;
+            uint16_t *o = a.out + (static_cast<size_t>(s) * a.num_q_heads + head0 + h) * kHeadDim + d0;
+            *reinterpret_cast<uint32_t *>(o) = 0u;
+        }
+        return;
+    }
+    const int t_end = min(ctx, t_begin + a.split_tokens);
+    const int b_begin = t_begin / kBlockSize;
+    const int b_end = (t_end + kBlockSize - 1) / kBlockSize;
+    const int per_wave = (b_end - b_begin + kWaves - 1) / kWaves;
+    const int wb_begin = min(b_end, b_begin + w * per_wave);
+    const int wb_end = min(b_end, wb_begin + per_wave);
+
+    // Query of the 4 heads, in the score layout: qv[h][i] = dims 32i+8kq..+7.
+    h8 qv[kGroup][4];
+    {
+        const uint16_t *qbase = a.q + (static_cast<size_t>(s) * a.num_q_heads + head0) * kHeadDim;
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                qv[h][i] = *reinterpret_cast<const h8 *>(qbase + h * kHeadDim + 32 * i + 8 * kq);
+    }
+
+    // Block-table entries of this wave's blocks go to LDS up front (a wave
+    // never owns more than 64 blocks), so the loop reads them without a
+    // memory load that would have to wait behind the K/V loads in flight.
+    const int32_t *table = a.tables + static_cast<size_t>(s) * a.max_blocks;
+    __shared__ int tbl_lds[kWaves][64];
+    if (lane < wb_end - wb_begin) tbl_lds[w][lane] = table[wb_begin + lane];
+    wave_lds_sync();
+    const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
+    const size_t tile_bytes = tile_elems() * sizeof(uint16_t);
+    const char *k_layer = reinterpret_cast<const char *>(a.k_layer);
+    const char *v_layer = reinterpret_cast<const char *>(a.v_layer);
+    // per-lane byte offsets inside a tile
+    const uint32_t k_off = static_cast<uint32_t>(kt * kHeadDim * 2 + 16 * kq);  // + 64 i
+    const uint32_t v_off = static_cast<uint32_t>(lane * 16);                    // + 1024 c
+
+    float m_run = -INFINITY;  // running max of head kq (log2 units), same in all lanes of that head
+    float l_run = 0.0f;       // this lane's share of the running sum of head kq
+    float o[kGroup][8];       // value layout: o[h][e] for dim 8vj+e over tokens of row vt
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
+
+    h8 kb[NBUF][4], vb[NBUF][4];
+
+    // Issues the 8 loads of block b into register buffer buf.  Blocks past
+    // the wave's run are issued through empty resources (no memory traffic),
+    // so every pipeline step issues the same number of loads.
+    auto issue = [&](int buf, int b) {
+        const bool live = b < wb_end;
+        uint32_t phys = static_cast<uint32_t>(
+            __builtin_amdgcn_readfirstlane(tbl_lds[w][live ? b - wb_begin : 0]));
+        phys = phys > last_block ? last_block : phys;
+        const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
+        const int bytes = live ? static_cast<int>(tile_bytes) : 0;
+        const __amdgpu_buffer_rsrc_t kr = tile_rsrc(k_layer + base, bytes);
+        const __amdgpu_buffer_rsrc_t vr = tile_rsrc(v_layer + base, bytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kb[buf][i] = load_tile16(kr, k_off + 64u * i);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vb[buf][c] = load_tile16(vr, v_off + 1024u * c);
+    };
+
+    auto consume = [&](int buf, int b) {
+        // ---- scores: partial dots over this lane's 32 dims, 4 heads ----
+        float acc[kGroup];
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) {
+            float x = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const h2x4 qq = pairs(qv[h][i]);
+                const h2x4 kk = pairs(kb[buf][i]);
+#pragma unroll
+                for (int p = 0; p < 4; ++p) x = __builtin_amdgcn_fdot2(qq.v[p], kk.v[p], x, false);
+            }
+            acc[h] = x;
+        }
+        // ---- 4-lane transpose-reduce: lane keeps head kq ----
+        const bool hi2 = (kq & 2) != 0;
+        const bool hi1 = (kq & 1) != 0;
+        float keep0 = hi2 ? acc[2] : acc[0];
+        float keep1 = hi2 ? acc[3] : acc[1];
+        const float send0 = hi2 ? acc[0] : acc[2];
+        const float send1 = hi2 ? acc[1] : acc[3];
+        keep0 += dpp_quad_xor2(send0);
+        keep1 += dpp_quad_xor2(send1);
+        float sc = hi1 ? keep1 : keep0;
+        sc += dpp_quad_xor1(hi1 ? keep0 : keep1);
+        sc *= a.scale_log2e;
+
+        // ---- mask the tail of the sequence's last block ----
+        const int valid = ctx - b * kBlockSize;  // >= 1
+        const bool partial = valid < kBlockSize;
+        if (partial && kt >= valid) sc = -INFINITY;
+
+        // ---- online softmax with a lazily raised max ----
+        if (__builtin_amdgcn_ballot_w64(sc > m_run + kTau) != 0) {
+            float bm = sc;
+            bm = fmaxf(bm, dpp_row_ror4(bm));
+            bm = fmaxf(bm, dpp_row_ror8(bm));
+            bm = fmaxf(bm, shfl_xor(bm, 16));
+            bm = fmaxf(bm, shfl_xor(bm, 32));
+            const float m_new = fmaxf(m_run, bm);
+            const float alpha = fast_exp2(m_run - m_new);
+            l_run *= alpha;
+            m_run = m_new;
+            if (lane < 4) alpha_lds[w][lane] = alpha;
+            wave_lds_sync();
+            const float4 al = *reinterpret_cast<const float4 *>(alpha_lds[w]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o[0][e] *= al.x;
+                o[1][e] *= al.y;
+                o[2][e] *= al.z;
+                o[3][e] *= al.w;
+            }
+        }
+        const float p = fast_exp2(sc - m_run);
+        l_run += p;
+        p_lds[w][lane] = p;  // index 4*kt + kq == lane
+        wave_lds_sync();
+
+        // ---- P V ----
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float4 pc = *reinterpret_cast<const float4 *>(&p_lds[w][4 * (4 * c + vt)]);
+            h8 vv = vb[buf][c];
+            if (partial && 4 * c + vt >= valid) vv = h8(0);  // stale slots may hold anything
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = static_cast<float>(vv[e]);
+                o[0][e] = fmaf(pc.x, x, o[0][e]);
+                o[1][e] = fmaf(pc.y, x, o[1][e]);
+                o[2][e] = fmaf(pc.z, x, o[2][e]);
+                o[3][e] = fmaf(pc.w, x, o[3][e]);
+            }
+        }
+        wave_lds_sync();  // p_lds is rewritten by the next block
+    };
+
+    // Software pipeline over this wave's blocks with NBUF register buffers:
+    // block b + NBUF - 1 is issued before block b is consumed.
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) issue(i, wb_begin + i);
+    for (int base = wb_begin; base < wb_end; base += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+            issue((u + NBUF - 1) % NBUF, base + u + NBUF - 1);
+            if (base + u < wb_end) consume(u, base + u);
+        }
+    }
+
+    // ---- per-wave totals ----
+    l_run += dpp_row_ror4(l_run);
+    l_run += dpp_row_ror8(l_run);
+    l_run += shfl_xor(l_run, 16);
+    l_run += shfl_xor(l_run, 32);
+    if (lane < 4) {
+        m_lds[w][lane] = m_run;
+        l_lds[w][lane] = l_run;
+    }
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+        float4 *dst = reinterpret_cast<float4 *>(&o_lds[w][vt][h][8 * vj]);
+        dst[0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+        dst[1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+    }
+    __syncthreads();
+
+    // ---- merge the four waves: thread -> (head, 2 dims) ----
+    const int h = tid >> 6;
+    const int d0 = (tid & 63) * 2;
+    float mw[kWaves], M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) {
+        mw[x] = m_lds[x][h];
+        M = fmaxf(M, mw[x]);
+    }
+    float L = 0.0f, O0 = 0.0f, O1 = 0.0f;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) {
+        const float wgt = mw[x] == -INFINITY ? 0.0f : fast_exp2(mw[x] - M);
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float2 v = *reinterpret_cast<const float2 *>(&o_lds[x][r][h][d0]);
+            s0 += v.x;
+            s1 += v.y;
+        }
+        L += wgt * l_lds[x][h];
+        O0 += wgt * s0;
+        O1 += wgt * s1;
+    }
+    const size_t row = static_cast<size_t>(s) * a.num_q_heads + head0 + h;
+    if (single) {
+        const _Float16 r0 = static_cast<_Float16>(O0 / L);
+        const _Float16 r1 = static_cast<_Float16>(O1 / L);
+        h2 pr = {r0, r1};
+        *reinterpret_cast<h2 *>(a.out + row * kHeadDim + d0) = pr;
+    } else {
+        const size_t slot = row * a.max_splits + split;
+        *reinterpret_cast<float2 *>(a.o_part + slot * kHeadDim + d0) = make_float2(O0, O1);
+        if (d0 == 0) *reinterpret_cast<float2 *>(a.ml_part + slot * 2) = make_float2(M, L);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// decode_merge: 256 threads = two (sequence, query head) rows of 128 dims.
+//   M = max_i m_i,  L = sum_i 2^(m_i - M) l_i,  out = sum_i 2^(m_i - M) o_i / L
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 2 + (threadIdx.x >> 7);
+    const int d = threadIdx.x & 127;
+    if (row >= static_cast<int64_t>(a.batch) * a.num_q_heads) return;
+    const int s = static_cast<int>(row / a.num_q_heads);
+    const int ctx = clamp_ctx(a.ctx_lens[s], a.max_ctx, a.max_blocks);
+    const int ns = (ctx + a.split_tokens - 1) / a.split_tokens;
+    uint16_t *out = a.out + row * kHeadDim + d;
+    if (ns == 0) {
+        *out = 0;
+        return;
+    }
+    const float *ml = a.ml_part + row * a.max_splits * 2;
+    const float *op = a.o_part + row * a.max_splits * kHeadDim + d;
+    float M = -INFINITY;
+    for (int i = 0; i < ns; ++i) M = fmaxf(M, ml[2 * i]);
+    float L = 0.0f, O = 0.0f;
+    for (int i = 0; i < ns; ++i) {
+        const float wgt = fast_exp2(ml[2 * i] - M);
+        L += wgt * ml[2 * i + 1];
+        O += wgt * op[static_cast<int64_t>(i) * kHeadDim];
+    }
+    const _Float16 r = static_cast<_Float16>(O / L);
+    *reinterpret_cast<_Float16 *>(out) = r;
+}
+
+}  // namespace
+
+hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream) {
+    const int64_t total = static_cast<int64_t>(a.n_tokens) * a.num_kv_heads * (kHeadDim / 8);
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(write_kv_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
+    const dim3 grid(a.max_splits, a.num_kv_heads, a.batch);
+    hipLaunchKernelGGL(decode_partial_kernel<3>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream) {
+    const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(static_cast<uint32_t>((rows + 1) / 2)), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace pa

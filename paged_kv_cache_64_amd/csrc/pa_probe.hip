@@ -1,0 +1,72 @@
+// pa_probe.hip -- measurement helpers, built as libpa_probe.so (not part of
+// the decode path):
+//   pa_probe_read  streams a buffer with 16-byte loads and folds it into one
+//                  word per work-group; gives the HBM read bandwidth this GPU
+//                  reaches, a second denominator next to the published peak
+//   pa_probe_copy  plain 16-byte copy of a known size; its FETCH_SIZE and
+//                  WRITE_SIZE counter readings calibrate those counters
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4 *src, size_t n16, uint32_t *sink) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * kThreads * kUnroll;
+    uint32_t acc = 0;
+    for (size_t base = static_cast<size_t>(blockIdx.x) * kThreads * kUnroll + threadIdx.x; base < n16;
+         base += stride) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const size_t i = base + static_cast<size_t>(u) * kThreads;
+            v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4(0);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    __shared__ uint32_t red[kThreads];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
+        if (threadIdx.x < off) red[threadIdx.x] ^= red[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(kThreads) void probe_copy_kernel(uint4 *dst, const uint4 *src, size_t n16) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+// Work-groups used by pa_probe_read; `sink` must hold this many uint32.
+int32_t pa_probe_read_groups(void) { return 256 * 8; }
+
+// bytes must be a multiple of 16; src 16-byte aligned.  Returns a hipError_t.
+int32_t pa_probe_read(const void *src, size_t bytes, void *sink, hipStream_t stream) {
+    if (!src || !sink || bytes % 16 != 0) return static_cast<int32_t>(hipErrorInvalidValue);
+    hipLaunchKernelGGL(probe_read_kernel, dim3(pa_probe_read_groups()), dim3(kThreads), 0, stream,
+                       static_cast<const u32x4 *>(src), bytes / 16, static_cast<uint32_t *>(sink));
+    return static_cast<int32_t>(hipGetLastError());
+}
+
+int32_t pa_probe_copy(void *dst, const void *src, size_t bytes, hipStream_t stream) {
+    if (!src || !dst || bytes % 16 != 0) return static_cast<int32_t>(hipErrorInvalidValue);
+    hipLaunchKernelGGL(probe_copy_kernel, dim3(256 * 8), dim3(kThreads), 0, stream, static_cast<uint4 *>(dst),
+                       static_cast<const uint4 *>(src), bytes / 16);
+    return static_cast<int32_t>(hipGetLastError());
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+"""CPU tests of the C ABI: the library loads, exports what include/pa.h
+declares, sizes pools as the pages do, and rejects bad arguments before any
+GPU work is enqueued (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_64_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+# Fake, aligned, never-dereferenced device addresses for validation paths.
+FAKE = 1 << 20
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def _desc(layers=32, blocks=64, bs=16, hkv=8, d=128, dtype=pa.PA_F16):
+    return pa.PoolDesc(layers, blocks, bs, hkv, d, dtype)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pa.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert declared == sorted(pa.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_pool_bytes_matches_the_pages_sizing(lib):
+    # one block of one layer, K + V: 16 x 8 x 256 x 2 = 65,536 B
+    assert 2 * pa.pa_pool_bytes(_desc(layers=1, blocks=1)) == 65536
+    # 32 layers: 2,048 KiB per block
+    assert 2 * pa.pa_pool_bytes(_desc(layers=32, blocks=1)) == 2048 * 1024
+    # 128 KiB per token over 32 layers
+    assert 2 * pa.pa_pool_bytes(_desc(layers=32, blocks=1)) // 16 == 128 * 1024
+    assert pa.pa_pool_bytes(_desc(blocks=0)) == 0
+    assert lib.pa_pool_bytes(None) == 0
+
+
+def test_status_strings(lib):
+    for code in (pa.PA_OK, pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED, pa.PA_ERR_WORKSPACE,
+                 pa.PA_ERR_HIP):
+        assert pa.pa_status_string(code)
+    assert pa.pa_status_string(42) == "unknown status"
+
+
+def test_pool_create_checks(lib):
+    h = ctypes.c_void_p()
+    d = _desc()
+    assert lib.pa_pool_create(ctypes.byref(d), FAKE, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_pool_create(ctypes.byref(d), None, FAKE, ctypes.byref(h)) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_pool_create(ctypes.byref(d), FAKE + 2, FAKE, ctypes.byref(h)) == pa.PA_ERR_INVALID_ARG
+    bad = _desc(d=64)
+    assert lib.pa_pool_create(ctypes.byref(bad), FAKE, FAKE, ctypes.byref(h)) == pa.PA_ERR_UNSUPPORTED
+    bad = _desc(bs=32)
+    assert lib.pa_pool_create(ctypes.byref(bad), FAKE, FAKE, ctypes.byref(h)) == pa.PA_ERR_UNSUPPORTED
+    handle = pa.pa_pool_create(d, FAKE, FAKE)
+    assert handle
+    pa.pa_pool_destroy(handle)
+    assert lib.pa_pool_destroy(None) == pa.PA_OK
+
+
+@pytest.fixture
+def pool(lib):
+    handle = pa.pa_pool_create(_desc(layers=2, blocks=64), FAKE, FAKE)
+    yield handle
+    pa.pa_pool_destroy(handle)
+
+
+def test_write_kv_validation(lib, pool):
+    assert lib.pa_write_kv(pool, 0, FAKE, FAKE, FAKE, 0, None) == pa.PA_OK       # no-op
+    assert lib.pa_write_kv(pool, 2, FAKE, FAKE, FAKE, 4, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_write_kv(pool, -1, FAKE, FAKE, FAKE, 4, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_write_kv(pool, 0, None, FAKE, FAKE, 4, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_write_kv(pool, 0, FAKE, FAKE, FAKE, -1, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_write_kv(pool, 0, FAKE + 8, FAKE, FAKE, 4, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_write_kv(None, 0, FAKE, FAKE, FAKE, 4, None) == pa.PA_ERR_INVALID_ARG
+
+
+def _decode(lib, pool, layer=0, q=FAKE, out=FAKE, tables=FAKE, width=16, lens=FAKE, batch=4,
+            hq=32, max_ctx=256, scale=0.088, ws=FAKE, ws_bytes=1 << 30):
+    return lib.pa_decode(pool, layer, q, out, tables, width, lens, batch, hq, max_ctx, scale, ws,
+                         ws_bytes, None)
+
+
+def test_decode_validation(lib, pool):
+    assert _decode(lib, pool, batch=0) == pa.PA_OK                          # no-op
+    assert _decode(lib, pool, layer=2) == pa.PA_ERR_INVALID_ARG
+    assert _decode(lib, pool, hq=12) == pa.PA_ERR_INVALID_ARG               # not a multiple of 8
+    assert _decode(lib, pool, hq=16) == pa.PA_ERR_UNSUPPORTED               # group of 2
+    assert _decode(lib, pool, max_ctx=257) == pa.PA_ERR_INVALID_ARG         # > width * 16
+    assert _decode(lib, pool, batch=-1) == pa.PA_ERR_INVALID_ARG
+    assert _decode(lib, pool, q=None) == pa.PA_ERR_INVALID_ARG
+    assert _decode(lib, pool, q=FAKE + 4) == pa.PA_ERR_INVALID_ARG          # misaligned
+    assert _decode(lib, pool, scale=float("nan")) == pa.PA_ERR_INVALID_ARG
+    assert _decode(lib, pool, batch=70000) == pa.PA_ERR_UNSUPPORTED
+    need = pa.pa_decode_workspace_bytes(pool, 4, 32, 256)
+    assert need > 0
+    assert _decode(lib, pool, ws_bytes=need - 1) == pa.PA_ERR_WORKSPACE
+    assert _decode(lib, pool, ws=None) == pa.PA_ERR_WORKSPACE
+    assert _decode(lib, pool, ws=FAKE + 16) == pa.PA_ERR_INVALID_ARG        # workspace alignment
+    assert lib.pa_decode_merge(pool, FAKE, FAKE, 4, 32, 256, FAKE, need - 1, None) == pa.PA_ERR_WORKSPACE
+
+
+def test_split_plan_and_workspace(lib, pool, monkeypatch):
+    monkeypatch.delenv("PA_SPLIT_TOKENS", raising=False)
+    for batch, max_ctx in [(1, 256), (8, 4096), (32, 4096), (64, 8192), (256, 8192), (3, 1)]:
+        s = pa.pa_decode_split_tokens(pool, batch, 32, max_ctx)
+        assert s % 64 == 0 and 64 <= s <= 4096
+        splits = -(-max_ctx // s)
+        ws = pa.pa_decode_workspace_bytes(pool, batch, 32, max_ctx)
+        if splits == 1:
+            assert ws == 0
+        else:
+            rows = batch * 32 * splits
+            assert ws >= rows * (128 + 2) * 4
+    monkeypatch.setenv("PA_SPLIT_TOKENS", "128")
+    assert pa.pa_decode_split_tokens(pool, 32, 32, 4096) == 128
+    monkeypatch.setenv("PA_SPLIT_TOKENS", "100")     # not a multiple of 64: ignored
+    assert pa.pa_decode_split_tokens(pool, 32, 32, 4096) % 64 == 0
+    assert pa.pa_decode_split_tokens(pool, 32, 32, 4096) != 100

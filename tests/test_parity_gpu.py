@@ -1,0 +1,216 @@
+"""GPU parity: libpa (through the C ABI) against the fp64 oracle.
+
+Tolerance for the F16 output: max |err| <= 2e-3 and relative L2 <= 1e-3 over
+each case.  Integer and byte work (pa_write_kv) is checked bit-exactly.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+import paged_kv_cache_64_amd as pa
+from tests.gpu_harness import Staged, compare, report, slots_of
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 100, 255, 256, 257, 1000, 4097]
+
+
+@pytest.fixture(autouse=True)
+def _no_split_override(monkeypatch):
+    monkeypatch.delenv("PA_SPLIT_TOKENS", raising=False)
+
+
+def _poison_tails(st, layer=0):
+    """Writes NaN into the slots of each sequence's last block that lie past its context."""
+    w = st.w
+    _, tables = st.host[layer][0], st.host[layer][1]
+    slots = []
+    for s, ctx in enumerate(w.ctx_lens):
+        ctx = int(ctx)
+        if ctx % w.block_size == 0 or ctx == 0:
+            continue
+        end = (ctx + w.block_size - 1) // w.block_size * w.block_size
+        slots += slots_of(tables[s], range(ctx, end), w.block_size)
+    if not slots:
+        return 0
+    n = len(slots)
+    nan = torch.full((n, w.num_kv_heads, w.head_dim), float("nan"), dtype=torch.float16,
+                     device="cuda")
+    st.pool.write(layer, nan, nan.clone(), torch.tensor(slots, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    return n
+
+
+def test_write_kv_lands_in_the_documented_layout():
+    report("write_kv layout")
+    pool = pa.Pool(2, 8, fill=0.0)
+    rng = np.random.default_rng(0)
+    n = 40
+    slots = rng.choice(8 * 16, size=n, replace=False).astype(np.int32)
+    slots[3] = -1           # skipped
+    slots[7] = 8 * 16       # past the pool: skipped
+    k = rng.standard_normal((n, 8, 128)).astype(np.float16)
+    v = rng.standard_normal((n, 8, 128)).astype(np.float16)
+    pool.write(1, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+               torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    kp = pool.k.cpu().numpy()          # [layer, block, head, offset, dim]
+    vp = pool.v.cpu().numpy()
+    want_k = np.zeros_like(kp)
+    want_v = np.zeros_like(vp)
+    for i, sl in enumerate(slots):
+        if 0 <= sl < 8 * 16:
+            want_k[1, sl // 16, :, sl % 16, :] = k[i]
+            want_v[1, sl // 16, :, sl % 16, :] = v[i]
+    assert np.array_equal(kp.view(np.uint16), want_k.view(np.uint16))
+    assert np.array_equal(vp.view(np.uint16), want_v.view(np.uint16))
+    pool.close()
+
+
+def test_small_ragged_batch_with_poisoned_tails():
+    w = workloads.custom(RAGGED, seed=11)
+    st = Staged(w)
+    npois = _poison_tails(st)
+    report("ragged", poisoned_slots=npois, split=st.pool.split_tokens(w.batch, 32, w.max_context_len))
+    compare("ragged", st.decode(0), st.reference(0))
+    st.close()
+
+
+@pytest.mark.parametrize("split", [64, 128, 192, 1024, 4096])
+def test_split_lengths_agree_with_oracle_and_phases(monkeypatch, split):
+    w = workloads.custom(RAGGED, seed=12)
+    st = Staged(w)
+    _poison_tails(st)
+    monkeypatch.setenv("PA_SPLIT_TOKENS", str(split))
+    assert st.pool.split_tokens(w.batch, 32, w.max_context_len) == split
+    a = st.decode(0)
+    b = st.decode(0, phases=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    compare(f"split{split}", a, st.reference(0))
+    st.close()
+
+
+def test_empty_contexts_give_zeros():
+    w = workloads.custom([0, 5, 0, 33], seed=13)
+    st = Staged(w)
+    out = st.decode(0)
+    compare("empty", out, st.reference(0))
+    assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+    w0 = workloads.custom([0, 0, 0], seed=14)
+    w0.pool_blocks = 4
+    st0 = Staged(w0)
+    out0 = torch.full((3, 32, 128), 7.0, dtype=torch.float16, device="cuda")
+    q = torch.zeros_like(out0)
+    tables = torch.zeros((3, 1), dtype=torch.int32, device="cuda")
+    st0.pool.decode(0, q, out0, tables, st0.lens, 0, 0.1)
+    torch.cuda.synchronize()
+    assert torch.all(out0 == 0)
+    st.close()
+    st0.close()
+
+
+def test_context_of_one_returns_v0_exactly():
+    w = workloads.custom([1] * 6, seed=15)
+    st = Staged(w)
+    _poison_tails(st)
+    out = st.decode(0).cpu().numpy()
+    _, tables, ids, _, v = st.host[0]
+    for s in range(w.batch):
+        blk = tables[s, 0]
+        v0 = v[np.searchsorted(ids, blk), 0]            # [Hkv, d]
+        want = np.repeat(v0, 4, axis=0)                  # contiguous groups of 4 q heads
+        assert np.array_equal(out[s].view(np.uint16), want.view(np.uint16))
+    st.close()
+
+
+def test_block_relabelling_is_bitwise_invariant():
+    w = workloads.custom(RAGGED[:10], seed=16)
+    st = Staged(w)
+    a = st.decode(0)
+    q, tables, ids, k, v = st.host[0]
+    pi = np.random.default_rng(3).permutation(w.pool_blocks).astype(np.int32)
+    st2 = Staged(w)
+    st2.pool.k.fill_(float("nan"))
+    st2.pool.v.fill_(float("nan"))
+    st2.pool.write_blocks(0, torch.from_numpy(pi[ids]).cuda(), torch.from_numpy(k).cuda(),
+                          torch.from_numpy(v).cuda())
+    held = w.blocks_held()
+    t2 = tables.copy()
+    for s in range(w.batch):
+        t2[s, :held[s]] = pi[tables[s, :held[s]]]
+    st2.dev[0] = (st2.dev[0][0], torch.from_numpy(t2).cuda())
+    b = st2.decode(0)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    st.close()
+    st2.close()
+
+
+def test_doubling_values_doubles_output_exactly():
+    w = workloads.custom(RAGGED[:12], seed=17)
+    st = Staged(w)
+    a = st.decode(0)
+    q, tables, ids, k, v = st.host[0]
+    st.pool.write_blocks(0, torch.from_numpy(ids).cuda(), torch.from_numpy(k).cuda(),
+                         torch.from_numpy(v).cuda() * 2)
+    b = st.decode(0)
+    # exact wherever F16 keeps full precision (2x commutes with rounding there)
+    normal = a.float().abs() >= 2.0 ** -13
+    assert torch.equal((a.float() * 2).half()[normal].view(torch.int16), b[normal].view(torch.int16))
+    assert torch.all(((a.float() * 2) - b.float()).abs()[~normal] <= 2.0 ** -24)
+    st.close()
+
+
+def test_shared_prefix_blocks_and_duplicate_entries():
+    lens = [48 + x for x in (0, 5, 16, 40, 77, 1)]
+    w = workloads.custom(lens, seed=18, prefix_groups=(2, 3, 3))
+    st = Staged(w)
+    _poison_tails(st)
+    compare("shared", st.decode(0), st.reference(0))
+    # one table naming the same physical block twice
+    q, tables, ids, k, v = st.host[0]
+    tables = tables.copy()
+    tables[0, 1] = tables[0, 0]
+    st.host[0] = (q, tables, ids, k, v)
+    st.dev[0] = (st.dev[0][0], torch.from_numpy(tables).cuda())
+    compare("duplicate", st.decode(0), st.reference(0))
+    st.close()
+
+
+def test_lengths_past_the_hint_are_truncated():
+    w = workloads.custom([300, 90, 17], seed=19)
+    st = Staged(w)
+    out = st.decode(0, max_context_len=100)
+    w_trunc = np.minimum(w.ctx_lens, 100)
+    saved = w.ctx_lens
+    w.ctx_lens = w_trunc
+    ref = st.reference(0)
+    w.ctx_lens = saved
+    compare("truncated", out, ref)
+    st.close()
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 5])
+def test_config_full_parity(k):
+    w = workloads.config(k)
+    st = Staged(w)
+    split = st.pool.split_tokens(w.batch, 32, w.max_context_len)
+    report(f"config{k}", batch=w.batch, max_ctx=w.max_context_len, split=split)
+    compare(f"config{k}", st.decode(0, phases=True), st.reference(0))
+    st.close()
+
+
+def test_config3_sampled_layers_and_sequences():
+    """The 32-layer pool at full size; three layers are written and checked
+    on sampled sequences (the others hold NaN and are never read)."""
+    w = workloads.config(3)
+    layers = (0, 17, 31)
+    st = Staged(w, layers=layers, pool_layers=32)
+    rng = np.random.default_rng(3)
+    for layer in layers:
+        seqs = np.sort(rng.choice(w.batch, size=4, replace=False))
+        out = st.decode(layer, phases=True).cpu().numpy()[seqs]
+        compare(f"config3 layer{layer} seqs{list(seqs)}", out, st.reference(layer, seqs))
+    st.close()

@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import math
 import os
+import threading
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
@@ -48,13 +49,24 @@ def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def _normal_f16(rng: np.random.Generator, shape, boost=None) -> np.ndarray:
-    buf = np.empty(shape, dtype=np.float32)
-    rng.standard_normal(out=buf, dtype=np.float32)
+_scratch = threading.local()
+
+
+def _normal_f16(rng: np.random.Generator, shape, boost=None, out=None) -> np.ndarray:
+    """N(0, 1) drawn in float32 (optionally some rows scaled), rounded to F16."""
+    n = int(np.prod(shape))
+    buf = getattr(_scratch, "buf", None)
+    if buf is None or buf.size < n:
+        buf = _scratch.buf = np.empty(n, dtype=np.float32)
+    view = buf[:n].reshape(shape)
+    rng.standard_normal(out=view, dtype=np.float32)
     if boost is not None:
         mask, factor = boost
-        buf[mask] *= np.float32(factor)
-    return buf.astype(np.float16)
+        view[mask] *= np.float32(factor)
+    if out is None:
+        return view.astype(np.float16)
+    np.copyto(out, view, casting="same_kind")
+    return out
 
 
 @dataclass
@@ -155,6 +167,7 @@ class Workload:
         k = np.empty((n,) + shape, dtype=np.float16)
         v = np.empty((n,) + shape, dtype=np.float16)
         chunks = np.unique(rank // _CHUNK_BLOCKS)
+        full = n == all_ids.shape[0]
 
         def fill(c):
             lo = c * _CHUNK_BLOCKS
@@ -164,6 +177,10 @@ class Workload:
                 mask = _rng(self.seed, _BOOST, layer, c).random(
                     (cnt, self.block_size, self.num_kv_heads)) < self.key_boost_prob
                 boost = (mask, self.key_boost)
+            if full:
+                _normal_f16(_rng(self.seed, _K, layer, c), (cnt,) + shape, boost, k[lo:lo + cnt])
+                _normal_f16(_rng(self.seed, _V, layer, c), (cnt,) + shape, None, v[lo:lo + cnt])
+                return
             kc = _normal_f16(_rng(self.seed, _K, layer, c), (cnt,) + shape, boost)
             vc = _normal_f16(_rng(self.seed, _V, layer, c), (cnt,) + shape)
             sel = np.nonzero((rank >= lo) & (rank < lo + cnt))[0]
