@@ -5,7 +5,10 @@ Default workload: the full 32-layer decode step of the 8B geometry -- batch 32,
 every context 4096 tokens, 32 query heads / 8 KV heads, head_dim 128,
 block_size 16, F16 K/V ~ N(0, 1), a fresh random block table per layer in a
 pool of twice the needed blocks.  One step = for each of the 32 layers:
-pa_write_kv of the newest token's K/V, pa_decode_partial, pa_decode_merge.
+pa_decode_partial with the newest token's K/V (it stores them into their
+slots and attends over the whole context: the first phase of
+pa_append_decode), then pa_decode_merge (which returns at once when a single
+split covers the context).
 
 Prints one JSON line: achieved KV GB/s (value), decode tokens/s, the fraction
 of HBM peak, a roofline record for the dominant kernel (decode_partial), and
@@ -68,6 +71,9 @@ def main():
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB three times (to scale the FETCH_SIZE "
+                         "and WRITE_SIZE counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -86,6 +92,20 @@ def main():
     lib = pa.load_library()
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.calibrate_copy:
+        plib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_64_amd", "libpa_probe.so"))
+        plib.pa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+        plib.pa_probe_copy.restype = ctypes.c_int32
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            assert plib.pa_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes,
+                                      torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
+        return
     w = workloads.config(args.config, args.seed)
     B, HQ, HKV, D = w.block_size, w.num_q_heads, w.num_kv_heads, w.head_dim
     log(f"workload: {w.name}; pool {w.layers} layers x {w.pool_blocks} blocks")
@@ -94,7 +114,7 @@ def main():
     t_stage = time.time()
     pool = pa.Pool(w.layers, w.pool_blocks, HKV, D, B, device=dev, fill=0.0)
     lens_dev = torch.from_numpy(w.ctx_lens.copy()).to(dev)
-    q_dev, tables_dev, knew, vnew, slots = [], [], [], [], []
+    q_dev, tables_dev, knew, vnew = [], [], [], []
     host0 = None
     ctx = w.ctx_lens.astype(np.int64)
     for layer in range(w.layers):
@@ -105,18 +125,16 @@ def main():
         tables = w.tables(layer)
         q_dev.append(torch.from_numpy(q).to(dev))
         tables_dev.append(torch.from_numpy(tables).to(dev))
-        # the step's newest token (position ctx-1) is rewritten with its own values
-        live = ctx > 0
+        # the step's newest token (position ctx-1) is stored again with its own values,
+        # so every timed step sees the same pool
         pos = np.maximum(ctx - 1, 0)
         blk = tables[np.arange(w.batch), pos // B]
         rank = np.searchsorted(ids, blk)
         rank = np.minimum(rank, len(ids) - 1) if len(ids) else rank
         kn = k[rank, pos % B] if len(ids) else np.zeros((w.batch, HKV, D), np.float16)
         vn = v[rank, pos % B] if len(ids) else np.zeros((w.batch, HKV, D), np.float16)
-        sl = np.where(live, blk.astype(np.int64) * B + pos % B, -1).astype(np.int32)
         knew.append(torch.from_numpy(np.ascontiguousarray(kn)).to(dev))
         vnew.append(torch.from_numpy(np.ascontiguousarray(vn)).to(dev))
-        slots.append(torch.from_numpy(sl).to(dev))
         if layer == 0 and not args.no_cpu_baseline:
             host0 = (q, tables, ids, k, v)
         del ids, k, v
@@ -137,21 +155,19 @@ def main():
     scale = ctypes.c_float(w.scale)
 
     # pre-marshalled argument tuples: the launch loop only calls into the library
-    write_args = [(h, L, knew[L].data_ptr(), vnew[L].data_ptr(), slots[L].data_ptr(), w.batch, sptr)
-                  for L in range(w.layers)]
-    part_args = [(h, L, q_dev[L].data_ptr(), outs[L].data_ptr(), tables_dev[L].data_ptr(), width,
-                  lens_dev.data_ptr(), w.batch, HQ, mcl, scale, ws.data_ptr(), ws_bytes, sptr)
+    part_args = [(h, L, q_dev[L].data_ptr(), knew[L].data_ptr(), vnew[L].data_ptr(),
+                  outs[L].data_ptr(), tables_dev[L].data_ptr(), width, lens_dev.data_ptr(),
+                  w.batch, HQ, mcl, scale, ws.data_ptr(), ws_bytes, sptr)
                  for L in range(w.layers)]
     merge_args = [(h, outs[L].data_ptr(), lens_dev.data_ptr(), w.batch, HQ, mcl, ws.data_ptr(),
                    ws_bytes, sptr) for L in range(w.layers)]
-    f_write, f_part, f_merge = lib.pa_write_kv, lib.pa_decode_partial, lib.pa_decode_merge
+    f_part, f_merge = lib.pa_decode_partial, lib.pa_decode_merge
 
     def step(events=None):
         for L in range(w.layers):
-            rc = f_write(*write_args[L])
             if events is not None:
                 events[L][0].record(stream)
-            rc |= f_part(*part_args[L])
+            rc = f_part(*part_args[L])
             if events is not None:
                 events[L][1].record(stream)
             rc |= f_merge(*merge_args[L])
@@ -159,8 +175,15 @@ def main():
                 raise RuntimeError(f"library call failed in layer {L}: {rc}")
 
     kv_bytes_step = w.kv_bytes()
-    cold_flush = kv_bytes_step < (4 << 30)   # small steps would run from the 256 MB cache
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if cold_flush else None
+    plib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_64_amd", "libpa_probe.so"))
+    plib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    plib.pa_probe_read.restype = ctypes.c_int32
+    sink = torch.empty(plib.pa_probe_read_groups(), dtype=torch.int32, device=dev)
+    # small steps would run from the 256 MB last-level cache: between timed
+    # steps, read (not write, which would leave dirty lines to drain) 1 GiB
+    cold_flush = kv_bytes_step < (4 << 30)
+    flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev) if cold_flush else None
 
     for _ in range(args.warmup):
         step()
@@ -168,23 +191,34 @@ def main():
     log(f"warmup done ({args.warmup} steps); split={split} tokens, workspace={ws_bytes} B, "
         f"cold flush between steps: {cold_flush}")
 
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(w.layers)] for _ in range(args.steps)]
+    # Timed region 1 (the headline): K whole steps, events only around each step.
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if flush is not None:
-            flush.zero_()
+        if flush_buf is not None:
+            plib.pa_probe_read(flush_buf.data_ptr(), flush_buf.numel(), sink.data_ptr(), sptr)
         step_ev[i][0].record(stream)
-        step(ev[i])
+        step()
         step_ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = [a.elapsed_time(b) for a, b in step_ev]
-    part_us = [1e3 * a.elapsed_time(b) for e in ev for a, b in e]
     ms_per_step = float(np.mean(step_ms))
+
+    # Timed region 2 (the roofline record): the same K steps with an event pair
+    # around every decode_partial launch; event records between launches cost
+    # a few microseconds each, which is why region 1 carries none.
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(w.layers)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if flush_buf is not None:
+            plib.pa_probe_read(flush_buf.data_ptr(), flush_buf.numel(), sink.data_ptr(), sptr)
+        step(ev[i])
+    torch.cuda.synchronize()
+    part_us = [1e3 * a.elapsed_time(b) for e in ev for a, b in e]
     log(f"timed {args.steps} steps: mean {ms_per_step:.4f} ms, min {min(step_ms):.4f} ms, "
         f"wall {1e3 * wall / args.steps:.4f} ms/step; decode_partial mean {np.mean(part_us):.2f} us")
 
@@ -198,14 +232,9 @@ def main():
     # ---- HBM read probe: the bandwidth this GPU reaches on a plain stream ----
     probe = None
     if not args.no_probe:
-        plib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_64_amd", "libpa_probe.so"))
-        plib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                       ctypes.c_void_p]
-        plib.pa_probe_read.restype = ctypes.c_int32
         nbytes = 4 << 30
         buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         buf.fill_(1)
-        sink = torch.empty(plib.pa_probe_read_groups(), dtype=torch.int32, device=dev)
         for _ in range(2):
             plib.pa_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), sptr)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -225,34 +254,43 @@ def main():
     if host0 is not None:
         import oracle
 
-        q, tables, ids, k, v = host0
-        kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, w.ctx_lens, B)
         threads = len(os.sched_getaffinity(0))
-        # one decode of layer 0 for the parity sample
-        lib.pa_decode(h, 0, q_dev[0].data_ptr(), outs[0].data_ptr(), tables_dev[0].data_ptr(), width,
-                      lens_dev.data_ptr(), w.batch, HQ, mcl, scale, ws.data_ptr(), ws_bytes, sptr)
-        torch.cuda.synchronize()
-        gpu0 = outs[0].cpu().numpy().astype(np.float64)
-        done, done_bytes, errs, refs, diffs = 0, 0, [], [], []
-        t_cpu = time.perf_counter()
-        order = np.random.default_rng(0).permutation(w.batch)
-        chunk = 4
-        while done < w.batch and time.perf_counter() - t_cpu < args.cpu_seconds:
-            seqs = np.sort(order[done:done + chunk])
-            ref = oracle.decode(q[seqs], kc, vc, t2[seqs], w.ctx_lens[seqs], w.scale, B,
-                                threads=threads)
-            errs.append(float(np.abs(gpu0[seqs] - ref).max()))
-            refs.append(float((ref ** 2).sum()))
-            diffs.append(float(((gpu0[seqs] - ref) ** 2).sum()))
-            done += len(seqs)
-            done_bytes += int(w.ctx_lens[seqs].astype(np.int64).sum()) * HKV * D * 4
-        cpu_s = time.perf_counter() - t_cpu
+        errs, refs, diffs = [], [], []
+        done_seqs, done_bytes, cpu_s = 0, 0, 0.0
+        layer = 0
+        while layer < w.layers and cpu_s < args.cpu_seconds:
+            if layer == 0:
+                q, tables, ids, k, v = host0
+            else:
+                ids, k, v = w.kv_blocks(layer)
+                q, tables = w.q(layer), w.tables(layer)
+            kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, w.ctx_lens, B)
+            # the GPU result of this layer (read-only decode of the staged pool)
+            lib.pa_decode(h, layer, q_dev[layer].data_ptr(), outs[layer].data_ptr(),
+                          tables_dev[layer].data_ptr(), width, lens_dev.data_ptr(), w.batch, HQ,
+                          mcl, scale, ws.data_ptr(), ws_bytes, sptr)
+            torch.cuda.synchronize()
+            gpu = outs[layer].cpu().numpy().astype(np.float64)
+            for lo in range(0, w.batch, 8):
+                seqs = np.arange(lo, min(w.batch, lo + 8))
+                t_cpu = time.perf_counter()
+                ref = oracle.decode(q[seqs], kc, vc, t2[seqs], w.ctx_lens[seqs], w.scale, B,
+                                    threads=threads)
+                cpu_s += time.perf_counter() - t_cpu
+                errs.append(float(np.abs(gpu[seqs] - ref).max()))
+                refs.append(float((ref ** 2).sum()))
+                diffs.append(float(((gpu[seqs] - ref) ** 2).sum()))
+                done_seqs += len(seqs)
+                done_bytes += int(w.ctx_lens[seqs].astype(np.int64).sum()) * HKV * D * 4
+                if cpu_s >= args.cpu_seconds:
+                    break
+            layer += 1
         cpu = {"value": round(done_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"layer 0, {done} of {w.batch} sequences ({done_bytes} B of K/V), "
-                         f"fp64, {cpu_s:.1f} s",
-               "tokens_per_s_equiv": round(done / cpu_s / w.layers, 4)}
-        parity = {"sequences": done, "max_abs_err": max(errs),
+               "sample": f"{done_seqs} (sequence, layer) rows of the same step over layers "
+                         f"0..{layer - 1} ({done_bytes} B of K/V), fp64, {cpu_s:.1f} s of oracle time",
+               "tokens_per_s_equiv": round(done_bytes / (w.kv_bytes() / w.batch) / cpu_s, 4)}
+        parity = {"rows": done_seqs, "max_abs_err": max(errs),
                   "rel_l2": (sum(diffs) / sum(refs)) ** 0.5}
         log(f"oracle: {cpu['value']} GB/s on {threads} threads; parity {parity}")
 

@@ -145,16 +145,37 @@ pa_status pa_decode(pa_pool *pool, int32_t layer, const void *q_dev, void *out_d
                     int32_t max_context_len, float scale, void *workspace_dev,
                     size_t workspace_bytes, hipStream_t stream);
 
-/* First phase of pa_decode: one work-group per (sequence, KV head, context
- * split) attends to its split and writes the unnormalised partial output,
- * running max and running sum (fp32) into the workspace.  When a single split
- * covers max_context_len it writes the final F16 output instead and
- * pa_decode_merge has nothing to do. */
-pa_status pa_decode_partial(pa_pool *pool, int32_t layer, const void *q_dev, void *out_dev,
-                            const int32_t *block_tables_dev, int32_t max_blocks_per_seq,
-                            const int32_t *context_lens_dev, int32_t batch, int32_t num_q_heads,
-                            int32_t max_context_len, float scale, void *workspace_dev,
-                            size_t workspace_bytes, hipStream_t stream);
+/* One decode step of one layer that also stores this step's token: for each
+ * sequence s with ctx = context_lens[s] >= 1, the K and V of its newest
+ * position ctx - 1 are written to the slot its table gives for that position
+ * (table[(ctx-1) / block_size] * block_size + (ctx-1) % block_size), and
+ * attention then runs over positions [0, ctx) exactly as pa_decode does.
+ * The result equals pa_write_kv of those slots followed by pa_decode, in one
+ * launch fewer: the new values are used from registers, and the pool write
+ * only serves later calls.  The pages describe the attention kernel as doing
+ * both: it "writes new keys and values to the right places and reads a
+ * request's history through its block table" ("vLLM Architecture and
+ * Installation", Example 3).
+ *   k_new_dev, v_new_dev: F16 [batch][num_kv_heads][head_dim], 16-byte aligned
+ * Other arguments as pa_decode.  The newest position's block must not be
+ * shared with a sequence that is decoded concurrently. */
+pa_status pa_append_decode(pa_pool *pool, int32_t layer, const void *q_dev, const void *k_new_dev,
+                           const void *v_new_dev, void *out_dev, const int32_t *block_tables_dev,
+                           int32_t max_blocks_per_seq, const int32_t *context_lens_dev, int32_t batch,
+                           int32_t num_q_heads, int32_t max_context_len, float scale,
+                           void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+
+/* First phase of pa_decode (k_new_dev = v_new_dev = NULL) or of
+ * pa_append_decode (both non-null): one work-group per (sequence, KV head,
+ * context split) attends to its split and writes the unnormalised partial
+ * output, running max and running sum (fp32) into the workspace.  When a
+ * single split covers max_context_len it writes the final F16 output instead
+ * and pa_decode_merge has nothing to do. */
+pa_status pa_decode_partial(pa_pool *pool, int32_t layer, const void *q_dev, const void *k_new_dev,
+                            const void *v_new_dev, void *out_dev, const int32_t *block_tables_dev,
+                            int32_t max_blocks_per_seq, const int32_t *context_lens_dev, int32_t batch,
+                            int32_t num_q_heads, int32_t max_context_len, float scale,
+                            void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
 
 /* Second phase of pa_decode: merges the per-split partials of every
  * (sequence, query head) by their log-sum-exp weights, divides by the merged

@@ -25,7 +25,7 @@ PA_F16 = 1
 
 EXPORTS = ("pa_pool_bytes", "pa_pool_create", "pa_pool_destroy", "pa_write_kv",
            "pa_decode_split_tokens", "pa_decode_workspace_bytes", "pa_decode",
-           "pa_decode_partial", "pa_decode_merge", "pa_status_string")
+           "pa_append_decode", "pa_decode_partial", "pa_decode_merge", "pa_status_string")
 
 
 class PaError(RuntimeError):
@@ -65,10 +65,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_split_tokens.argtypes = [_P, _I, _I, _I]
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode_workspace_bytes.argtypes = [_P, _I, _I, _I]
-    for name in ("pa_decode", "pa_decode_partial"):
+    lib.pa_decode.restype = _I
+    lib.pa_decode.argtypes = [_P, _I, _P, _P, _P, _I, _P, _I, _I, _I, ctypes.c_float, _P,
+                              ctypes.c_size_t, _P]
+    for name in ("pa_append_decode", "pa_decode_partial"):
         fn = getattr(lib, name)
         fn.restype = _I
-        fn.argtypes = [_P, _I, _P, _P, _P, _I, _P, _I, _I, _I, ctypes.c_float, _P,
+        fn.argtypes = [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, ctypes.c_float, _P,
                        ctypes.c_size_t, _P]
     lib.pa_decode_merge.restype = _I
     lib.pa_decode_merge.argtypes = [_P, _P, _P, _I, _I, _I, _P, ctypes.c_size_t, _P]
@@ -145,27 +148,37 @@ def pa_decode_workspace_bytes(handle, batch, num_q_heads, max_context_len) -> in
                                                         max_context_len))
 
 
-def _decode_call(name, handle, layer, q, out, block_tables, max_blocks_per_seq, context_lens,
-                 batch, num_q_heads, max_context_len, scale, workspace, workspace_bytes, stream):
-    fn = getattr(load_library(), name)
-    _check(fn(handle, layer, _ptr(q), _ptr(out), _ptr(block_tables), max_blocks_per_seq,
-              _ptr(context_lens), batch, num_q_heads, max_context_len, float(scale),
-              _ptr(workspace), int(workspace_bytes), _stream(stream)), name)
-
-
 def pa_decode(handle, layer, q, out, block_tables, max_blocks_per_seq, context_lens, batch,
               num_q_heads, max_context_len, scale, workspace, workspace_bytes, stream=None):
-    _decode_call("pa_decode", handle, layer, q, out, block_tables, max_blocks_per_seq,
-                 context_lens, batch, num_q_heads, max_context_len, scale, workspace,
-                 workspace_bytes, stream)
+    _check(load_library().pa_decode(handle, layer, _ptr(q), _ptr(out), _ptr(block_tables),
+                                    max_blocks_per_seq, _ptr(context_lens), batch, num_q_heads,
+                                    max_context_len, float(scale), _ptr(workspace),
+                                    int(workspace_bytes), _stream(stream)), "pa_decode")
 
 
-def pa_decode_partial(handle, layer, q, out, block_tables, max_blocks_per_seq, context_lens,
-                      batch, num_q_heads, max_context_len, scale, workspace, workspace_bytes,
-                      stream=None):
-    _decode_call("pa_decode_partial", handle, layer, q, out, block_tables, max_blocks_per_seq,
+def _new_kv_call(name, handle, layer, q, k_new, v_new, out, block_tables, max_blocks_per_seq,
                  context_lens, batch, num_q_heads, max_context_len, scale, workspace,
-                 workspace_bytes, stream)
+                 workspace_bytes, stream):
+    fn = getattr(load_library(), name)
+    _check(fn(handle, layer, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(block_tables),
+              max_blocks_per_seq, _ptr(context_lens), batch, num_q_heads, max_context_len,
+              float(scale), _ptr(workspace), int(workspace_bytes), _stream(stream)), name)
+
+
+def pa_append_decode(handle, layer, q, k_new, v_new, out, block_tables, max_blocks_per_seq,
+                     context_lens, batch, num_q_heads, max_context_len, scale, workspace,
+                     workspace_bytes, stream=None):
+    _new_kv_call("pa_append_decode", handle, layer, q, k_new, v_new, out, block_tables,
+                 max_blocks_per_seq, context_lens, batch, num_q_heads, max_context_len, scale,
+                 workspace, workspace_bytes, stream)
+
+
+def pa_decode_partial(handle, layer, q, k_new, v_new, out, block_tables, max_blocks_per_seq,
+                      context_lens, batch, num_q_heads, max_context_len, scale, workspace,
+                      workspace_bytes, stream=None):
+    _new_kv_call("pa_decode_partial", handle, layer, q, k_new, v_new, out, block_tables,
+                 max_blocks_per_seq, context_lens, batch, num_q_heads, max_context_len, scale,
+                 workspace, workspace_bytes, stream)
 
 
 def pa_decode_merge(handle, out, context_lens, batch, num_q_heads, max_context_len, workspace,
@@ -254,16 +267,26 @@ class Pool:
         return batch, hq, int(block_tables.shape[1])
 
     def decode(self, layer, q, out, block_tables, context_lens, max_context_len, scale,
-               workspace=None, stream=None, phases=False):
+               workspace=None, stream=None, phases=False, k_new=None, v_new=None):
+        """pa_decode, or pa_append_decode when k_new/v_new ([batch, Hkv, d]) are given;
+        phases=True issues the same work as pa_decode_partial + pa_decode_merge."""
         batch, hq, width = self._check_decode(q, out, block_tables, context_lens, max_context_len)
+        if (k_new is None) != (v_new is None):
+            raise ValueError("k_new and v_new go together")
+        if k_new is not None:
+            _expect(k_new, torch.float16, (batch, self.num_kv_heads, self.head_dim), "k_new")
+            _expect(v_new, torch.float16, (batch, self.num_kv_heads, self.head_dim), "v_new")
         if workspace is None:
             workspace = self.workspace(batch, hq, max_context_len, q.device)
         ws, ws_bytes = workspace
         if phases:
-            pa_decode_partial(self.handle, layer, q, out, block_tables, width, context_lens, batch,
-                              hq, max_context_len, scale, ws, ws_bytes, stream)
+            pa_decode_partial(self.handle, layer, q, k_new, v_new, out, block_tables, width,
+                              context_lens, batch, hq, max_context_len, scale, ws, ws_bytes, stream)
             pa_decode_merge(self.handle, out, context_lens, batch, hq, max_context_len, ws,
                             ws_bytes, stream)
+        elif k_new is not None:
+            pa_append_decode(self.handle, layer, q, k_new, v_new, out, block_tables, width,
+                             context_lens, batch, hq, max_context_len, scale, ws, ws_bytes, stream)
         else:
             pa_decode(self.handle, layer, q, out, block_tables, width, context_lens, batch, hq,
                       max_context_len, scale, ws, ws_bytes, stream)

@@ -26,10 +26,11 @@ using pa::kHeadDim;
 using pa::kMaxSplitTokens;
 using pa::kSplitQuantum;
 
-// Work-groups the split plan aims for: MI355X has 256 compute units and the
-// split kernel keeps two work-groups resident per unit; four rounds of those
-// give the dispatcher room to balance ragged batches.
-constexpr int64_t kTargetWorkGroups = 256 * 2 * 4;
+// Work-groups the split plan aims for: one per compute unit of MI355X (256).
+// Longer splits keep each wave's load pipeline full for longer and avoid the
+// merge; measured on the 8B geometry, splits that give about one
+// work-group per unit were the fastest at batch 1, 8 and 32.
+constexpr int64_t kTargetWorkGroups = 256;
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -91,7 +92,8 @@ pa_status check_decode_shape(const pa_pool *pool, int32_t batch, int32_t num_q_h
     return PA_OK;
 }
 
-pa_status fill_decode_args(pa_pool *pool, int32_t layer, const void *q, void *out, const int32_t *tables,
+pa_status fill_decode_args(pa_pool *pool, int32_t layer, const void *q, const void *k_new, const void *v_new,
+                           void *out, const int32_t *tables,
                            int32_t max_blocks, const int32_t *ctx_lens, int32_t batch, int32_t num_q_heads,
                            int32_t max_ctx, float scale, void *ws, size_t ws_bytes, pa::DecodeArgs *a,
                            Plan *plan_out) {
@@ -104,6 +106,8 @@ pa_status fill_decode_args(pa_pool *pool, int32_t layer, const void *q, void *ou
         return PA_OK;
     }
     if (!q || !out || !ctx_lens || (max_ctx > 0 && !tables)) return PA_ERR_INVALID_ARG;
+    if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_INVALID_ARG;
+    if (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))) return PA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(tables, 4) || !aligned(ctx_lens, 4))
         return PA_ERR_INVALID_ARG;
     const Plan plan = make_plan(pool, batch, num_q_heads, max_ctx);
@@ -116,6 +120,8 @@ pa_status fill_decode_args(pa_pool *pool, int32_t layer, const void *q, void *ou
     a->k_layer = static_cast<const uint16_t *>(pool->k) + layer_off;
     a->v_layer = static_cast<const uint16_t *>(pool->v) + layer_off;
     a->q = static_cast<const uint16_t *>(q);
+    a->k_new = static_cast<const uint16_t *>(k_new);
+    a->v_new = static_cast<const uint16_t *>(v_new);
     a->tables = tables;
     a->ctx_lens = ctx_lens;
     a->out = static_cast<uint16_t *>(out);
@@ -195,14 +201,15 @@ size_t pa_decode_workspace_bytes(const pa_pool *pool, int32_t batch, int32_t num
     return make_plan(pool, batch, num_q_heads, max_context_len).workspace;
 }
 
-pa_status pa_decode_partial(pa_pool *pool, int32_t layer, const void *q_dev, void *out_dev,
-                            const int32_t *block_tables_dev, int32_t max_blocks_per_seq,
-                            const int32_t *context_lens_dev, int32_t batch, int32_t num_q_heads,
-                            int32_t max_context_len, float scale, void *workspace_dev, size_t workspace_bytes,
-                            hipStream_t stream) {
+pa_status pa_decode_partial(pa_pool *pool, int32_t layer, const void *q_dev, const void *k_new_dev,
+                            const void *v_new_dev, void *out_dev, const int32_t *block_tables_dev,
+                            int32_t max_blocks_per_seq, const int32_t *context_lens_dev, int32_t batch,
+                            int32_t num_q_heads, int32_t max_context_len, float scale, void *workspace_dev,
+                            size_t workspace_bytes, hipStream_t stream) {
     pa::DecodeArgs a{};
     Plan plan{};
-    pa_status st = fill_decode_args(pool, layer, q_dev, out_dev, block_tables_dev, max_blocks_per_seq,
+    pa_status st = fill_decode_args(pool, layer, q_dev, k_new_dev, v_new_dev, out_dev, block_tables_dev,
+                                    max_blocks_per_seq,
                                     context_lens_dev, batch, num_q_heads, max_context_len, scale, workspace_dev,
                                     workspace_bytes, &a, &plan);
     if (st != PA_OK || batch == 0) return st;
@@ -236,13 +243,27 @@ pa_status pa_decode_merge(pa_pool *pool, void *out_dev, const int32_t *context_l
     return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_append_decode(pa_pool *pool, int32_t layer, const void *q_dev, const void *k_new_dev,
+                           const void *v_new_dev, void *out_dev, const int32_t *block_tables_dev,
+                           int32_t max_blocks_per_seq, const int32_t *context_lens_dev, int32_t batch,
+                           int32_t num_q_heads, int32_t max_context_len, float scale, void *workspace_dev,
+                           size_t workspace_bytes, hipStream_t stream) {
+    if (!k_new_dev || !v_new_dev) return PA_ERR_INVALID_ARG;
+    pa_status st = pa_decode_partial(pool, layer, q_dev, k_new_dev, v_new_dev, out_dev, block_tables_dev,
+                                     max_blocks_per_seq, context_lens_dev, batch, num_q_heads, max_context_len,
+                                     scale, workspace_dev, workspace_bytes, stream);
+    if (st != PA_OK || batch == 0) return st;
+    return pa_decode_merge(pool, out_dev, context_lens_dev, batch, num_q_heads, max_context_len, workspace_dev,
+                           workspace_bytes, stream);
+}
+
 pa_status pa_decode(pa_pool *pool, int32_t layer, const void *q_dev, void *out_dev,
                     const int32_t *block_tables_dev, int32_t max_blocks_per_seq, const int32_t *context_lens_dev,
                     int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale,
                     void *workspace_dev, size_t workspace_bytes, hipStream_t stream) {
-    pa_status st = pa_decode_partial(pool, layer, q_dev, out_dev, block_tables_dev, max_blocks_per_seq,
-                                     context_lens_dev, batch, num_q_heads, max_context_len, scale, workspace_dev,
-                                     workspace_bytes, stream);
+    pa_status st = pa_decode_partial(pool, layer, q_dev, nullptr, nullptr, out_dev, block_tables_dev,
+                                     max_blocks_per_seq, context_lens_dev, batch, num_q_heads, max_context_len,
+                                     scale, workspace_dev, workspace_bytes, stream);
     if (st != PA_OK || batch == 0) return st;
     return pa_decode_merge(pool, out_dev, context_lens_dev, batch, num_q_heads, max_context_len, workspace_dev,
                            workspace_bytes, stream);

@@ -40,6 +40,8 @@ struct DecodeArgs {
     const uint16_t *k_layer;      // this layer's K base
     const uint16_t *v_layer;      // this layer's V base
     const uint16_t *q;            // [batch][num_q_heads][kHeadDim]
+    const uint16_t *k_new;        // [batch][num_kv_heads][kHeadDim] newest token's K, or null
+    const uint16_t *v_new;        // [batch][num_kv_heads][kHeadDim] newest token's V, or null
     const int32_t *tables;        // [batch][max_blocks]
     const int32_t *ctx_lens;      // [batch]
     uint16_t *out;                // [batch][num_q_heads][kHeadDim] (single-split launches)

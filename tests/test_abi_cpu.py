@@ -112,6 +112,13 @@ def test_decode_validation(lib, pool):
     assert _decode(lib, pool, ws=None) == pa.PA_ERR_WORKSPACE
     assert _decode(lib, pool, ws=FAKE + 16) == pa.PA_ERR_INVALID_ARG        # workspace alignment
     assert lib.pa_decode_merge(pool, FAKE, FAKE, 4, 32, 256, FAKE, need - 1, None) == pa.PA_ERR_WORKSPACE
+    # the appending variant needs both new-token tensors, aligned
+    assert lib.pa_append_decode(pool, 0, FAKE, None, FAKE, FAKE, FAKE, 16, FAKE, 4, 32, 256, 0.088,
+                                FAKE, 1 << 30, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_append_decode(pool, 0, FAKE, FAKE + 8, FAKE, FAKE, FAKE, 16, FAKE, 4, 32, 256,
+                                0.088, FAKE, 1 << 30, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_partial(pool, 0, FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, 4, 32, 256, 0.088,
+                                 FAKE, 1 << 30, None) == pa.PA_ERR_INVALID_ARG
 
 
 def test_split_plan_and_workspace(lib, pool, monkeypatch):

@@ -214,3 +214,53 @@ def test_config3_sampled_layers_and_sequences():
         out = st.decode(layer, phases=True).cpu().numpy()[seqs]
         compare(f"config3 layer{layer} seqs{list(seqs)}", out, st.reference(layer, seqs))
     st.close()
+
+
+@pytest.mark.parametrize("split", [None, 64, 256])
+def test_append_decode_writes_the_newest_token_and_attends_to_it(monkeypatch, split):
+    """pa_append_decode == pa_write_kv(newest slots) + pa_decode, with fresh K/V
+    for each sequence's newest position (the pool holds other values there)."""
+    if split:
+        monkeypatch.setenv("PA_SPLIT_TOKENS", str(split))
+    lens = [1, 16, 17, 100, 257, 1000, 0, 4097]
+    w = workloads.custom(lens, seed=21)
+    st = Staged(w)
+    _poison_tails(st)
+    q, tables, ids, k, v = st.host[0]
+    rng = np.random.default_rng(5)
+    k_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+    v_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+    qd, td = st.dev[0]
+    out = torch.empty_like(qd)
+    st.pool.decode(0, qd, out, td, st.lens, w.max_context_len, w.scale,
+                   k_new=torch.from_numpy(k_new).cuda(), v_new=torch.from_numpy(v_new).cuda())
+    torch.cuda.synchronize()
+    # the oracle sees the new values in the newest slots
+    k2, v2 = k.copy(), v.copy()
+    newest = []
+    for s, c in enumerate(lens):
+        if c == 0:
+            continue
+        blk = tables[s, (c - 1) // 16]
+        r = np.searchsorted(ids, blk)
+        k2[r, (c - 1) % 16] = k_new[s]
+        v2[r, (c - 1) % 16] = v_new[s]
+        newest.append((s, blk, (c - 1) % 16))
+    st.host[0] = (q, tables, ids, k2, v2)
+    compare(f"append split={split}", out, st.reference(0))
+    # the pool now holds them (bit-exact), in the documented layout
+    kp = st.pool.k[0].cpu().numpy()
+    vp = st.pool.v[0].cpu().numpy()
+    for s, blk, off in newest:
+        assert np.array_equal(kp[blk, :, off, :].view(np.uint16), k_new[s].view(np.uint16))
+        assert np.array_equal(vp[blk, :, off, :].view(np.uint16), v_new[s].view(np.uint16))
+    # and a read-only decode afterwards gives the same bits
+    again = st.decode(0)
+    assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+    # phases: partial (with new K/V) + merge give the same bits too
+    out3 = torch.empty_like(qd)
+    st.pool.decode(0, qd, out3, td, st.lens, w.max_context_len, w.scale, phases=True,
+                   k_new=torch.from_numpy(k_new).cuda(), v_new=torch.from_numpy(v_new).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(out3.view(torch.int16), out.view(torch.int16))
+    st.close()
