@@ -185,6 +185,49 @@ pa_status pa_decode_merge(pa_pool *pool, void *out_dev, const int32_t *context_l
                           int32_t batch, int32_t num_q_heads, int32_t max_context_len,
                           const void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Planned decode: the schedule is built on the host ----------------
+ * An engine's scheduler keeps every request's length on the host (the pages'
+ * block-table program tracks `lengths` next to the tables: "vLLM
+ * Architecture and Installation", Example 3).  From those lengths
+ * pa_decode_plan cuts each sequence's context into pieces so that about 256
+ * work-groups (one per MI355X compute unit) do near-equal work, orders the
+ * pieces longest first, and lists the sequences that were cut (only those are
+ * merged).  One plan serves every layer of a step.  For a batch of equal
+ * lengths the plan is one piece per sequence and no merge. */
+typedef struct {
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t max_context_len;  /* largest context in the plan */
+    int32_t num_items;        /* pieces (work-groups per KV head) */
+    int32_t num_merges;       /* sequences cut into more than one piece */
+    int32_t num_slots;        /* partial records per query head */
+    int32_t max_piece_tokens; /* longest piece */
+    size_t plan_bytes;        /* bytes of the serialised plan */
+    size_t workspace_bytes;   /* device workspace pa_decode_run needs (0: none) */
+} pa_plan_info;
+
+/* Builds the schedule for host-side context lengths (int32 [batch], >= 0).
+ * Always fills *info.  With plan_host == NULL it only sizes the plan; else it
+ * writes info->plan_bytes bytes into plan_host (PA_ERR_WORKSPACE if
+ * plan_host_bytes is smaller).  The caller copies those bytes to a 16-byte
+ * aligned device buffer for pa_decode_run.  Host-only: enqueues nothing. */
+pa_status pa_decode_plan(const pa_pool *pool, const int32_t *context_lens_host, int32_t batch,
+                         int32_t num_q_heads, void *plan_host, size_t plan_host_bytes,
+                         pa_plan_info *info);
+
+/* One decode step of one layer on a planned schedule: the plan's pieces, then
+ * the merge of the cut sequences.  k_new_dev/v_new_dev (both or neither)
+ * append the newest token as pa_append_decode does.  q, out, tables, scale and
+ * stream as pa_decode; the context lengths come from the plan, whose device
+ * copy plan_dev must stay unchanged until the work completes.  A damaged plan
+ * cannot make the kernels access memory outside the given buffers, but its
+ * results are unspecified. */
+pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info,
+                        const void *plan_dev, const void *q_dev, const void *k_new_dev,
+                        const void *v_new_dev, void *out_dev, const int32_t *block_tables_dev,
+                        int32_t max_blocks_per_seq, float scale, void *workspace_dev,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* Static English text for a status code. */
 const char *pa_status_string(pa_status status);
 

@@ -25,7 +25,8 @@ PA_F16 = 1
 
 EXPORTS = ("pa_pool_bytes", "pa_pool_create", "pa_pool_destroy", "pa_write_kv",
            "pa_decode_split_tokens", "pa_decode_workspace_bytes", "pa_decode",
-           "pa_append_decode", "pa_decode_partial", "pa_decode_merge", "pa_status_string")
+           "pa_append_decode", "pa_decode_partial", "pa_decode_merge", "pa_decode_plan",
+           "pa_decode_run", "pa_status_string")
 
 
 class PaError(RuntimeError):
@@ -38,6 +39,14 @@ class PoolDesc(ctypes.Structure):
     _fields_ = [("num_layers", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("max_context_len", ctypes.c_int32), ("num_items", ctypes.c_int32),
+                ("num_merges", ctypes.c_int32), ("num_slots", ctypes.c_int32),
+                ("max_piece_tokens", ctypes.c_int32), ("plan_bytes", ctypes.c_size_t),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -75,6 +84,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                        ctypes.c_size_t, _P]
     lib.pa_decode_merge.restype = _I
     lib.pa_decode_merge.argtypes = [_P, _P, _P, _I, _I, _I, _P, ctypes.c_size_t, _P]
+    lib.pa_decode_plan.restype = _I
+    lib.pa_decode_plan.argtypes = [_P, _P, _I, _I, _P, ctypes.c_size_t, ctypes.POINTER(PlanInfo)]
+    lib.pa_decode_run.restype = _I
+    lib.pa_decode_run.argtypes = [_P, _I, ctypes.POINTER(PlanInfo), _P, _P, _P, _P, _P, _P, _I,
+                                  ctypes.c_float, _P, ctypes.c_size_t, _P]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [_I]
     _lib = lib
@@ -189,6 +203,41 @@ def pa_decode_merge(handle, out, context_lens, batch, num_q_heads, max_context_l
            "pa_decode_merge")
 
 
+def pa_decode_plan(handle, context_lens_host, num_q_heads):
+    """Host schedule for int32 host lengths: returns (PlanInfo, int32 numpy plan)."""
+    import numpy as np
+
+    lens = np.ascontiguousarray(context_lens_host, dtype=np.int32)
+    info = PlanInfo()
+    lib = load_library()
+    ptr = lens.ctypes.data_as(_P) if lens.size else None
+    _check(lib.pa_decode_plan(handle, ptr, int(lens.shape[0]), num_q_heads, None, 0,
+                              ctypes.byref(info)), "pa_decode_plan")
+    plan = np.zeros(max(1, info.plan_bytes // 4), dtype=np.int32)
+    _check(lib.pa_decode_plan(handle, ptr, int(lens.shape[0]), num_q_heads,
+                              plan.ctypes.data_as(_P), plan.nbytes, ctypes.byref(info)),
+           "pa_decode_plan")
+    return info, plan
+
+
+def pa_decode_run(handle, layer, info, plan_dev, q, k_new, v_new, out, block_tables,
+                  max_blocks_per_seq, scale, workspace, workspace_bytes, stream=None):
+    _check(load_library().pa_decode_run(handle, layer, ctypes.byref(info), _ptr(plan_dev), _ptr(q),
+                                        _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(block_tables),
+                                        max_blocks_per_seq, float(scale), _ptr(workspace),
+                                        int(workspace_bytes), _stream(stream)), "pa_decode_run")
+
+
+class Plan:
+    """A host schedule (pa_decode_plan) and its device copy."""
+
+    def __init__(self, handle, context_lens_host, num_q_heads, device="cuda"):
+        self.info, self.host = pa_decode_plan(handle, context_lens_host, num_q_heads)
+        self.dev = torch.from_numpy(self.host).to(device)
+        n = self.info.workspace_bytes
+        self.workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
 # ---------------------------------------------------------------------------
 # a torch-owning convenience wrapper
 # ---------------------------------------------------------------------------
@@ -245,6 +294,26 @@ class Pool:
         self.write(layer, k_blocks.reshape(n, self.num_kv_heads, self.head_dim).contiguous(),
                    v_blocks.reshape(n, self.num_kv_heads, self.head_dim).contiguous(),
                    slots.to(torch.int32).contiguous(), stream)
+
+    def plan(self, context_lens_host, num_q_heads=None):
+        return Plan(self.handle, context_lens_host, num_q_heads or 4 * self.num_kv_heads,
+                    self.k.device)
+
+    def run(self, layer, plan, q, out, block_tables, scale, k_new=None, v_new=None, stream=None):
+        """pa_decode_run on a Plan from plan()."""
+        batch = plan.info.batch
+        _expect(q, torch.float16, (batch, plan.info.num_q_heads, self.head_dim), "q")
+        _expect(out, torch.float16, (batch, plan.info.num_q_heads, self.head_dim), "out")
+        _expect(block_tables, torch.int32, (batch, block_tables.shape[1]), "block_tables")
+        if (k_new is None) != (v_new is None):
+            raise ValueError("k_new and v_new go together")
+        if k_new is not None:
+            _expect(k_new, torch.float16, (batch, self.num_kv_heads, self.head_dim), "k_new")
+            _expect(v_new, torch.float16, (batch, self.num_kv_heads, self.head_dim), "v_new")
+        pa_decode_run(self.handle, layer, plan.info, plan.dev, q, k_new, v_new, out, block_tables,
+                      int(block_tables.shape[1]), scale, plan.workspace, plan.info.workspace_bytes,
+                      stream)
+        return out
 
     def split_tokens(self, batch, num_q_heads, max_context_len):
         return pa_decode_split_tokens(self.handle, batch, num_q_heads, max_context_len)

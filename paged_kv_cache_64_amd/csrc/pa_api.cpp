@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <new>
+#include <vector>
 
 #include "pa_internal.h"
 
@@ -140,9 +141,154 @@ pa_status fill_decode_args(pa_pool *pool, int32_t layer, const void *q, const vo
     return PA_OK;
 }
 
+// ---- host-side schedule for pa_decode_plan / pa_decode_run --------------
+// Pieces are cut so that about kTargetWorkGroups work-groups do near-equal
+// work: M = ceil(total_blocks / (kTargetWorkGroups / Hkv)) blocks per piece,
+// clamped to [kWaves, kMaxSplitTokens / kBlockSize]; a sequence of n blocks
+// becomes ceil(n / M) pieces of near-equal length, and the pieces are
+// dispatched longest first.
+struct PlanItem {
+    int32_t s, t_begin, t_end, ctx, slot;
+};
+
+size_t planned_workspace(int64_t slots, int32_t num_q_heads, size_t *o_bytes) {
+    const size_t recs = static_cast<size_t>(slots) * num_q_heads;
+    *o_bytes = round_up(static_cast<int64_t>(recs * kHeadDim * sizeof(float)), 256);
+    return recs ? *o_bytes + recs * 2 * sizeof(float) : 0;
+}
+
 }  // namespace
 
 extern "C" {
+
+pa_status pa_decode_plan(const pa_pool *pool, const int32_t *context_lens_host, int32_t batch, int32_t num_q_heads,
+                         void *plan_host, size_t plan_host_bytes, pa_plan_info *info) {
+    try {
+        if (!pool || !info || batch < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
+        if (batch > 0 && !context_lens_host) return PA_ERR_INVALID_ARG;
+        if (num_q_heads % pool->desc.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+        if (num_q_heads != kGroup * pool->desc.num_kv_heads) return PA_ERR_UNSUPPORTED;
+        if (batch > (1 << 24)) return PA_ERR_UNSUPPORTED;
+        int64_t total_blocks = 0;
+        int32_t max_ctx = 0;
+        for (int32_t s = 0; s < batch; ++s) {
+            if (context_lens_host[s] < 0) return PA_ERR_INVALID_ARG;
+            total_blocks += (context_lens_host[s] + kBlockSize - 1) / kBlockSize;
+            max_ctx = std::max(max_ctx, context_lens_host[s]);
+        }
+        const int64_t items_target = std::max<int64_t>(1, kTargetWorkGroups / pool->desc.num_kv_heads);
+        const int64_t piece = std::min<int64_t>(kMaxSplitTokens / kBlockSize,
+                                                std::max<int64_t>(pa::kWaves, (total_blocks + items_target - 1) / items_target));
+        std::vector<PlanItem> items;
+        std::vector<int32_t> merges;
+        items.reserve(static_cast<size_t>(batch) + static_cast<size_t>(total_blocks / piece) + 1);
+        int32_t slots = 0;
+        for (int32_t s = 0; s < batch; ++s) {
+            const int32_t ctx = context_lens_host[s];
+            const int64_t nb = (ctx + kBlockSize - 1) / kBlockSize;
+            const int64_t np = nb == 0 ? 1 : (nb + piece - 1) / piece;
+            if (np == 1) {
+                items.push_back({s, 0, ctx, ctx, -1});
+                continue;
+            }
+            const int64_t base = nb / np, extra = nb % np;
+            int64_t b0 = 0;
+            merges.insert(merges.end(), {s, slots, static_cast<int32_t>(np), 0});
+            for (int64_t i = 0; i < np; ++i) {
+                const int64_t b1 = b0 + base + (i < extra ? 1 : 0);
+                items.push_back({s, static_cast<int32_t>(b0 * kBlockSize),
+                                 static_cast<int32_t>(std::min<int64_t>(ctx, b1 * kBlockSize)), ctx, slots++});
+                b0 = b1;
+            }
+        }
+        std::stable_sort(items.begin(), items.end(), [](const PlanItem &x, const PlanItem &y) {
+            return (x.t_end - x.t_begin) > (y.t_end - y.t_begin);
+        });
+        int32_t longest = 0;
+        for (const PlanItem &it : items) longest = std::max(longest, it.t_end - it.t_begin);
+        const size_t n_items = items.size(), n_merges = merges.size() / pa::kMergeInts;
+        if (n_items > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+        pa_plan_info inf{};
+        inf.batch = batch;
+        inf.num_q_heads = num_q_heads;
+        inf.max_context_len = max_ctx;
+        inf.num_items = static_cast<int32_t>(n_items);
+        inf.num_merges = static_cast<int32_t>(n_merges);
+        inf.num_slots = slots;
+        inf.max_piece_tokens = longest;
+        inf.plan_bytes = sizeof(int32_t) * (pa::kPlanHeader + pa::kItemInts * n_items + pa::kMergeInts * n_merges);
+        size_t o_bytes = 0;
+        inf.workspace_bytes = planned_workspace(slots, num_q_heads, &o_bytes);
+        *info = inf;
+        if (!plan_host) return PA_OK;  // size query
+        if (plan_host_bytes < inf.plan_bytes) return PA_ERR_WORKSPACE;
+        int32_t *p = static_cast<int32_t *>(plan_host);
+        const int32_t header[pa::kPlanHeader] = {pa::kPlanMagic, batch, num_q_heads, inf.num_items,
+                                                 inf.num_merges, slots, max_ctx, 0};
+        std::copy(header, header + pa::kPlanHeader, p);
+        p += pa::kPlanHeader;
+        for (const PlanItem &it : items) {
+            const int32_t rec[pa::kItemInts] = {it.s, it.t_begin, it.t_end, it.ctx, it.slot, 0, 0, 0};
+            std::copy(rec, rec + pa::kItemInts, p);
+            p += pa::kItemInts;
+        }
+        std::copy(merges.begin(), merges.end(), p);
+        return PA_OK;
+    } catch (...) {
+        return PA_ERR_INVALID_ARG;
+    }
+}
+
+pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, const void *plan_dev,
+                        const void *q_dev, const void *k_new_dev, const void *v_new_dev, void *out_dev,
+                        const int32_t *block_tables_dev, int32_t max_blocks_per_seq, float scale,
+                        void *workspace_dev, size_t workspace_bytes, hipStream_t stream) {
+    if (!pool || !info || layer < 0 || layer >= pool->desc.num_layers) return PA_ERR_INVALID_ARG;
+    if (info->batch < 0 || info->num_q_heads != kGroup * pool->desc.num_kv_heads) return PA_ERR_INVALID_ARG;
+    if (info->batch == 0 || info->num_items == 0) return PA_OK;
+    if (!plan_dev || !q_dev || !out_dev || !aligned(plan_dev, 16) || !aligned(q_dev, 16) || !aligned(out_dev, 16))
+        return PA_ERR_INVALID_ARG;
+    if ((k_new_dev == nullptr) != (v_new_dev == nullptr)) return PA_ERR_INVALID_ARG;
+    if (k_new_dev && (!aligned(k_new_dev, 16) || !aligned(v_new_dev, 16))) return PA_ERR_INVALID_ARG;
+    if (info->max_context_len > 0 && (!block_tables_dev || !aligned(block_tables_dev, 4))) return PA_ERR_INVALID_ARG;
+    if (max_blocks_per_seq < 0 ||
+        static_cast<int64_t>(info->max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlockSize)
+        return PA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+    size_t o_bytes = 0;
+    const size_t need = planned_workspace(info->num_slots, info->num_q_heads, &o_bytes);
+    if (need > 0 && (!workspace_dev || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace_dev, 256)) return PA_ERR_INVALID_ARG;
+    const size_t layer_off = static_cast<size_t>(layer) *
+                             pa::layer_elems(pool->desc.num_blocks, pool->desc.num_kv_heads);
+    pa::DecodeArgs a{};
+    a.k_layer = static_cast<const uint16_t *>(pool->k) + layer_off;
+    a.v_layer = static_cast<const uint16_t *>(pool->v) + layer_off;
+    a.q = static_cast<const uint16_t *>(q_dev);
+    a.k_new = static_cast<const uint16_t *>(k_new_dev);
+    a.v_new = static_cast<const uint16_t *>(v_new_dev);
+    a.tables = block_tables_dev;
+    a.out = static_cast<uint16_t *>(out_dev);
+    a.o_part = need ? static_cast<float *>(workspace_dev) : nullptr;
+    a.ml_part = need ? reinterpret_cast<float *>(static_cast<char *>(workspace_dev) + o_bytes) : nullptr;
+    a.batch = info->batch;
+    a.num_q_heads = info->num_q_heads;
+    a.num_kv_heads = pool->desc.num_kv_heads;
+    a.num_blocks = pool->desc.num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.max_ctx = info->max_context_len;
+    a.split_tokens = kMaxSplitTokens;
+    a.max_splits = 1;
+    a.scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    a.items = static_cast<const int32_t *>(plan_dev) + pa::kPlanHeader;
+    a.merges = a.items + static_cast<size_t>(pa::kItemInts) * info->num_items;
+    a.num_items = info->num_items;
+    a.num_merges = info->num_merges;
+    a.num_slots = info->num_slots;
+    if (pa::launch_decode_partial(a, stream) != hipSuccess) return PA_ERR_HIP;
+    if (info->num_merges > 0 && pa::launch_decode_merge_planned(a, stream) != hipSuccess) return PA_ERR_HIP;
+    return PA_OK;
+}
 
 size_t pa_pool_bytes(const pa_pool_desc *desc) {
     if (!desc_ok(desc)) return 0;

@@ -56,10 +56,28 @@ struct DecodeArgs {
     int32_t split_tokens;         // multiple of kSplitQuantum
     int32_t max_splits;           // ceil(max_ctx / split_tokens)
     float scale_log2e;            // scale * log2(e)
+    // Host-planned schedule (null for the fixed-split grid): items of 8 int32
+    // {seq, t_begin, t_end, ctx, slot (-1: direct output), 0, 0, 0} and merges
+    // of 4 int32 {seq, first slot, pieces, 0}; partial record of query head h
+    // of a piece = slot * num_q_heads + h.
+    const int32_t *items;
+    const int32_t *merges;
+    int32_t num_items;
+    int32_t num_merges;
+    int32_t num_slots;
 };
+
+// Serialised host plan: a header of kPlanHeader int32, then the items, then
+// the merges.
+constexpr int kPlanHeader = 8;
+constexpr int kItemInts = 8;
+constexpr int kMergeInts = 4;
+constexpr int32_t kPlanMagic = 0x50414e31;  // "PAN1"
+
 
 hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace pa

@@ -141,9 +141,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
 // ---------------------------------------------------------------------------
 template <int NBUF>
 __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
-    const int split = blockIdx.x;
     const int g = blockIdx.y;
-    const int s = blockIdx.z;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     const int lane = tid & 63;
@@ -156,22 +154,47 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     __shared__ float l_lds[kWaves][4];
     __shared__ float o_lds[kWaves][4][kGroup][kHeadDim];
 
-    const int ctx = clamp_ctx(a.ctx_lens[s], a.max_ctx, a.max_blocks);
-    const int t_begin = split * a.split_tokens;
+    // This work-group's piece of one sequence: tokens [t_begin, t_end) of
+    // sequence s (context ctx), and where its result goes -- the final F16
+    // output (direct) or partial record rec_base + h * rec_stride of query
+    // head h.
+    int s, ctx, t_begin, t_end;
+    bool direct;
+    int64_t rec_base, rec_stride;
+    if (a.items != nullptr) {
+        // Plan entries are clamped so a damaged plan cannot index outside
+        // q, out, the tables or the workspace.
+        const int32_t *it = a.items + kItemInts * static_cast<size_t>(blockIdx.x);
+        s = min(max(it[0], 0), a.batch - 1);
+        ctx = min(max(it[3], 0), a.max_blocks * kBlockSize);
+        t_begin = max(it[1], 0);
+        t_end = min(it[2], ctx);
+        const int slot = min(it[4], a.num_slots - 1);
+        direct = slot < 0;
+        rec_base = static_cast<int64_t>(slot) * a.num_q_heads;
+        rec_stride = 1;
+    } else {
+        const int split = blockIdx.x;
+        s = blockIdx.z;
+        ctx = clamp_ctx(a.ctx_lens[s], a.max_ctx, a.max_blocks);
+        t_begin = split * a.split_tokens;
+        t_end = min(ctx, t_begin + a.split_tokens);
+        direct = a.max_splits == 1;
+        rec_base = static_cast<int64_t>(s) * a.num_q_heads * a.max_splits + split;
+        rec_stride = a.max_splits;
+    }
     const int head0 = g * kGroup;
-    const bool single = a.max_splits == 1;
 
-    if (t_begin >= ctx) {
-        // Nothing to attend to.  With one split this work-group owns the
-        // output row, which is zero for an empty context.
-        if (single && split == 0) {
+    if (t_begin >= t_end) {
+        // Nothing to attend to.  A direct piece that starts at 0 owns an
+        // empty context, whose output row is zero.
+        if (direct && t_begin == 0) {
             const int h = tid >> 6, d0 = (tid & 63) * 2;
             uint16_t *o = a.out + (static_cast<size_t>(s) * a.num_q_heads + head0 + h) * kHeadDim + d0;
             *reinterpret_cast<uint32_t *>(o) = 0u;
         }
         return;
     }
-    const int t_end = min(ctx, t_begin + a.split_tokens);
     const int b_begin = t_begin / kBlockSize;
     const int b_end = (t_end + kBlockSize - 1) / kBlockSize;
     const int per_wave = (b_end - b_begin + kWaves - 1) / kWaves;
@@ -294,7 +317,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         sc *= a.scale_log2e;
 
         // ---- mask the tail of the sequence's last block ----
-        const int valid = ctx - b * kBlockSize;  // >= 1
+        const int valid = t_end - b * kBlockSize;  // >= 1; pieces end on block edges or at ctx
         const bool partial = valid < kBlockSize;
         if (partial && kt >= valid) sc = -INFINITY;
 
@@ -397,13 +420,13 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         O1 += wgt * s1;
     }
     const size_t row = static_cast<size_t>(s) * a.num_q_heads + head0 + h;
-    if (single) {
+    if (direct) {
         const _Float16 r0 = static_cast<_Float16>(O0 / L);
         const _Float16 r1 = static_cast<_Float16>(O1 / L);
         h2 pr = {r0, r1};
         *reinterpret_cast<h2 *>(a.out + row * kHeadDim + d0) = pr;
     } else {
-        const size_t slot = row * a.max_splits + split;
+        const size_t slot = static_cast<size_t>(rec_base + static_cast<int64_t>(head0 + h) * rec_stride);
         *reinterpret_cast<float2 *>(a.o_part + slot * kHeadDim + d0) = make_float2(O0, O1);
         if (d0 == 0) *reinterpret_cast<float2 *>(a.ml_part + slot * 2) = make_float2(M, L);
     }
@@ -439,6 +462,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     *reinterpret_cast<_Float16 *>(out) = r;
 }
 
+// ---------------------------------------------------------------------------
+// decode_merge_planned: grid (merge entry, query-head pair); the pieces of
+// sequence s are records first .. first + n - 1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a) {
+    const int32_t *m = a.merges + kMergeInts * static_cast<size_t>(blockIdx.x);
+    const int s = min(max(m[0], 0), a.batch - 1);
+    const int first = max(m[1], 0);
+    const int n = min(m[2], a.num_slots - first);
+    const int h = blockIdx.y * 2 + (threadIdx.x >> 7);
+    const int d = threadIdx.x & 127;
+    if (h >= a.num_q_heads) return;
+    uint16_t *out = a.out + (static_cast<size_t>(s) * a.num_q_heads + h) * kHeadDim + d;
+    if (n <= 0) {
+        *out = 0;
+        return;
+    }
+    float M = -INFINITY;
+    for (int i = 0; i < n; ++i) M = fmaxf(M, a.ml_part[(static_cast<size_t>(first + i) * a.num_q_heads + h) * 2]);
+    float L = 0.0f, O = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        const size_t rec = static_cast<size_t>(first + i) * a.num_q_heads + h;
+        const float wgt = fast_exp2(a.ml_part[rec * 2] - M);
+        L += wgt * a.ml_part[rec * 2 + 1];
+        O += wgt * a.o_part[rec * kHeadDim + d];
+    }
+    const _Float16 r = static_cast<_Float16>(O / L);
+    *reinterpret_cast<_Float16 *>(out) = r;
+}
+
 }  // namespace
 
 hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream) {
@@ -449,7 +502,7 @@ hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
-    const dim3 grid(a.max_splits, a.num_kv_heads, a.batch);
+    const dim3 grid = a.items ? dim3(a.num_items, a.num_kv_heads, 1) : dim3(a.max_splits, a.num_kv_heads, a.batch);
     hipLaunchKernelGGL(decode_partial_kernel<PA_DECODE_NBUF>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
@@ -458,6 +511,12 @@ hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(static_cast<uint32_t>((rows + 1) / 2)), dim3(256), 0,
                        stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL(decode_merge_planned_kernel, dim3(a.num_merges, (a.num_q_heads + 1) / 2), dim3(256), 0, stream,
+                       a);
     return hipGetLastError();
 }
 

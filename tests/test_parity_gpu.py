@@ -264,3 +264,69 @@ def test_append_decode_writes_the_newest_token_and_attends_to_it(monkeypatch, sp
     torch.cuda.synchronize()
     assert torch.equal(out3.view(torch.int16), out.view(torch.int16))
     st.close()
+
+
+def _planned(st, layer=0, k_new=None, v_new=None):
+    plan = st.pool.plan(st.w.ctx_lens)
+    q, tables = st.dev[layer]
+    out = torch.empty_like(q)
+    st.pool.run(layer, plan, q, out, tables, st.w.scale, k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    return out, plan
+
+
+def test_planned_run_ragged_with_poisoned_tails():
+    w = workloads.custom(RAGGED + [0, 3, 8192], seed=31, max_blocks=520)
+    st = Staged(w)
+    _poison_tails(st)
+    out, plan = _planned(st)
+    report("planned ragged", items=plan.info.num_items, merges=plan.info.num_merges,
+           longest=plan.info.max_piece_tokens)
+    compare("planned ragged", out, st.reference(0))
+    st.close()
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 5])
+def test_planned_run_configs(k):
+    w = workloads.config(k)
+    st = Staged(w)
+    out, plan = _planned(st)
+    report(f"planned config{k}", items=plan.info.num_items, merges=plan.info.num_merges,
+           longest=plan.info.max_piece_tokens)
+    compare(f"planned config{k}", out, st.reference(0))
+    st.close()
+
+
+def test_planned_uniform_batch_equals_single_split_decode_bitwise():
+    w = workloads.custom([4096] * 32, seed=32)
+    st = Staged(w)
+    out, plan = _planned(st)
+    assert plan.info.num_items == 32 and plan.info.num_merges == 0
+    ref = st.decode(0)       # one split per sequence too
+    assert st.pool.split_tokens(32, 32, 4096) == 4096
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    st.close()
+
+
+def test_planned_run_appends_the_newest_token():
+    lens = [1, 17, 300, 5000, 0, 64]
+    w = workloads.custom(lens, seed=33)
+    st = Staged(w)
+    _poison_tails(st)
+    q, tables, ids, k, v = st.host[0]
+    rng = np.random.default_rng(9)
+    k_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+    v_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+    out, plan = _planned(st, k_new=torch.from_numpy(k_new).cuda(), v_new=torch.from_numpy(v_new).cuda())
+    assert plan.info.num_merges > 0
+    k2, v2 = k.copy(), v.copy()
+    for s, c in enumerate(lens):
+        if c:
+            r = np.searchsorted(ids, tables[s, (c - 1) // 16])
+            k2[r, (c - 1) % 16] = k_new[s]
+            v2[r, (c - 1) % 16] = v_new[s]
+    st.host[0] = (q, tables, ids, k2, v2)
+    compare("planned append", out, st.reference(0))
+    again, _ = _planned(st)
+    assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+    st.close()

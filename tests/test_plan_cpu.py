@@ -1,0 +1,119 @@
+"""CPU tests of the host schedule built by pa_decode_plan (integer work: exact)."""
+import numpy as np
+import pytest
+
+import paged_kv_cache_64_amd as pa
+import workloads
+
+FAKE = 1 << 20
+
+
+@pytest.fixture
+def pool():
+    handle = pa.pa_pool_create(pa.PoolDesc(1, 64, 16, 8, 128, pa.PA_F16), FAKE, FAKE)
+    yield handle
+    pa.pa_pool_destroy(handle)
+
+
+def _decode_plan(info, plan):
+    assert plan[0] == 0x50414E31
+    assert plan[1] == info.batch and plan[2] == info.num_q_heads
+    assert plan[3] == info.num_items and plan[4] == info.num_merges and plan[5] == info.num_slots
+    items = plan[8:8 + 8 * info.num_items].reshape(-1, 8)
+    merges = plan[8 + 8 * info.num_items:8 + 8 * info.num_items + 4 * info.num_merges].reshape(-1, 4)
+    return items, merges
+
+
+def _check_cover(lens, info, plan):
+    items, merges = _decode_plan(info, plan)
+    pieces = {}
+    for s, t0, t1, ctx, slot, *_ in items:
+        assert ctx == lens[s] and 0 <= t0 <= t1 <= ctx
+        assert t0 % 16 == 0 and (t1 % 16 == 0 or t1 == ctx)
+        pieces.setdefault(s, []).append((t0, t1, slot))
+    assert sorted(pieces) == list(range(len(lens)))
+    for s, ps in pieces.items():
+        ps.sort()
+        assert ps[0][0] == 0 and ps[-1][1] == lens[s]
+        for (a0, a1, _), (b0, b1, _) in zip(ps, ps[1:]):
+            assert a1 == b0
+        if len(ps) == 1:
+            assert ps[0][2] == -1           # written directly, no merge
+    # longest first
+    lengths = items[:, 2] - items[:, 1]
+    assert np.all(np.diff(lengths) <= 0)
+    # merges: exactly the cut sequences, with contiguous slots
+    cut = {s for s, ps in pieces.items() if len(ps) > 1}
+    assert {int(m[0]) for m in merges} == cut
+    for s, first, n, _ in merges:
+        assert sorted(p[2] for p in pieces[s]) == list(range(first, first + n))
+    assert info.num_slots == sum(len(pieces[s]) for s in cut)
+    assert info.max_piece_tokens == int(lengths.max()) if len(lengths) else True
+    assert info.max_piece_tokens <= 4096
+    return items, merges
+
+
+def test_uniform_batch_is_one_piece_per_sequence(pool):
+    lens = [4096] * 32
+    info, plan = pa.pa_decode_plan(pool, lens, 32)
+    items, merges = _check_cover(lens, info, plan)
+    assert info.num_items == 32 and info.num_merges == 0 and info.workspace_bytes == 0
+
+
+def test_ragged_batch_is_cut_into_near_equal_pieces(pool):
+    lens = list(workloads.config(4).ctx_lens)
+    info, plan = pa.pa_decode_plan(pool, lens, 32)
+    items, merges = _check_cover(lens, info, plan)
+    # pieces of a cut sequence differ by at most one block
+    per = {}
+    for s, t0, t1, *_ in items:
+        per.setdefault(s, []).append(t1 - t0)
+    for s, ls in per.items():
+        if len(ls) > 1:
+            full = [x for x in ls if x % 16 == 0]
+            assert max(full) - min(full) <= 16 if full else True
+    assert info.workspace_bytes >= info.num_slots * 32 * 130 * 4
+
+
+def test_small_batches_get_small_pieces(pool):
+    lens = [256]
+    info, plan = pa.pa_decode_plan(pool, lens, 32)
+    _check_cover(lens, info, plan)
+    assert info.num_items == 4 and info.num_merges == 1      # 4 pieces of 64 tokens
+    lens = [1, 0, 17, 4097, 0]
+    info, plan = pa.pa_decode_plan(pool, lens, 32)
+    _check_cover(lens, info, plan)
+
+
+def test_prefix_workload_plan(pool):
+    lens = list(workloads.config(5).ctx_lens)
+    info, plan = pa.pa_decode_plan(pool, lens, 32)
+    _check_cover(lens, info, plan)
+
+
+def test_plan_validation(pool):
+    lib = pa.load_library()
+    info = pa.PlanInfo()
+    lens = np.array([5, -1], np.int32)
+    assert lib.pa_decode_plan(pool, lens.ctypes.data, 2, 32, None, 0, info) == pa.PA_ERR_INVALID_ARG
+    lens = np.array([5, 7], np.int32)
+    assert lib.pa_decode_plan(pool, lens.ctypes.data, 2, 16, None, 0, info) == pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_decode_plan(pool, None, 2, 32, None, 0, info) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_plan(pool, lens.ctypes.data, 2, 32, None, 0, info) == pa.PA_OK
+    small = np.zeros(2, np.int32)
+    assert lib.pa_decode_plan(pool, lens.ctypes.data, 2, 32, small.ctypes.data, 8, info) == pa.PA_ERR_WORKSPACE
+    info0, plan0 = pa.pa_decode_plan(pool, [], 32)
+    assert info0.num_items == 0
+    # run with an empty plan is a no-op; a bad layer is rejected before any launch
+    assert lib.pa_decode_run(pool, 0, info0, FAKE, FAKE, None, None, FAKE, FAKE, 1, 0.1, None, 0,
+                             None) == pa.PA_OK
+    info1, _ = pa.pa_decode_plan(pool, [100], 32)
+    assert lib.pa_decode_run(pool, 3, info1, FAKE, FAKE, None, None, FAKE, FAKE, 7, 0.1, FAKE,
+                             1 << 20, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_run(pool, 0, info1, FAKE, FAKE, None, None, FAKE, FAKE, 6, 0.1, FAKE,
+                             1 << 20, None) == pa.PA_ERR_INVALID_ARG      # table too narrow
+    assert lib.pa_decode_run(pool, 0, info1, FAKE, FAKE, FAKE, None, FAKE, FAKE, 7, 0.1, FAKE,
+                             1 << 20, None) == pa.PA_ERR_INVALID_ARG      # k_new without v_new
+    if info1.workspace_bytes:
+        assert lib.pa_decode_run(pool, 0, info1, FAKE, FAKE, None, None, FAKE, FAKE, 7, 0.1, FAKE,
+                                 info1.workspace_bytes - 1, None) == pa.PA_ERR_WORKSPACE
