@@ -4,11 +4,12 @@
 Default workload: the full 32-layer decode step of the 8B geometry -- batch 32,
 every context 4096 tokens, 32 query heads / 8 KV heads, head_dim 128,
 block_size 16, F16 K/V ~ N(0, 1), a fresh random block table per layer in a
-pool of twice the needed blocks.  One step = for each of the 32 layers:
-pa_decode_partial with the newest token's K/V (it stores them into their
-slots and attends over the whole context: the first phase of
-pa_append_decode), then pa_decode_merge (which returns at once when a single
-split covers the context).
+pool of twice the needed blocks.  One step = build the schedule on the host
+from the step's context lengths (pa_decode_plan), copy it to the GPU
+asynchronously, then for each of the 32 layers pa_decode_run with the newest
+token's K/V: it stores them into their slots and attends over the whole
+context (for this batch the schedule is one piece per sequence, so each layer
+is one kernel launch and nothing is merged).
 
 Prints one JSON line: achieved KV GB/s (value), decode tokens/s, the fraction
 of HBM peak, a roofline record for the dominant kernel (decode_partial), and
@@ -113,7 +114,6 @@ def main():
     # ---- stage the pool through pa_write_kv, layer by layer ----
     t_stage = time.time()
     pool = pa.Pool(w.layers, w.pool_blocks, HKV, D, B, device=dev, fill=0.0)
-    lens_dev = torch.from_numpy(w.ctx_lens.copy()).to(dev)
     q_dev, tables_dev, knew, vnew = [], [], [], []
     host0 = None
     ctx = w.ctx_lens.astype(np.int64)
@@ -145,35 +145,48 @@ def main():
 
     mcl = w.max_context_len
     width = w.max_blocks
-    split = pool.split_tokens(w.batch, HQ, mcl)
-    ws_bytes = pool.workspace_bytes(w.batch, HQ, mcl)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    outs = [torch.empty_like(q) for q in q_dev]
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     h = pool.handle
     scale = ctypes.c_float(w.scale)
+    outs = [torch.empty_like(q) for q in q_dev]
 
-    # pre-marshalled argument tuples: the launch loop only calls into the library
-    part_args = [(h, L, q_dev[L].data_ptr(), knew[L].data_ptr(), vnew[L].data_ptr(),
-                  outs[L].data_ptr(), tables_dev[L].data_ptr(), width, lens_dev.data_ptr(),
-                  w.batch, HQ, mcl, scale, ws.data_ptr(), ws_bytes, sptr)
-                 for L in range(w.layers)]
-    merge_args = [(h, outs[L].data_ptr(), lens_dev.data_ptr(), w.batch, HQ, mcl, ws.data_ptr(),
-                   ws_bytes, sptr) for L in range(w.layers)]
-    f_part, f_merge = lib.pa_decode_partial, lib.pa_decode_merge
+    # the schedule: sized once, rebuilt on the host every step into one of two
+    # pinned buffers and copied to the GPU without blocking the host
+    lens_host = np.ascontiguousarray(w.ctx_lens, dtype=np.int32)
+    info = pa.PlanInfo()
+    rc = lib.pa_decode_plan(h, lens_host.ctypes.data, w.batch, HQ, None, 0, ctypes.byref(info))
+    assert rc == 0, rc
+    plan_words = max(1, info.plan_bytes // 4)
+    plan_pinned = [torch.zeros(plan_words, dtype=torch.int32).pin_memory() for _ in range(2)]
+    plan_dev = torch.zeros(plan_words, dtype=torch.int32, device=dev)
+    ws_bytes = info.workspace_bytes
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    f_plan, f_run = lib.pa_decode_plan, lib.pa_decode_run
+    run_args = [(h, L, ctypes.byref(info), plan_dev.data_ptr(), q_dev[L].data_ptr(),
+                 knew[L].data_ptr(), vnew[L].data_ptr(), outs[L].data_ptr(),
+                 tables_dev[L].data_ptr(), width, scale, ws.data_ptr(), ws_bytes, sptr)
+                for L in range(w.layers)]
+    nstep = [0]
 
     def step(events=None):
+        buf = plan_pinned[nstep[0] % 2]
+        nstep[0] += 1
+        rc = f_plan(h, lens_host.ctypes.data, w.batch, HQ, buf.data_ptr(), buf.numel() * 4,
+                    ctypes.byref(info))
+        if rc != 0:
+            raise RuntimeError(f"pa_decode_plan failed: {rc}")
+        plan_dev.copy_(buf, non_blocking=True)
         for L in range(w.layers):
             if events is not None:
                 events[L][0].record(stream)
-            rc = f_part(*part_args[L])
+            rc = f_run(*run_args[L])
             if events is not None:
                 events[L][1].record(stream)
-            rc |= f_merge(*merge_args[L])
             if rc != 0:
-                raise RuntimeError(f"library call failed in layer {L}: {rc}")
+                raise RuntimeError(f"pa_decode_run failed in layer {L}: {rc}")
 
+    split = info.max_piece_tokens
     kv_bytes_step = w.kv_bytes()
     plib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_64_amd", "libpa_probe.so"))
     plib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
@@ -188,8 +201,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps); split={split} tokens, workspace={ws_bytes} B, "
-        f"cold flush between steps: {cold_flush}")
+    log(f"warmup done ({args.warmup} steps); plan: {info.num_items} pieces, longest {split} "
+        f"tokens, {info.num_merges} merges, workspace={ws_bytes} B; cold flush between steps: "
+        f"{cold_flush}")
 
     # Timed region 1 (the headline): K whole steps, events only around each step.
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -208,8 +222,9 @@ def main():
     ms_per_step = float(np.mean(step_ms))
 
     # Timed region 2 (the roofline record): the same K steps with an event pair
-    # around every decode_partial launch; event records between launches cost
-    # a few microseconds each, which is why region 1 carries none.
+    # around every layer's pa_decode_run -- one decode_partial launch when the
+    # schedule merges nothing; event records between launches cost a few
+    # microseconds each, which is why region 1 carries none.
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
            for _ in range(w.layers)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -266,9 +281,10 @@ def main():
                 q, tables = w.q(layer), w.tables(layer)
             kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, w.ctx_lens, B)
             # the GPU result of this layer (read-only decode of the staged pool)
-            lib.pa_decode(h, layer, q_dev[layer].data_ptr(), outs[layer].data_ptr(),
-                          tables_dev[layer].data_ptr(), width, lens_dev.data_ptr(), w.batch, HQ,
-                          mcl, scale, ws.data_ptr(), ws_bytes, sptr)
+            rc = f_run(h, layer, ctypes.byref(info), plan_dev.data_ptr(), q_dev[layer].data_ptr(),
+                       None, None, outs[layer].data_ptr(), tables_dev[layer].data_ptr(), width,
+                       scale, ws.data_ptr(), ws_bytes, sptr)
+            assert rc == 0, rc
             torch.cuda.synchronize()
             gpu = outs[layer].cpu().numpy().astype(np.float64)
             for lo in range(0, w.batch, 8):
@@ -310,14 +326,20 @@ def main():
         "config": {"workload": w.name, "layers": w.layers, "batch": w.batch,
                    "context": int(w.ctx_lens.max()), "q_heads": HQ, "kv_heads": HKV,
                    "head_dim": D, "block_size": B, "pool_blocks_per_layer": w.pool_blocks,
-                   "split_tokens": split, "cold_flush_between_steps": cold_flush},
+                   "schedule": {"pieces": info.num_items, "longest_piece_tokens": split,
+                                "merged_sequences": info.num_merges},
+                   "cold_flush_between_steps": cold_flush},
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_step": kv_bytes_step,
+        "kv_unique_bytes_per_step": w.kv_unique_bytes(),
+        "unique_kv_GBps": round(w.kv_unique_bytes() / (ms_per_step * 1e-3) / 1e9, 2),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "decode_partial_kernel",
+                     "traffic": traffic if info.num_merges == 0 else None,
+                     "kernel": "decode_partial_kernel" if info.num_merges == 0
+                     else "decode_partial_kernel + decode_merge_planned_kernel",
                      "bytes_per_launch": kb["total"],
                      "mean_launch_us": round(part_mean_s * 1e6, 3)},
         "hbm_read_probe_GBps": round(probe, 1) if probe else None,

@@ -207,7 +207,7 @@ pa_status pa_decode_plan(const pa_pool *pool, const int32_t *context_lens_host, 
         int32_t longest = 0;
         for (const PlanItem &it : items) longest = std::max(longest, it.t_end - it.t_begin);
         const size_t n_items = items.size(), n_merges = merges.size() / pa::kMergeInts;
-        if (n_items > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+        if (static_cast<int64_t>(n_items) * pool->desc.num_kv_heads > 0x7fffffff) return PA_ERR_UNSUPPORTED;
         pa_plan_info inf{};
         inf.batch = batch;
         inf.num_q_heads = num_q_heads;

@@ -141,7 +141,10 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
 // ---------------------------------------------------------------------------
 template <int NBUF>
 __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
-    const int g = blockIdx.y;
+    // Planned launches number work-groups item-major with the KV head fastest,
+    // so the heads of one piece -- whose tiles share each 32 KiB block of
+    // K and of V -- run side by side, as in the fixed-split grid.
+    const int g = a.items != nullptr ? static_cast<int>(blockIdx.x % a.num_kv_heads) : static_cast<int>(blockIdx.y);
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     const int lane = tid & 63;
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     if (a.items != nullptr) {
         // Plan entries are clamped so a damaged plan cannot index outside
         // q, out, the tables or the workspace.
-        const int32_t *it = a.items + kItemInts * static_cast<size_t>(blockIdx.x);
+        const int32_t *it = a.items + kItemInts * static_cast<size_t>(blockIdx.x / a.num_kv_heads);
         s = min(max(it[0], 0), a.batch - 1);
         ctx = min(max(it[3], 0), a.max_blocks * kBlockSize);
         t_begin = max(it[1], 0);
@@ -502,7 +505,8 @@ hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
-    const dim3 grid = a.items ? dim3(a.num_items, a.num_kv_heads, 1) : dim3(a.max_splits, a.num_kv_heads, a.batch);
+    const dim3 grid = a.items ? dim3(static_cast<uint32_t>(static_cast<int64_t>(a.num_items) * a.num_kv_heads), 1, 1)
+                              : dim3(a.max_splits, a.num_kv_heads, a.batch);
     hipLaunchKernelGGL(decode_partial_kernel<PA_DECODE_NBUF>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }

@@ -196,6 +196,26 @@ class Workload:
         return ids, k, v
 
     # -- accounting (what the step must read; used for reporting) -----------
+    def kv_unique_bytes(self) -> int:
+        """K+V bytes of the distinct (block, offset) slots the step reads, over all
+        layers: shared prefix blocks count once."""
+        per_token = self.num_kv_heads * self.head_dim * 2 * 2
+        total = 0
+        held = self.blocks_held()
+        for layer in range(self.layers if self.fresh_tables_per_layer else 1):
+            t = self.tables(layer)
+            used = {}
+            for s in range(self.batch):
+                ctx = int(self.ctx_lens[s])
+                for j in range(int(held[s])):
+                    n = min(self.block_size, ctx - j * self.block_size)
+                    b = int(t[s, j])
+                    used[b] = max(used.get(b, 0), n)
+            total += sum(used.values()) * per_token
+        if not self.fresh_tables_per_layer:
+            total *= self.layers
+        return total
+
     def kv_bytes(self, layers: int | None = None) -> int:
         """K+V bytes every sequence reads once per layer (logical)."""
         per_token = self.num_kv_heads * self.head_dim * 2 * 2
