@@ -72,6 +72,8 @@ def main():
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--cascade", action="store_true",
+                    help="for a workload with shared prefixes, schedule with pa_cascade_plan")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB three times (to scale the FETCH_SIZE "
                          "and WRITE_SIZE counters) and exit")
@@ -155,16 +157,33 @@ def main():
     # pinned buffers and copied to the GPU without blocking the host
     lens_host = np.ascontiguousarray(w.ctx_lens, dtype=np.int32)
     info = pa.PlanInfo()
-    rc = lib.pa_decode_plan(h, lens_host.ctypes.data, w.batch, HQ, None, 0, ctypes.byref(info))
+    cascade = args.cascade and w.prefix_groups is not None
+    if cascade:
+        n_groups, gsize, pblocks = w.prefix_groups
+        group_host = np.repeat(np.arange(n_groups, dtype=np.int32), gsize)
+        plen_host = np.full(n_groups, pblocks * B, dtype=np.int32)
+
+    def make_plan(dst, nbytes):
+        if cascade:
+            return lib.pa_cascade_plan(h, lens_host.ctypes.data, w.batch, group_host.ctypes.data,
+                                       plen_host.ctypes.data, n_groups, HQ, dst, nbytes,
+                                       ctypes.byref(info))
+        return lib.pa_decode_plan(h, lens_host.ctypes.data, w.batch, HQ, dst, nbytes,
+                                  ctypes.byref(info))
+
+    rc = make_plan(None, 0)
     assert rc == 0, rc
     plan_words = max(1, info.plan_bytes // 4)
     plan_pinned = [torch.zeros(plan_words, dtype=torch.int32).pin_memory() for _ in range(2)]
     plan_dev = torch.zeros(plan_words, dtype=torch.int32, device=dev)
     ws_bytes = info.workspace_bytes
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    f_plan, f_run = lib.pa_decode_plan, lib.pa_decode_run
+    f_run = lib.pa_decode_run
+    # a cascade plan whose newest tokens lie in shared blocks cannot append them
+    append = info.shared_newest == 0
     run_args = [(h, L, ctypes.byref(info), plan_dev.data_ptr(), q_dev[L].data_ptr(),
-                 knew[L].data_ptr(), vnew[L].data_ptr(), outs[L].data_ptr(),
+                 knew[L].data_ptr() if append else None, vnew[L].data_ptr() if append else None,
+                 outs[L].data_ptr(),
                  tables_dev[L].data_ptr(), width, scale, ws.data_ptr(), ws_bytes, sptr)
                 for L in range(w.layers)]
     nstep = [0]
@@ -172,8 +191,7 @@ def main():
     def step(events=None):
         buf = plan_pinned[nstep[0] % 2]
         nstep[0] += 1
-        rc = f_plan(h, lens_host.ctypes.data, w.batch, HQ, buf.data_ptr(), buf.numel() * 4,
-                    ctypes.byref(info))
+        rc = make_plan(buf.data_ptr(), buf.numel() * 4)
         if rc != 0:
             raise RuntimeError(f"pa_decode_plan failed: {rc}")
         plan_dev.copy_(buf, non_blocking=True)
@@ -327,7 +345,9 @@ def main():
                    "context": int(w.ctx_lens.max()), "q_heads": HQ, "kv_heads": HKV,
                    "head_dim": D, "block_size": B, "pool_blocks_per_layer": w.pool_blocks,
                    "schedule": {"pieces": info.num_items, "longest_piece_tokens": split,
-                                "merged_sequences": info.num_merges},
+                                "merged_sequences": info.num_merges,
+                                "shared_prefix_pieces": info.num_prefix_items,
+                                "appends_newest_token": append},
                    "cold_flush_between_steps": cold_flush},
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),

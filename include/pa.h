@@ -202,6 +202,9 @@ typedef struct {
     int32_t num_merges;       /* sequences cut into more than one piece */
     int32_t num_slots;        /* partial records per query head */
     int32_t max_piece_tokens; /* longest piece */
+    int32_t num_prefix_items; /* shared-prefix pieces (pa_cascade_plan) */
+    int32_t num_members;      /* member entries of the shared-prefix pieces */
+    int32_t shared_newest;    /* members whose newest token lies in the shared prefix */
     size_t plan_bytes;        /* bytes of the serialised plan */
     size_t workspace_bytes;   /* device workspace pa_decode_run needs (0: none) */
 } pa_plan_info;
@@ -215,9 +218,28 @@ pa_status pa_decode_plan(const pa_pool *pool, const int32_t *context_lens_host, 
                          int32_t num_q_heads, void *plan_host, size_t plan_host_bytes,
                          pa_plan_info *info);
 
+/* Shared-prefix (cascade) schedule.  Sequences may be grouped: member s of
+ * group G = prefix_group_host[s] (-1: none) shares the physical blocks of its
+ * first prefix_len_host[G] tokens (a multiple of block_size, at most its
+ * context) with every other member -- their table rows hold the same ids
+ * there, as reference-counted prefix blocks do ("Reading Inference Engine
+ * Codebases", Examples 3 and 12).  The prefix is then read once per group of
+ * up to 16 members instead of once per member: its tiles feed the members'
+ * stacked query heads (16 x 4 = 64 rows per KV head) through MFMA, and each
+ * member's prefix and suffix results are merged by their log-sum-exp weights.
+ * The result is the same attention as pa_decode_plan's.  The block ids of a
+ * group's prefix are read from its first member's table row.  Other arguments
+ * and the two-call sizing as pa_decode_plan. */
+pa_status pa_cascade_plan(const pa_pool *pool, const int32_t *context_lens_host, int32_t batch,
+                          const int32_t *prefix_group_host, const int32_t *prefix_len_host,
+                          int32_t num_groups, int32_t num_q_heads, void *plan_host,
+                          size_t plan_host_bytes, pa_plan_info *info);
+
 /* One decode step of one layer on a planned schedule: the plan's pieces, then
  * the merge of the cut sequences.  k_new_dev/v_new_dev (both or neither)
- * append the newest token as pa_append_decode does.  q, out, tables, scale and
+ * append the newest token as pa_append_decode does (rejected with
+ * PA_ERR_INVALID_ARG when info->shared_newest > 0: that token would land in
+ * a shared block).  q, out, tables, scale and
  * stream as pa_decode; the context lengths come from the plan, whose device
  * copy plan_dev must stay unchanged until the work completes.  A damaged plan
  * cannot make the kernels access memory outside the given buffers, but its

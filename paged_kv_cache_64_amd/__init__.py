@@ -26,7 +26,7 @@ PA_F16 = 1
 EXPORTS = ("pa_pool_bytes", "pa_pool_create", "pa_pool_destroy", "pa_write_kv",
            "pa_decode_split_tokens", "pa_decode_workspace_bytes", "pa_decode",
            "pa_append_decode", "pa_decode_partial", "pa_decode_merge", "pa_decode_plan",
-           "pa_decode_run", "pa_status_string")
+           "pa_cascade_plan", "pa_decode_run", "pa_status_string")
 
 
 class PaError(RuntimeError):
@@ -45,7 +45,9 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("max_context_len", ctypes.c_int32), ("num_items", ctypes.c_int32),
                 ("num_merges", ctypes.c_int32), ("num_slots", ctypes.c_int32),
-                ("max_piece_tokens", ctypes.c_int32), ("plan_bytes", ctypes.c_size_t),
+                ("max_piece_tokens", ctypes.c_int32), ("num_prefix_items", ctypes.c_int32),
+                ("num_members", ctypes.c_int32), ("shared_newest", ctypes.c_int32),
+                ("plan_bytes", ctypes.c_size_t),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -86,6 +88,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_merge.argtypes = [_P, _P, _P, _I, _I, _I, _P, ctypes.c_size_t, _P]
     lib.pa_decode_plan.restype = _I
     lib.pa_decode_plan.argtypes = [_P, _P, _I, _I, _P, ctypes.c_size_t, ctypes.POINTER(PlanInfo)]
+    lib.pa_cascade_plan.restype = _I
+    lib.pa_cascade_plan.argtypes = [_P, _P, _I, _P, _P, _I, _I, _P, ctypes.c_size_t,
+                                    ctypes.POINTER(PlanInfo)]
     lib.pa_decode_run.restype = _I
     lib.pa_decode_run.argtypes = [_P, _I, ctypes.POINTER(PlanInfo), _P, _P, _P, _P, _P, _P, _I,
                                   ctypes.c_float, _P, ctypes.c_size_t, _P]
@@ -220,6 +225,27 @@ def pa_decode_plan(handle, context_lens_host, num_q_heads):
     return info, plan
 
 
+def pa_cascade_plan(handle, context_lens_host, prefix_group_host, prefix_len_host, num_q_heads):
+    """Shared-prefix schedule: returns (PlanInfo, int32 numpy plan)."""
+    import numpy as np
+
+    lens = np.ascontiguousarray(context_lens_host, dtype=np.int32)
+    grp = np.ascontiguousarray(prefix_group_host, dtype=np.int32)
+    plen = np.ascontiguousarray(prefix_len_host, dtype=np.int32)
+    if grp.shape != lens.shape:
+        raise ValueError("prefix_group must have one entry per sequence")
+    info = PlanInfo()
+    lib = load_library()
+    args = (lens.ctypes.data_as(_P) if lens.size else None, int(lens.shape[0]),
+            grp.ctypes.data_as(_P) if grp.size else None,
+            plen.ctypes.data_as(_P) if plen.size else None, int(plen.shape[0]), num_q_heads)
+    _check(lib.pa_cascade_plan(handle, *args, None, 0, ctypes.byref(info)), "pa_cascade_plan")
+    plan = np.zeros(max(1, info.plan_bytes // 4), dtype=np.int32)
+    _check(lib.pa_cascade_plan(handle, *args, plan.ctypes.data_as(_P), plan.nbytes,
+                               ctypes.byref(info)), "pa_cascade_plan")
+    return info, plan
+
+
 def pa_decode_run(handle, layer, info, plan_dev, q, k_new, v_new, out, block_tables,
                   max_blocks_per_seq, scale, workspace, workspace_bytes, stream=None):
     _check(load_library().pa_decode_run(handle, layer, ctypes.byref(info), _ptr(plan_dev), _ptr(q),
@@ -229,10 +255,16 @@ def pa_decode_run(handle, layer, info, plan_dev, q, k_new, v_new, out, block_tab
 
 
 class Plan:
-    """A host schedule (pa_decode_plan) and its device copy."""
+    """A host schedule (pa_decode_plan, or pa_cascade_plan when prefix groups are
+    given) and its device copy."""
 
-    def __init__(self, handle, context_lens_host, num_q_heads, device="cuda"):
-        self.info, self.host = pa_decode_plan(handle, context_lens_host, num_q_heads)
+    def __init__(self, handle, context_lens_host, num_q_heads, device="cuda",
+                 prefix_group=None, prefix_len=None):
+        if prefix_group is None:
+            self.info, self.host = pa_decode_plan(handle, context_lens_host, num_q_heads)
+        else:
+            self.info, self.host = pa_cascade_plan(handle, context_lens_host, prefix_group,
+                                                   prefix_len, num_q_heads)
         self.dev = torch.from_numpy(self.host).to(device)
         n = self.info.workspace_bytes
         self.workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
@@ -295,9 +327,9 @@ class Pool:
                    v_blocks.reshape(n, self.num_kv_heads, self.head_dim).contiguous(),
                    slots.to(torch.int32).contiguous(), stream)
 
-    def plan(self, context_lens_host, num_q_heads=None):
+    def plan(self, context_lens_host, num_q_heads=None, prefix_group=None, prefix_len=None):
         return Plan(self.handle, context_lens_host, num_q_heads or 4 * self.num_kv_heads,
-                    self.k.device)
+                    self.k.device, prefix_group, prefix_len)
 
     def run(self, layer, plan, q, out, block_tables, scale, k_new=None, v_new=None, stream=None):
         """pa_decode_run on a Plan from plan()."""

@@ -157,57 +157,132 @@ size_t planned_workspace(int64_t slots, int32_t num_q_heads, size_t *o_bytes) {
     return recs ? *o_bytes + recs * 2 * sizeof(float) : 0;
 }
 
-}  // namespace
 
-extern "C" {
-
-pa_status pa_decode_plan(const pa_pool *pool, const int32_t *context_lens_host, int32_t batch, int32_t num_q_heads,
-                         void *plan_host, size_t plan_host_bytes, pa_plan_info *info) {
+// Builds the serialised schedule.  Without groups every sequence is cut into
+// near-equal pieces (see above).  With groups, sequence s of group G attends
+// to the shared prefix [0, prefix_len[G]) through prefix pieces of up to
+// kMaxPrefixPieceBlocks blocks, each serving up to kMaxMembers members at once,
+// and to its own suffix [prefix_len[G], ctx) through ordinary pieces; all its
+// records are merged.
+pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, int32_t num_q_heads,
+                     const int32_t *group_of, const int32_t *prefix_len, int32_t num_groups, void *plan_host,
+                     size_t plan_host_bytes, pa_plan_info *info) {
     try {
         if (!pool || !info || batch < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
-        if (batch > 0 && !context_lens_host) return PA_ERR_INVALID_ARG;
+        if (batch > 0 && !lens) return PA_ERR_INVALID_ARG;
         if (num_q_heads % pool->desc.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
         if (num_q_heads != kGroup * pool->desc.num_kv_heads) return PA_ERR_UNSUPPORTED;
-        if (batch > (1 << 24)) return PA_ERR_UNSUPPORTED;
+        if (batch > (1 << 24) || num_groups > (1 << 24)) return PA_ERR_UNSUPPORTED;
+        for (int32_t gi = 0; gi < num_groups; ++gi)
+            if (prefix_len[gi] < 0 || prefix_len[gi] % kBlockSize != 0) return PA_ERR_INVALID_ARG;
+        std::vector<int32_t> plen(batch, 0);
+        std::vector<std::vector<int32_t>> members(num_groups);
         int64_t total_blocks = 0;
         int32_t max_ctx = 0;
         for (int32_t s = 0; s < batch; ++s) {
-            if (context_lens_host[s] < 0) return PA_ERR_INVALID_ARG;
-            total_blocks += (context_lens_host[s] + kBlockSize - 1) / kBlockSize;
-            max_ctx = std::max(max_ctx, context_lens_host[s]);
+            if (lens[s] < 0) return PA_ERR_INVALID_ARG;
+            max_ctx = std::max(max_ctx, lens[s]);
+            if (group_of) {
+                const int32_t gi = group_of[s];
+                if (gi < -1 || gi >= num_groups) return PA_ERR_INVALID_ARG;
+                if (gi >= 0 && prefix_len[gi] > 0) {
+                    if (prefix_len[gi] > lens[s]) return PA_ERR_INVALID_ARG;
+                    plen[s] = prefix_len[gi];
+                    members[gi].push_back(s);
+                }
+            }
+            total_blocks += (lens[s] - plen[s] + kBlockSize - 1) / kBlockSize;
         }
+        for (int32_t gi = 0; gi < num_groups; ++gi)
+            if (!members[gi].empty())
+                total_blocks += static_cast<int64_t>(prefix_len[gi] / kBlockSize) *
+                                ((members[gi].size() + pa::kMaxMembers - 1) / pa::kMaxMembers);
         const int64_t items_target = std::max<int64_t>(1, kTargetWorkGroups / pool->desc.num_kv_heads);
         const int64_t piece = std::min<int64_t>(kMaxSplitTokens / kBlockSize,
                                                 std::max<int64_t>(pa::kWaves, (total_blocks + items_target - 1) / items_target));
-        std::vector<PlanItem> items;
-        std::vector<int32_t> merges;
-        items.reserve(static_cast<size_t>(batch) + static_cast<size_t>(total_blocks / piece) + 1);
+        auto cut = [](int64_t nb, int64_t maxp) { return nb == 0 ? int64_t{0} : (nb + maxp - 1) / maxp; };
+
+        // records: each member owns a contiguous run (prefix pieces, then its
+        // suffix pieces); a sequence without prefix owns one only when cut
+        std::vector<int32_t> first(batch, -1), n_prefix(batch, 0);
         int32_t slots = 0;
+        int32_t shared_newest = 0;
+        std::vector<int32_t> merges;
         for (int32_t s = 0; s < batch; ++s) {
-            const int32_t ctx = context_lens_host[s];
-            const int64_t nb = (ctx + kBlockSize - 1) / kBlockSize;
-            const int64_t np = nb == 0 ? 1 : (nb + piece - 1) / piece;
-            if (np == 1) {
+            const int64_t suffix_blocks = (lens[s] - plen[s] + kBlockSize - 1) / kBlockSize;
+            const int64_t np_suffix = cut(suffix_blocks, piece);
+            if (plen[s] > 0) {
+                n_prefix[s] = static_cast<int32_t>(cut(plen[s] / kBlockSize, pa::kMaxPrefixPieceBlocks));
+                const int64_t n = n_prefix[s] + np_suffix;
+                first[s] = slots;
+                slots += static_cast<int32_t>(n);
+                merges.insert(merges.end(), {s, first[s], static_cast<int32_t>(n), 0});
+                if (lens[s] == plen[s]) ++shared_newest;
+            } else if (np_suffix > 1) {
+                first[s] = slots;
+                slots += static_cast<int32_t>(np_suffix);
+                merges.insert(merges.end(), {s, first[s], static_cast<int32_t>(np_suffix), 0});
+            }
+        }
+        // ordinary pieces (whole contexts, or the suffixes of members)
+        std::vector<PlanItem> items;
+        for (int32_t s = 0; s < batch; ++s) {
+            const int32_t ctx = lens[s];
+            const int64_t nb = (ctx - plen[s] + kBlockSize - 1) / kBlockSize;
+            const int64_t np = cut(nb, piece);
+            if (np == 0) {
+                if (plen[s] == 0) items.push_back({s, 0, 0, 0, -1});  // empty context: zero output
+                continue;
+            }
+            if (np == 1 && plen[s] == 0) {
                 items.push_back({s, 0, ctx, ctx, -1});
                 continue;
             }
             const int64_t base = nb / np, extra = nb % np;
             int64_t b0 = 0;
-            merges.insert(merges.end(), {s, slots, static_cast<int32_t>(np), 0});
+            const int32_t slot0 = first[s] + n_prefix[s];
             for (int64_t i = 0; i < np; ++i) {
                 const int64_t b1 = b0 + base + (i < extra ? 1 : 0);
-                items.push_back({s, static_cast<int32_t>(b0 * kBlockSize),
-                                 static_cast<int32_t>(std::min<int64_t>(ctx, b1 * kBlockSize)), ctx, slots++});
+                items.push_back({s, static_cast<int32_t>(plen[s] + b0 * kBlockSize),
+                                 static_cast<int32_t>(std::min<int64_t>(ctx, plen[s] + b1 * kBlockSize)), ctx,
+                                 static_cast<int32_t>(slot0 + i)});
                 b0 = b1;
             }
         }
         std::stable_sort(items.begin(), items.end(), [](const PlanItem &x, const PlanItem &y) {
             return (x.t_end - x.t_begin) > (y.t_end - y.t_begin);
         });
+        // prefix pieces: per group, per subgroup of <= kMaxMembers members, per piece
+        std::vector<int32_t> pitems, mlist;
+        for (int32_t gi = 0; gi < num_groups; ++gi) {
+            const std::vector<int32_t> &mem = members[gi];
+            if (mem.empty()) continue;
+            const int64_t nb = prefix_len[gi] / kBlockSize;
+            const int64_t np = cut(nb, pa::kMaxPrefixPieceBlocks);
+            const int64_t base = nb / np, extra = nb % np;
+            for (size_t m0 = 0; m0 < mem.size(); m0 += pa::kMaxMembers) {
+                const size_t cnt = std::min<size_t>(pa::kMaxMembers, mem.size() - m0);
+                int64_t b0 = 0;
+                for (int64_t p = 0; p < np; ++p) {
+                    const int64_t b1 = b0 + base + (p < extra ? 1 : 0);
+                    pitems.insert(pitems.end(), {mem[m0], static_cast<int32_t>(b0 * kBlockSize),
+                                                 static_cast<int32_t>(b1 * kBlockSize), static_cast<int32_t>(cnt),
+                                                 static_cast<int32_t>(mlist.size() / pa::kMemberInts), 0, 0, 0});
+                    for (size_t j = 0; j < cnt; ++j) {
+                        const int32_t s = mem[m0 + j];
+                        mlist.insert(mlist.end(), {s, first[s] + static_cast<int32_t>(p)});
+                    }
+                    b0 = b1;
+                }
+            }
+        }
         int32_t longest = 0;
         for (const PlanItem &it : items) longest = std::max(longest, it.t_end - it.t_begin);
         const size_t n_items = items.size(), n_merges = merges.size() / pa::kMergeInts;
-        if (static_cast<int64_t>(n_items) * pool->desc.num_kv_heads > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+        const size_t n_pitems = pitems.size() / pa::kPrefixItemInts, n_members = mlist.size() / pa::kMemberInts;
+        if (static_cast<int64_t>(std::max(n_items, n_pitems)) * pool->desc.num_kv_heads > 0x7fffffff ||
+            n_merges > 0x7fffffff || n_members > 0x7fffffff)
+            return PA_ERR_UNSUPPORTED;
         pa_plan_info inf{};
         inf.batch = batch;
         inf.num_q_heads = num_q_heads;
@@ -216,7 +291,11 @@ pa_status pa_decode_plan(const pa_pool *pool, const int32_t *context_lens_host, 
         inf.num_merges = static_cast<int32_t>(n_merges);
         inf.num_slots = slots;
         inf.max_piece_tokens = longest;
-        inf.plan_bytes = sizeof(int32_t) * (pa::kPlanHeader + pa::kItemInts * n_items + pa::kMergeInts * n_merges);
+        inf.num_prefix_items = static_cast<int32_t>(n_pitems);
+        inf.num_members = static_cast<int32_t>(n_members);
+        inf.shared_newest = shared_newest;
+        inf.plan_bytes = sizeof(int32_t) * (pa::kPlanHeader + pa::kItemInts * n_items + merges.size() +
+                                            pitems.size() + mlist.size());
         size_t o_bytes = 0;
         inf.workspace_bytes = planned_workspace(slots, num_q_heads, &o_bytes);
         *info = inf;
@@ -224,19 +303,37 @@ pa_status pa_decode_plan(const pa_pool *pool, const int32_t *context_lens_host, 
         if (plan_host_bytes < inf.plan_bytes) return PA_ERR_WORKSPACE;
         int32_t *p = static_cast<int32_t *>(plan_host);
         const int32_t header[pa::kPlanHeader] = {pa::kPlanMagic, batch, num_q_heads, inf.num_items,
-                                                 inf.num_merges, slots, max_ctx, 0};
-        std::copy(header, header + pa::kPlanHeader, p);
-        p += pa::kPlanHeader;
+                                                 inf.num_merges, slots, max_ctx, inf.num_prefix_items};
+        p = std::copy(header, header + pa::kPlanHeader, p);
         for (const PlanItem &it : items) {
             const int32_t rec[pa::kItemInts] = {it.s, it.t_begin, it.t_end, it.ctx, it.slot, 0, 0, 0};
-            std::copy(rec, rec + pa::kItemInts, p);
-            p += pa::kItemInts;
+            p = std::copy(rec, rec + pa::kItemInts, p);
         }
-        std::copy(merges.begin(), merges.end(), p);
+        p = std::copy(merges.begin(), merges.end(), p);
+        p = std::copy(pitems.begin(), pitems.end(), p);
+        std::copy(mlist.begin(), mlist.end(), p);
         return PA_OK;
     } catch (...) {
         return PA_ERR_INVALID_ARG;
     }
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_plan(const pa_pool *pool, const int32_t *context_lens_host, int32_t batch, int32_t num_q_heads,
+                         void *plan_host, size_t plan_host_bytes, pa_plan_info *info) {
+    return build_plan(pool, context_lens_host, batch, num_q_heads, nullptr, nullptr, 0, plan_host, plan_host_bytes,
+                      info);
+}
+
+pa_status pa_cascade_plan(const pa_pool *pool, const int32_t *context_lens_host, int32_t batch,
+                          const int32_t *prefix_group_host, const int32_t *prefix_len_host, int32_t num_groups,
+                          int32_t num_q_heads, void *plan_host, size_t plan_host_bytes, pa_plan_info *info) {
+    if (num_groups < 0 || (num_groups > 0 && (!prefix_group_host || !prefix_len_host))) return PA_ERR_INVALID_ARG;
+    return build_plan(pool, context_lens_host, batch, num_q_heads, prefix_group_host, prefix_len_host, num_groups,
+                      plan_host, plan_host_bytes, info);
 }
 
 pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, const void *plan_dev,
@@ -245,11 +342,12 @@ pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, 
                         void *workspace_dev, size_t workspace_bytes, hipStream_t stream) {
     if (!pool || !info || layer < 0 || layer >= pool->desc.num_layers) return PA_ERR_INVALID_ARG;
     if (info->batch < 0 || info->num_q_heads != kGroup * pool->desc.num_kv_heads) return PA_ERR_INVALID_ARG;
-    if (info->batch == 0 || info->num_items == 0) return PA_OK;
+    if (info->batch == 0 || (info->num_items == 0 && info->num_prefix_items == 0)) return PA_OK;
     if (!plan_dev || !q_dev || !out_dev || !aligned(plan_dev, 16) || !aligned(q_dev, 16) || !aligned(out_dev, 16))
         return PA_ERR_INVALID_ARG;
     if ((k_new_dev == nullptr) != (v_new_dev == nullptr)) return PA_ERR_INVALID_ARG;
     if (k_new_dev && (!aligned(k_new_dev, 16) || !aligned(v_new_dev, 16))) return PA_ERR_INVALID_ARG;
+    if (k_new_dev && info->shared_newest > 0) return PA_ERR_INVALID_ARG;  // newest token in a shared block
     if (info->max_context_len > 0 && (!block_tables_dev || !aligned(block_tables_dev, 4))) return PA_ERR_INVALID_ARG;
     if (max_blocks_per_seq < 0 ||
         static_cast<int64_t>(info->max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlockSize)
@@ -285,7 +383,12 @@ pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, 
     a.num_items = info->num_items;
     a.num_merges = info->num_merges;
     a.num_slots = info->num_slots;
-    if (pa::launch_decode_partial(a, stream) != hipSuccess) return PA_ERR_HIP;
+    a.prefix_items = a.merges + static_cast<size_t>(pa::kMergeInts) * info->num_merges;
+    a.members = a.prefix_items + static_cast<size_t>(pa::kPrefixItemInts) * info->num_prefix_items;
+    a.num_prefix_items = info->num_prefix_items;
+    a.num_members = info->num_members;
+    if (info->num_items > 0 && pa::launch_decode_partial(a, stream) != hipSuccess) return PA_ERR_HIP;
+    if (info->num_prefix_items > 0 && pa::launch_decode_prefix(a, stream) != hipSuccess) return PA_ERR_HIP;
     if (info->num_merges > 0 && pa::launch_decode_merge_planned(a, stream) != hipSuccess) return PA_ERR_HIP;
     return PA_OK;
 }

@@ -65,6 +65,13 @@ struct DecodeArgs {
     int32_t num_items;
     int32_t num_merges;
     int32_t num_slots;
+    // Shared-prefix (cascade) pieces: 8 int32 {first member's seq, t_begin,
+    // t_end, members (<= kMaxMembers), offset into the member list, 0, 0, 0};
+    // member entries of 2 int32 {seq, slot}.
+    const int32_t *prefix_items;
+    const int32_t *members;
+    int32_t num_prefix_items;
+    int32_t num_members;
 };
 
 // Serialised host plan: a header of kPlanHeader int32, then the items, then
@@ -72,6 +79,10 @@ struct DecodeArgs {
 constexpr int kPlanHeader = 8;
 constexpr int kItemInts = 8;
 constexpr int kMergeInts = 4;
+constexpr int kPrefixItemInts = 8;
+constexpr int kMemberInts = 2;
+constexpr int kMaxMembers = 16;        // 16 members x 4 query heads = 64 stacked rows
+constexpr int kMaxPrefixPieceBlocks = 32;
 constexpr int32_t kPlanMagic = 0x50414e31;  // "PAN1"
 
 
@@ -79,5 +90,6 @@ hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_prefix(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace pa

@@ -495,6 +495,198 @@ __global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a)
     *reinterpret_cast<_Float16 *>(out) = r;
 }
 
+// ---------------------------------------------------------------------------
+// decode_prefix: shared-prefix (cascade) pieces.  Sequences of a group share
+// the physical blocks of a common prefix (reference-counted blocks, "Reading
+// Inference Engine Codebases", Examples 3 and 12); one work-group per (piece,
+// KV head) reads each prefix K/V tile once for all members.  Up to 16
+// members x 4 query heads = 64 stacked query rows make Q K^T and P V real
+// dense tiles, computed with v_mfma_f32_16x16x16_f16:
+//   wave w owns rows 16w .. 16w+15: row 16w + 4r + j is member 4w + r, query
+//   head 4g + j.  In the lane layout of the MFMA (lane l, n = l % 16,
+//   r = l / 16):
+//   S^T = K . Q^T   A = K tile   (lane: token n, dims {32i + 8r + 4u + c})
+//                   B = Q^T      (lane: row n, the same dims)
+//                   D = S^T      (lane: tokens 4r + c of row n)
+//   O   = P . V     A = P        (lane: row n, tokens 4r + c) -- D of S^T as is
+//                   B = V        (lane: tokens 4r + c, dim 16 dt + n) read
+//                                 from a per-wave LDS copy of the V tile
+//                   D = O        (lane: rows 4r + c, dim 16 dt + n)
+// Each member's result is a partial record (o, m, l), merged with the
+// member's own suffix pieces by decode_merge_planned.
+// ---------------------------------------------------------------------------
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+struct h4x2 {
+    h4 v[2];
+};
+__device__ __forceinline__ h4x2 quads(h8 x) { return __builtin_bit_cast(h4x2, x); }
+
+constexpr int kVRow = kHeadDim + 8;  // padded LDS row of the staged V tile (halves)
+
+__global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
+    const int g = static_cast<int>(blockIdx.x % a.num_kv_heads);
+    const int32_t *it = a.prefix_items + kPrefixItemInts * static_cast<size_t>(blockIdx.x / a.num_kv_heads);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int n = lane & 15, r = lane >> 4;
+
+    __shared__ int tbl_lds[kMaxPrefixPieceBlocks];
+    __shared__ _Float16 v_lds[kWaves][kBlockSize][kVRow];
+    __shared__ float alpha_lds[kWaves][16];
+    __shared__ float ml_lds[kWaves][16][2];
+
+    // Plan entries are clamped so a damaged plan cannot index outside the
+    // buffers.
+    const int first_seq = min(max(it[0], 0), a.batch - 1);
+    const int b_begin = max(it[1], 0) / kBlockSize;
+    const int t_end = min(it[2], a.max_blocks * kBlockSize);
+    const int b_end = min((t_end + kBlockSize - 1) / kBlockSize, b_begin + kMaxPrefixPieceBlocks);
+    const int n_members = min(min(max(it[3], 0), kMaxMembers), a.num_members);
+    const int moff = min(max(it[4], 0), max(a.num_members - n_members, 0));
+    if (b_begin >= b_end || a.num_slots <= 0) return;
+
+    // this lane's query row (as the B operand) and its member
+    const int member = 4 * w + (n >> 2);
+    const bool row_valid = member < n_members;
+    h8 qv[4];
+    if (row_valid) {
+        const int sq = min(max(a.members[kMemberInts * (moff + member)], 0), a.batch - 1);
+        const uint16_t *qrow = a.q + (static_cast<size_t>(sq) * a.num_q_heads + g * kGroup + (n & 3)) * kHeadDim;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[i] = *reinterpret_cast<const h8 *>(qrow + 32 * i + 8 * r);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[i] = h8(0);
+    }
+
+    // the prefix's block ids, from the first member's table row
+    const int32_t *table = a.tables + static_cast<size_t>(first_seq) * a.max_blocks;
+    if (tid < b_end - b_begin) tbl_lds[tid] = table[b_begin + tid];
+    __syncthreads();
+
+    const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
+    const size_t tile_bytes = tile_elems() * sizeof(uint16_t);
+    const char *k_layer = reinterpret_cast<const char *>(a.k_layer);
+    const char *v_layer = reinterpret_cast<const char *>(a.v_layer);
+    const uint32_t k_off = static_cast<uint32_t>(n * kHeadDim * 2 + 16 * r);  // + 64 i
+    const uint32_t v_off = static_cast<uint32_t>(lane * 16);                  // + 1024 c
+
+    float m_run = -INFINITY;  // running max of row n (log2 units)
+    float l_run = 0.0f;       // this lane's share of row n's running sum
+    f4 acc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
+
+    h8 kb[2][4], vb[2][4];
+    auto issue = [&](int buf, int b) {
+        const bool live = b < b_end;
+        uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tbl_lds[live ? b - b_begin : 0]));
+        phys = phys > last_block ? last_block : phys;
+        const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
+        const int bytes = live ? static_cast<int>(tile_bytes) : 0;
+        const __amdgpu_buffer_rsrc_t kr = tile_rsrc(k_layer + base, bytes);
+        const __amdgpu_buffer_rsrc_t vr = tile_rsrc(v_layer + base, bytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kb[buf][i] = load_tile16(kr, k_off + 64u * i);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vb[buf][c] = load_tile16(vr, v_off + 1024u * c);
+    };
+
+    auto consume = [&](int buf, int b) {
+        // S^T for this wave's 16 rows
+        f4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const h4x2 kk = quads(kb[buf][i]);
+            const h4x2 qq = quads(qv[i]);
+            st = __builtin_amdgcn_mfma_f32_16x16x16f16(kk.v[0], qq.v[0], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x16f16(kk.v[1], qq.v[1], st, 0, 0, 0);
+        }
+        const int valid = min(kBlockSize, t_end - b * kBlockSize);
+        float sc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sc[c] = (4 * r + c < valid) ? st[c] * a.scale_log2e : -INFINITY;
+        const float bmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        if (__builtin_amdgcn_ballot_w64(bmax > m_run + kTau) != 0) {
+            float bm = bmax;
+            bm = fmaxf(bm, shfl_xor(bm, 16));
+            bm = fmaxf(bm, shfl_xor(bm, 32));
+            const float m_new = fmaxf(m_run, bm);
+            const float alpha = fast_exp2(m_run - m_new);
+            l_run *= alpha;
+            m_run = m_new;
+            if (r == 0) alpha_lds[w][n] = alpha;
+            wave_lds_sync();
+            const float4 al = *reinterpret_cast<const float4 *>(&alpha_lds[w][4 * r]);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                acc[dt][0] *= al.x;
+                acc[dt][1] *= al.y;
+                acc[dt][2] *= al.z;
+                acc[dt][3] *= al.w;
+            }
+        }
+        // weights enter P V as F16; the running sum adds the same rounded
+        // values, so numerator and denominator use identical weights
+        h4 pa;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pa[c] = static_cast<_Float16>(fast_exp2(sc[c] - m_run));
+            l_run += static_cast<float>(pa[c]);
+        }
+        // stage V (token 4c + r, dims 8n .. 8n+7 in this lane) into LDS
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            h8 vv = vb[buf][c];
+            if (4 * c + r >= valid) vv = h8(0);
+            *reinterpret_cast<h8 *>(&v_lds[w][4 * c + r][8 * n]) = vv;
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            h4 vbv;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) vbv[c] = v_lds[w][4 * r + c][16 * dt + n];
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vbv, acc[dt], 0, 0, 0);
+        }
+        wave_lds_sync();  // the next block restages V
+    };
+
+    issue(0, b_begin);
+    for (int b = b_begin; b < b_end; b += 2) {
+        issue(1, b + 1);
+        consume(0, b);
+        issue(0, b + 2);
+        if (b + 1 < b_end) consume(1, b + 1);
+    }
+
+    // row sums over the four lane groups; (m, l) of rows 4r + c via LDS
+    l_run += shfl_xor(l_run, 16);
+    l_run += shfl_xor(l_run, 32);
+    if (r == 0) {
+        ml_lds[w][n][0] = m_run;
+        ml_lds[w][n][1] = l_run;
+    }
+    wave_lds_sync();
+    const int my_member = 4 * w + r;  // rows 4r + c of the O layout
+    if (my_member < n_members) {
+        const int32_t *mem = a.members + kMemberInts * (moff + my_member);
+        const int slot = min(max(mem[1], 0), a.num_slots - 1);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const size_t rec = static_cast<size_t>(slot) * a.num_q_heads + g * kGroup + c;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) a.o_part[rec * kHeadDim + 16 * dt + n] = acc[dt][c];
+            if (n == 0) {
+                a.ml_part[rec * 2] = ml_lds[w][4 * r + c][0];
+                a.ml_part[rec * 2 + 1] = ml_lds[w][4 * r + c][1];
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream) {
@@ -521,6 +713,12 @@ hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(decode_merge_planned_kernel, dim3(a.num_merges, (a.num_q_heads + 1) / 2), dim3(256), 0, stream,
                        a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_prefix(const DecodeArgs &a, hipStream_t stream) {
+    const uint32_t groups = static_cast<uint32_t>(static_cast<int64_t>(a.num_prefix_items) * a.num_kv_heads);
+    hipLaunchKernelGGL(decode_prefix_kernel, dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

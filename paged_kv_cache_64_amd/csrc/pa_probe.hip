@@ -47,9 +47,39 @@ __global__ __launch_bounds__(kThreads) void probe_copy_kernel(uint4 *dst, const 
         dst[i] = src[i];
 }
 
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// One v_mfma_f32_16x16x16_f16 on row-major 16x16 inputs, with operands and
+// result moved in the lane layout the prefix kernel relies on:
+//   A: lane l holds A[l % 16][4 (l / 16) + c], c < 4
+//   B: lane l holds B[4 (l / 16) + c][l % 16]
+//   D: lane l holds D[4 (l / 16) + c][l % 16]
+__global__ __launch_bounds__(64) void probe_mfma_kernel(const _Float16 *a, const _Float16 *b, float *d) {
+    const int l = threadIdx.x, m = l % 16, r = l / 16;
+    h4 av, bv;
+    for (int c = 0; c < 4; ++c) {
+        av[c] = a[m * 16 + 4 * r + c];
+        bv[c] = b[(4 * r + c) * 16 + m];
+    }
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, acc, 0, 0, 0);
+    for (int c = 0; c < 4; ++c) d[(4 * r + c) * 16 + m] = acc[c];
+}
+
 }  // namespace
 
 extern "C" {
+
+// Lane-layout check of the 16x16x16 f16 MFMA: a, b F16 [16][16], d fp32
+// [16][16], one wave.  Returns a hipError_t.
+int32_t pa_probe_mfma_16x16x16(const void *a, const void *b, void *d, hipStream_t stream) {
+    if (!a || !b || !d) return static_cast<int32_t>(hipErrorInvalidValue);
+    hipLaunchKernelGGL(probe_mfma_kernel, dim3(1), dim3(64), 0, stream, static_cast<const _Float16 *>(a),
+                       static_cast<const _Float16 *>(b), static_cast<float *>(d));
+    return static_cast<int32_t>(hipGetLastError());
+}
+
 
 // Work-groups used by pa_probe_read; `sink` must hold this many uint32.
 int32_t pa_probe_read_groups(void) { return 256 * 8; }

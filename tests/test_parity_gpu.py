@@ -330,3 +330,71 @@ def test_planned_run_appends_the_newest_token():
     again, _ = _planned(st)
     assert torch.equal(again.view(torch.int16), out.view(torch.int16))
     st.close()
+
+
+def _cascade(st, group, plen, k_new=None, v_new=None):
+    plan = st.pool.plan(st.w.ctx_lens, prefix_group=group, prefix_len=plen)
+    q, tables = st.dev[0]
+    out = torch.empty_like(q)
+    st.pool.run(0, plan, q, out, tables, st.w.scale, k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    return out, plan
+
+
+@pytest.mark.parametrize("groups,gsize,pblocks,extra", [(2, 3, 3, [0, 5, 16, 40, 77, 1]),
+                                                        (1, 20, 5, list(range(0, 200, 10))),
+                                                        (3, 16, 40, [int(x) for x in np.arange(48) * 37 % 900])])
+def test_cascade_matches_oracle(groups, gsize, pblocks, extra):
+    lens = [pblocks * 16 + e for e in extra]
+    assert len(lens) == groups * gsize
+    w = workloads.custom(lens, seed=40 + groups, prefix_groups=(groups, gsize, pblocks))
+    st = Staged(w)
+    _poison_tails(st)
+    group = np.repeat(np.arange(groups), gsize).astype(np.int32)
+    plen = np.full(groups, pblocks * 16, np.int32)
+    out, plan = _cascade(st, group, plen)
+    report("cascade", groups=groups, members=gsize, prefix_items=plan.info.num_prefix_items,
+           merges=plan.info.num_merges)
+    compare(f"cascade g{groups}x{gsize}", out, st.reference(0))
+    # the same attention as the plain planned schedule
+    plain, _ = _planned(st)
+    compare(f"cascade vs planned g{groups}x{gsize}", out,
+            plain.cpu().numpy().astype(np.float64), max_abs=2e-3, rel_l2=1e-3)
+    st.close()
+
+
+def test_cascade_with_ungrouped_sequences_and_append():
+    lens = [64 + 3, 64 + 100, 64 + 17, 500, 0, 64 + 1]
+    w = workloads.custom(lens[:3] + lens[5:] + lens[3:5], seed=44, prefix_groups=(1, 4, 4))
+    st = Staged(w)
+    _poison_tails(st)
+    group = np.array([0, 0, 0, 0, -1, -1], np.int32)
+    plen = np.array([64], np.int32)
+    q, tables, ids, k, v = st.host[0]
+    rng = np.random.default_rng(11)
+    k_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+    v_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+    out, plan = _cascade(st, group, plen, torch.from_numpy(k_new).cuda(),
+                         torch.from_numpy(v_new).cuda())
+    assert plan.info.shared_newest == 0 and plan.info.num_prefix_items > 0
+    k2, v2 = k.copy(), v.copy()
+    for s, c in enumerate(w.ctx_lens):
+        if c:
+            r = np.searchsorted(ids, tables[s, (c - 1) // 16])
+            k2[r, (c - 1) % 16] = k_new[s]
+            v2[r, (c - 1) % 16] = v_new[s]
+    st.host[0] = (q, tables, ids, k2, v2)
+    compare("cascade append", out, st.reference(0))
+    st.close()
+
+
+def test_cascade_prefix_workload_full():
+    w = workloads.config(5)
+    st = Staged(w)
+    group = np.repeat(np.arange(16), 16).astype(np.int32)
+    plen = np.full(16, 2048, np.int32)
+    out, plan = _cascade(st, group, plen)
+    report("cascade config5", prefix_items=plan.info.num_prefix_items, items=plan.info.num_items,
+           merges=plan.info.num_merges)
+    compare("cascade config5", out, st.reference(0))
+    st.close()

@@ -117,3 +117,84 @@ def test_plan_validation(pool):
     if info1.workspace_bytes:
         assert lib.pa_decode_run(pool, 0, info1, FAKE, FAKE, None, None, FAKE, FAKE, 7, 0.1, FAKE,
                                  info1.workspace_bytes - 1, None) == pa.PA_ERR_WORKSPACE
+
+
+def _decode_cascade(info, plan):
+    off = 8 + 8 * info.num_items + 4 * info.num_merges
+    pitems = plan[off:off + 8 * info.num_prefix_items].reshape(-1, 8)
+    off += 8 * info.num_prefix_items
+    mlist = plan[off:off + 2 * info.num_members].reshape(-1, 2)
+    return pitems, mlist
+
+
+def test_cascade_plan_covers_prefix_and_suffix_once(pool):
+    w = workloads.config(5)
+    lens = w.ctx_lens
+    group = np.repeat(np.arange(16), 16).astype(np.int32)
+    plen = np.full(16, 2048, np.int32)
+    info, plan = pa.pa_cascade_plan(pool, lens, group, plen, 32)
+    items, merges = _decode_plan(info, plan)
+    pitems, mlist = _decode_cascade(info, plan)
+    assert info.num_merges == 256                    # every member merges prefix + suffix
+    assert info.shared_newest == int((lens == 2048).sum())
+    # suffix pieces cover [2048, ctx) of every sequence exactly
+    cover = {}
+    for s, t0, t1, ctx, slot, *_ in items:
+        assert ctx == lens[s] and 2048 <= t0 < t1 <= ctx and slot >= 0
+        cover.setdefault(s, []).append((t0, t1, slot))
+    for s in range(256):
+        ps = sorted(cover.get(s, []))
+        if lens[s] == 2048:
+            assert not ps
+            continue
+        assert ps[0][0] == 2048 and ps[-1][1] == lens[s]
+        assert all(a[1] == b[0] for a, b in zip(ps, ps[1:]))
+    # prefix pieces: per group, pieces tile [0, 2048) in whole blocks, 16 members each
+    by_group = {}
+    for first_seq, t0, t1, nm, moff, *_ in pitems:
+        assert nm == 16 and t0 % 16 == 0 and t1 % 16 == 0 and t1 - t0 <= 32 * 16
+        mem = mlist[moff:moff + nm]
+        assert set(mem[:, 0]) == set(range(16 * group[first_seq], 16 * group[first_seq] + 16))
+        by_group.setdefault(group[first_seq], []).append((t0, t1, mem))
+    assert len(by_group) == 16
+    for g, ps in by_group.items():
+        ps.sort(key=lambda x: x[0])
+        assert ps[0][0] == 0 and ps[-1][1] == 2048
+    # each sequence's records: a contiguous run holding its prefix and suffix pieces exactly once
+    recs = {}
+    for s, slot in mlist:
+        recs.setdefault(s, []).append(slot)
+    for s, t0, t1, ctx, slot, *_ in items:
+        recs.setdefault(s, []).append(slot)
+    for s, first, n, _ in merges:
+        assert sorted(recs[s]) == list(range(first, first + n))
+
+
+def test_cascade_plan_validation_and_subgroups(pool):
+    lens = np.array([100, 40, 64, 300] + [64] * 20, np.int32)
+    group = np.array([0, 0, -1, 0] + [1] * 20, np.int32)
+    plen = np.array([32, 64], np.int32)
+    info, plan = pa.pa_cascade_plan(pool, lens, group, plen, 32)
+    pitems, mlist = _decode_cascade(info, plan)
+    assert sorted(pitems[:, 3].tolist()) == [3, 4, 16]            # group 1 split 16 + 4
+    lib = pa.load_library()
+    i2 = pa.PlanInfo()
+    bad = np.array([30, 64], np.int32)                            # not whole blocks
+    assert lib.pa_cascade_plan(pool, lens.ctypes.data, len(lens), group.ctypes.data,
+                               bad.ctypes.data, 2, 32, None, 0, i2) == pa.PA_ERR_INVALID_ARG
+    too_long = np.array([128, 64], np.int32)                      # longer than member 1's context
+    assert lib.pa_cascade_plan(pool, lens.ctypes.data, len(lens), group.ctypes.data,
+                               too_long.ctypes.data, 2, 32, None, 0, i2) == pa.PA_ERR_INVALID_ARG
+    g_bad = group.copy()
+    g_bad[0] = 5
+    assert lib.pa_cascade_plan(pool, lens.ctypes.data, len(lens), g_bad.ctypes.data,
+                               plen.ctypes.data, 2, 32, None, 0, i2) == pa.PA_ERR_INVALID_ARG
+
+
+def test_cascade_run_rejects_appending_into_a_shared_block(pool):
+    lens = np.array([64, 80], np.int32)                 # sequence 0's newest token is in the prefix
+    info, _ = pa.pa_cascade_plan(pool, lens, np.array([0, 0], np.int32), np.array([64], np.int32), 32)
+    assert info.shared_newest == 1
+    lib = pa.load_library()
+    assert lib.pa_decode_run(pool, 0, info, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, 0.1, FAKE,
+                             1 << 30, None) == pa.PA_ERR_INVALID_ARG
