@@ -72,6 +72,8 @@ def main():
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--cascade", action="store_true",
                     help="for a workload with shared prefixes, schedule with pa_cascade_plan")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -255,6 +257,31 @@ def main():
     log(f"timed {args.steps} steps: mean {ms_per_step:.4f} ms, min {min(step_ms):.4f} ms, "
         f"wall {1e3 * wall / args.steps:.4f} ms/step; decode_partial mean {np.mean(part_us):.2f} us")
 
+    # optional: the same step captured once in a HIP graph and replayed
+    graph_ms = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            sptr_saved = sptr
+            run_args[:] = [a[:-1] + (side.cuda_stream,) for a in run_args]
+            with torch.cuda.graph(graph, stream=side):
+                step()
+            run_args[:] = [a[:-1] + (sptr_saved,) for a in run_args]
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = a_ev.elapsed_time(b_ev) / args.steps
+        log(f"HIP graph replay: {graph_ms:.4f} ms/step")
+
     kv_gbps = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = w.batch / (ms_per_step * 1e-3)
     kb = roofline.split_kernel_bytes(w.ctx_lens, HQ, HKV, D, B)
@@ -362,6 +389,7 @@ def main():
                      else "decode_partial_kernel + decode_merge_planned_kernel",
                      "bytes_per_launch": kb["total"],
                      "mean_launch_us": round(part_mean_s * 1e6, 3)},
+        "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
         "hbm_read_probe_GBps": round(probe, 1) if probe else None,
         "pct_of_probe": round(100 * kv_gbps / probe, 2) if probe else None,
         "cpu_baseline": cpu,
