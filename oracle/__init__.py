@@ -32,6 +32,18 @@ def _load():
         lib.pa_oracle_kv_bytes_per_token.argtypes = [ctypes.c_int32] * 4
         lib.pa_oracle_page_bytes.restype = ctypes.c_int64
         lib.pa_oracle_page_bytes.argtypes = [ctypes.c_int32] * 5
+        lib.pa_oracle_e4m3_to_f64.restype = ctypes.c_double
+        lib.pa_oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.pa_oracle_f64_to_e4m3.restype = ctypes.c_uint8
+        lib.pa_oracle_f64_to_e4m3.argtypes = [ctypes.c_double]
+        lib.pa_oracle_quantize_e4m3.restype = ctypes.c_uint8
+        lib.pa_oracle_quantize_e4m3.argtypes = [ctypes.c_uint16, ctypes.c_float]
+        lib.pa_oracle_decode_e4m3.restype = ctypes.c_int
+        lib.pa_oracle_decode_e4m3.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_void_p, ctypes.c_int32]
         lib.pa_oracle_decode.restype = ctypes.c_int
         lib.pa_oracle_decode.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -123,3 +135,51 @@ def relabelled_cache(ids, k_blocks, v_blocks, tables, ctx_lens, block_size):
         out_tables[s, :held[s]] = pos
     n, b, hkv, d = k_blocks.shape
     return k_blocks.reshape(n * b, hkv, d), v_blocks.reshape(n * b, hkv, d), out_tables
+
+
+def e4m3_to_f64(code: int) -> float:
+    """E4M3 code -> exact double (the oracle's own decoder)."""
+    return _load().pa_oracle_e4m3_to_f64(int(code) & 0xFF)
+
+
+def f64_to_e4m3(x: float) -> int:
+    """double -> E4M3 code: nearest, ties to even, saturating at 448."""
+    return int(_load().pa_oracle_f64_to_e4m3(float(x)))
+
+
+def quantize_e4m3(values_f16, scale: float) -> np.ndarray:
+    """Codes an FP8 pool holds for F16 values written with this scale:
+    fl32(fl32(x) * fl32(1/scale)) rounded to nearest even, saturating."""
+    v = np.ascontiguousarray(values_f16, dtype=np.float16)
+    inv = float(np.float32(1.0 / scale))
+    lib = _load()
+    flat = v.reshape(-1).view(np.uint16)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    table = {}
+    for i, b in enumerate(flat):
+        c = table.get(b)
+        if c is None:
+            c = table[b] = lib.pa_oracle_quantize_e4m3(int(b), inv)
+        out[i] = c
+    return out.reshape(v.shape)
+
+
+def decode_e4m3(q, k_codes, v_codes, block_tables, ctx_lens, scale, block_size, k_scale, v_scale,
+                threads=0):
+    """fp64 attention over FP8 (E4M3) slot caches [num_slots, Hkv, d] of codes."""
+    q = np.ascontiguousarray(q, dtype=np.float16)
+    k_codes = np.ascontiguousarray(k_codes, dtype=np.uint8)
+    v_codes = np.ascontiguousarray(v_codes, dtype=np.uint8)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    batch, hq, d = q.shape
+    num_slots, hkv, d2 = k_codes.shape
+    assert d2 == d and v_codes.shape == k_codes.shape
+    out = np.empty((batch, hq, d), dtype=np.float64)
+    rc = _load().pa_oracle_decode_e4m3(
+        _ptr(q.view(np.uint16)), _ptr(k_codes), _ptr(v_codes), num_slots, _ptr(tables),
+        tables.shape[1], _ptr(lens), batch, hq, hkv, d, block_size, float(scale), float(k_scale),
+        float(v_scale), _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its inputs (code {rc})")
+    return out

@@ -34,11 +34,12 @@
  *  - the same physical block may appear in several tables (and twice in one
  *    table); each occurrence is simply read.
  *
- * Parity pins (tests/test_oracle_pins.py): brute force over a contiguous
- * cache, torch's scaled_dot_product_attention in fp64, permutation of block
- * ids, ctx = 1, identical keys, the two-token sigmoid form, V scaling, the
- * pages' slot example and sizing figures.  No function here is
- * "parity unpinned".
+ * Parity pins (tests/test_oracle_pins.py, tests/test_oracle_fp8.py): brute
+ * force over a contiguous cache, torch's scaled_dot_product_attention in fp64,
+ * permutation of block ids, ctx = 1, identical keys, the two-token sigmoid
+ * form, V scaling, the pages' slot example and sizing figures; the E4M3
+ * decoder and encoder against the format's closed forms and torch's
+ * float8_e4m3fn.  No function here is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -201,6 +202,157 @@ int pa_oracle_decode(const uint16_t *q, const uint16_t *k_slots, const uint16_t 
         for (int32_t i = 0; i < head_dim; ++i)
             o[i] /= l;
 
+        free(z);
+        free(qd);
+    }
+    return failed ? 3 : 0;
+}
+
+/* ---- FP8 E4M3 (OCP "e4m3fn") key/value storage ---------------------------
+ * The pages state only that an FP8 KV cache stores one byte per value and
+ * halves the page ("vLLM Architecture and Installation", Example 6); the
+ * format is read as OCP E4M3: 1 sign bit, 4 exponent bits (bias 7), 3
+ * fraction bits, no infinities, S.1111.111 = NaN, largest finite 448.  A
+ * stored code means code_value * scale for a per-layer scale of K or of V. */
+
+/* code -> double, from the format definition:
+ *   e == 0            : frac * 2^-9 (subnormal)
+ *   e == 15, frac == 7: NaN
+ *   otherwise         : (8 + frac) * 2^(e - 10) */
+double pa_oracle_e4m3_to_f64(uint8_t code)
+{
+    const int sign = (code >> 7) & 1;
+    const int e = (code >> 3) & 0xf;
+    const int frac = code & 0x7;
+    double v;
+    if (e == 15 && frac == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)frac, -9);
+    else
+        v = ldexp((double)(8 + frac), e - 10);
+    return sign ? -v : v;
+}
+
+/* double -> code: round to nearest, ties to even, magnitudes beyond 448
+ * saturate to 448 (no infinities in the format); NaN -> 0x7f.  Written as a
+ * search over the 127 non-negative finite codes, which are ordered by value. */
+uint8_t pa_oracle_f64_to_e4m3(double x)
+{
+    if (isnan(x))
+        return 0x7f;
+    const int neg = signbit(x) ? 1 : 0;
+    double a = fabs(x);
+    uint8_t best = 0;
+    if (a >= 448.0) {
+        best = 0x7e;
+    } else {
+        /* the largest code whose value is <= a, then compare with the next */
+        uint8_t lo = 0;
+        for (uint8_t c = 0; c < 0x7f; ++c)
+            if (pa_oracle_e4m3_to_f64(c) <= a)
+                lo = c;
+        const double vlo = pa_oracle_e4m3_to_f64(lo);
+        if (lo == 0x7e || vlo == a) {
+            best = lo;
+        } else {
+            const double vhi = pa_oracle_e4m3_to_f64((uint8_t)(lo + 1));
+            const double dlo = a - vlo, dhi = vhi - a;
+            if (dlo < dhi)
+                best = lo;
+            else if (dhi < dlo)
+                best = (uint8_t)(lo + 1);
+            else
+                best = (lo & 1) ? (uint8_t)(lo + 1) : lo; /* tie: even code */
+        }
+    }
+    return (uint8_t)(best | (neg << 7));
+}
+
+/* The stored code of an F16 value written into an FP8 pool with scale s:
+ * the product fl32(fl32(x) * r), r = fl32(1 / s), rounded as above. */
+uint8_t pa_oracle_quantize_e4m3(uint16_t f16_bits, float inv_scale)
+{
+    const float x = (float)pa_oracle_f16_to_f64(f16_bits);
+    const float y = x * inv_scale;
+    return pa_oracle_f64_to_e4m3((double)y);
+}
+
+/* Decode step over FP8 pools: identical to pa_oracle_decode except that a
+ * key or value component is code_value * k_scale (or v_scale). */
+int pa_oracle_decode_e4m3(const uint16_t *q, const uint8_t *k_slots, const uint8_t *v_slots,
+                          int64_t num_slots, const int32_t *block_tables, int32_t max_blocks,
+                          const int32_t *ctx_lens, int32_t batch, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, double scale,
+                          double k_scale, double v_scale, double *out, int32_t num_threads)
+{
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks < 0 || num_q_heads % num_kv_heads != 0)
+        return 1;
+    for (int32_t s = 0; s < batch; ++s) {
+        const int64_t ctx = ctx_lens[s];
+        if (ctx < 0 || ctx > (int64_t)max_blocks * block_size)
+            return 2;
+        const int32_t *row = block_tables + (int64_t)s * max_blocks;
+        for (int64_t t = 0; t < ctx; ++t) {
+            const int64_t slot = pa_oracle_slot(row, block_size, t);
+            if (slot < 0 || slot >= num_slots)
+                return 2;
+        }
+    }
+    const int32_t group = num_q_heads / num_kv_heads;
+    const int64_t rows = (int64_t)batch * num_q_heads;
+    int failed = 0;
+#ifdef _OPENMP
+    if (num_threads <= 0)
+        num_threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads) reduction(| : failed)
+#endif
+    for (int64_t r = 0; r < rows; ++r) {
+        const int32_t s = (int32_t)(r / num_q_heads);
+        const int32_t h = (int32_t)(r % num_q_heads);
+        const int32_t g = h / group;
+        const int64_t ctx = ctx_lens[s];
+        const int32_t *row = block_tables + (int64_t)s * max_blocks;
+        double *o = out + r * head_dim;
+        for (int32_t i = 0; i < head_dim; ++i)
+            o[i] = 0.0;
+        if (ctx == 0)
+            continue;
+        double *z = (double *)malloc(sizeof(double) * (size_t)ctx);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)head_dim);
+        if (!z || !qd) {
+            free(z);
+            free(qd);
+            failed |= 1;
+            continue;
+        }
+        for (int32_t i = 0; i < head_dim; ++i)
+            qd[i] = pa_oracle_f16_to_f64(q[r * head_dim + i]);
+        double m = -INFINITY;
+        for (int64_t t = 0; t < ctx; ++t) {
+            const int64_t slot = pa_oracle_slot(row, block_size, t);
+            const uint8_t *kr = k_slots + (slot * num_kv_heads + g) * head_dim;
+            double dot = 0.0;
+            for (int32_t i = 0; i < head_dim; ++i)
+                dot += qd[i] * (pa_oracle_e4m3_to_f64(kr[i]) * k_scale);
+            z[t] = scale * dot;
+            if (z[t] > m)
+                m = z[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < ctx; ++t) {
+            z[t] = exp(z[t] - m);
+            l += z[t];
+        }
+        for (int64_t t = 0; t < ctx; ++t) {
+            const int64_t slot = pa_oracle_slot(row, block_size, t);
+            const uint8_t *vr = v_slots + (slot * num_kv_heads + g) * head_dim;
+            for (int32_t i = 0; i < head_dim; ++i)
+                o[i] += z[t] * (pa_oracle_e4m3_to_f64(vr[i]) * v_scale);
+        }
+        for (int32_t i = 0; i < head_dim; ++i)
+            o[i] /= l;
         free(z);
         free(qd);
     }

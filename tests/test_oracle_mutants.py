@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 from oracle import build as oracle_build
+import tests.test_oracle_fp8 as fp8_pins
 import tests.test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle_build.LIB), "pa_oracle.c")
@@ -30,12 +31,19 @@ MUTANTS = {
                            "for (int64_t t = 0; t < ctx; ++t) {\n            z[t] = (t == ctx - 1 && ctx > 1) ? 0.0 : exp"),
     "q head as kv index in V": ("(slot * num_kv_heads + g) * head_dim;\n            for (int32_t i = 0; i < head_dim; ++i)\n                o[i]",
                                 "(slot * num_kv_heads + (h % num_kv_heads)) * head_dim;\n            for (int32_t i = 0; i < head_dim; ++i)\n                o[i]"),
+    "e4m3 exponent bias": ("ldexp((double)(8 + frac), e - 10)", "ldexp((double)(8 + frac), e - 11)"),
+    "e4m3 ties round up": ("best = (lo & 1) ? (uint8_t)(lo + 1) : lo; /* tie: even code */",
+                           "best = (uint8_t)(lo + 1);"),
+    "e4m3 overflow to NaN": ("        best = 0x7e;\n    } else {", "        best = 0x7f;\n    } else {"),
+    "fp8 k_scale dropped": ("(pa_oracle_e4m3_to_f64(kr[i]) * k_scale)", "(pa_oracle_e4m3_to_f64(kr[i]))"),
 }
 
 
 def _pin_calls():
     calls = []
-    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+    members = inspect.getmembers(pins, inspect.isfunction) + \
+        inspect.getmembers(fp8_pins, inspect.isfunction)
+    for name, fn in members:
         if not name.startswith("test_"):
             continue
         marks = getattr(fn, "pytestmark", [])
