@@ -4,7 +4,9 @@
 Default workload: the full 32-layer decode step of the 8B geometry -- batch 32,
 every context 4096 tokens, 32 query heads / 8 KV heads, head_dim 128,
 block_size 16, F16 K/V ~ N(0, 1), a fresh random block table per layer in a
-pool of twice the needed blocks.  One step = build the schedule on the host
+pool of twice the needed blocks.  --kv-dtype fp8 stores the same values as
+E4M3 codes (per-layer key and value scales 0.02: N(0, 1) values span about
++-250 of the format's +-448) and reads half the bytes.  One step = build the schedule on the host
 from the step's context lengths (pa_decode_plan), copy it to the GPU
 asynchronously, then for each of the 32 layers pa_decode_run with the newest
 token's K/V: it stores them into their slots and attends over the whole
@@ -30,7 +32,10 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: achieved KV GB/s (% HBM peak) and decode tokens/s"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_64_amd", "csrc", "pa_kernels.hip")
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partial_c3_counters.txt")
+COUNTERS_FILES = {"f16": os.path.join(ROOT, "profiles", "decode_partial_c3_counters.txt"),
+                  "fp8": os.path.join(ROOT, "profiles", "decode_partial_fp8_c3_counters.txt")}
+COUNTERS_CONFIG = 3          # the workload the counter files were taken on
+FP8_SCALE = 0.02
 
 
 def log(msg):
@@ -42,13 +47,14 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def read_counters():
+def read_counters(kv_dtype):
     """HBM traffic per decode_partial launch from the committed rocprofv3 summary,
     or None when it is missing or was taken on other kernel source."""
-    if not os.path.exists(COUNTERS_FILE):
+    path = COUNTERS_FILES[kv_dtype]
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line:
                 key, val = line.split(":", 1)
@@ -70,6 +76,8 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--kv-dtype", choices=("f16", "fp8"), default="f16",
+                    help="K/V storage: F16, or FP8 E4M3 codes with per-layer scales")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -111,18 +119,27 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
         return
+    if args.cascade and args.kv_dtype == "fp8":
+        print("--cascade needs an F16 pool (the shared-prefix kernel reads F16 tiles)",
+              file=sys.stderr)
+        sys.exit(2)
     w = workloads.config(args.config, args.seed)
     B, HQ, HKV, D = w.block_size, w.num_q_heads, w.num_kv_heads, w.head_dim
     log(f"workload: {w.name}; pool {w.layers} layers x {w.pool_blocks} blocks")
 
     # ---- stage the pool through pa_write_kv, layer by layer ----
     t_stage = time.time()
-    pool = pa.Pool(w.layers, w.pool_blocks, HKV, D, B, device=dev, fill=0.0)
+    fp8 = args.kv_dtype == "fp8"
+    eb = 1 if fp8 else 2
+    pool = pa.Pool(w.layers, w.pool_blocks, HKV, D, B, device=dev, fill=0.0,
+                   dtype=pa.PA_FP8_E4M3 if fp8 else pa.PA_F16)
     q_dev, tables_dev, knew, vnew = [], [], [], []
     host0 = None
     ctx = w.ctx_lens.astype(np.int64)
     for layer in range(w.layers):
         ids, k, v = w.kv_blocks(layer)
+        if fp8:
+            pool.set_scales(layer, FP8_SCALE, FP8_SCALE)
         pool.write_blocks(layer, torch.from_numpy(ids).to(dev), torch.from_numpy(k).to(dev),
                           torch.from_numpy(v).to(dev))
         q = w.q(layer)
@@ -207,7 +224,7 @@ def main():
                 raise RuntimeError(f"pa_decode_run failed in layer {L}: {rc}")
 
     split = info.max_piece_tokens
-    kv_bytes_step = w.kv_bytes()
+    kv_bytes_step = w.kv_bytes(elem_bytes=eb)
     plib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_64_amd", "libpa_probe.so"))
     plib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                    ctypes.c_void_p]
@@ -284,10 +301,10 @@ def main():
 
     kv_gbps = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = w.batch / (ms_per_step * 1e-3)
-    kb = roofline.split_kernel_bytes(w.ctx_lens, HQ, HKV, D, B)
+    kb = roofline.split_kernel_bytes(w.ctx_lens, HQ, HKV, D, B, kv_elem_bytes=eb)
     part_mean_s = float(np.mean(part_us)) * 1e-6
     achieved = kb["total"] / part_mean_s / 1e9
-    traffic = read_counters()
+    traffic = read_counters(args.kv_dtype) if args.config == COUNTERS_CONFIG else None
 
     # ---- HBM read probe: the bandwidth this GPU reaches on a plain stream ----
     probe = None
@@ -325,6 +342,9 @@ def main():
                 ids, k, v = w.kv_blocks(layer)
                 q, tables = w.q(layer), w.tables(layer)
             kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, w.ctx_lens, B)
+            if fp8:   # the codes the pool holds, computed by the oracle from the F16 values
+                kc = oracle.quantize_e4m3(kc, FP8_SCALE)
+                vc = oracle.quantize_e4m3(vc, FP8_SCALE)
             # the GPU result of this layer (read-only decode of the staged pool)
             rc = f_run(h, layer, ctypes.byref(info), plan_dev.data_ptr(), q_dev[layer].data_ptr(),
                        None, None, outs[layer].data_ptr(), tables_dev[layer].data_ptr(), width,
@@ -335,14 +355,18 @@ def main():
             for lo in range(0, w.batch, 8):
                 seqs = np.arange(lo, min(w.batch, lo + 8))
                 t_cpu = time.perf_counter()
-                ref = oracle.decode(q[seqs], kc, vc, t2[seqs], w.ctx_lens[seqs], w.scale, B,
-                                    threads=threads)
+                if fp8:
+                    ref = oracle.decode_e4m3(q[seqs], kc, vc, t2[seqs], w.ctx_lens[seqs], w.scale,
+                                             B, FP8_SCALE, FP8_SCALE, threads=threads)
+                else:
+                    ref = oracle.decode(q[seqs], kc, vc, t2[seqs], w.ctx_lens[seqs], w.scale, B,
+                                        threads=threads)
                 cpu_s += time.perf_counter() - t_cpu
                 errs.append(float(np.abs(gpu[seqs] - ref).max()))
                 refs.append(float((ref ** 2).sum()))
                 diffs.append(float(((gpu[seqs] - ref) ** 2).sum()))
                 done_seqs += len(seqs)
-                done_bytes += int(w.ctx_lens[seqs].astype(np.int64).sum()) * HKV * D * 4
+                done_bytes += int(w.ctx_lens[seqs].astype(np.int64).sum()) * HKV * D * 2 * eb
                 if cpu_s >= args.cpu_seconds:
                     break
             layer += 1
@@ -350,7 +374,7 @@ def main():
                "kind": "oracle",
                "sample": f"{done_seqs} (sequence, layer) rows of the same step over layers "
                          f"0..{layer - 1} ({done_bytes} B of K/V), fp64, {cpu_s:.1f} s of oracle time",
-               "tokens_per_s_equiv": round(done_bytes / (w.kv_bytes() / w.batch) / cpu_s, 4)}
+               "tokens_per_s_equiv": round(done_bytes / (kv_bytes_step / w.batch) / cpu_s, 4)}
         parity = {"rows": done_seqs, "max_abs_err": max(errs),
                   "rel_l2": (sum(diffs) / sum(refs)) ** 0.5}
         log(f"oracle: {cpu['value']} GB/s on {threads} threads; parity {parity}")
@@ -366,9 +390,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "fp8_e4m3" if fp8 else "f16",
         "data": "synthetic",
-        "config": {"workload": w.name, "layers": w.layers, "batch": w.batch,
+        "config": {"workload": w.name, "kv_dtype": args.kv_dtype, "layers": w.layers, "batch": w.batch,
                    "context": int(w.ctx_lens.max()), "q_heads": HQ, "kv_heads": HKV,
                    "head_dim": D, "block_size": B, "pool_blocks_per_layer": w.pool_blocks,
                    "schedule": {"pieces": info.num_items, "longest_piece_tokens": split,
@@ -379,8 +403,8 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_step": kv_bytes_step,
-        "kv_unique_bytes_per_step": w.kv_unique_bytes(),
-        "unique_kv_GBps": round(w.kv_unique_bytes() / (ms_per_step * 1e-3) / 1e9, 2),
+        "kv_unique_bytes_per_step": w.kv_unique_bytes(eb),
+        "unique_kv_GBps": round(w.kv_unique_bytes(eb) / (ms_per_step * 1e-3) / 1e9, 2),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -38,8 +38,10 @@
  * clamp them so that a bad value cannot make them read or write outside the
  * pool or the tables; the numbers produced from such a value are unspecified.
  *
- * Geometry supported by this build: head_dim 128, block_size 16, F16, and
- * num_q_heads = 4 * num_kv_heads.  Other values return PA_ERR_UNSUPPORTED.
+ * Geometry supported by this build: head_dim 128, block_size 16, F16 or FP8
+ * (E4M3) keys and values, F16 queries and outputs, and num_q_heads = 4 *
+ * num_kv_heads.  Other values return PA_ERR_UNSUPPORTED.  The shared-prefix
+ * schedule (pa_cascade_plan) runs on F16 pools only.
  */
 #ifndef PA_H
 #define PA_H
@@ -62,7 +64,8 @@ typedef enum {
 } pa_status;
 
 typedef enum {
-    PA_F16 = 1 /* IEEE binary16 keys, values, queries and outputs */
+    PA_F16 = 1,      /* IEEE binary16 keys and values */
+    PA_FP8_E4M3 = 2  /* one byte per key/value: OCP FP8 E4M3 code x a per-layer scale */
 } pa_dtype;
 
 /* Geometry of one KV pool.  The pool holds num_layers independent layers of
@@ -76,14 +79,16 @@ typedef struct {
     int32_t block_size;   /* tokens per block; must be 16 */
     int32_t num_kv_heads;
     int32_t head_dim;     /* must be 128 */
-    int32_t dtype;        /* a pa_dtype; must be PA_F16 */
+    int32_t dtype;        /* a pa_dtype: PA_F16 or PA_FP8_E4M3 */
 } pa_pool_desc;
 
 /* Opaque host-side handle. */
 typedef struct pa_pool pa_pool;
 
 /* Bytes of ONE of the two pool buffers (K or V):
- * num_layers * num_blocks * block_size * num_kv_heads * head_dim * 2.
+ * num_layers * num_blocks * block_size * num_kv_heads * head_dim * element
+ * size (2 for PA_F16, 1 for PA_FP8_E4M3: an FP8 cache halves the page,
+ * "vLLM Architecture and Installation", Example 6).
  * Both buffers have this size; 256-byte alignment is required.  Device layout
  * of each buffer (row-major, F16):
  *     [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
@@ -95,6 +100,20 @@ size_t pa_pool_bytes(const pa_pool_desc *desc);
  * into a handle.  Writes *out only on PA_OK.  Touches no device memory. */
 pa_status pa_pool_create(const pa_pool_desc *desc, void *k_pool_dev, void *v_pool_dev,
                          pa_pool **out);
+
+/* Per-layer scales of an FP8 pool (default 1).  An FP8 key/value cache
+ * stores one byte per value, which halves the block size and doubles the
+ * token capacity (vLLM architecture page, Example 6, the FP8 lever; the
+ * batching-and-scheduling page repeats the 1 MiB FP8 block for the 8B
+ * shape).  The pages fix neither the 8-bit format nor the scaling: this
+ * library reads them as OCP E4M3 with one scale per layer for keys and one
+ * for values.  A stored code c means
+ * value(c) * k_scale (keys) or * v_scale (values).  pa_write_kv and the
+ * appending decode store c = E4M3 round-to-nearest-even of fl32(x *
+ * fl32(1/scale)), clamped to +-448 (the format has no infinities; NaN stays
+ * NaN).  Scales must be finite and > 0; they are read when later calls are
+ * enqueued.  For F16 pools they are stored and ignored. */
+pa_status pa_pool_set_scales(pa_pool *pool, int32_t layer, float k_scale, float v_scale);
 
 /* Frees the handle (host memory only); never frees the device buffers.
  * A null pool is accepted and ignored. */

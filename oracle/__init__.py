@@ -153,14 +153,10 @@ def quantize_e4m3(values_f16, scale: float) -> np.ndarray:
     v = np.ascontiguousarray(values_f16, dtype=np.float16)
     inv = float(np.float32(1.0 / scale))
     lib = _load()
-    flat = v.reshape(-1).view(np.uint16)
-    out = np.empty(flat.shape, dtype=np.uint8)
-    table = {}
-    for i, b in enumerate(flat):
-        c = table.get(b)
-        if c is None:
-            c = table[b] = lib.pa_oracle_quantize_e4m3(int(b), inv)
-        out[i] = c
+    # one call of the oracle's routine per F16 bit pattern, then a lookup
+    table = np.fromiter((lib.pa_oracle_quantize_e4m3(b, inv) for b in range(1 << 16)),
+                        dtype=np.uint8, count=1 << 16)
+    out = table[v.reshape(-1).view(np.uint16)]
     return out.reshape(v.shape)
 
 

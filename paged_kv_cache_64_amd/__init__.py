@@ -22,8 +22,9 @@ PA_ERR_UNSUPPORTED = -2
 PA_ERR_WORKSPACE = -3
 PA_ERR_HIP = -4
 PA_F16 = 1
+PA_FP8_E4M3 = 2
 
-EXPORTS = ("pa_pool_bytes", "pa_pool_create", "pa_pool_destroy", "pa_write_kv",
+EXPORTS = ("pa_pool_bytes", "pa_pool_create", "pa_pool_set_scales", "pa_pool_destroy", "pa_write_kv",
            "pa_decode_split_tokens", "pa_decode_workspace_bytes", "pa_decode",
            "pa_append_decode", "pa_decode_partial", "pa_decode_merge", "pa_decode_plan",
            "pa_cascade_plan", "pa_decode_run", "pa_status_string")
@@ -68,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_pool_bytes.argtypes = [ctypes.POINTER(PoolDesc)]
     lib.pa_pool_create.restype = _I
     lib.pa_pool_create.argtypes = [ctypes.POINTER(PoolDesc), _P, _P, ctypes.POINTER(_P)]
+    lib.pa_pool_set_scales.restype = _I
+    lib.pa_pool_set_scales.argtypes = [_P, _I, ctypes.c_float, ctypes.c_float]
     lib.pa_pool_destroy.restype = _I
     lib.pa_pool_destroy.argtypes = [_P]
     lib.pa_write_kv.restype = _I
@@ -147,6 +150,11 @@ def pa_pool_create(desc: PoolDesc, k_pool, v_pool) -> int:
     _check(load_library().pa_pool_create(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
                                          ctypes.byref(handle)), "pa_pool_create")
     return handle.value
+
+
+def pa_pool_set_scales(handle, layer, k_scale, v_scale) -> None:
+    _check(load_library().pa_pool_set_scales(handle, layer, float(k_scale), float(v_scale)),
+           "pa_pool_set_scales")
 
 
 def pa_pool_destroy(handle: int) -> None:
@@ -282,20 +290,33 @@ class Pool:
     """
 
     def __init__(self, num_layers, num_blocks, num_kv_heads=8, head_dim=128, block_size=16,
-                 device="cuda", fill=float("nan")):
-        self.desc = PoolDesc(num_layers, num_blocks, block_size, num_kv_heads, head_dim, PA_F16)
+                 device="cuda", fill=float("nan"), dtype=PA_F16):
+        self.desc = PoolDesc(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype)
         nbytes = pa_pool_bytes(self.desc)
         if nbytes == 0:
             raise ValueError("invalid pool geometry")
         shape = (num_layers, num_blocks, num_kv_heads, block_size, head_dim)
-        self.k = torch.empty(nbytes // 2, dtype=torch.float16, device=device).view(shape)
-        self.v = torch.empty(nbytes // 2, dtype=torch.float16, device=device).view(shape)
-        if fill is not None:
-            self.k.fill_(fill)
-            self.v.fill_(fill)
+        self.dtype = dtype
+        if dtype == PA_FP8_E4M3:
+            # raw E4M3 codes; NaN is 0x7f
+            self.k = torch.empty(nbytes, dtype=torch.uint8, device=device).view(shape)
+            self.v = torch.empty(nbytes, dtype=torch.uint8, device=device).view(shape)
+            if fill is not None:
+                code = 0x7F if fill != fill else 0
+                self.k.fill_(code)
+                self.v.fill_(code)
+        else:
+            self.k = torch.empty(nbytes // 2, dtype=torch.float16, device=device).view(shape)
+            self.v = torch.empty(nbytes // 2, dtype=torch.float16, device=device).view(shape)
+            if fill is not None:
+                self.k.fill_(fill)
+                self.v.fill_(fill)
         self.handle = pa_pool_create(self.desc, self.k, self.v)
         self.num_layers, self.num_blocks = num_layers, num_blocks
         self.num_kv_heads, self.head_dim, self.block_size = num_kv_heads, head_dim, block_size
+
+    def set_scales(self, layer, k_scale, v_scale):
+        pa_pool_set_scales(self.handle, layer, k_scale, v_scale)
 
     def close(self):
         if getattr(self, "handle", None):

@@ -17,6 +17,12 @@ struct pa_pool {
     pa_pool_desc desc;
     void *k;
     void *v;
+    std::vector<float> k_scale;  // per layer (FP8 pools); 1 until set
+    std::vector<float> v_scale;
+    int32_t elem_bytes() const { return desc.dtype == PA_FP8_E4M3 ? 1 : 2; }
+    size_t layer_offset(int32_t layer) const {
+        return static_cast<size_t>(layer) * pa::layer_bytes(desc.num_blocks, desc.num_kv_heads, elem_bytes());
+    }
 };
 
 namespace {
@@ -41,7 +47,17 @@ bool desc_ok(const pa_pool_desc *d) {
 }
 
 bool desc_supported(const pa_pool_desc *d) {
-    return d->block_size == kBlockSize && d->head_dim == kHeadDim && d->dtype == PA_F16;
+    return d->block_size == kBlockSize && d->head_dim == kHeadDim && (d->dtype == PA_F16 || d->dtype == PA_FP8_E4M3);
+}
+
+float inv_scale(float s) { return static_cast<float>(1.0 / static_cast<double>(s)); }
+
+void set_scales(const pa_pool *pool, int32_t layer, pa::DecodeArgs *a) {
+    const float ks = pool->k_scale[layer], vs = pool->v_scale[layer];
+    a->elem_bytes = pool->elem_bytes();
+    a->v_scale = vs;
+    a->inv_k_scale = inv_scale(ks);
+    a->inv_v_scale = inv_scale(vs);
 }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -116,10 +132,9 @@ pa_status fill_decode_args(pa_pool *pool, int32_t layer, const void *q, const vo
         if (!ws || ws_bytes < plan.workspace) return PA_ERR_WORKSPACE;
         if (!aligned(ws, 256)) return PA_ERR_INVALID_ARG;
     }
-    const size_t layer_off = static_cast<size_t>(layer) *
-                             pa::layer_elems(pool->desc.num_blocks, pool->desc.num_kv_heads);
-    a->k_layer = static_cast<const uint16_t *>(pool->k) + layer_off;
-    a->v_layer = static_cast<const uint16_t *>(pool->v) + layer_off;
+    a->k_layer = static_cast<const char *>(pool->k) + pool->layer_offset(layer);
+    a->v_layer = static_cast<const char *>(pool->v) + pool->layer_offset(layer);
+    set_scales(pool, layer, a);
     a->q = static_cast<const uint16_t *>(q);
     a->k_new = static_cast<const uint16_t *>(k_new);
     a->v_new = static_cast<const uint16_t *>(v_new);
@@ -136,7 +151,8 @@ pa_status fill_decode_args(pa_pool *pool, int32_t layer, const void *q, const vo
     a->max_ctx = max_ctx;
     a->split_tokens = plan.split_tokens;
     a->max_splits = plan.max_splits;
-    a->scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    a->scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634 *
+                                        (pool->elem_bytes() == 1 ? pool->k_scale[layer] : 1.0f));
     *plan_out = plan;
     return PA_OK;
 }
@@ -357,11 +373,11 @@ pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, 
     const size_t need = planned_workspace(info->num_slots, info->num_q_heads, &o_bytes);
     if (need > 0 && (!workspace_dev || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace_dev, 256)) return PA_ERR_INVALID_ARG;
-    const size_t layer_off = static_cast<size_t>(layer) *
-                             pa::layer_elems(pool->desc.num_blocks, pool->desc.num_kv_heads);
+    if (info->num_prefix_items > 0 && pool->elem_bytes() != 2) return PA_ERR_UNSUPPORTED;  // cascade: F16 pools
     pa::DecodeArgs a{};
-    a.k_layer = static_cast<const uint16_t *>(pool->k) + layer_off;
-    a.v_layer = static_cast<const uint16_t *>(pool->v) + layer_off;
+    a.k_layer = static_cast<const char *>(pool->k) + pool->layer_offset(layer);
+    a.v_layer = static_cast<const char *>(pool->v) + pool->layer_offset(layer);
+    set_scales(pool, layer, &a);
     a.q = static_cast<const uint16_t *>(q_dev);
     a.k_new = static_cast<const uint16_t *>(k_new_dev);
     a.v_new = static_cast<const uint16_t *>(v_new_dev);
@@ -377,7 +393,8 @@ pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, 
     a.max_ctx = info->max_context_len;
     a.split_tokens = kMaxSplitTokens;
     a.max_splits = 1;
-    a.scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    a.scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634 *
+                                       (pool->elem_bytes() == 1 ? pool->k_scale[layer] : 1.0f));
     a.items = static_cast<const int32_t *>(plan_dev) + pa::kPlanHeader;
     a.merges = a.items + static_cast<size_t>(pa::kItemInts) * info->num_items;
     a.num_items = info->num_items;
@@ -395,7 +412,7 @@ pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, 
 
 size_t pa_pool_bytes(const pa_pool_desc *desc) {
     if (!desc_ok(desc)) return 0;
-    const size_t elem = desc->dtype == PA_F16 ? 2 : 0;
+    const size_t elem = desc->dtype == PA_F16 ? 2 : desc->dtype == PA_FP8_E4M3 ? 1 : 0;
     return static_cast<size_t>(desc->num_layers) * desc->num_blocks * desc->block_size * desc->num_kv_heads *
            desc->head_dim * elem;
 }
@@ -406,10 +423,27 @@ pa_status pa_pool_create(const pa_pool_desc *desc, void *k_pool_dev, void *v_poo
     if (!aligned(k_pool_dev, 256) || !aligned(v_pool_dev, 256)) return PA_ERR_INVALID_ARG;
     pa_pool *p = new (std::nothrow) pa_pool;
     if (!p) return PA_ERR_INVALID_ARG;
-    p->desc = *desc;
-    p->k = k_pool_dev;
-    p->v = v_pool_dev;
+    try {
+        p->desc = *desc;
+        p->k = k_pool_dev;
+        p->v = v_pool_dev;
+        p->k_scale.assign(desc->num_layers, 1.0f);
+        p->v_scale.assign(desc->num_layers, 1.0f);
+    } catch (...) {
+        delete p;
+        return PA_ERR_INVALID_ARG;
+    }
     *out = p;
+    return PA_OK;
+}
+
+pa_status pa_pool_set_scales(pa_pool *pool, int32_t layer, float k_scale, float v_scale) {
+    if (!pool || layer < 0 || layer >= pool->desc.num_layers) return PA_ERR_INVALID_ARG;
+    if (!(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+        return PA_ERR_INVALID_ARG;
+    if (!std::isfinite(1.0f / k_scale) || !std::isfinite(1.0f / v_scale)) return PA_ERR_INVALID_ARG;
+    pool->k_scale[layer] = k_scale;
+    pool->v_scale[layer] = v_scale;
     return PA_OK;
 }
 
@@ -425,11 +459,12 @@ pa_status pa_write_kv(pa_pool *pool, int32_t layer, const void *k_new_dev, const
     if (!k_new_dev || !v_new_dev || !slot_mapping_dev) return PA_ERR_INVALID_ARG;
     if (!aligned(k_new_dev, 16) || !aligned(v_new_dev, 16) || !aligned(slot_mapping_dev, 4))
         return PA_ERR_INVALID_ARG;
-    const size_t layer_off = static_cast<size_t>(layer) *
-                             pa::layer_elems(pool->desc.num_blocks, pool->desc.num_kv_heads);
     pa::WriteKvArgs a{};
-    a.k_layer = static_cast<uint16_t *>(pool->k) + layer_off;
-    a.v_layer = static_cast<uint16_t *>(pool->v) + layer_off;
+    a.k_layer = static_cast<char *>(pool->k) + pool->layer_offset(layer);
+    a.v_layer = static_cast<char *>(pool->v) + pool->layer_offset(layer);
+    a.elem_bytes = pool->elem_bytes();
+    a.inv_k_scale = inv_scale(pool->k_scale[layer]);
+    a.inv_v_scale = inv_scale(pool->v_scale[layer]);
     a.k_new = static_cast<const uint16_t *>(k_new_dev);
     a.v_new = static_cast<const uint16_t *>(v_new_dev);
     a.slot_mapping = slot_mapping_dev;

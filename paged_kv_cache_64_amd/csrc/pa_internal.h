@@ -20,14 +20,18 @@ constexpr int kMaxSplitTokens = kWaves * 64 * kBlockSize;  // a wave owns at mos
 // Device layout of one pool buffer (K or V), F16, row-major:
 //   [num_layers][num_blocks][num_kv_heads][kBlockSize][kHeadDim]
 // One (block, KV head) tile of kBlockSize x kHeadDim is contiguous.
+// Elements are F16 (2 bytes) or FP8 E4M3 codes (1 byte).
 __host__ __device__ inline size_t tile_elems() { return static_cast<size_t>(kBlockSize) * kHeadDim; }
-__host__ __device__ inline size_t layer_elems(int32_t num_blocks, int32_t num_kv_heads) {
-    return static_cast<size_t>(num_blocks) * num_kv_heads * tile_elems();
+__host__ __device__ inline size_t layer_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t elem_bytes) {
+    return static_cast<size_t>(num_blocks) * num_kv_heads * tile_elems() * elem_bytes;
 }
 
 struct WriteKvArgs {
-    uint16_t *k_layer;            // this layer's K base
-    uint16_t *v_layer;            // this layer's V base
+    char *k_layer;                // this layer's K base (bytes)
+    char *v_layer;                // this layer's V base (bytes)
+    int32_t elem_bytes;           // 2: F16 pool, 1: FP8 E4M3 pool
+    float inv_k_scale;            // FP8: stored code = e4m3(x * inv_scale)
+    float inv_v_scale;
     const uint16_t *k_new;        // [n_tokens][num_kv_heads][kHeadDim]
     const uint16_t *v_new;
     const int32_t *slot_mapping;  // [n_tokens]
@@ -37,8 +41,12 @@ struct WriteKvArgs {
 };
 
 struct DecodeArgs {
-    const uint16_t *k_layer;      // this layer's K base
-    const uint16_t *v_layer;      // this layer's V base
+    const char *k_layer;          // this layer's K base (bytes)
+    const char *v_layer;          // this layer's V base (bytes)
+    int32_t elem_bytes;           // 2: F16 pool, 1: FP8 E4M3 pool
+    float v_scale;                // FP8: value = code * scale (K's scale is folded into scale_log2e)
+    float inv_k_scale;
+    float inv_v_scale;
     const uint16_t *q;            // [batch][num_q_heads][kHeadDim]
     const uint16_t *k_new;        // [batch][num_kv_heads][kHeadDim] newest token's K, or null
     const uint16_t *v_new;        // [batch][num_kv_heads][kHeadDim] newest token's V, or null

@@ -31,6 +31,10 @@ namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+// Raw tile data in native vectors (HIP's uint4/uint2 are classes, and arrays
+// of them are not promoted to registers).
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 struct h2x4 {
     h2 v[4];
 };
@@ -92,6 +96,51 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *tile, in
 __device__ __forceinline__ h8 load_tile16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, PA_KV_LOAD_AUX));
 }
+__device__ __forceinline__ u4 load_raw16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, PA_KV_LOAD_AUX));
+}
+__device__ __forceinline__ u2 load_raw8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, PA_KV_LOAD_AUX));
+}
+
+// ---- FP8 (OCP E4M3 on gfx950) storage --------------------------------------
+// Codes are written as round-to-nearest-even of fl32(x * inv_scale) after a
+// clamp to +-448 (the format has no infinities); NaN stays NaN.  Every code
+// is exactly representable in F16 and fp32.
+__device__ __forceinline__ float fp8_clamp(float x) {
+    return __builtin_isnan(x) ? x : __builtin_amdgcn_fmed3f(x, 448.0f, -448.0f);
+}
+__device__ __forceinline__ uint32_t fp8_encode4(float a, float b, float c, float d) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(a), fp8_clamp(b), 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(c), fp8_clamp(d), r, true);
+    return static_cast<uint32_t>(r);
+}
+// 8 F16 values -> 8 codes
+__device__ __forceinline__ u2 fp8_encode8(h8 x, float inv) {
+    u2 r;
+    r.x = fp8_encode4(static_cast<float>(x[0]) * inv, static_cast<float>(x[1]) * inv, static_cast<float>(x[2]) * inv,
+                      static_cast<float>(x[3]) * inv);
+    r.y = fp8_encode4(static_cast<float>(x[4]) * inv, static_cast<float>(x[5]) * inv, static_cast<float>(x[6]) * inv,
+                      static_cast<float>(x[7]) * inv);
+    return r;
+}
+// 8 codes -> 8 fp32 values
+__device__ __forceinline__ void fp8_decode8(u2 raw, float *f) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.x), false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.x), true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.y), false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.y), true);
+    f[0] = a[0], f[1] = a[1], f[2] = b[0], f[3] = b[1], f[4] = c[0], f[5] = c[1], f[6] = d[0], f[7] = d[1];
+}
+// 8 codes -> 8 F16 values (exact)
+__device__ __forceinline__ h8 fp8_decode8_h(u2 raw) {
+    float f[8];
+    fp8_decode8(raw, f);
+    h8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = static_cast<_Float16>(f[e]);
+    return r;
+}
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_ctx, int max_blocks) {
     ctx = ctx < 0 ? 0 : ctx;
@@ -116,10 +165,17 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
     if (slot < 0 || slot >= a.num_slots) return;
     const int64_t blk = slot / kBlockSize;
     const int64_t off = slot % kBlockSize;
-    const int64_t dst = ((blk * a.num_kv_heads + head) * kBlockSize + off) * kHeadDim + chunk * 8;
+    const int64_t dst = ((blk * a.num_kv_heads + head) * kBlockSize + off) * kHeadDim + chunk * 8;  // elements
     const int64_t src = row * kHeadDim + chunk * 8;
-    *reinterpret_cast<uint4 *>(a.k_layer + dst) = *reinterpret_cast<const uint4 *>(a.k_new + src);
-    *reinterpret_cast<uint4 *>(a.v_layer + dst) = *reinterpret_cast<const uint4 *>(a.v_new + src);
+    if (a.elem_bytes == 1) {
+        const h8 kx = *reinterpret_cast<const h8 *>(a.k_new + src);
+        const h8 vx = *reinterpret_cast<const h8 *>(a.v_new + src);
+        *reinterpret_cast<u2 *>(a.k_layer + dst) = fp8_encode8(kx, a.inv_k_scale);
+        *reinterpret_cast<u2 *>(a.v_layer + dst) = fp8_encode8(vx, a.inv_v_scale);
+    } else {
+        *reinterpret_cast<uint4 *>(a.k_layer + 2 * dst) = *reinterpret_cast<const uint4 *>(a.k_new + src);
+        *reinterpret_cast<uint4 *>(a.v_layer + 2 * dst) = *reinterpret_cast<const uint4 *>(a.v_new + src);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -138,8 +194,13 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
 //   V layout in registers: load c, lane l holds token 4c + l/16, dims
 //     8(l%16) .. +7 -- each load instruction is 1 KiB contiguous.
 //   Weights go from the score lanes to the value lanes through 256 B of LDS.
+// FP8 pools (2 KiB tiles): lane l holds token l/4, dims
+//   {64i + 16(l%4) + e : i < 2, e < 16} (two 16-byte loads) and, for V, token
+//   4c + l/16, dims 8(l%16) .. +7 (four 8-byte loads, 512 B contiguous each);
+//   codes are converted to F16 (K, for v_dot2) and fp32 (V) in registers, K's
+//   scale is folded into the score scale and V's into the output.
 // ---------------------------------------------------------------------------
-template <int NBUF>
+template <int NBUF, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     // Planned launches number work-groups item-major with the KV head fastest,
     // so the heads of one piece -- whose tiles share each 32 KiB block of
@@ -204,7 +265,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     const int wb_begin = min(b_end, b_begin + w * per_wave);
     const int wb_end = min(b_end, wb_begin + per_wave);
 
-    // Query of the 4 heads, in the score layout: qv[h][i] = dims 32i+8kq..+7.
+    // Query of the 4 heads in the score layout: chunk i of 8 dims starts at
+    // dim 32i + 8kq (F16 pools) or 64(i/2) + 16kq + 8(i%2) (FP8 pools).
+    auto chunk_dim = [&](int i) { return FP8 ? 64 * (i >> 1) + 16 * kq + 8 * (i & 1) : 32 * i + 8 * kq; };
     h8 qv[kGroup][4];
     {
         const uint16_t *qbase = a.q + (static_cast<size_t>(s) * a.num_q_heads + head0) * kHeadDim;
@@ -212,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         for (int h = 0; h < kGroup; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                qv[h][i] = *reinterpret_cast<const h8 *>(qbase + h * kHeadDim + 32 * i + 8 * kq);
+                qv[h][i] = *reinterpret_cast<const h8 *>(qbase + h * kHeadDim + chunk_dim(i));
     }
 
     // The newest token (position ctx-1) when this call also appends it: the
@@ -223,20 +286,44 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     const bool owns_new = a.k_new != nullptr && new_tok >= t_begin && new_tok < t_end;
     const int new_blk = new_tok / kBlockSize;
     const int new_off = new_tok % kBlockSize;
-    h8 kn[4], vn;
+    u4 kn[4], vn;  // the newest token's K (this lane's dims) and V, in the pool's encoding
     if (owns_new) {
         const size_t row = (static_cast<size_t>(s) * a.num_kv_heads + g) * kHeadDim;
+        if (FP8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kn[i] = *reinterpret_cast<const h8 *>(a.k_new + row + 32 * i + 8 * kq);
-        vn = *reinterpret_cast<const h8 *>(a.v_new + row + 8 * vj);
-        if (w == 0 && lane < 32) {
+            for (int i = 0; i < 2; ++i) {
+                const h8 lo = *reinterpret_cast<const h8 *>(a.k_new + row + 64 * i + 16 * kq);
+                const h8 hi = *reinterpret_cast<const h8 *>(a.k_new + row + 64 * i + 16 * kq + 8);
+                const u2 cl = fp8_encode8(lo, a.inv_k_scale), ch = fp8_encode8(hi, a.inv_k_scale);
+                kn[i] = u4{cl.x, cl.y, ch.x, ch.y};
+            }
+            kn[2] = kn[3] = u4(0u);
+            const u2 cv = fp8_encode8(*reinterpret_cast<const h8 *>(a.v_new + row + 8 * vj), a.inv_v_scale);
+            vn = u4{cv.x, cv.y, 0u, 0u};
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kn[i] = *reinterpret_cast<const u4 *>(a.k_new + row + 32 * i + 8 * kq);
+            vn = *reinterpret_cast<const u4 *>(a.v_new + row + 8 * vj);
+        }
+        // store the row: F16 rows are 16 chunks of 16 B per tensor, FP8 rows 8
+        const int chunks = FP8 ? 8 : 16;
+        if (w == 0 && lane < 2 * chunks) {
             uint32_t phys = static_cast<uint32_t>(a.tables[static_cast<size_t>(s) * a.max_blocks + new_blk]);
             phys = phys > static_cast<uint32_t>(a.num_blocks - 1) ? static_cast<uint32_t>(a.num_blocks - 1) : phys;
-            const size_t dst = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_elems() +
-                               static_cast<size_t>(new_off) * kHeadDim + 8 * (lane & 15);
-            const uint16_t *src = (lane < 16 ? a.k_new : a.v_new) + row + 8 * (lane & 15);
-            uint16_t *pool = const_cast<uint16_t *>(lane < 16 ? a.k_layer : a.v_layer);
-            *reinterpret_cast<uint4 *>(pool + dst) = *reinterpret_cast<const uint4 *>(src);
+            const bool is_k = lane < chunks;
+            const int c = is_k ? lane : lane - chunks;
+            const size_t elems = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_elems() +
+                                 static_cast<size_t>(new_off) * kHeadDim;
+            char *pool = const_cast<char *>(is_k ? a.k_layer : a.v_layer);
+            const uint16_t *src = (is_k ? a.k_new : a.v_new) + row;
+            if (FP8) {
+                const float inv = is_k ? a.inv_k_scale : a.inv_v_scale;
+                const u2 lo = fp8_encode8(*reinterpret_cast<const h8 *>(src + 16 * c), inv);
+                const u2 hi = fp8_encode8(*reinterpret_cast<const h8 *>(src + 16 * c + 8), inv);
+                *reinterpret_cast<u4 *>(pool + elems + 16 * c) = u4{lo.x, lo.y, hi.x, hi.y};
+            } else {
+                *reinterpret_cast<u4 *>(pool + 2 * elems + 16 * c) = *reinterpret_cast<const u4 *>(src + 8 * c);
+            }
         }
     }
 
@@ -248,12 +335,13 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     if (lane < wb_end - wb_begin) tbl_lds[w][lane] = table[wb_begin + lane];
     wave_lds_sync();
     const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
-    const size_t tile_bytes = tile_elems() * sizeof(uint16_t);
-    const char *k_layer = reinterpret_cast<const char *>(a.k_layer);
-    const char *v_layer = reinterpret_cast<const char *>(a.v_layer);
+    constexpr int kElem = FP8 ? 1 : 2;
+    const size_t tile_bytes = tile_elems() * kElem;
+    const char *k_layer = a.k_layer;
+    const char *v_layer = a.v_layer;
     // per-lane byte offsets inside a tile
-    const uint32_t k_off = static_cast<uint32_t>(kt * kHeadDim * 2 + 16 * kq);  // + 64 i
-    const uint32_t v_off = static_cast<uint32_t>(lane * 16);                    // + 1024 c
+    const uint32_t k_off = static_cast<uint32_t>(kt * kHeadDim * kElem + 16 * kq);  // + 64 i
+    const uint32_t v_off = static_cast<uint32_t>(lane * 8 * kElem);                 // + 512 kElem c
 
     float m_run = -INFINITY;  // running max of head kq (log2 units), same in all lanes of that head
     float l_run = 0.0f;       // this lane's share of the running sum of head kq
@@ -263,9 +351,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
 
-    h8 kb[NBUF][4], vb[NBUF][4];
+    u4 kb[NBUF][4], vb[NBUF][4];  // raw tile data (FP8: K uses [0..1], V uses .x .y)
 
-    // Issues the 8 loads of block b into register buffer buf.  Blocks past
+    // Issues the loads of block b into register buffer buf.  Blocks past
     // the wave's run are issued through empty resources (no memory traffic),
     // so every pipeline step issues the same number of loads.
     auto issue = [&](int buf, int b) {
@@ -277,10 +365,20 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         const int bytes = live ? static_cast<int>(tile_bytes) : 0;
         const __amdgpu_buffer_rsrc_t kr = tile_rsrc(k_layer + base, bytes);
         const __amdgpu_buffer_rsrc_t vr = tile_rsrc(v_layer + base, bytes);
+        if (FP8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kb[buf][i] = load_tile16(kr, k_off + 64u * i);
+            for (int i = 0; i < 2; ++i) kb[buf][i] = load_raw16(kr, k_off + 64u * i);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) vb[buf][c] = load_tile16(vr, v_off + 1024u * c);
+            for (int c = 0; c < 4; ++c) {
+                const u2 v2 = load_raw8(vr, v_off + 512u * c);
+                vb[buf][c] = u4{v2.x, v2.y, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kb[buf][i] = load_raw16(kr, k_off + 64u * i);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) vb[buf][c] = load_raw16(vr, v_off + 1024u * c);
+        }
     };
 
     auto consume = [&](int buf, int b) {
@@ -292,6 +390,17 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) vb[buf][c] = (4 * c + vt == new_off) ? vn : vb[buf][c];
         }
+        // K chunks as F16
+        h8 kc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (FP8) {
+                const u4 r = kb[buf][i >> 1];
+                kc[i] = fp8_decode8_h((i & 1) ? u2{r.z, r.w} : u2{r.x, r.y});
+            } else {
+                kc[i] = __builtin_bit_cast(h8, kb[buf][i]);
+            }
+        }
         // ---- scores: partial dots over this lane's 32 dims, 4 heads ----
         float acc[kGroup];
 #pragma unroll
@@ -300,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const h2x4 qq = pairs(qv[h][i]);
-                const h2x4 kk = pairs(kb[buf][i]);
+                const h2x4 kk = pairs(kc[i]);
 #pragma unroll
                 for (int p = 0; p < 4; ++p) x = __builtin_amdgcn_fdot2(qq.v[p], kk.v[p], x, false);
             }
@@ -355,11 +464,19 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float4 pc = *reinterpret_cast<const float4 *>(&p_lds[w][4 * (4 * c + vt)]);
-            h8 vv = vb[buf][c];
-            if (partial && 4 * c + vt >= valid) vv = h8(0);  // stale slots may hold anything
+            u4 vr = vb[buf][c];
+            if (partial && 4 * c + vt >= valid) vr = u4(0u);  // stale slots may hold anything
+            float vf[8];
+            if (FP8) {
+                fp8_decode8(u2{vr.x, vr.y}, vf);
+            } else {
+                const h8 vv = __builtin_bit_cast(h8, vr);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vf[e] = static_cast<float>(vv[e]);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = static_cast<float>(vv[e]);
+                const float x = vf[e];
                 o[0][e] = fmaf(pc.x, x, o[0][e]);
                 o[1][e] = fmaf(pc.y, x, o[1][e]);
                 o[2][e] = fmaf(pc.z, x, o[2][e]);
@@ -421,6 +538,10 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         L += wgt * l_lds[x][h];
         O0 += wgt * s0;
         O1 += wgt * s1;
+    }
+    if (FP8) {  // V's scale
+        O0 *= a.v_scale;
+        O1 *= a.v_scale;
     }
     const size_t row = static_cast<size_t>(s) * a.num_q_heads + head0 + h;
     if (direct) {
@@ -567,9 +688,9 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
     __syncthreads();
 
     const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
-    const size_t tile_bytes = tile_elems() * sizeof(uint16_t);
-    const char *k_layer = reinterpret_cast<const char *>(a.k_layer);
-    const char *v_layer = reinterpret_cast<const char *>(a.v_layer);
+    const size_t tile_bytes = tile_elems() * sizeof(uint16_t);  // F16 pools only
+    const char *k_layer = a.k_layer;
+    const char *v_layer = a.v_layer;
     const uint32_t k_off = static_cast<uint32_t>(n * kHeadDim * 2 + 16 * r);  // + 64 i
     const uint32_t v_off = static_cast<uint32_t>(lane * 16);                  // + 1024 c
 
@@ -699,7 +820,10 @@ hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream) {
 hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
     const dim3 grid = a.items ? dim3(static_cast<uint32_t>(static_cast<int64_t>(a.num_items) * a.num_kv_heads), 1, 1)
                               : dim3(a.max_splits, a.num_kv_heads, a.batch);
-    hipLaunchKernelGGL(decode_partial_kernel<PA_DECODE_NBUF>, grid, dim3(256), 0, stream, a);
+    if (a.elem_bytes == 1)
+        hipLaunchKernelGGL((decode_partial_kernel<PA_DECODE_NBUF, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_partial_kernel<PA_DECODE_NBUF, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

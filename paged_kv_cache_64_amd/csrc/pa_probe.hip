@@ -67,9 +67,45 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(const _Float16 *a, const
     for (int c = 0; c < 4; ++c) d[(4 * r + c) * 16 + m] = acc[c];
 }
 
+// FP8 (OCP E4M3 on gfx950) conversions as the decode kernels use them.
+__global__ __launch_bounds__(256) void probe_fp8_decode_kernel(const uint8_t *codes, float *out) {
+    const int i = threadIdx.x;  // 128 threads x 2 codes
+    if (i >= 128) return;
+    const int packed = codes[2 * i] | (codes[2 * i + 1] << 8);
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(packed, false);
+    out[2 * i] = f[0];
+    out[2 * i + 1] = f[1];
+}
+
+__global__ __launch_bounds__(256) void probe_fp8_encode_kernel(const _Float16 *in, int n, float inv_scale,
+                                                               uint8_t *out) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float x = static_cast<float>(in[i]) * inv_scale;
+    if (!__builtin_isnan(x)) x = __builtin_amdgcn_fmed3f(x, 448.0f, -448.0f);
+    const int r = __builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false);
+    out[i] = static_cast<uint8_t>(r & 0xff);
+}
+
 }  // namespace
 
 extern "C" {
+
+// FP8 decode of all 256 codes (codes: uint8 [256], out: fp32 [256]).
+int32_t pa_probe_fp8_decode(const void *codes, void *out, hipStream_t stream) {
+    hipLaunchKernelGGL(probe_fp8_decode_kernel, dim3(1), dim3(256), 0, stream, static_cast<const uint8_t *>(codes),
+                       static_cast<float *>(out));
+    return static_cast<int32_t>(hipGetLastError());
+}
+
+// FP8 encode of n F16 values times inv_scale (clamped to +-448 unless NaN).
+int32_t pa_probe_fp8_encode(const void *in, int32_t n, float inv_scale, void *out, hipStream_t stream) {
+    if (n <= 0) return 0;
+    hipLaunchKernelGGL(probe_fp8_encode_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
+                       static_cast<const _Float16 *>(in), n, inv_scale, static_cast<uint8_t *>(out));
+    return static_cast<int32_t>(hipGetLastError());
+}
+
 
 // Lane-layout check of the 16x16x16 f16 MFMA: a, b F16 [16][16], d fp32
 // [16][16], one wave.  Returns a hipError_t.

@@ -43,23 +43,27 @@ def kv_bytes_per_token_layer(num_kv_heads, head_dim, elem_bytes=2):
     return num_kv_heads * head_dim * 2 * elem_bytes
 
 
-def split_kernel_bytes(ctx_lens, num_q_heads, num_kv_heads, head_dim, block_size, elem_bytes=2):
+def split_kernel_bytes(ctx_lens, num_q_heads, num_kv_heads, head_dim, block_size,
+                       kv_elem_bytes=2):
     """Algorithmic bytes of one partial-attention launch (one layer): all K/V of
-    every context, each query once, each table entry read once."""
+    every context (kv_elem_bytes per value: 2 for F16, 1 for FP8), each F16
+    query once, each table entry read once."""
     kv = 0
     table = 0
     for c in ctx_lens:
         c = int(c)
-        kv += c * kv_bytes_per_token_layer(num_kv_heads, head_dim, elem_bytes)
+        kv += c * kv_bytes_per_token_layer(num_kv_heads, head_dim, kv_elem_bytes)
         table += 4 * (-(-c // block_size))
-    q = len(ctx_lens) * num_q_heads * head_dim * elem_bytes
+    q = len(ctx_lens) * num_q_heads * head_dim * 2
     return {"kv": kv, "q": q, "table": table, "total": kv + q + table}
 
 
-def step_bytes(ctx_lens, num_q_heads, num_kv_heads, head_dim, block_size, layers, elem_bytes=2):
+def step_bytes(ctx_lens, num_q_heads, num_kv_heads, head_dim, block_size, layers,
+               kv_elem_bytes=2):
     """Algorithmic bytes of a whole decode step: per layer the split-kernel bytes
     plus the F16 output, plus the new token's K/V written per sequence."""
-    per = split_kernel_bytes(ctx_lens, num_q_heads, num_kv_heads, head_dim, block_size, elem_bytes)
-    out = len(ctx_lens) * num_q_heads * head_dim * elem_bytes
-    new_kv = len(ctx_lens) * kv_bytes_per_token_layer(num_kv_heads, head_dim, elem_bytes)
+    per = split_kernel_bytes(ctx_lens, num_q_heads, num_kv_heads, head_dim, block_size,
+                             kv_elem_bytes)
+    out = len(ctx_lens) * num_q_heads * head_dim * 2
+    new_kv = len(ctx_lens) * kv_bytes_per_token_layer(num_kv_heads, head_dim, kv_elem_bytes)
     return layers * (per["total"] + out + new_kv)

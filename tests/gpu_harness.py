@@ -24,16 +24,22 @@ def report(name, **kw):
 class Staged:
     """A workload's layers written into a device pool, plus host copies for the oracle."""
 
-    def __init__(self, w, layers=(0,), pool_layers=None, fill=float("nan"), keep_host=True):
+    def __init__(self, w, layers=(0,), pool_layers=None, fill=float("nan"), keep_host=True,
+                 dtype=pa.PA_F16, kv_scales=(1.0, 1.0)):
+        """dtype PA_FP8_E4M3 stores codes; kv_scales = (k_scale, v_scale) for every layer."""
         self.w = w
         self.layers = tuple(layers)
         nl = pool_layers if pool_layers is not None else max(self.layers) + 1
         self.pool = pa.Pool(nl, w.pool_blocks, w.num_kv_heads, w.head_dim, w.block_size,
-                            fill=fill)
+                            fill=fill, dtype=dtype)
+        self.fp8 = dtype == pa.PA_FP8_E4M3
+        self.kv_scales = tuple(float(x) for x in kv_scales)
         self.lens = torch.from_numpy(w.ctx_lens.copy()).cuda()
         self.host = {}
         self.dev = {}
         for layer in self.layers:
+            if self.fp8:
+                self.pool.set_scales(layer, *self.kv_scales)
             ids, k, v = w.kv_blocks(layer)
             self.pool.write_blocks(layer, torch.from_numpy(ids).cuda(), torch.from_numpy(k).cuda(),
                                    torch.from_numpy(v).cuda())
@@ -61,8 +67,12 @@ class Staged:
             seqs = np.asarray(seqs)
             q, tables, lens = q[seqs], tables[seqs], lens[seqs]
         kc, vc, tables = oracle.relabelled_cache(ids, k, v, tables, lens, self.w.block_size)
-        return oracle.decode(q, kc, vc, tables, lens, self.w.scale if scale is None else scale,
-                             self.w.block_size)
+        scale = self.w.scale if scale is None else scale
+        if self.fp8:
+            ks, vs = self.kv_scales
+            return oracle.decode_e4m3(q, oracle.quantize_e4m3(kc, ks), oracle.quantize_e4m3(vc, vs),
+                                      tables, lens, scale, self.w.block_size, ks, vs)
+        return oracle.decode(q, kc, vc, tables, lens, scale, self.w.block_size)
 
     def close(self):
         self.pool.close()

@@ -49,6 +49,30 @@ def test_pool_bytes_matches_the_pages_sizing(lib):
     assert lib.pa_pool_bytes(None) == 0
 
 
+def test_fp8_pool_bytes_halve(lib):
+    # an FP8 cache stores one byte per value: 1,024 KiB per block over 32 layers
+    fp8 = _desc(layers=32, blocks=1, dtype=pa.PA_FP8_E4M3)
+    assert 2 * pa.pa_pool_bytes(fp8) == 1024 * 1024
+    assert pa.pa_pool_bytes(_desc(layers=3, blocks=7, dtype=pa.PA_FP8_E4M3)) * 2 == \
+        pa.pa_pool_bytes(_desc(layers=3, blocks=7))
+    assert pa.pa_pool_bytes(_desc(dtype=3)) == 0
+
+
+def test_set_scales_validation(lib):
+    handle = pa.pa_pool_create(_desc(layers=2, blocks=4, dtype=pa.PA_FP8_E4M3), FAKE, FAKE)
+    try:
+        pa.pa_pool_set_scales(handle, 1, 0.1, 0.0173)
+        for layer, ks, vs in [(-1, 1.0, 1.0), (2, 1.0, 1.0), (0, 0.0, 1.0), (0, 1.0, -1.0),
+                              (0, float("nan"), 1.0), (0, 1.0, float("inf")),
+                              (0, 1e-45, 1.0)]:       # 1/scale overflows fp32
+            assert lib.pa_pool_set_scales(handle, layer, ks, vs) == pa.PA_ERR_INVALID_ARG
+        assert lib.pa_pool_set_scales(None, 0, 1.0, 1.0) == pa.PA_ERR_INVALID_ARG
+    finally:
+        pa.pa_pool_destroy(handle)
+    with pytest.raises(ValueError):
+        pa.Pool(1, 4, dtype=3, device="cpu")
+
+
 def test_status_strings(lib):
     for code in (pa.PA_OK, pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED, pa.PA_ERR_WORKSPACE,
                  pa.PA_ERR_HIP):

@@ -196,10 +196,10 @@ class Workload:
         return ids, k, v
 
     # -- accounting (what the step must read; used for reporting) -----------
-    def kv_unique_bytes(self) -> int:
+    def kv_unique_bytes(self, elem_bytes: int = 2) -> int:
         """K+V bytes of the distinct (block, offset) slots the step reads, over all
         layers: shared prefix blocks count once."""
-        per_token = self.num_kv_heads * self.head_dim * 2 * 2
+        per_token = self.num_kv_heads * self.head_dim * 2 * elem_bytes
         total = 0
         held = self.blocks_held()
         for layer in range(self.layers if self.fresh_tables_per_layer else 1):
@@ -216,9 +216,10 @@ class Workload:
             total *= self.layers
         return total
 
-    def kv_bytes(self, layers: int | None = None) -> int:
-        """K+V bytes every sequence reads once per layer (logical)."""
-        per_token = self.num_kv_heads * self.head_dim * 2 * 2
+    def kv_bytes(self, layers: int | None = None, elem_bytes: int = 2) -> int:
+        """K+V bytes every sequence reads once per layer (logical); elem_bytes 2
+        for F16 storage, 1 for FP8."""
+        per_token = self.num_kv_heads * self.head_dim * 2 * elem_bytes
         return int(self.ctx_lens.astype(np.int64).sum()) * per_token * (layers or self.layers)
 
 
