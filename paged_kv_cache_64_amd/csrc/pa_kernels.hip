@@ -35,6 +35,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 // of them are not promoted to registers).
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 struct h2x4 {
     h2 v[4];
 };
@@ -90,6 +92,10 @@ constexpr int kRsrcDword3 = 0x00020000;
 #ifndef PA_DECODE_NBUF
 #define PA_DECODE_NBUF 3
 #endif
+// FP8 tiles are half the size, so the FP8 kernel keeps more of them in flight.
+#ifndef PA_DECODE_NBUF_FP8
+#define PA_DECODE_NBUF_FP8 3
+#endif
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *tile, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), static_cast<short>(0), bytes, kRsrcDword3);
 }
@@ -124,22 +130,17 @@ __device__ __forceinline__ u2 fp8_encode8(h8 x, float inv) {
                       static_cast<float>(x[7]) * inv);
     return r;
 }
-// 8 codes -> 8 fp32 values
-__device__ __forceinline__ void fp8_decode8(u2 raw, float *f) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.x), false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.x), true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.y), false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.y), true);
-    f[0] = a[0], f[1] = a[1], f[2] = b[0], f[3] = b[1], f[4] = c[0], f[5] = c[1], f[6] = d[0], f[7] = d[1];
+// Codes 0,1 (HI = false) or 2,3 (HI = true) of a word -> two F16 values.
+// Every E4M3 value is exact in F16; at scale 1 the conversion is exact.
+template <bool HI>
+__device__ __forceinline__ h2 fp8_pair_f16(uint32_t word) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(word), 1.0f, HI);
 }
-// 8 codes -> 8 F16 values (exact)
-__device__ __forceinline__ h8 fp8_decode8_h(u2 raw) {
-    float f[8];
-    fp8_decode8(raw, f);
-    h8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = static_cast<_Float16>(f[e]);
-    return r;
+// 8 codes (2 words) -> 8 F16 values in order
+__device__ __forceinline__ h8 fp8_decode8_h(uint32_t w0, uint32_t w1) {
+    const h2 a = fp8_pair_f16<false>(w0), b = fp8_pair_f16<true>(w0);
+    const h2 c = fp8_pair_f16<false>(w1), d = fp8_pair_f16<true>(w1);
+    return h8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_ctx, int max_blocks) {
@@ -196,9 +197,14 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
 //   Weights go from the score lanes to the value lanes through 256 B of LDS.
 // FP8 pools (2 KiB tiles): lane l holds token l/4, dims
 //   {64i + 16(l%4) + e : i < 2, e < 16} (two 16-byte loads) and, for V, token
-//   4c + l/16, dims 8(l%16) .. +7 (four 8-byte loads, 512 B contiguous each);
-//   codes are converted to F16 (K, for v_dot2) and fp32 (V) in registers, K's
-//   scale is folded into the score scale and V's into the output.
+//   4c + l/16, dims 8(l%16) .. +7 (four 8-byte loads, 512 B contiguous each).
+//   Keys are converted to F16 for v_dot2.  P V runs on the matrix cores: per
+//   block, eight v_mfma_f32_16x16x16_f16 with A = P (rows = the 4 heads, k =
+//   the 16 tokens, k-slot 4(l/16) + c standing for token 4c + l/16) and B = V
+//   (n = l%16 standing for dim 8(l%16) + j in MFMA j), which is the V register
+//   layout once a byte permute gathers one dim of the lane's four tokens; P
+//   reaches the A layout through 128 B of LDS as F16.  K's scale is folded
+//   into the score scale and V's into the output.
 // ---------------------------------------------------------------------------
 template <int NBUF, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
@@ -345,11 +351,17 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
 
     float m_run = -INFINITY;  // running max of head kq (log2 units), same in all lanes of that head
     float l_run = 0.0f;       // this lane's share of the running sum of head kq
-    float o[kGroup][8];       // value layout: o[h][e] for dim 8vj+e over tokens of row vt
+    float o[kGroup][8];       // F16 pools, value layout: o[h][e] for dim 8vj+e over tokens of row vt
+    f4 oacc[8];               // FP8 pools, MFMA j's result: oacc[j][r] = head r, dim 8(l%16) + j
 #pragma unroll
     for (int h = 0; h < kGroup; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oacc[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    // FP8: P of the current block as F16, [head][4 (t % 4) + t / 4], so that
+    // lane l's A operand (tokens 4c + l/16, c < 4) is 8 contiguous bytes
+    __shared__ _Float16 p16_lds[kWaves][kGroup * kBlockSize];
 
     u4 kb[NBUF][4], vb[NBUF][4];  // raw tile data (FP8: K uses [0..1], V uses .x .y)
 
@@ -396,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) {
             if (FP8) {
                 const u4 r = kb[buf][i >> 1];
-                kc[i] = fp8_decode8_h((i & 1) ? u2{r.z, r.w} : u2{r.x, r.y});
+                kc[i] = (i & 1) ? fp8_decode8_h(r.z, r.w) : fp8_decode8_h(r.x, r.y);
             } else {
                 kc[i] = __builtin_bit_cast(h8, kb[buf][i]);
             }
@@ -447,40 +459,69 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
             if (lane < 4) alpha_lds[w][lane] = alpha;
             wave_lds_sync();
             const float4 al = *reinterpret_cast<const float4 *>(alpha_lds[w]);
+            if (FP8) {
+                const f4 a4 = {al.x, al.y, al.z, al.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                o[0][e] *= al.x;
-                o[1][e] *= al.y;
-                o[2][e] *= al.z;
-                o[3][e] *= al.w;
+                for (int j = 0; j < 8; ++j) oacc[j] *= a4;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    o[0][e] *= al.x;
+                    o[1][e] *= al.y;
+                    o[2][e] *= al.z;
+                    o[3][e] *= al.w;
+                }
             }
         }
         const float p = fast_exp2(sc - m_run);
         l_run += p;
-        p_lds[w][lane] = p;  // index 4*kt + kq == lane
-        wave_lds_sync();
-
-        // ---- P V ----
+        if (FP8) {
+            p16_lds[w][kq * kBlockSize + 4 * (kt & 3) + (kt >> 2)] = static_cast<_Float16>(p);
+            wave_lds_sync();
+            // ---- P V on the matrix cores ----
+            // A: rows m = l%16 read head m%4 (rows 4..15 repeat heads 0..3, so every
+            // lane group of the result holds all four heads)
+            const h4 pa = *reinterpret_cast<const h4 *>(&p16_lds[w][(lane & 3) * kBlockSize + 4 * vt]);
+            uint32_t vw[4][2];  // raw codes of token 4c + vt; stale slots may hold anything
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float4 pc = *reinterpret_cast<const float4 *>(&p_lds[w][4 * (4 * c + vt)]);
-            u4 vr = vb[buf][c];
-            if (partial && 4 * c + vt >= valid) vr = u4(0u);  // stale slots may hold anything
-            float vf[8];
-            if (FP8) {
-                fp8_decode8(u2{vr.x, vr.y}, vf);
-            } else {
-                const h8 vv = __builtin_bit_cast(h8, vr);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vf[e] = static_cast<float>(vv[e]);
+            for (int c = 0; c < 4; ++c) {
+                const bool dead = partial && 4 * c + vt >= valid;
+                vw[c][0] = dead ? 0u : vb[buf][c].x;
+                vw[c][1] = dead ? 0u : vb[buf][c].y;
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = vf[e];
-                o[0][e] = fmaf(pc.x, x, o[0][e]);
-                o[1][e] = fmaf(pc.y, x, o[1][e]);
-                o[2][e] = fmaf(pc.z, x, o[2][e]);
-                o[3][e] = fmaf(pc.w, x, o[3][e]);
+            for (int jp = 0; jp < 4; ++jp) {
+                // bytes {c0 dim j, c1 dim j, c0 dim j+1, c1 dim j+1}, j = 2 jp
+                const uint32_t sel = (jp & 1) ? 0x07030602u : 0x05010400u;
+                const int wd = jp >> 1;
+                const uint32_t t01 = __builtin_amdgcn_perm(vw[1][wd], vw[0][wd], sel);
+                const uint32_t t23 = __builtin_amdgcn_perm(vw[3][wd], vw[2][wd], sel);
+                const h2 a01 = fp8_pair_f16<false>(t01), b01 = fp8_pair_f16<true>(t01);
+                const h2 a23 = fp8_pair_f16<false>(t23), b23 = fp8_pair_f16<true>(t23);
+                const h4 v0 = {a01.x, a01.y, a23.x, a23.y};  // dim 2jp of tokens c = 0..3
+                const h4 v1 = {b01.x, b01.y, b23.x, b23.y};  // dim 2jp + 1
+                oacc[2 * jp] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v0, oacc[2 * jp], 0, 0, 0);
+                oacc[2 * jp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v1, oacc[2 * jp + 1], 0, 0, 0);
+            }
+        } else {
+            p_lds[w][lane] = p;  // index 4*kt + kq == lane
+            wave_lds_sync();
+
+            // ---- P V ----
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float4 pc = *reinterpret_cast<const float4 *>(&p_lds[w][4 * (4 * c + vt)]);
+                u4 vr = vb[buf][c];
+                if (partial && 4 * c + vt >= valid) vr = u4(0u);  // stale slots may hold anything
+                const h8 vv = __builtin_bit_cast(h8, vr);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = static_cast<float>(vv[e]);
+                    o[0][e] = fmaf(pc.x, x, o[0][e]);
+                    o[1][e] = fmaf(pc.y, x, o[1][e]);
+                    o[2][e] = fmaf(pc.z, x, o[2][e]);
+                    o[3][e] = fmaf(pc.w, x, o[3][e]);
+                }
             }
         }
         wave_lds_sync();  // p_lds is rewritten by the next block
@@ -507,11 +548,22 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         m_lds[w][lane] = m_run;
         l_lds[w][lane] = l_run;
     }
+    if (FP8) {
+        // every lane group holds all four heads: group vt stores head vt (row 0)
+        float ov[8];
 #pragma unroll
-    for (int h = 0; h < kGroup; ++h) {
-        float4 *dst = reinterpret_cast<float4 *>(&o_lds[w][vt][h][8 * vj]);
-        dst[0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-        dst[1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+        for (int j = 0; j < 8; ++j)
+            ov[j] = vt == 0 ? oacc[j][0] : vt == 1 ? oacc[j][1] : vt == 2 ? oacc[j][2] : oacc[j][3];
+        float4 *dst = reinterpret_cast<float4 *>(&o_lds[w][0][vt][8 * vj]);
+        dst[0] = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        dst[1] = make_float4(ov[4], ov[5], ov[6], ov[7]);
+    } else {
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) {
+            float4 *dst = reinterpret_cast<float4 *>(&o_lds[w][vt][h][8 * vj]);
+            dst[0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+            dst[1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+        }
     }
     __syncthreads();
 
@@ -529,8 +581,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     for (int x = 0; x < kWaves; ++x) {
         const float wgt = mw[x] == -INFINITY ? 0.0f : fast_exp2(mw[x] - M);
         float s0 = 0.0f, s1 = 0.0f;
+        constexpr int kRows = FP8 ? 1 : 4;  // FP8: the MFMA already summed the token rows
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < kRows; ++r) {
             const float2 v = *reinterpret_cast<const float2 *>(&o_lds[x][r][h][d0]);
             s0 += v.x;
             s1 += v.y;
@@ -636,8 +689,6 @@ __global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a)
 // Each member's result is a partial record (o, m, l), merged with the
 // member's own suffix pieces by decode_merge_planned.
 // ---------------------------------------------------------------------------
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef float f4 __attribute__((ext_vector_type(4)));
 struct h4x2 {
     h4 v[2];
 };
@@ -821,7 +872,7 @@ hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
     const dim3 grid = a.items ? dim3(static_cast<uint32_t>(static_cast<int64_t>(a.num_items) * a.num_kv_heads), 1, 1)
                               : dim3(a.max_splits, a.num_kv_heads, a.batch);
     if (a.elem_bytes == 1)
-        hipLaunchKernelGGL((decode_partial_kernel<PA_DECODE_NBUF, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_partial_kernel<PA_DECODE_NBUF_FP8, true>), grid, dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL((decode_partial_kernel<PA_DECODE_NBUF, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();

@@ -47,6 +47,7 @@ __global__ __launch_bounds__(kThreads) void probe_copy_kernel(uint4 *dst, const 
         dst[i] = src[i];
 }
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -77,6 +78,13 @@ __global__ __launch_bounds__(256) void probe_fp8_decode_kernel(const uint8_t *co
     out[2 * i + 1] = f[1];
 }
 
+// The direct FP8 -> F16 pair conversion at scale 1 (4 codes per thread).
+__global__ __launch_bounds__(64) void probe_fp8_decode_f16_kernel(const uint32_t *codes, h2 *out) {
+    const int i = threadIdx.x;  // 64 threads x 4 codes
+    out[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(codes[i]), 1.0f, false);
+    out[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(codes[i]), 1.0f, true);
+}
+
 __global__ __launch_bounds__(256) void probe_fp8_encode_kernel(const _Float16 *in, int n, float inv_scale,
                                                                uint8_t *out) {
     const int i = blockIdx.x * 256 + threadIdx.x;
@@ -95,6 +103,13 @@ extern "C" {
 int32_t pa_probe_fp8_decode(const void *codes, void *out, hipStream_t stream) {
     hipLaunchKernelGGL(probe_fp8_decode_kernel, dim3(1), dim3(256), 0, stream, static_cast<const uint8_t *>(codes),
                        static_cast<float *>(out));
+    return static_cast<int32_t>(hipGetLastError());
+}
+
+// FP8 -> F16 decode of all 256 codes (codes: uint8 [256], out: F16 [256]).
+int32_t pa_probe_fp8_decode_f16(const void *codes, void *out, hipStream_t stream) {
+    hipLaunchKernelGGL(probe_fp8_decode_f16_kernel, dim3(1), dim3(64), 0, stream,
+                       static_cast<const uint32_t *>(codes), static_cast<h2 *>(out));
     return static_cast<int32_t>(hipGetLastError());
 }
 
