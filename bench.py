@@ -214,14 +214,14 @@ def main():
         if rc != 0:
             raise RuntimeError(f"pa_decode_plan failed: {rc}")
         plan_dev.copy_(buf, non_blocking=True)
+        if events is not None:
+            events[0].record(stream)
         for L in range(w.layers):
-            if events is not None:
-                events[L][0].record(stream)
             rc = f_run(*run_args[L])
-            if events is not None:
-                events[L][1].record(stream)
             if rc != 0:
                 raise RuntimeError(f"pa_decode_run failed in layer {L}: {rc}")
+        if events is not None:
+            events[1].record(stream)
 
     split = info.max_piece_tokens
     kv_bytes_step = w.kv_bytes(elem_bytes=eb)
@@ -259,18 +259,18 @@ def main():
     ms_per_step = float(np.mean(step_ms))
 
     # Timed region 2 (the roofline record): the same K steps with an event pair
-    # around every layer's pa_decode_run -- one decode_partial launch when the
-    # schedule merges nothing; event records between launches cost a few
-    # microseconds each, which is why region 1 carries none.
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(w.layers)] for _ in range(args.steps)]
+    # around each step's back-to-back pa_decode_run launches (after the plan
+    # upload) -- one decode_partial launch per layer when the schedule merges
+    # nothing -- so a launch's time is the pair's interval over the layers.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         if flush_buf is not None:
             plib.pa_probe_read(flush_buf.data_ptr(), flush_buf.numel(), sink.data_ptr(), sptr)
         step(ev[i])
     torch.cuda.synchronize()
-    part_us = [1e3 * a.elapsed_time(b) for e in ev for a, b in e]
+    part_us = [1e3 * a.elapsed_time(b) / w.layers for a, b in ev]
     log(f"timed {args.steps} steps: mean {ms_per_step:.4f} ms, min {min(step_ms):.4f} ms, "
         f"wall {1e3 * wall / args.steps:.4f} ms/step; decode_partial mean {np.mean(part_us):.2f} us")
 
