@@ -44,6 +44,12 @@ def _load():
             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_void_p, ctypes.c_int32]
+        lib.pa_oracle_prefill.restype = ctypes.c_int
+        lib.pa_oracle_prefill.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_double, ctypes.c_void_p, ctypes.c_int32]
         lib.pa_oracle_decode.restype = ctypes.c_int
         lib.pa_oracle_decode.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -111,6 +117,39 @@ def decode(q, k_slots, v_slots, block_tables, ctx_lens, scale, block_size, threa
         _ptr(q.view(np.uint16)), _ptr(k_slots.view(np.uint16)), _ptr(v_slots.view(np.uint16)),
         num_slots, _ptr(tables), tables.shape[1], _ptr(lens), batch, hq, hkv, d, block_size,
         float(scale), _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its inputs (code {rc})")
+    return out
+
+
+def prefill(q, k_slots, v_slots, block_tables, query_start, seq_lens, scale, block_size,
+            threads=0):
+    """fp64 output [total_q, num_q_heads, head_dim] of a chunked-prefill / mixed
+    step: sequence s owns packed query rows query_start[s] .. query_start[s+1]-1
+    (its last q_len positions, already in the cache) and query j sees positions
+    0 .. seq_lens[s] - q_len + j.
+
+    q: F16 [total_q, Hq, d]; k_slots/v_slots: F16 [num_slots, Hkv, d];
+    block_tables: int32 [batch, max_blocks]; query_start: int32 [batch + 1];
+    seq_lens: int32 [batch].
+    """
+    q = np.ascontiguousarray(q, dtype=np.float16)
+    k_slots = np.ascontiguousarray(k_slots, dtype=np.float16)
+    v_slots = np.ascontiguousarray(v_slots, dtype=np.float16)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    starts = np.ascontiguousarray(query_start, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    batch = lens.shape[0]
+    total_q, hq, d = q.shape
+    num_slots, hkv, d2 = k_slots.shape
+    assert d2 == d and v_slots.shape == k_slots.shape
+    assert tables.ndim == 2 and tables.shape[0] == batch and starts.shape == (batch + 1,)
+    assert int(starts[-1]) == total_q
+    out = np.empty((total_q, hq, d), dtype=np.float64)
+    rc = _load().pa_oracle_prefill(
+        _ptr(q.view(np.uint16)), _ptr(k_slots.view(np.uint16)), _ptr(v_slots.view(np.uint16)),
+        num_slots, _ptr(tables), tables.shape[1], _ptr(starts), _ptr(lens), batch, hq, hkv, d,
+        block_size, float(scale), _ptr(out), int(threads))
     if rc != 0:
         raise ValueError(f"oracle rejected its inputs (code {rc})")
     return out

@@ -32,9 +32,13 @@
  *    the last block are never read;
  *  - ctx_s == 0 gives an all-zero output row;
  *  - the same physical block may appear in several tables (and twice in one
- *    table); each occurrence is simply read.
+ *    table); each occurrence is simply read;
+ *  - in a chunked-prefill step (pa_oracle_prefill) the chunk's keys and
+ *    values are already stored and query j of a q_len-token chunk sees
+ *    positions 0 .. seq_len - q_len + j.
  *
- * Parity pins (tests/test_oracle_pins.py, tests/test_oracle_fp8.py): brute
+ * Parity pins (tests/test_oracle_pins.py, tests/test_oracle_fp8.py,
+ * tests/test_oracle_prefill.py): brute
  * force over a contiguous cache, torch's scaled_dot_product_attention in fp64,
  * permutation of block ids, ctx = 1, identical keys, the two-token sigmoid
  * form, V scaling, the pages' slot example and sizing figures; the E4M3
@@ -194,6 +198,131 @@ int pa_oracle_decode(const uint16_t *q, const uint16_t *k_slots, const uint16_t 
 
         /* weighted sum of values */
         for (int64_t t = 0; t < ctx; ++t) {
+            const int64_t slot = pa_oracle_slot(row, block_size, t);
+            const uint16_t *vr = v_slots + (slot * num_kv_heads + g) * head_dim;
+            for (int32_t i = 0; i < head_dim; ++i)
+                o[i] += z[t] * pa_oracle_f16_to_f64(vr[i]);
+        }
+        for (int32_t i = 0; i < head_dim; ++i)
+            o[i] /= l;
+
+        free(z);
+        free(qd);
+    }
+    return failed ? 3 : 0;
+}
+
+/*
+ * Chunked prefill / mixed step of attention, one layer.
+ *
+ * "Batching and Scheduling", Example 5, and "vLLM Architecture and
+ * Installation", Example 5: a step gives each request some number of new
+ * tokens under a token budget -- one for a decoding request, a chunk of the
+ * prompt for a prefilling one -- and there is no separate prefill or decode
+ * phase.  Reading (stated): the new tokens' keys and values are already in
+ * the cache when attention runs (as for the decode step), the chunk of
+ * sequence s holds its last q_len_s positions, and query j of the chunk
+ * (position p = seq_len_s - q_len_s + j) attends to positions 0 .. p of its
+ * own sequence (causal attention over the paged history and the chunk).
+ *
+ *   q            F16 bits [total_q][num_q_heads][head_dim], the chunks packed
+ *                in sequence order; sequence s owns rows
+ *                query_start[s] .. query_start[s+1]-1
+ *   k_slots      F16 bits [num_slots][num_kv_heads][head_dim]
+ *   v_slots      F16 bits [num_slots][num_kv_heads][head_dim]
+ *   block_tables int32    [batch][max_blocks]
+ *   query_start  int32    [batch + 1], query_start[0] == 0, nondecreasing
+ *   seq_lens     int32    [batch], seq_lens[s] >= q_len_s (tokens in the
+ *                cache after this step's writes)
+ *   out          double   [total_q][num_q_heads][head_dim]
+ *
+ * Row (j, h) of sequence s, with n = seq_len_s - q_len_s + j + 1 visible
+ * positions and g = h / (num_q_heads/num_kv_heads):
+ *   z[t] = scale * sum_i q[row][h][i] * K[slot(s,t)][g][i]     t = 0 .. n-1
+ *   out[row][h][i] = sum_t exp(z[t] - max z) * V[slot(s,t)][g][i] / sum_t exp(z[t] - max z)
+ * in double, sums in increasing t.
+ *
+ * Returns 0 on success, 1 on a bad geometry, 2 when the query offsets,
+ * lengths or table entries do not fit the arrays, 3 on allocation failure.
+ */
+int pa_oracle_prefill(const uint16_t *q, const uint16_t *k_slots, const uint16_t *v_slots,
+                      int64_t num_slots, const int32_t *block_tables, int32_t max_blocks,
+                      const int32_t *query_start, const int32_t *seq_lens, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, double scale, double *out, int32_t num_threads)
+{
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks < 0 || num_q_heads % num_kv_heads != 0)
+        return 1;
+    if (query_start[0] != 0)
+        return 2;
+    for (int32_t s = 0; s < batch; ++s) {
+        const int64_t q_len = (int64_t)query_start[s + 1] - query_start[s];
+        const int64_t len = seq_lens[s];
+        if (q_len < 0 || len < q_len || len > (int64_t)max_blocks * block_size)
+            return 2;
+        const int32_t *row = block_tables + (int64_t)s * max_blocks;
+        for (int64_t t = 0; t < len; ++t) {
+            const int64_t slot = pa_oracle_slot(row, block_size, t);
+            if (slot < 0 || slot >= num_slots)
+                return 2;
+        }
+    }
+
+    const int32_t group = num_q_heads / num_kv_heads;
+    const int64_t total_q = query_start[batch];
+    const int64_t rows = total_q * num_q_heads;
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (num_threads <= 0)
+        num_threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads) reduction(| : failed)
+#endif
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t qi = r / num_q_heads; /* packed query row */
+        const int32_t h = (int32_t)(r % num_q_heads);
+        const int32_t g = h / group;
+        int32_t s = 0; /* the sequence owning query row qi */
+        while (query_start[s + 1] <= qi)
+            ++s;
+        const int64_t q_len = (int64_t)query_start[s + 1] - query_start[s];
+        const int64_t j = qi - query_start[s];
+        const int64_t n = (int64_t)seq_lens[s] - q_len + j + 1; /* positions 0 .. n-1 */
+        const int32_t *row = block_tables + (int64_t)s * max_blocks;
+        const uint16_t *qh = q + r * head_dim;
+        double *o = out + r * head_dim;
+
+        for (int32_t i = 0; i < head_dim; ++i)
+            o[i] = 0.0;
+        double *z = (double *)malloc(sizeof(double) * (size_t)n);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)head_dim);
+        if (!z || !qd) {
+            free(z);
+            free(qd);
+            failed |= 1;
+            continue;
+        }
+        for (int32_t i = 0; i < head_dim; ++i)
+            qd[i] = pa_oracle_f16_to_f64(qh[i]);
+
+        double m = -INFINITY;
+        for (int64_t t = 0; t < n; ++t) {
+            const int64_t slot = pa_oracle_slot(row, block_size, t);
+            const uint16_t *kr = k_slots + (slot * num_kv_heads + g) * head_dim;
+            double dot = 0.0;
+            for (int32_t i = 0; i < head_dim; ++i)
+                dot += qd[i] * pa_oracle_f16_to_f64(kr[i]);
+            z[t] = scale * dot;
+            if (z[t] > m)
+                m = z[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < n; ++t) {
+            z[t] = exp(z[t] - m);
+            l += z[t];
+        }
+        for (int64_t t = 0; t < n; ++t) {
             const int64_t slot = pa_oracle_slot(row, block_size, t);
             const uint16_t *vr = v_slots + (slot * num_kv_heads + g) * head_dim;
             for (int32_t i = 0; i < head_dim; ++i)

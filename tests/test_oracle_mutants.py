@@ -2,7 +2,8 @@
 
 Each mutant is a textual edit of oracle/pa_oracle.c compiled with gcc into a
 temporary library (CPU only).  The pin tests of test_oracle_pins.py are then
-run against it; at least one must fail.
+run against it (with those of test_oracle_fp8.py and test_oracle_prefill.py);
+at least one must fail.
 """
 import ctypes
 import inspect
@@ -15,6 +16,7 @@ import oracle
 from oracle import build as oracle_build
 import tests.test_oracle_fp8 as fp8_pins
 import tests.test_oracle_pins as pins
+import tests.test_oracle_prefill as prefill_pins
 
 SRC = os.path.join(os.path.dirname(oracle_build.LIB), "pa_oracle.c")
 
@@ -36,13 +38,21 @@ MUTANTS = {
                            "best = (uint8_t)(lo + 1);"),
     "e4m3 overflow to NaN": ("        best = 0x7e;\n    } else {", "        best = 0x7f;\n    } else {"),
     "fp8 k_scale dropped": ("(pa_oracle_e4m3_to_f64(kr[i]) * k_scale)", "(pa_oracle_e4m3_to_f64(kr[i]))"),
+    "prefill causal limit off by one": ("const int64_t n = (int64_t)seq_lens[s] - q_len + j + 1;",
+                                        "const int64_t n = (int64_t)seq_lens[s] - q_len + j;"),
+    "prefill ignores the history": ("const int64_t n = (int64_t)seq_lens[s] - q_len + j + 1;",
+                                    "const int64_t n = j + 1;"),
+    "prefill row owner": ("while (query_start[s + 1] <= qi)", "while (query_start[s + 1] < qi)"),
+    "prefill kv head = h mod Hkv": ("const int32_t g = h / group;\n        int32_t s = 0;",
+                                    "const int32_t g = h % num_kv_heads;\n        int32_t s = 0;"),
 }
 
 
 def _pin_calls():
     calls = []
     members = inspect.getmembers(pins, inspect.isfunction) + \
-        inspect.getmembers(fp8_pins, inspect.isfunction)
+        inspect.getmembers(fp8_pins, inspect.isfunction) + \
+        inspect.getmembers(prefill_pins, inspect.isfunction)
     for name, fn in members:
         if not name.startswith("test_"):
             continue
