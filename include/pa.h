@@ -224,6 +224,8 @@ typedef struct {
     int32_t num_prefix_items; /* shared-prefix pieces (pa_cascade_plan) */
     int32_t num_members;      /* member entries of the shared-prefix pieces */
     int32_t shared_newest;    /* members whose newest token lies in the shared prefix */
+    int32_t num_prefill_items; /* chunked-prefill pieces (pa_prefill_plan) */
+    int32_t num_q_rows;       /* rows of q and out: batch, or the step's query tokens */
     size_t plan_bytes;        /* bytes of the serialised plan */
     size_t workspace_bytes;   /* device workspace pa_decode_run needs (0: none) */
 } pa_plan_info;
@@ -268,6 +270,41 @@ pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info,
                         const void *v_new_dev, void *out_dev, const int32_t *block_tables_dev,
                         int32_t max_blocks_per_seq, float scale, void *workspace_dev,
                         size_t workspace_bytes, hipStream_t stream);
+
+/* ---- Chunked prefill / mixed step -------------------------------------
+ * A step gives every scheduled request some number of new tokens under a
+ * token budget: one for a decoding request, a chunk of its prompt for a
+ * prefilling one, with no separate prefill and decode phases ("Batching and
+ * Scheduling", Example 5; "vLLM Architecture and Installation", Example 5).
+ * Sequence s brings q_len_s = query_start[s+1] - query_start[s] new tokens
+ * (>= 0), whose keys and values are already stored in their slots
+ * (pa_write_kv), and has seq_len_s >= q_len_s tokens in the cache in all.
+ * Its query rows are q rows query_start[s] .. query_start[s+1]-1, packed in
+ * sequence order ([num_q_rows][num_q_heads][head_dim] F16, num_q_rows =
+ * query_start[batch]); query j of the chunk sits at position
+ * p = seq_len_s - q_len_s + j and attends to positions 0 .. p of its own
+ * sequence (causal attention through the block table).  Output rows match
+ * the query rows.
+ *
+ * pa_prefill_plan builds the schedule on the host from query_start_host
+ * (int32 [batch + 1], query_start_host[0] == 0, nondecreasing) and
+ * seq_lens_host (int32 [batch]): one-token rows become decode pieces as in
+ * pa_decode_plan; longer chunks are cut into tiles of 64 query tokens whose
+ * causal key ranges are cut into near-equal pieces for the matrix-core
+ * prefill kernel; rows cut into several pieces are merged.  Sizing, the
+ * two-call protocol and the device copy as pa_decode_plan. */
+pa_status pa_prefill_plan(const pa_pool *pool, const int32_t *query_start_host,
+                          const int32_t *seq_lens_host, int32_t batch, int32_t num_q_heads,
+                          void *plan_host, size_t plan_host_bytes, pa_plan_info *info);
+
+/* One layer of a chunked-prefill / mixed step on a pa_prefill_plan schedule.
+ * q_dev and out_dev hold info->num_q_rows packed rows.  F16 pools only
+ * (PA_ERR_UNSUPPORTED for an FP8 pool when the plan has prefill pieces).
+ * Tables, scale, workspace and stream as pa_decode_run. */
+pa_status pa_prefill_run(pa_pool *pool, int32_t layer, const pa_plan_info *info,
+                         const void *plan_dev, const void *q_dev, void *out_dev,
+                         const int32_t *block_tables_dev, int32_t max_blocks_per_seq, float scale,
+                         void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
 
 /* Static English text for a status code. */
 const char *pa_status_string(pa_status status);

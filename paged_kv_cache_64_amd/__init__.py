@@ -27,7 +27,8 @@ PA_FP8_E4M3 = 2
 EXPORTS = ("pa_pool_bytes", "pa_pool_create", "pa_pool_set_scales", "pa_pool_destroy", "pa_write_kv",
            "pa_decode_split_tokens", "pa_decode_workspace_bytes", "pa_decode",
            "pa_append_decode", "pa_decode_partial", "pa_decode_merge", "pa_decode_plan",
-           "pa_cascade_plan", "pa_decode_run", "pa_status_string")
+           "pa_cascade_plan", "pa_decode_run", "pa_prefill_plan", "pa_prefill_run",
+           "pa_status_string")
 
 
 class PaError(RuntimeError):
@@ -48,6 +49,7 @@ class PlanInfo(ctypes.Structure):
                 ("num_merges", ctypes.c_int32), ("num_slots", ctypes.c_int32),
                 ("max_piece_tokens", ctypes.c_int32), ("num_prefix_items", ctypes.c_int32),
                 ("num_members", ctypes.c_int32), ("shared_newest", ctypes.c_int32),
+                ("num_prefill_items", ctypes.c_int32), ("num_q_rows", ctypes.c_int32),
                 ("plan_bytes", ctypes.c_size_t),
                 ("workspace_bytes", ctypes.c_size_t)]
 
@@ -94,6 +96,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_cascade_plan.restype = _I
     lib.pa_cascade_plan.argtypes = [_P, _P, _I, _P, _P, _I, _I, _P, ctypes.c_size_t,
                                     ctypes.POINTER(PlanInfo)]
+    lib.pa_prefill_plan.restype = _I
+    lib.pa_prefill_plan.argtypes = [_P, _P, _P, _I, _I, _P, ctypes.c_size_t, ctypes.POINTER(PlanInfo)]
+    lib.pa_prefill_run.restype = _I
+    lib.pa_prefill_run.argtypes = [_P, _I, ctypes.POINTER(PlanInfo), _P, _P, _P, _P, _I,
+                                   ctypes.c_float, _P, ctypes.c_size_t, _P]
     lib.pa_decode_run.restype = _I
     lib.pa_decode_run.argtypes = [_P, _I, ctypes.POINTER(PlanInfo), _P, _P, _P, _P, _P, _P, _I,
                                   ctypes.c_float, _P, ctypes.c_size_t, _P]
@@ -262,13 +269,43 @@ def pa_decode_run(handle, layer, info, plan_dev, q, k_new, v_new, out, block_tab
                                         int(workspace_bytes), _stream(stream)), "pa_decode_run")
 
 
+def pa_prefill_plan(handle, query_start_host, seq_lens_host, num_q_heads):
+    """Chunked-prefill / mixed-step schedule: returns (PlanInfo, int32 numpy plan)."""
+    import numpy as np
+
+    qs = np.ascontiguousarray(query_start_host, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    if qs.shape != (lens.shape[0] + 1,):
+        raise ValueError("query_start must have batch + 1 entries")
+    info = PlanInfo()
+    lib = load_library()
+    args = (qs.ctypes.data_as(_P), lens.ctypes.data_as(_P) if lens.size else None,
+            int(lens.shape[0]), num_q_heads)
+    _check(lib.pa_prefill_plan(handle, *args, None, 0, ctypes.byref(info)), "pa_prefill_plan")
+    plan = np.zeros(max(1, info.plan_bytes // 4), dtype=np.int32)
+    _check(lib.pa_prefill_plan(handle, *args, plan.ctypes.data_as(_P), plan.nbytes,
+                               ctypes.byref(info)), "pa_prefill_plan")
+    return info, plan
+
+
+def pa_prefill_run(handle, layer, info, plan_dev, q, out, block_tables, max_blocks_per_seq, scale,
+                   workspace, workspace_bytes, stream=None):
+    _check(load_library().pa_prefill_run(handle, layer, ctypes.byref(info), _ptr(plan_dev), _ptr(q),
+                                         _ptr(out), _ptr(block_tables), max_blocks_per_seq,
+                                         float(scale), _ptr(workspace), int(workspace_bytes),
+                                         _stream(stream)), "pa_prefill_run")
+
+
 class Plan:
     """A host schedule (pa_decode_plan, or pa_cascade_plan when prefix groups are
     given) and its device copy."""
 
     def __init__(self, handle, context_lens_host, num_q_heads, device="cuda",
-                 prefix_group=None, prefix_len=None):
-        if prefix_group is None:
+                 prefix_group=None, prefix_len=None, query_start=None):
+        if query_start is not None:
+            self.info, self.host = pa_prefill_plan(handle, query_start, context_lens_host,
+                                                   num_q_heads)
+        elif prefix_group is None:
             self.info, self.host = pa_decode_plan(handle, context_lens_host, num_q_heads)
         else:
             self.info, self.host = pa_cascade_plan(handle, context_lens_host, prefix_group,
@@ -366,6 +403,22 @@ class Pool:
         pa_decode_run(self.handle, layer, plan.info, plan.dev, q, k_new, v_new, out, block_tables,
                       int(block_tables.shape[1]), scale, plan.workspace, plan.info.workspace_bytes,
                       stream)
+        return out
+
+    def prefill_plan(self, query_start, seq_lens, num_q_heads=None):
+        """pa_prefill_plan from host int32 query_start [batch + 1] and seq_lens [batch]."""
+        return Plan(self.handle, seq_lens, num_q_heads or 4 * self.num_kv_heads, self.k.device,
+                    query_start=query_start)
+
+    def prefill_run(self, layer, plan, q, out, block_tables, scale, stream=None):
+        """pa_prefill_run on a Plan from prefill_plan(); q/out [num_q_rows, Hq, d] F16."""
+        rows = plan.info.num_q_rows
+        _expect(q, torch.float16, (rows, plan.info.num_q_heads, self.head_dim), "q")
+        _expect(out, torch.float16, (rows, plan.info.num_q_heads, self.head_dim), "out")
+        _expect(block_tables, torch.int32, (plan.info.batch, block_tables.shape[1]), "block_tables")
+        pa_prefill_run(self.handle, layer, plan.info, plan.dev, q, out, block_tables,
+                       int(block_tables.shape[1]), scale, plan.workspace,
+                       plan.info.workspace_bytes, stream)
         return out
 
     def split_tokens(self, batch, num_q_heads, max_context_len):

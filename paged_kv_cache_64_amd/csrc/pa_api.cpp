@@ -144,6 +144,7 @@ pa_status fill_decode_args(pa_pool *pool, int32_t layer, const void *q, const vo
     a->o_part = plan.workspace ? static_cast<float *>(ws) : nullptr;
     a->ml_part = plan.workspace ? reinterpret_cast<float *>(static_cast<char *>(ws) + plan.o_bytes) : nullptr;
     a->batch = batch;
+    a->num_q_rows = batch;
     a->num_q_heads = num_q_heads;
     a->num_kv_heads = pool->desc.num_kv_heads;
     a->num_blocks = pool->desc.num_blocks;
@@ -232,12 +233,12 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
                 const int64_t n = n_prefix[s] + np_suffix;
                 first[s] = slots;
                 slots += static_cast<int32_t>(n);
-                merges.insert(merges.end(), {s, first[s], static_cast<int32_t>(n), 0});
+                merges.insert(merges.end(), {s, first[s], static_cast<int32_t>(n), s});
                 if (lens[s] == plen[s]) ++shared_newest;
             } else if (np_suffix > 1) {
                 first[s] = slots;
                 slots += static_cast<int32_t>(np_suffix);
-                merges.insert(merges.end(), {s, first[s], static_cast<int32_t>(np_suffix), 0});
+                merges.insert(merges.end(), {s, first[s], static_cast<int32_t>(np_suffix), s});
             }
         }
         // ordinary pieces (whole contexts, or the suffixes of members)
@@ -310,6 +311,8 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
         inf.num_prefix_items = static_cast<int32_t>(n_pitems);
         inf.num_members = static_cast<int32_t>(n_members);
         inf.shared_newest = shared_newest;
+        inf.num_prefill_items = 0;
+        inf.num_q_rows = batch;
         inf.plan_bytes = sizeof(int32_t) * (pa::kPlanHeader + pa::kItemInts * n_items + merges.size() +
                                             pitems.size() + mlist.size());
         size_t o_bytes = 0;
@@ -322,7 +325,7 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
                                                  inf.num_merges, slots, max_ctx, inf.num_prefix_items};
         p = std::copy(header, header + pa::kPlanHeader, p);
         for (const PlanItem &it : items) {
-            const int32_t rec[pa::kItemInts] = {it.s, it.t_begin, it.t_end, it.ctx, it.slot, 0, 0, 0};
+            const int32_t rec[pa::kItemInts] = {it.s, it.t_begin, it.t_end, it.ctx, it.slot, it.s, 0, 0};
             p = std::copy(rec, rec + pa::kItemInts, p);
         }
         p = std::copy(merges.begin(), merges.end(), p);
@@ -334,31 +337,177 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
     }
 }
 
-}  // namespace
+// Schedule of a chunked-prefill / mixed step.  One-token rows are decode
+// pieces cut exactly as build_plan cuts contexts (item field 5 carries the
+// packed q/out row).  A longer chunk is cut into tiles of kPrefillTile query
+// tokens; tile i of sequence s has its first query at position
+// pos0 = seq_len - q_len + kPrefillTile * i and sees keys [0, pos0 + n_q)
+// causally.  Key ranges are cut into near-equal pieces of at most P blocks,
+// P = ceil(total tile blocks / (kTargetWorkGroups / Hkv)) clamped to
+// [8, kMaxPrefillPieceBlocks]; a tile cut into np pieces owns n_q * np
+// records (token k's come at base + k * np) and one merge per query token.
+// Both kinds of pieces are dispatched longest first.
+pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, const int32_t *lens, int32_t batch,
+                           int32_t num_q_heads, void *plan_host, size_t plan_host_bytes, pa_plan_info *info) {
+    try {
+        if (!pool || !info || batch < 0 || num_q_heads <= 0 || !query_start) return PA_ERR_INVALID_ARG;
+        if (batch > 0 && !lens) return PA_ERR_INVALID_ARG;
+        if (num_q_heads % pool->desc.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+        if (num_q_heads != kGroup * pool->desc.num_kv_heads) return PA_ERR_UNSUPPORTED;
+        if (batch > (1 << 24)) return PA_ERR_UNSUPPORTED;
+        if (query_start[0] != 0) return PA_ERR_INVALID_ARG;
+        int32_t max_ctx = 0;
+        int64_t dec_blocks = 0, tile_blocks = 0;
+        for (int32_t s = 0; s < batch; ++s) {
+            const int64_t q_len = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
+            if (q_len < 0 || lens[s] < q_len) return PA_ERR_INVALID_ARG;
+            max_ctx = std::max(max_ctx, lens[s]);
+            if (q_len == 1) dec_blocks += (lens[s] + kBlockSize - 1) / kBlockSize;
+            for (int64_t j0 = 0; j0 < q_len; j0 += pa::kPrefillTile) {
+                if (q_len == 1) break;
+                const int64_t kend = lens[s] - q_len + std::min<int64_t>(q_len, j0 + pa::kPrefillTile);
+                tile_blocks += (kend + kBlockSize - 1) / kBlockSize;
+            }
+        }
+        const int32_t num_q_rows = query_start[batch];
+        if (num_q_rows > (1 << 24)) return PA_ERR_UNSUPPORTED;
+        const int64_t items_target = std::max<int64_t>(1, kTargetWorkGroups / pool->desc.num_kv_heads);
+        auto cut = [](int64_t nb, int64_t maxp) { return nb == 0 ? int64_t{0} : (nb + maxp - 1) / maxp; };
 
-extern "C" {
-
-pa_status pa_decode_plan(const pa_pool *pool, const int32_t *context_lens_host, int32_t batch, int32_t num_q_heads,
-                         void *plan_host, size_t plan_host_bytes, pa_plan_info *info) {
-    return build_plan(pool, context_lens_host, batch, num_q_heads, nullptr, nullptr, 0, plan_host, plan_host_bytes,
-                      info);
+        int64_t slots = 0;  // records per query head
+        std::vector<int32_t> merges;
+        // decode rows
+        std::vector<PlanItem> items;
+        std::vector<int32_t> item_row;
+        const int64_t piece = std::min<int64_t>(kMaxSplitTokens / kBlockSize,
+                                                std::max<int64_t>(pa::kWaves, cut(dec_blocks, items_target)));
+        for (int32_t s = 0; s < batch; ++s) {
+            if (query_start[s + 1] - query_start[s] != 1) continue;
+            const int32_t ctx = lens[s], row = query_start[s];
+            const int64_t nb = (ctx + kBlockSize - 1) / kBlockSize;
+            const int64_t np = cut(nb, piece);
+            if (np <= 1) {
+                items.push_back({s, 0, ctx, ctx, -1});
+                item_row.push_back(row);
+                continue;
+            }
+            merges.insert(merges.end(), {s, static_cast<int32_t>(slots), static_cast<int32_t>(np), row});
+            const int64_t base = nb / np, extra = nb % np;
+            int64_t b0 = 0;
+            for (int64_t i = 0; i < np; ++i) {
+                const int64_t b1 = b0 + base + (i < extra ? 1 : 0);
+                items.push_back({s, static_cast<int32_t>(b0 * kBlockSize),
+                                 static_cast<int32_t>(std::min<int64_t>(ctx, b1 * kBlockSize)), ctx,
+                                 static_cast<int32_t>(slots + i)});
+                item_row.push_back(row);
+                b0 = b1;
+            }
+            slots += np;
+        }
+        std::vector<size_t> order(items.size());
+        for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+        std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) {
+            return (items[x].t_end - items[x].t_begin) > (items[y].t_end - items[y].t_begin);
+        });
+        // prefill tiles
+        struct PrefillItem {
+            int32_t f[pa::kPrefillItemInts];
+        };
+        std::vector<PrefillItem> pitems;
+        const int64_t ppiece = std::min<int64_t>(pa::kMaxPrefillPieceBlocks,
+                                                 std::max<int64_t>(8, cut(tile_blocks, items_target)));
+        for (int32_t s = 0; s < batch; ++s) {
+            const int64_t q_len = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
+            if (q_len < 2) continue;
+            for (int64_t j0 = 0; j0 < q_len; j0 += pa::kPrefillTile) {
+                const int32_t n_q = static_cast<int32_t>(std::min<int64_t>(pa::kPrefillTile, q_len - j0));
+                const int32_t pos0 = static_cast<int32_t>(lens[s] - q_len + j0);
+                const int32_t kend = pos0 + n_q;
+                const int32_t row0 = static_cast<int32_t>(query_start[s] + j0);
+                const int64_t nb = (kend + kBlockSize - 1) / kBlockSize;
+                const int64_t np = cut(nb, ppiece);
+                if (slots + static_cast<int64_t>(n_q) * np > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+                const int32_t base_slot = np > 1 ? static_cast<int32_t>(slots) : -1;
+                if (np > 1) {
+                    for (int32_t k = 0; k < n_q; ++k)
+                        merges.insert(merges.end(), {s, static_cast<int32_t>(slots + k * np), static_cast<int32_t>(np),
+                                                     row0 + k});
+                    slots += static_cast<int64_t>(n_q) * np;
+                }
+                const int64_t base = nb / np, extra = nb % np;
+                int64_t b0 = 0;
+                for (int64_t p = 0; p < np; ++p) {
+                    const int64_t b1 = b0 + base + (p < extra ? 1 : 0);
+                    PrefillItem it{};
+                    const int32_t f[pa::kPrefillItemInts] = {
+                        s, row0, n_q, pos0, static_cast<int32_t>(b0 * kBlockSize),
+                        static_cast<int32_t>(std::min<int64_t>(kend, b1 * kBlockSize)), base_slot,
+                        static_cast<int32_t>(np), static_cast<int32_t>(p), 0, 0, 0};
+                    std::copy(f, f + pa::kPrefillItemInts, it.f);
+                    pitems.push_back(it);
+                    b0 = b1;
+                }
+            }
+        }
+        std::stable_sort(pitems.begin(), pitems.end(), [](const PrefillItem &x, const PrefillItem &y) {
+            return (x.f[5] - x.f[4]) > (y.f[5] - y.f[4]);
+        });
+        int32_t longest = 0;
+        for (const PlanItem &it : items) longest = std::max(longest, it.t_end - it.t_begin);
+        const size_t n_items = items.size(), n_merges = merges.size() / pa::kMergeInts, n_pf = pitems.size();
+        if (static_cast<int64_t>(std::max(n_items, n_pf)) * pool->desc.num_kv_heads > 0x7fffffff ||
+            n_merges > 0x7fffffff)
+            return PA_ERR_UNSUPPORTED;
+        pa_plan_info inf{};
+        inf.batch = batch;
+        inf.num_q_heads = num_q_heads;
+        inf.max_context_len = max_ctx;
+        inf.num_items = static_cast<int32_t>(n_items);
+        inf.num_merges = static_cast<int32_t>(n_merges);
+        inf.num_slots = static_cast<int32_t>(slots);
+        inf.max_piece_tokens = longest;
+        inf.num_prefill_items = static_cast<int32_t>(n_pf);
+        inf.num_q_rows = num_q_rows;
+        inf.plan_bytes = sizeof(int32_t) * (pa::kPlanHeader + pa::kItemInts * n_items + merges.size() +
+                                            pa::kPrefillItemInts * n_pf);
+        size_t o_bytes = 0;
+        inf.workspace_bytes = planned_workspace(slots, num_q_heads, &o_bytes);
+        *info = inf;
+        if (!plan_host) return PA_OK;
+        if (plan_host_bytes < inf.plan_bytes) return PA_ERR_WORKSPACE;
+        int32_t *p = static_cast<int32_t *>(plan_host);
+        const int32_t header[pa::kPlanHeader] = {pa::kPlanMagic, batch, num_q_heads, inf.num_items,
+                                                 inf.num_merges, inf.num_slots, max_ctx, 0};
+        p = std::copy(header, header + pa::kPlanHeader, p);
+        for (size_t i : order) {
+            const PlanItem &it = items[i];
+            const int32_t rec[pa::kItemInts] = {it.s, it.t_begin, it.t_end, it.ctx, it.slot, item_row[i], 0, 0};
+            p = std::copy(rec, rec + pa::kItemInts, p);
+        }
+        p = std::copy(merges.begin(), merges.end(), p);
+        for (const PrefillItem &it : pitems) p = std::copy(it.f, it.f + pa::kPrefillItemInts, p);
+        return PA_OK;
+    } catch (...) {
+        return PA_ERR_INVALID_ARG;
+    }
 }
 
-pa_status pa_cascade_plan(const pa_pool *pool, const int32_t *context_lens_host, int32_t batch,
-                          const int32_t *prefix_group_host, const int32_t *prefix_len_host, int32_t num_groups,
-                          int32_t num_q_heads, void *plan_host, size_t plan_host_bytes, pa_plan_info *info) {
-    if (num_groups < 0 || (num_groups > 0 && (!prefix_group_host || !prefix_len_host))) return PA_ERR_INVALID_ARG;
-    return build_plan(pool, context_lens_host, batch, num_q_heads, prefix_group_host, prefix_len_host, num_groups,
-                      plan_host, plan_host_bytes, info);
-}
-
-pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, const void *plan_dev,
-                        const void *q_dev, const void *k_new_dev, const void *v_new_dev, void *out_dev,
-                        const int32_t *block_tables_dev, int32_t max_blocks_per_seq, float scale,
-                        void *workspace_dev, size_t workspace_bytes, hipStream_t stream) {
+// One layer on a serialised schedule (pa_decode_plan, pa_cascade_plan or
+// pa_prefill_plan): decode pieces, shared-prefix pieces, prefill pieces, then
+// the merges.
+pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const void *plan_dev, const void *q_dev,
+                   const void *k_new_dev, const void *v_new_dev, void *out_dev, const int32_t *block_tables_dev,
+                   int32_t max_blocks_per_seq, float scale, void *workspace_dev, size_t workspace_bytes,
+                   hipStream_t stream) {
     if (!pool || !info || layer < 0 || layer >= pool->desc.num_layers) return PA_ERR_INVALID_ARG;
     if (info->batch < 0 || info->num_q_heads != kGroup * pool->desc.num_kv_heads) return PA_ERR_INVALID_ARG;
-    if (info->batch == 0 || (info->num_items == 0 && info->num_prefix_items == 0)) return PA_OK;
+    if (info->num_items < 0 || info->num_prefix_items < 0 || info->num_prefill_items < 0 || info->num_merges < 0 ||
+        info->num_slots < 0 || info->num_members < 0 || info->num_q_rows < 0)
+        return PA_ERR_INVALID_ARG;
+    if (info->batch == 0 || (info->num_items == 0 && info->num_prefix_items == 0 && info->num_prefill_items == 0))
+        return PA_OK;
+    if (info->num_q_rows == 0) return PA_ERR_INVALID_ARG;
+    if (k_new_dev && info->num_q_rows != info->batch) return PA_ERR_INVALID_ARG;
     if (!plan_dev || !q_dev || !out_dev || !aligned(plan_dev, 16) || !aligned(q_dev, 16) || !aligned(out_dev, 16))
         return PA_ERR_INVALID_ARG;
     if ((k_new_dev == nullptr) != (v_new_dev == nullptr)) return PA_ERR_INVALID_ARG;
@@ -386,6 +535,7 @@ pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, 
     a.o_part = need ? static_cast<float *>(workspace_dev) : nullptr;
     a.ml_part = need ? reinterpret_cast<float *>(static_cast<char *>(workspace_dev) + o_bytes) : nullptr;
     a.batch = info->batch;
+    a.num_q_rows = info->num_q_rows;
     a.num_q_heads = info->num_q_heads;
     a.num_kv_heads = pool->desc.num_kv_heads;
     a.num_blocks = pool->desc.num_blocks;
@@ -404,10 +554,57 @@ pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, 
     a.members = a.prefix_items + static_cast<size_t>(pa::kPrefixItemInts) * info->num_prefix_items;
     a.num_prefix_items = info->num_prefix_items;
     a.num_members = info->num_members;
+    a.prefill_items = a.members + static_cast<size_t>(pa::kMemberInts) * info->num_members;
+    a.num_prefill_items = info->num_prefill_items;
     if (info->num_items > 0 && pa::launch_decode_partial(a, stream) != hipSuccess) return PA_ERR_HIP;
     if (info->num_prefix_items > 0 && pa::launch_decode_prefix(a, stream) != hipSuccess) return PA_ERR_HIP;
+    if (info->num_prefill_items > 0 && pa::launch_prefill(a, stream) != hipSuccess) return PA_ERR_HIP;
     if (info->num_merges > 0 && pa::launch_decode_merge_planned(a, stream) != hipSuccess) return PA_ERR_HIP;
     return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_plan(const pa_pool *pool, const int32_t *context_lens_host, int32_t batch, int32_t num_q_heads,
+                         void *plan_host, size_t plan_host_bytes, pa_plan_info *info) {
+    return build_plan(pool, context_lens_host, batch, num_q_heads, nullptr, nullptr, 0, plan_host, plan_host_bytes,
+                      info);
+}
+
+pa_status pa_cascade_plan(const pa_pool *pool, const int32_t *context_lens_host, int32_t batch,
+                          const int32_t *prefix_group_host, const int32_t *prefix_len_host, int32_t num_groups,
+                          int32_t num_q_heads, void *plan_host, size_t plan_host_bytes, pa_plan_info *info) {
+    if (num_groups < 0 || (num_groups > 0 && (!prefix_group_host || !prefix_len_host))) return PA_ERR_INVALID_ARG;
+    return build_plan(pool, context_lens_host, batch, num_q_heads, prefix_group_host, prefix_len_host, num_groups,
+                      plan_host, plan_host_bytes, info);
+}
+
+pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, const void *plan_dev,
+                        const void *q_dev, const void *k_new_dev, const void *v_new_dev, void *out_dev,
+                        const int32_t *block_tables_dev, int32_t max_blocks_per_seq, float scale,
+                        void *workspace_dev, size_t workspace_bytes, hipStream_t stream) {
+    if (info && info->num_prefill_items != 0) return PA_ERR_INVALID_ARG;  // a pa_prefill_plan schedule
+    return run_plan(pool, layer, info, plan_dev, q_dev, k_new_dev, v_new_dev, out_dev, block_tables_dev,
+                    max_blocks_per_seq, scale, workspace_dev, workspace_bytes, stream);
+}
+
+pa_status pa_prefill_plan(const pa_pool *pool, const int32_t *query_start_host, const int32_t *seq_lens_host,
+                          int32_t batch, int32_t num_q_heads, void *plan_host, size_t plan_host_bytes,
+                          pa_plan_info *info) {
+    return build_mixed_plan(pool, query_start_host, seq_lens_host, batch, num_q_heads, plan_host, plan_host_bytes,
+                            info);
+}
+
+pa_status pa_prefill_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, const void *plan_dev,
+                         const void *q_dev, void *out_dev, const int32_t *block_tables_dev,
+                         int32_t max_blocks_per_seq, float scale, void *workspace_dev, size_t workspace_bytes,
+                         hipStream_t stream) {
+    if (info && (info->num_prefix_items != 0 || info->num_members != 0)) return PA_ERR_INVALID_ARG;
+    if (pool && info && info->num_prefill_items > 0 && pool->elem_bytes() != 2) return PA_ERR_UNSUPPORTED;
+    return run_plan(pool, layer, info, plan_dev, q_dev, nullptr, nullptr, out_dev, block_tables_dev,
+                    max_blocks_per_seq, scale, workspace_dev, workspace_bytes, stream);
 }
 
 size_t pa_pool_bytes(const pa_pool_desc *desc) {

@@ -80,13 +80,25 @@ struct DecodeArgs {
     const int32_t *members;
     int32_t num_prefix_items;
     int32_t num_members;
+    // chunked-prefill pieces (prefill_kernel) and the packed query rows
+    const int32_t *prefill_items;
+    int32_t num_prefill_items;
+    int32_t num_q_rows;  // rows of q / out: batch for a decode step, total query tokens for a mixed one
 };
 
-// Serialised host plan: a header of kPlanHeader int32, then the items, then
-// the merges.
+// Serialised host plan: a header of kPlanHeader int32, then the decode items,
+// the merges, the shared-prefix items, their members and the prefill items.
+//   decode item  {s, t_begin, t_end, ctx, record slot or -1, q/out row, 0, 0}
+//   merge        {s, first record slot, records, out row}
+//   prefill item {s, first q/out row, query tokens (<= kPrefillTile), position
+//                 of the first, key begin, key end, record base or -1,
+//                 pieces of the tile, this piece, 0, 0, 0}
 constexpr int kPlanHeader = 8;
 constexpr int kItemInts = 8;
 constexpr int kMergeInts = 4;
+constexpr int kPrefillItemInts = 12;
+constexpr int kPrefillTile = 64;             // query tokens per prefill work-group (16 per wave)
+constexpr int kMaxPrefillPieceBlocks = 256;  // key blocks per prefill piece
 constexpr int kPrefixItemInts = 8;
 constexpr int kMemberInts = 2;
 constexpr int kMaxMembers = 16;        // 16 members x 4 query heads = 64 stacked rows
@@ -99,5 +111,6 @@ hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_prefix(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace pa

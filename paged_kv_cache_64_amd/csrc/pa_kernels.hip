@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     // sequence s (context ctx), and where its result goes -- the final F16
     // output (direct) or partial record rec_base + h * rec_stride of query
     // head h.
-    int s, ctx, t_begin, t_end;
+    int s, ctx, t_begin, t_end, qrow;  // qrow: this sequence's row of q and out
     bool direct;
     int64_t rec_base, rec_stride;
     if (a.items != nullptr) {
@@ -236,6 +236,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         // q, out, the tables or the workspace.
         const int32_t *it = a.items + kItemInts * static_cast<size_t>(blockIdx.x / a.num_kv_heads);
         s = min(max(it[0], 0), a.batch - 1);
+        qrow = min(max(it[5], 0), a.num_q_rows - 1);
         ctx = min(max(it[3], 0), a.max_blocks * kBlockSize);
         t_begin = max(it[1], 0);
         t_end = min(it[2], ctx);
@@ -246,6 +247,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     } else {
         const int split = blockIdx.x;
         s = blockIdx.z;
+        qrow = s;
         ctx = clamp_ctx(a.ctx_lens[s], a.max_ctx, a.max_blocks);
         t_begin = split * a.split_tokens;
         t_end = min(ctx, t_begin + a.split_tokens);
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         // empty context, whose output row is zero.
         if (direct && t_begin == 0) {
             const int h = tid >> 6, d0 = (tid & 63) * 2;
-            uint16_t *o = a.out + (static_cast<size_t>(s) * a.num_q_heads + head0 + h) * kHeadDim + d0;
+            uint16_t *o = a.out + (static_cast<size_t>(qrow) * a.num_q_heads + head0 + h) * kHeadDim + d0;
             *reinterpret_cast<uint32_t *>(o) = 0u;
         }
         return;
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     auto chunk_dim = [&](int i) { return FP8 ? 64 * (i >> 1) + 16 * kq + 8 * (i & 1) : 32 * i + 8 * kq; };
     h8 qv[kGroup][4];
     {
-        const uint16_t *qbase = a.q + (static_cast<size_t>(s) * a.num_q_heads + head0) * kHeadDim;
+        const uint16_t *qbase = a.q + (static_cast<size_t>(qrow) * a.num_q_heads + head0) * kHeadDim;
 #pragma unroll
         for (int h = 0; h < kGroup; ++h)
 #pragma unroll
@@ -596,7 +598,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         O0 *= a.v_scale;
         O1 *= a.v_scale;
     }
-    const size_t row = static_cast<size_t>(s) * a.num_q_heads + head0 + h;
+    const size_t row = static_cast<size_t>(qrow) * a.num_q_heads + head0 + h;
     if (direct) {
         const _Float16 r0 = static_cast<_Float16>(O0 / L);
         const _Float16 r1 = static_cast<_Float16>(O1 / L);
@@ -645,13 +647,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a) {
     const int32_t *m = a.merges + kMergeInts * static_cast<size_t>(blockIdx.x);
-    const int s = min(max(m[0], 0), a.batch - 1);
+    const int row = min(max(m[3], 0), a.num_q_rows - 1);  // the output row
     const int first = max(m[1], 0);
     const int n = min(m[2], a.num_slots - first);
     const int h = blockIdx.y * 2 + (threadIdx.x >> 7);
     const int d = threadIdx.x & 127;
     if (h >= a.num_q_heads) return;
-    uint16_t *out = a.out + (static_cast<size_t>(s) * a.num_q_heads + h) * kHeadDim + d;
+    uint16_t *out = a.out + (static_cast<size_t>(row) * a.num_q_heads + h) * kHeadDim + d;
     if (n <= 0) {
         *out = 0;
         return;
@@ -859,6 +861,262 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// prefill: chunked-prefill pieces of a mixed step ("Batching and Scheduling",
+// Example 5), F16 pools.  One work-group per (piece, KV head); a piece is a
+// tile of up to kPrefillTile query tokens of one sequence against a range of
+// its key blocks.  The tile's queries sit at positions pos0 .. pos0+n_q-1 and
+// query t sees keys 0 .. pos0 + t (causal).  Wave w owns query tokens
+// 16w .. 16w+15 and their 64 rows as four 16-row tiles, one per query head
+// 4g + rt of the KV head's group; row n of a tile is token 16w + n.
+// Key blocks come two at a time: the work-group copies the pair's K and V
+// tiles (16 KiB) into LDS once -- each wave a quarter, 1 KiB per load
+// instruction -- double-buffered, one barrier per pair, and each wave reads
+// its MFMA operands from there (rows padded to 136 halves: conflict-free).
+//   S^T = K . Q^T  v_mfma_f32_16x16x32_f16 per 32 dims and block:
+//                  A = K   (lane l: token pi(l%16) of the block, 8 dims)
+//                  B = Q^T (lane l: row l%16, the same 8 dims)
+//                  D = S^T (lane l: tokens 4c + l/16, c < 4, of row l%16),
+//                  pi(m) = 4 (m%4) + m/4 making D's token order that of the
+//                  value operand
+//   O  += P . V    v_mfma_f32_16x16x32_f16 per dim j < 8 and block pair:
+//                  A = P   (lane l: row l%16, tokens 4c + l/16 of both
+//                           blocks -- D of S^T as is, rounded to F16)
+//                  B = V   (lane l: the same 8 tokens, dim 8(l%16) + j)
+//                  D = O   (lane l: rows 4(l/16) + c, dim 8(l%16) + j)
+// Each wave computes only up to its last query's position.  The softmax max
+// is raised lazily as in the decode kernel; a row that sees no key of the
+// piece keeps (m, l) = (-inf, 0).  A tile cut into several pieces writes
+// partial records (token k of piece p at record base + k * pieces + p) for
+// decode_merge_planned; a single piece writes F16 rows.
+// ---------------------------------------------------------------------------
+constexpr int kKvRow = kHeadDim + 8;  // padded LDS row (halves)
+
+__global__ __launch_bounds__(256, 1) void prefill_kernel(DecodeArgs a) {
+    const int g = static_cast<int>(blockIdx.x % a.num_kv_heads);
+    const int32_t *it = a.prefill_items + kPrefillItemInts * static_cast<size_t>(blockIdx.x / a.num_kv_heads);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int n = lane & 15, r = lane >> 4;
+
+    __shared__ int tbl_lds[kMaxPrefillPieceBlocks];
+    __shared__ _Float16 kv_lds[2][2][2][kBlockSize][kKvRow];  // [buffer][K, V][block of the pair][row][dim]
+    __shared__ float alpha_lds[kWaves][kGroup][16];
+    __shared__ float ml_lds[kWaves][kGroup][16][2];
+
+    // Plan entries are clamped so a damaged plan cannot index outside q, out,
+    // the tables, the pool or the workspace.
+    const int s = min(max(it[0], 0), a.batch - 1);
+    const int row0 = max(it[1], 0);
+    const int n_q = min(max(it[2], 0), kPrefillTile);
+    const int pos0 = max(it[3], 0);
+    const int cap = a.max_blocks * kBlockSize;
+    const int t_lo = min(max(it[4], 0), cap) & ~(kBlockSize - 1);
+    const int t_hi = min(min(it[5], cap), pos0 + n_q);
+    const int base_slot = it[6];
+    const int np = max(it[7], 1);
+    const int piece = min(max(it[8], 0), np - 1);
+    const bool direct = base_slot < 0;
+    if (!direct && a.num_slots <= 0) return;
+    const int b_lo = t_lo / kBlockSize;
+    const int b_hi = max(b_lo, min((t_hi + kBlockSize - 1) / kBlockSize, b_lo + kMaxPrefillPieceBlocks));
+
+    const int32_t *table = a.tables + static_cast<size_t>(s) * a.max_blocks;
+    for (int i = tid; i < b_hi - b_lo; i += 256) tbl_lds[i] = table[b_lo + i];
+    __syncthreads();
+
+    // this wave's query tokens and the keys they can see in this piece
+    const int tok0 = 16 * w;
+    const int rows_w = min(16, n_q - tok0);  // may be <= 0: the wave then only helps with the copies
+    const int w_end = rows_w > 0 ? min(t_hi, pos0 + tok0 + rows_w) : t_lo;
+    const int qp = pos0 + tok0 + n;  // position of row n
+
+    // Q of the four row tiles, as the B operand of S^T: dims 32kk + 8r .. +7
+    h8 qv[kGroup][4];
+    {
+        const bool row_ok = n < rows_w;
+        const size_t qr = static_cast<size_t>(min(max(row0 + tok0 + n, 0), a.num_q_rows - 1));
+#pragma unroll
+        for (int rt = 0; rt < kGroup; ++rt) {
+            const uint16_t *qrow = a.q + (qr * a.num_q_heads + g * kGroup + rt) * kHeadDim + 8 * r;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qv[rt][kk] = row_ok ? *reinterpret_cast<const h8 *>(qrow + 32 * kk) : h8(0);
+        }
+    }
+
+    f4 oacc[kGroup][8];
+    float m_run[kGroup], l_run[kGroup];  // row n of each tile (l: this lane's share)
+#pragma unroll
+    for (int rt = 0; rt < kGroup; ++rt) {
+        m_run[rt] = -INFINITY;
+        l_run[rt] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) oacc[rt][j] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // copies: wave w moves tensor w/2 (K, V) of block w%2 of the pair, 1 KiB per
+    // load instruction: lane l takes bytes 16 l + 1024 i, i.e. row l/16 + 4i,
+    // dims 8(l%16) .. +7
+    const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
+    const size_t tile_bytes = tile_elems() * sizeof(uint16_t);
+    const int cp_tensor = w >> 1, cp_blk = w & 1;
+    const char *cp_layer = cp_tensor ? a.v_layer : a.k_layer;
+    h8 stg[4];
+    auto fetch = [&](int b) {  // pair starting at block b
+        const int bb = b + cp_blk;
+        const bool live = bb < b_hi;
+        uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tbl_lds[live ? bb - b_lo : 0]));
+        phys = phys > last_block ? last_block : phys;
+        const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(cp_layer + base, live ? static_cast<int>(tile_bytes) : 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stg[i] = load_tile16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<h8 *>(&kv_lds[buf][cp_tensor][cp_blk][(lane >> 4) + 4 * i][8 * n]) = stg[i];
+    };
+
+    const int kpi = 4 * (n & 3) + (n >> 2);  // pi(n)
+    auto compute = [&](int buf, int b) {
+        bool vis[2][4], live_v[2][4];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int kp = (b + blk) * kBlockSize + 4 * c + r;
+                live_v[blk][c] = kp < w_end;
+                vis[blk][c] = kp < w_end && kp <= qp;
+            }
+        h8 pw[kGroup];
+#pragma unroll
+        for (int rt = 0; rt < kGroup; ++rt) {
+            float sc[8];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                f4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const h8 kx = *reinterpret_cast<const h8 *>(&kv_lds[buf][0][blk][kpi][32 * kk + 8 * r]);
+                    st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kx, qv[rt][kk], st, 0, 0, 0);
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) sc[4 * blk + c] = vis[blk][c] ? st[c] * a.scale_log2e : -INFINITY;
+            }
+            float bmax = sc[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
+            if (__builtin_amdgcn_ballot_w64(bmax > m_run[rt] + kTau) != 0) {
+                float bm = bmax;
+                bm = fmaxf(bm, shfl_xor(bm, 16));
+                bm = fmaxf(bm, shfl_xor(bm, 32));
+                const float m_new = fmaxf(m_run[rt], bm);
+                // a row that has seen no key yet keeps m = -inf (and alpha 1)
+                const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run[rt] - m_new);
+                l_run[rt] *= alpha;
+                m_run[rt] = m_new;
+                if (r == 0) alpha_lds[w][rt][n] = alpha;
+                wave_lds_sync();
+                const float4 al = *reinterpret_cast<const float4 *>(&alpha_lds[w][rt][4 * r]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    oacc[rt][j][0] *= al.x;
+                    oacc[rt][j][1] *= al.y;
+                    oacc[rt][j][2] *= al.z;
+                    oacc[rt][j][3] *= al.w;
+                }
+            }
+            // weights enter P V as F16; the running sum adds the same values
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const _Float16 pv = sc[i] == -INFINITY ? static_cast<_Float16>(0.0f)
+                                                        : static_cast<_Float16>(fast_exp2(sc[i] - m_run[rt]));
+                pw[rt][i] = pv;
+                l_run[rt] += static_cast<float>(pv);
+            }
+        }
+        // the value rows (tokens 4c + r of both blocks, dims 8n .. +7); rows
+        // past the keys this wave sees may hold anything
+        h8 vr[2][4];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const h8 x = *reinterpret_cast<const h8 *>(&kv_lds[buf][1][blk][4 * c + r][8 * n]);
+                vr[blk][c] = live_v[blk][c] ? x : h8(0);
+            }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const h8 bv = {vr[0][0][j], vr[0][1][j], vr[0][2][j], vr[0][3][j],
+                           vr[1][0][j], vr[1][1][j], vr[1][2][j], vr[1][3][j]};
+#pragma unroll
+            for (int rt = 0; rt < kGroup; ++rt)
+                oacc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[rt], bv, oacc[rt][j], 0, 0, 0);
+        }
+    };
+
+    // the work-group walks every pair of the piece; a wave computes the pairs
+    // below its last query's position
+    const int n_pairs = (b_hi - b_lo + 1) / 2;
+    const int w_pairs = w_end > t_lo ? ((w_end + kBlockSize - 1) / kBlockSize - b_lo + 1) / 2 : 0;
+    if (n_pairs > 0) {
+        fetch(b_lo);
+        commit(0);
+        __syncthreads();
+    }
+    for (int p = 0; p < n_pairs; ++p) {
+        const int buf = p & 1;
+        if (p + 1 < n_pairs) fetch(b_lo + 2 * (p + 1));
+        if (p < w_pairs) compute(buf, b_lo + 2 * p);
+        if (p + 1 < n_pairs) commit(buf ^ 1);
+        __syncthreads();
+    }
+    if (rows_w <= 0) return;
+
+    // (m, l) of every row to LDS; lane l then writes rows 4r + c of each tile
+#pragma unroll
+    for (int rt = 0; rt < kGroup; ++rt) {
+        float l = l_run[rt];
+        l += shfl_xor(l, 16);
+        l += shfl_xor(l, 32);
+        if (r == 0) {
+            ml_lds[w][rt][n][0] = m_run[rt];
+            ml_lds[w][rt][n][1] = l;
+        }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int rt = 0; rt < kGroup; ++rt) {
+        const int head = g * kGroup + rt;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int t = 4 * r + c;  // row of the tile
+            if (t >= rows_w) continue;
+            const int tok = tok0 + t;
+            const float m = ml_lds[w][rt][t][0], l = ml_lds[w][rt][t][1];
+            if (direct) {
+                const size_t qrow = static_cast<size_t>(min(row0 + tok, a.num_q_rows - 1));
+                const float inv = 1.0f / l;
+                h8 o;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[j] = static_cast<_Float16>(oacc[rt][j][c] * inv);
+                *reinterpret_cast<h8 *>(a.out + (qrow * a.num_q_heads + head) * kHeadDim + 8 * n) = o;
+            } else {
+                const int64_t slot64 = static_cast<int64_t>(base_slot) + static_cast<int64_t>(tok) * np + piece;
+                const size_t slot = static_cast<size_t>(min<int64_t>(slot64, a.num_slots - 1));
+                const size_t rec = slot * a.num_q_heads + head;
+                float4 *dst = reinterpret_cast<float4 *>(a.o_part + rec * kHeadDim + 8 * n);
+                dst[0] = make_float4(oacc[rt][0][c], oacc[rt][1][c], oacc[rt][2][c], oacc[rt][3][c]);
+                dst[1] = make_float4(oacc[rt][4][c], oacc[rt][5][c], oacc[rt][6][c], oacc[rt][7][c]);
+                if (n == 0) *reinterpret_cast<float2 *>(a.ml_part + rec * 2) = make_float2(m, l);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream) {
@@ -888,6 +1146,12 @@ hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(decode_merge_planned_kernel, dim3(a.num_merges, (a.num_q_heads + 1) / 2), dim3(256), 0, stream,
                        a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
+    const uint32_t groups = static_cast<uint32_t>(static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads);
+    hipLaunchKernelGGL(prefill_kernel, dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

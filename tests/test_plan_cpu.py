@@ -198,3 +198,117 @@ def test_cascade_run_rejects_appending_into_a_shared_block(pool):
     lib = pa.load_library()
     assert lib.pa_decode_run(pool, 0, info, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, 0.1, FAKE,
                              1 << 30, None) == pa.PA_ERR_INVALID_ARG
+
+
+# ---- chunked-prefill / mixed-step schedule (pa_prefill_plan) ----------------
+def _mixed_plan(info, plan):
+    items, merges = _decode_plan(info, plan)
+    off = 8 + 8 * info.num_items + 4 * info.num_merges
+    pf = plan[off:off + 12 * info.num_prefill_items].reshape(-1, 12)
+    assert plan.size * 4 >= info.plan_bytes and off + 12 * info.num_prefill_items == info.plan_bytes // 4
+    return items, merges, pf
+
+
+def _check_mixed(q_lens, lens, info, plan):
+    """Every query row is produced exactly once: a direct decode item, a direct
+    prefill piece, or the merge of a complete set of records."""
+    starts = np.concatenate([[0], np.cumsum(q_lens)]).astype(int)
+    items, merges, pf = _mixed_plan(info, plan)
+    assert info.num_q_rows == starts[-1] and info.num_prefix_items == 0
+    produced = {}
+    records = {}
+    for s, t0, t1, ctx, slot, row, *_ in items:
+        assert q_lens[s] == 1 and ctx == lens[s] and row == starts[s]
+        if slot < 0:
+            assert t0 == 0 and t1 == ctx
+            produced[row] = produced.get(row, 0) + 1
+        else:
+            records[slot] = records.get(slot, 0) + 1
+    tiles = {}
+    for s, row0, n_q, pos0, t0, t1, base, np_, p, *rest in pf:
+        assert q_lens[s] >= 2 and 1 <= n_q <= 64 and rest == [0, 0, 0]
+        assert starts[s] <= row0 and row0 + n_q <= starts[s + 1]
+        assert pos0 == lens[s] - q_lens[s] + (row0 - starts[s])
+        assert t0 % 16 == 0 and 0 <= t0 < t1 <= pos0 + n_q and 0 <= p < np_
+        tiles.setdefault((s, row0), []).append((t0, t1, base, np_, p, n_q, pos0))
+    for (s, row0), ps in tiles.items():
+        ps.sort()
+        n_q, pos0 = ps[0][5], ps[0][6]
+        assert ps[0][0] == 0 and ps[-1][1] == pos0 + n_q               # pieces cover the keys
+        for a, b in zip(ps, ps[1:]):
+            assert a[1] == b[0]
+        assert sorted(x[4] for x in ps) == list(range(len(ps))) and all(x[3] == len(ps) for x in ps)
+        if len(ps) == 1:
+            assert ps[0][2] == -1
+            for k in range(n_q):
+                produced[row0 + k] = produced.get(row0 + k, 0) + 1
+        else:
+            base = ps[0][2]
+            assert all(x[2] == base for x in ps) and base >= 0
+            for k in range(n_q):
+                for p in range(len(ps)):
+                    slot = base + k * len(ps) + p
+                    records[slot] = records.get(slot, 0) + 1
+    for s, first, n, row in merges:
+        assert all(records.get(first + i) == 1 for i in range(n))
+        produced[row] = produced.get(row, 0) + 1
+    assert sorted(records) == list(range(info.num_slots))
+    assert all(v == 1 for v in records.values())
+    assert produced == {r: 1 for r in range(starts[-1])}
+    # each kind is dispatched longest first
+    if len(items):
+        assert np.all(np.diff(items[:, 2] - items[:, 1]) <= 0)
+    if len(pf):
+        assert np.all(np.diff(pf[:, 5] - pf[:, 4]) <= 0)
+    return items, merges, pf
+
+
+@pytest.mark.parametrize("q_lens,hist", [
+    ([1] * 8, [100, 4095, 0, 16, 17, 2000, 300, 5]),
+    ([2, 1, 17, 64, 65, 1, 255, 0], [0, 33, 500, 0, 4000, 0, 17, 9]),
+    ([2016] + [1] * 32, [2016] + [4095] * 32),
+    ([255, 1], [2040, 300]),
+    ([4096], [0]),
+])
+def test_mixed_plan_produces_every_row_once(pool, q_lens, hist):
+    lens = [h + n for h, n in zip(hist, q_lens)]
+    starts = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    info, plan = pa.pa_prefill_plan(pool, starts, lens, 32)
+    _check_mixed(q_lens, lens, info, plan)
+    assert info.max_context_len == max(lens)
+
+
+def test_mixed_plan_long_chunk_is_cut_and_merged(pool):
+    q_lens, lens = [2048], [8192]
+    info, plan = pa.pa_prefill_plan(pool, [0, 2048], lens, 32)
+    items, merges, pf = _check_mixed(q_lens, lens, info, plan)
+    assert info.num_items == 0 and info.num_prefill_items > 32
+    assert info.num_merges > 0 and info.workspace_bytes > 0
+    assert (pf[:, 5] - pf[:, 4]).max() <= 256 * 16
+
+
+def test_mixed_plan_rejects_bad_offsets(pool):
+    lib = pa.load_library()
+    info = pa.PlanInfo()
+    import ctypes
+    def call(qs, lens):
+        qs = np.ascontiguousarray(qs, np.int32)
+        lens = np.ascontiguousarray(lens, np.int32)
+        return lib.pa_prefill_plan(pool, qs.ctypes.data, lens.ctypes.data, len(lens), 32, None, 0,
+                                   ctypes.byref(info))
+    assert call([0, 1, 3], [5, 9]) == 0
+    assert call([1, 2, 3], [5, 9]) == pa.PA_ERR_INVALID_ARG        # first offset not 0
+    assert call([0, 3, 2], [5, 9]) == pa.PA_ERR_INVALID_ARG        # decreasing
+    assert call([0, 6, 7], [5, 9]) == pa.PA_ERR_INVALID_ARG        # chunk longer than its sequence
+    assert lib.pa_prefill_plan(pool, None, None, 0, 32, None, 0, ctypes.byref(info)) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_prefill_plan(pool, np.zeros(3, np.int32).ctypes.data, np.ones(2, np.int32).ctypes.data,
+                               2, 16, None, 0, ctypes.byref(info)) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_decode_plans_carry_their_rows(pool):
+    lens = [5000, 17, 300]
+    info, plan = pa.pa_decode_plan(pool, lens, 32)
+    items, merges = _decode_plan(info, plan)
+    assert np.array_equal(items[:, 5], items[:, 0])
+    assert np.array_equal(merges[:, 3], merges[:, 0]) and info.num_q_rows == 3
+    assert info.num_prefill_items == 0

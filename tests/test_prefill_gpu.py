@@ -1,0 +1,182 @@
+"""GPU parity of the chunked-prefill / mixed step (pa_prefill_plan +
+pa_prefill_run) against the fp64 oracle (oracle.prefill).
+
+Sequence s brings q_len new tokens whose K/V are already in the pool; query j
+of its chunk sees positions 0 .. seq_len - q_len + j.  The pool holds every
+position below seq_len (the workload's blocks); slots past seq_len in the
+last block are NaN.  Tolerance as for decode: max |err| <= 2e-3, relative
+L2 <= 1e-3 over each case.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import paged_kv_cache_64_amd as pa
+from tests.gpu_harness import Staged, compare, report
+
+pytestmark = pytest.mark.gpu
+
+
+def _starts(q_lens):
+    return np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+
+
+class Mixed:
+    """A mixed step: sequences of lengths hist + q_len staged in a pool, with
+    packed query rows."""
+
+    def __init__(self, q_lens, hist, seed, dtype=pa.PA_F16, kv_scales=(1.0, 1.0)):
+        self.q_lens = list(q_lens)
+        self.lens = [h + n for h, n in zip(hist, q_lens)]
+        self.w = workloads.custom(self.lens, seed=seed)
+        self.st = Staged(self.w, dtype=dtype, kv_scales=kv_scales)
+        self.starts = _starts(self.q_lens)
+        self.q = self.w.q_rows(int(self.starts[-1]))
+        self.qd = torch.from_numpy(self.q).cuda()
+        self.poisoned = self._poison_tails()
+
+    def _poison_tails(self):
+        w, st = self.w, self.st
+        tables = st.host[0][1]
+        n = 0
+        for s, ctx in enumerate(self.lens):
+            if ctx % 16 == 0:
+                continue
+            blk = int(tables[s, (ctx - 1) // 16])
+            if st.fp8:
+                st.pool.k[0, blk, :, ctx % 16:, :] = 0x7F
+                st.pool.v[0, blk, :, ctx % 16:, :] = 0x7F
+            else:
+                st.pool.k[0, blk, :, ctx % 16:, :] = float("nan")
+                st.pool.v[0, blk, :, ctx % 16:, :] = float("nan")
+            n += 16 - ctx % 16
+        torch.cuda.synchronize()
+        return n
+
+    def run(self):
+        plan = self.st.pool.prefill_plan(self.starts, self.lens)
+        out = torch.empty_like(self.qd)
+        self.st.pool.prefill_run(0, plan, self.qd, out, self.st.dev[0][1], self.w.scale)
+        torch.cuda.synchronize()
+        return out, plan
+
+    def reference(self, rows=None):
+        q, tables, ids, k, v = self.st.host[0]
+        kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, self.w.ctx_lens, 16)
+        if rows is None:
+            return oracle.prefill(self.q, kc, vc, t2, self.starts, self.lens, self.w.scale, 16)
+        # sampled rows: each as a one-token step over its own visible prefix
+        owner = np.searchsorted(self.starts, rows, side="right") - 1
+        q_lens = np.array(self.q_lens)
+        seq_of = owner
+        vis = np.array(self.lens)[seq_of] - q_lens[seq_of] + (rows - self.starts[seq_of]) + 1
+        return oracle.prefill(self.q[rows], kc, vc, t2[seq_of], np.arange(len(rows) + 1, dtype=np.int32),
+                              vis.astype(np.int32), self.w.scale, 16)
+
+    def close(self):
+        self.st.close()
+
+
+@pytest.mark.parametrize("q_lens,hist", [
+    ([1, 2, 15, 16, 17, 63, 64, 65, 100, 1, 0, 255], [100, 0, 17, 5, 0, 64, 1, 33, 4000, 4095, 9, 2000]),
+    ([3, 1, 1, 130], [0, 7, 1, 1]),
+])
+def test_mixed_step_ragged(q_lens, hist):
+    m = Mixed(q_lens, hist, seed=70 + len(q_lens))
+    out, plan = m.run()
+    report("mixed ragged", rows=len(m.q), decode_items=plan.info.num_items,
+           prefill_items=plan.info.num_prefill_items, merges=plan.info.num_merges,
+           poisoned=m.poisoned)
+    compare("mixed ragged", out, m.reference())
+    m.close()
+
+
+@pytest.mark.parametrize("n", [2, 16, 17, 64, 65, 300])
+def test_whole_prompt_prefill(n):
+    m = Mixed([n], [0], seed=80 + n)
+    out, _ = m.run()
+    ref = m.reference()
+    compare(f"whole prompt {n}", out, ref)
+    # the first token sees only itself: its value row
+    v0 = m.st.pool.v[0, int(m.st.host[0][1][0, 0]), :, 0, :].cpu().numpy().astype(np.float64)
+    got0 = out[0].cpu().numpy().astype(np.float64)
+    assert np.array_equal(got0, np.repeat(v0, 4, axis=0).astype(np.float16).astype(np.float64))
+    m.close()
+
+
+def test_long_chunk_split_into_merged_pieces():
+    m = Mixed([300, 1, 1], [3000, 5000, 10], seed=90)
+    out, plan = m.run()
+    report("split pieces", prefill_items=plan.info.num_prefill_items, merges=plan.info.num_merges,
+           slots=plan.info.num_slots)
+    assert plan.info.num_merges > 0 and plan.info.num_prefill_items > 5
+    compare("split pieces", out, m.reference())
+    m.close()
+
+
+def test_chunked_prompt_matches_one_chunk():
+    """The same prompt as one chunk and as two consecutive chunks (the second
+    with the first as history) gives rows within tolerance of each other and
+    of the oracle."""
+    P, cut = 200, 77
+    whole = Mixed([P], [0], seed=95)
+    a, _ = whole.run()
+    ref = whole.reference()
+    compare("one chunk", a, ref)
+    # second chunk over the same pool and table: sequence length P, 123 new tokens
+    m2_starts = _starts([P - cut])
+    plan = whole.st.pool.prefill_plan(m2_starts, [P])
+    out2 = torch.empty((P - cut, 32, 128), dtype=torch.float16, device="cuda")
+    whole.st.pool.prefill_run(0, plan, whole.qd[cut:].contiguous(), out2, whole.st.dev[0][1], whole.w.scale)
+    torch.cuda.synchronize()
+    compare("second chunk", out2, ref[cut:])
+    compare("chunked vs whole", out2, a[cut:].cpu().numpy().astype(np.float64))
+    whole.close()
+
+
+def test_one_token_rows_equal_the_planned_decode_bitwise():
+    lens = [1, 17, 300, 4097, 64]
+    m = Mixed([1] * len(lens), [x - 1 for x in lens], seed=99)
+    out, _ = m.run()
+    plan = m.st.pool.plan(np.array(lens, np.int32))
+    out2 = torch.empty_like(m.qd)
+    m.st.pool.run(0, plan, m.qd, out2, m.st.dev[0][1], m.w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    compare("decode rows", out, m.reference())
+    m.close()
+
+
+def test_mixed_step_under_a_2048_token_budget_sampled():
+    """32 decoding sequences at 4096 tokens plus a 2016-token prompt chunk
+    (second chunk of a 4032-token prompt): 2048 tokens, the default budget of
+    smaller GPUs in the vLLM page, Example 5.  Rows are sampled."""
+    q_lens = [2016] + [1] * 32
+    hist = [2016] + [4095] * 32
+    m = Mixed(q_lens, hist, seed=101)
+    out, plan = m.run()
+    report("budget 2048", decode_items=plan.info.num_items, prefill_items=plan.info.num_prefill_items,
+           merges=plan.info.num_merges)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, 63, 64, 2015], rng.choice(2016, 24, replace=False),
+                                     2016 + np.arange(32)[::4]])).astype(np.int64)
+    compare("budget 2048 sampled", out[torch.from_numpy(rows).cuda()], m.reference(rows))
+    m.close()
+
+
+def test_fp8_pool_runs_decode_rows_but_not_prefill_tiles():
+    m = Mixed([1, 1, 40], [30, 300, 10], seed=103, dtype=pa.PA_FP8_E4M3, kv_scales=(0.1, 0.02))
+    with pytest.raises(pa.PaError) as e:
+        m.run()
+    assert e.value.status == pa.PA_ERR_UNSUPPORTED
+    m.close()
+    m = Mixed([1, 1], [30, 300], seed=104, dtype=pa.PA_FP8_E4M3, kv_scales=(0.1, 0.02))
+    out, _ = m.run()
+    q, tables, ids, k, v = m.st.host[0]
+    kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, m.w.ctx_lens, 16)
+    ref = oracle.decode_e4m3(m.q, oracle.quantize_e4m3(kc, 0.1), oracle.quantize_e4m3(vc, 0.02), t2,
+                             np.array(m.lens, np.int32), m.w.scale, 16, 0.1, 0.02)
+    compare("fp8 decode rows via prefill_run", out, ref)
+    m.close()

@@ -36,7 +36,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # stream purposes
-_META, _TABLE, _Q, _K, _V, _BOOST = range(6)
+_META, _TABLE, _Q, _K, _V, _BOOST, _QROWS = range(7)
 # blocks drawn per stream chunk (fixed, so results do not depend on threads)
 _CHUNK_BLOCKS = 256
 
@@ -148,6 +148,11 @@ class Workload:
         """F16 [batch, num_q_heads, head_dim]."""
         return _normal_f16(_rng(self.seed, _Q, layer),
                            (self.batch, self.num_q_heads, self.head_dim))
+
+    def q_rows(self, n_rows: int, layer: int = 0) -> np.ndarray:
+        """F16 [n_rows, num_q_heads, head_dim]: the packed query rows of a step
+        in which sequences bring several new tokens (chunked prefill)."""
+        return _normal_f16(_rng(self.seed, _QROWS, layer), (n_rows, self.num_q_heads, self.head_dim))
 
     def kv_blocks(self, layer: int = 0, ids: np.ndarray | None = None):
         """Contents of the referenced physical blocks of one layer.
