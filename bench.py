@@ -72,7 +72,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload 1..7 (default 3); 6 and 7 are mixed steps (chunked prefill)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
@@ -126,6 +127,11 @@ def main():
     w = workloads.config(args.config, args.seed)
     B, HQ, HKV, D = w.block_size, w.num_q_heads, w.num_kv_heads, w.head_dim
     log(f"workload: {w.name}; pool {w.layers} layers x {w.pool_blocks} blocks")
+    if w.q_lens is not None:
+        if args.kv_dtype != "f16" or args.cascade or args.graph:
+            print("mixed steps run on F16 pools, without --cascade or --graph", file=sys.stderr)
+            sys.exit(2)
+        return bench_mixed(args, w, dev)
 
     # ---- stage the pool through pa_write_kv, layer by layer ----
     t_stage = time.time()
@@ -416,6 +422,214 @@ def main():
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
         "hbm_read_probe_GBps": round(probe, 1) if probe else None,
         "pct_of_probe": round(100 * kv_gbps / probe, 2) if probe else None,
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+    }
+    print(json.dumps(line), flush=True)
+    pool.close()
+
+
+MIXED_METRIC = "mixed step (chunked prefill + decode): query tokens/s"
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def bench_mixed(args, w, dev):
+    """A step of workload 6 or 7: every layer runs pa_prefill_run on the step's
+    plan (decode pieces, prefill pieces, merges).  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_64_amd as pa
+
+    lib = pa.load_library()
+    B, HQ, HKV, D = w.block_size, w.num_q_heads, w.num_kv_heads, w.head_dim
+    qs = w.query_start
+    total_q = int(qs[-1])
+    lens_host = np.ascontiguousarray(w.ctx_lens, dtype=np.int32)
+    chunk_seqs = [s for s in range(w.batch) if w.q_lens[s] > 1]
+    dec_seqs = [s for s in range(w.batch) if w.q_lens[s] == 1]
+
+    t_stage = time.time()
+    pool = pa.Pool(w.layers, w.pool_blocks, HKV, D, B, device=dev, fill=0.0)
+    q_dev, tables_dev = [], []
+    host0 = None
+    for layer in range(w.layers):
+        ids, k, v = w.kv_blocks(layer)
+        pool.write_blocks(layer, torch.from_numpy(ids).to(dev), torch.from_numpy(k).to(dev),
+                          torch.from_numpy(v).to(dev))
+        q = w.q_rows(total_q, layer)
+        tables = w.tables(layer)
+        q_dev.append(torch.from_numpy(q).to(dev))
+        tables_dev.append(torch.from_numpy(tables).to(dev))
+        if layer == 0 and not args.no_cpu_baseline:
+            host0 = (q, tables, ids, k, v)
+        del ids, k, v
+    torch.cuda.synchronize()
+    log(f"staging took {time.time() - t_stage:.1f} s")
+
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    h = pool.handle
+    width = w.max_blocks
+    outs = [torch.empty_like(q) for q in q_dev]
+
+    def make(qs_h, lens_h):
+        info = pa.PlanInfo()
+        rc = lib.pa_prefill_plan(h, qs_h.ctypes.data, lens_h.ctypes.data, len(lens_h), HQ, None, 0,
+                                 ctypes.byref(info))
+        assert rc == 0, rc
+        return info
+
+    # the whole step's plan, rebuilt on the host every step (alternating
+    # pinned buffers) and uploaded without blocking the host
+    info = make(qs, lens_host)
+    words = max(1, info.plan_bytes // 4)
+    pinned = [torch.zeros(words, dtype=torch.int32).pin_memory() for _ in range(2)]
+    plan_dev = torch.zeros(words, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(info.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    scale = ctypes.c_float(w.scale)
+    nstep = [0]
+
+    def step():
+        buf = pinned[nstep[0] % 2]
+        nstep[0] += 1
+        rc = lib.pa_prefill_plan(h, qs.ctypes.data, lens_host.ctypes.data, w.batch, HQ, buf.data_ptr(),
+                                 buf.numel() * 4, ctypes.byref(info))
+        if rc != 0:
+            raise RuntimeError(f"pa_prefill_plan failed: {rc}")
+        plan_dev.copy_(buf, non_blocking=True)
+        for L in range(w.layers):
+            rc = lib.pa_prefill_run(h, L, ctypes.byref(info), plan_dev.data_ptr(), q_dev[L].data_ptr(),
+                                    outs[L].data_ptr(), tables_dev[L].data_ptr(), width, scale,
+                                    ws.data_ptr(), info.workspace_bytes, sptr)
+            if rc != 0:
+                raise RuntimeError(f"pa_prefill_run failed in layer {L}: {rc}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done; plan: {info.num_items} decode pieces, {info.num_prefill_items} prefill pieces, "
+        f"{info.num_merges} merges, workspace {info.workspace_bytes} B")
+
+    # Timed region 1 (the headline): K whole steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # Timed regions 2 and 3: the prompt chunk alone (the prefill kernel and its
+    # merge) and the decode rows alone, each as its own plan over all layers
+    def part(seqs):
+        sub_q = np.concatenate([[0], np.cumsum(w.q_lens[seqs])]).astype(np.int32)
+        sub_l = np.ascontiguousarray(lens_host[seqs])
+        inf = make(sub_q, sub_l)
+        ph = np.zeros(max(1, inf.plan_bytes // 4), np.int32)
+        assert lib.pa_prefill_plan(h, sub_q.ctypes.data, sub_l.ctypes.data, len(sub_l), HQ, ph.ctypes.data,
+                                   ph.nbytes, ctypes.byref(inf)) == 0
+        pd = torch.from_numpy(ph).to(dev)
+        wsp = torch.empty(max(inf.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in seqs])
+        rows_t = torch.from_numpy(rows).to(dev)
+        qp = [q[rows_t].contiguous() for q in q_dev]
+        tp = [t[torch.tensor(seqs, device=dev)].contiguous() for t in tables_dev]
+        op = [torch.empty_like(x) for x in qp]
+
+        def go():
+            for L in range(w.layers):
+                rc = lib.pa_prefill_run(h, L, ctypes.byref(inf), pd.data_ptr(), qp[L].data_ptr(), op[L].data_ptr(),
+                                        tp[L].data_ptr(), width, scale, wsp.data_ptr(), inf.workspace_bytes, sptr)
+                assert rc == 0, rc
+        go()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record(stream)
+            go()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) / w.layers * 1e3, inf
+
+    pf_us, pf_info = part(chunk_seqs)
+    dec_us, _ = part(dec_seqs)
+    vis = 0
+    for s in chunk_seqs:
+        n = int(w.q_lens[s])
+        hist = int(lens_host[s]) - n
+        vis += n * hist + n * (n + 1) // 2
+    pf_flops = 4 * D * HQ * vis
+    achieved = pf_flops / (pf_us * 1e-6) / 1e12
+    dec_bytes = int(lens_host[dec_seqs].astype(np.int64).sum()) * HKV * D * 2 * 2
+    log(f"step {ms_per_step:.4f} ms; prefill part {pf_us:.2f} us/layer ({achieved:.1f} TFLOP/s); "
+        f"decode part {dec_us:.2f} us/layer ({dec_bytes / (dec_us * 1e-6) / 1e9:.0f} GB/s)")
+
+    # the oracle on sampled rows of layer 0: baseline timing and a parity sample
+    cpu = None
+    parity = None
+    if host0 is not None:
+        import oracle
+
+        threads = len(os.sched_getaffinity(0))
+        q, tables, ids, k, v = host0
+        kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, w.ctx_lens, B)
+        gpu = outs[0].cpu().numpy().astype(np.float64)
+        owner = np.searchsorted(qs, np.arange(total_q), side="right") - 1
+        rng = np.random.default_rng(0)
+        order = rng.permutation(total_q)
+        done, cpu_s, errs, refs, diffs = 0, 0.0, [], [], []
+        while done < total_q and cpu_s < args.cpu_seconds:
+            rows = np.sort(order[done:done + 16])
+            own = owner[rows]
+            visn = (lens_host[own] - w.q_lens[own] + (rows - qs[own]) + 1).astype(np.int32)
+            t_cpu = time.perf_counter()
+            ref = oracle.prefill(q[rows], kc, vc, t2[own], np.arange(len(rows) + 1, dtype=np.int32), visn,
+                                 w.scale, B, threads=threads)
+            cpu_s += time.perf_counter() - t_cpu
+            errs.append(float(np.abs(gpu[rows] - ref).max()))
+            refs.append(float((ref ** 2).sum()))
+            diffs.append(float(((gpu[rows] - ref) ** 2).sum()))
+            done += len(rows)
+        # a step is every row of every layer; the sample is uniform over the rows
+        cpu = {"value": round(done / (cpu_s * w.layers), 4), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{done} of the {total_q} query rows of layer 0 drawn uniformly, fp64, "
+                         f"{cpu_s:.1f} s of oracle time, scaled to the {w.layers}-layer step"}
+        parity = {"rows": done, "max_abs_err": max(errs), "rel_l2": (sum(diffs) / sum(refs)) ** 0.5}
+        log(f"oracle: {cpu['value']} tokens/s on {threads} threads; parity {parity}")
+
+    line = {
+        "metric": MIXED_METRIC,
+        "value": round(total_q / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "sequences": w.batch,
+                   "query_tokens": total_q, "prompt_chunk_tokens": int(sum(w.q_lens[chunk_seqs])),
+                   "decode_rows": len(dec_seqs), "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
+                   "block_size": B,
+                   "schedule": {"decode_pieces": info.num_items, "prefill_pieces": info.num_prefill_items,
+                                "merges": info.num_merges}},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel" + (" + decode_merge_planned_kernel" if pf_info.num_merges else ""),
+                     "flops_per_layer": pf_flops, "mean_layer_us": round(pf_us, 3)},
+        "decode_rows_us_per_layer": round(dec_us, 3),
+        "decode_rows_GBps": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
         "cpu_baseline": cpu,
         "parity_sample": parity,
     }

@@ -97,7 +97,7 @@ constexpr int kPlanHeader = 8;
 constexpr int kItemInts = 8;
 constexpr int kMergeInts = 4;
 constexpr int kPrefillItemInts = 12;
-constexpr int kPrefillTile = 64;             // query tokens per prefill work-group (16 per wave)
+constexpr int kPrefillTile = 32;             // query tokens per prefill work-group (16 per wave pair)
 constexpr int kMaxPrefillPieceBlocks = 256;  // key blocks per prefill piece
 constexpr int kPrefixItemInts = 8;
 constexpr int kMemberInts = 2;

@@ -867,12 +867,13 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
 // tile of up to kPrefillTile query tokens of one sequence against a range of
 // its key blocks.  The tile's queries sit at positions pos0 .. pos0+n_q-1 and
 // query t sees keys 0 .. pos0 + t (causal).  Wave w owns query tokens
-// 16w .. 16w+15 and their 64 rows as four 16-row tiles, one per query head
-// 4g + rt of the KV head's group; row n of a tile is token 16w + n.
+// 16(w/2) .. +15 and query heads 4g + 2(w%2) + rt, rt < 2: two 16-row tiles
+// whose row n is token 16(w/2) + n.
 // Key blocks come two at a time: the work-group copies the pair's K and V
 // tiles (16 KiB) into LDS once -- each wave a quarter, 1 KiB per load
 // instruction -- double-buffered, one barrier per pair, and each wave reads
-// its MFMA operands from there (rows padded to 136 halves: conflict-free).
+// its MFMA operands from there once per pair (rows padded to 136 halves:
+// conflict-free).
 //   S^T = K . Q^T  v_mfma_f32_16x16x32_f16 per 32 dims and block:
 //                  A = K   (lane l: token pi(l%16) of the block, 8 dims)
 //                  B = Q^T (lane l: row l%16, the same 8 dims)
@@ -884,15 +885,18 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
 //                           blocks -- D of S^T as is, rounded to F16)
 //                  B = V   (lane l: the same 8 tokens, dim 8(l%16) + j)
 //                  D = O   (lane l: rows 4(l/16) + c, dim 8(l%16) + j)
-// Each wave computes only up to its last query's position.  The softmax max
-// is raised lazily as in the decode kernel; a row that sees no key of the
-// piece keeps (m, l) = (-inf, 0).  A tile cut into several pieces writes
-// partial records (token k of piece p at record base + k * pieces + p) for
-// decode_merge_planned; a single piece writes F16 rows.
+// Each wave computes only up to its last query's position, and masks only
+// the pairs that reach past its first query's position or its last key.
+// The softmax max is raised lazily as in the decode kernel (the comparison
+// runs on raw scores, the scale enters once through the exponent's FMA); a
+// row that sees no key of the piece keeps (m, l) = (-inf, 0).  A tile cut
+// into several pieces writes partial records (token k of piece p at record
+// base + k * pieces + p) for decode_merge_planned; a single piece writes F16
+// rows.
 // ---------------------------------------------------------------------------
 constexpr int kKvRow = kHeadDim + 8;  // padded LDS row (halves)
 
-__global__ __launch_bounds__(256, 1) void prefill_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) {
     const int g = static_cast<int>(blockIdx.x % a.num_kv_heads);
     const int32_t *it = a.prefill_items + kPrefillItemInts * static_cast<size_t>(blockIdx.x / a.num_kv_heads);
     const int tid = threadIdx.x;
@@ -902,8 +906,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(DecodeArgs a) {
 
     __shared__ int tbl_lds[kMaxPrefillPieceBlocks];
     __shared__ _Float16 kv_lds[2][2][2][kBlockSize][kKvRow];  // [buffer][K, V][block of the pair][row][dim]
-    __shared__ float alpha_lds[kWaves][kGroup][16];
-    __shared__ float ml_lds[kWaves][kGroup][16][2];
+    __shared__ float alpha_lds[kWaves][2][16];
+    __shared__ float ml_lds[kWaves][2][16][2];
 
     // Plan entries are clamped so a damaged plan cannot index outside q, out,
     // the tables, the pool or the workspace.
@@ -926,35 +930,40 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(DecodeArgs a) {
     for (int i = tid; i < b_hi - b_lo; i += 256) tbl_lds[i] = table[b_lo + i];
     __syncthreads();
 
-    // this wave's query tokens and the keys they can see in this piece
-    const int tok0 = 16 * w;
+    // this wave's query tokens and heads, and the keys its rows can see
+    const int tok0 = 16 * (w >> 1);
+    const int head0 = g * kGroup + 2 * (w & 1);
     const int rows_w = min(16, n_q - tok0);  // may be <= 0: the wave then only helps with the copies
     const int w_end = rows_w > 0 ? min(t_hi, pos0 + tok0 + rows_w) : t_lo;
     const int qp = pos0 + tok0 + n;  // position of row n
 
-    // Q of the four row tiles, as the B operand of S^T: dims 32kk + 8r .. +7
-    h8 qv[kGroup][4];
+    // Q of the two row tiles, as the B operand of S^T: dims 32kk + 8r .. +7
+    h8 qv[2][4];
     {
         const bool row_ok = n < rows_w;
         const size_t qr = static_cast<size_t>(min(max(row0 + tok0 + n, 0), a.num_q_rows - 1));
 #pragma unroll
-        for (int rt = 0; rt < kGroup; ++rt) {
-            const uint16_t *qrow = a.q + (qr * a.num_q_heads + g * kGroup + rt) * kHeadDim + 8 * r;
+        for (int rt = 0; rt < 2; ++rt) {
+            const uint16_t *qrow = a.q + (qr * a.num_q_heads + head0 + rt) * kHeadDim + 8 * r;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                qv[rt][kk] = row_ok ? *reinterpret_cast<const h8 *>(qrow + 32 * kk) : h8(0);
+            for (int kk = 0; kk < 4; ++kk) {
+                const h8 x = *reinterpret_cast<const h8 *>(qrow + 32 * kk);
+                qv[rt][kk] = row_ok ? x : h8(0);
+            }
         }
     }
 
-    f4 oacc[kGroup][8];
-    float m_run[kGroup], l_run[kGroup];  // row n of each tile (l: this lane's share)
+    f4 oacc[2][8];
+    float m_run[2], l_run[2];  // row n of each tile, log2 units (l: this lane's share)
 #pragma unroll
-    for (int rt = 0; rt < kGroup; ++rt) {
+    for (int rt = 0; rt < 2; ++rt) {
         m_run[rt] = -INFINITY;
         l_run[rt] = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) oacc[rt][j] = f4{0.f, 0.f, 0.f, 0.f};
     }
+    const float c_scale = a.scale_log2e;
+    const h2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 
     // copies: wave w moves tensor w/2 (K, V) of block w%2 of the pair, 1 KiB per
     // load instruction: lane l takes bytes 16 l + 1024 i, i.e. row l/16 + 4i,
@@ -982,35 +991,55 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(DecodeArgs a) {
 
     const int kpi = 4 * (n & 3) + (n >> 2);  // pi(n)
     auto compute = [&](int buf, int b) {
-        bool vis[2][4], live_v[2][4];
+        // the pair's K operands, read once for both row tiles
+        h8 kx[2][4];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int kp = (b + blk) * kBlockSize + 4 * c + r;
-                live_v[blk][c] = kp < w_end;
-                vis[blk][c] = kp < w_end && kp <= qp;
-            }
-        h8 pw[kGroup];
+            for (int kk = 0; kk < 4; ++kk)
+                kx[blk][kk] = *reinterpret_cast<const h8 *>(&kv_lds[buf][0][blk][kpi][32 * kk + 8 * r]);
+        f4 st[2][2];
 #pragma unroll
-        for (int rt = 0; rt < kGroup; ++rt) {
-            float sc[8];
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                f4 st = {0.f, 0.f, 0.f, 0.f};
+            for (int blk = 0; blk < 2; ++blk) st[rt][blk] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const h8 kx = *reinterpret_cast<const h8 *>(&kv_lds[buf][0][blk][kpi][32 * kk + 8 * r]);
-                    st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kx, qv[rt][kk], st, 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+                    st[rt][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kx[blk][kk], qv[rt][kk], st[rt][blk], 0, 0, 0);
+        // the value rows (tokens 4c + r of both blocks, dims 8n .. +7)
+        h8 vr[2][4];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) vr[blk][c] = *reinterpret_cast<const h8 *>(&kv_lds[buf][1][blk][4 * c + r][8 * n]);
+        // masks, only where the pair reaches past the first row's position or
+        // the last key this wave sees (keys there may be stale: zero their values)
+        const int k_last = b * kBlockSize + 2 * kBlockSize - 1;
+        const bool tail = k_last >= w_end;
+        if (k_last > pos0 + tok0 || tail) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int kp = (b + blk) * kBlockSize + 4 * c + r;
+                    const bool vis = kp < w_end && kp <= qp;
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) st[rt][blk][c] = vis ? st[rt][blk][c] : -INFINITY;
+                    if (tail && kp >= w_end) vr[blk][c] = h8(0);
                 }
+        }
+        h8 pw[2];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) sc[4 * blk + c] = vis[blk][c] ? st[c] * a.scale_log2e : -INFINITY;
-            }
-            float bmax = sc[0];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
-            if (__builtin_amdgcn_ballot_w64(bmax > m_run[rt] + kTau) != 0) {
-                float bm = bmax;
+        for (int rt = 0; rt < 2; ++rt) {
+            float bmax = fmaxf(fmaxf(st[rt][0][0], st[rt][0][1]), fmaxf(st[rt][0][2], st[rt][0][3]));
+            bmax = fmaxf(bmax, fmaxf(fmaxf(st[rt][1][0], st[rt][1][1]), fmaxf(st[rt][1][2], st[rt][1][3])));
+            const float mb = bmax * c_scale;
+            if (__builtin_amdgcn_ballot_w64(mb > m_run[rt] + kTau) != 0) {
+                float bm = mb;
                 bm = fmaxf(bm, shfl_xor(bm, 16));
                 bm = fmaxf(bm, shfl_xor(bm, 32));
                 const float m_new = fmaxf(m_run[rt], bm);
@@ -1029,31 +1058,28 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(DecodeArgs a) {
                     oacc[rt][j][3] *= al.w;
                 }
             }
-            // weights enter P V as F16; the running sum adds the same values
+            // weights exp2(s * scale - m) enter P V as F16; the running sum
+            // adds the same rounded values (masked scores give exp2(-inf) = 0)
+            const float neg_m = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const _Float16 pv = sc[i] == -INFINITY ? static_cast<_Float16>(0.0f)
-                                                        : static_cast<_Float16>(fast_exp2(sc[i] - m_run[rt]));
-                pw[rt][i] = pv;
-                l_run[rt] += static_cast<float>(pv);
-            }
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int c = 0; c < 4; c += 2) {
+                    const float p0 = fast_exp2(fmaf(st[rt][blk][c], c_scale, neg_m));
+                    const float p1 = fast_exp2(fmaf(st[rt][blk][c + 1], c_scale, neg_m));
+                    const h2 pp = {static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
+                    pw[rt][4 * blk + c] = pp.x;
+                    pw[rt][4 * blk + c + 1] = pp.y;
+                    l_run[rt] = __builtin_amdgcn_fdot2(pp, ones, l_run[rt], false);
+                }
         }
-        // the value rows (tokens 4c + r of both blocks, dims 8n .. +7); rows
-        // past the keys this wave sees may hold anything
-        h8 vr[2][4];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const h8 x = *reinterpret_cast<const h8 *>(&kv_lds[buf][1][blk][4 * c + r][8 * n]);
-                vr[blk][c] = live_v[blk][c] ? x : h8(0);
-            }
+        // P V: dim j of the lane's eight value rows
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const h8 bv = {vr[0][0][j], vr[0][1][j], vr[0][2][j], vr[0][3][j],
                            vr[1][0][j], vr[1][1][j], vr[1][2][j], vr[1][3][j]};
 #pragma unroll
-            for (int rt = 0; rt < kGroup; ++rt)
+            for (int rt = 0; rt < 2; ++rt)
                 oacc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[rt], bv, oacc[rt][j], 0, 0, 0);
         }
     };
@@ -1078,7 +1104,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(DecodeArgs a) {
 
     // (m, l) of every row to LDS; lane l then writes rows 4r + c of each tile
 #pragma unroll
-    for (int rt = 0; rt < kGroup; ++rt) {
+    for (int rt = 0; rt < 2; ++rt) {
         float l = l_run[rt];
         l += shfl_xor(l, 16);
         l += shfl_xor(l, 32);
@@ -1089,8 +1115,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(DecodeArgs a) {
     }
     wave_lds_sync();
 #pragma unroll
-    for (int rt = 0; rt < kGroup; ++rt) {
-        const int head = g * kGroup + rt;
+    for (int rt = 0; rt < 2; ++rt) {
+        const int head = head0 + rt;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int t = 4 * r + c;  // row of the tile

@@ -24,6 +24,16 @@ block_size 16, scale 1/sqrt(128)):
   5  one layer, 256 sequences in 16 groups of 16; each group shares 128
      physical prefix blocks (2048 tokens, reference count 16) and each
      sequence adds a private suffix of uniform [0, 6144] tokens
+Two mixed steps (chunked prefill under a token budget, "vLLM Architecture
+and Installation", Example 5; "Batching and Scheduling", Example 5): each
+sequence brings q_lens[s] new tokens, already stored, and ctx_lens[s] counts
+every token in the cache.
+  6  32 layers; 32 decoding sequences at 4096 tokens plus the second
+     2016-token chunk of a 4032-token prompt: 2048 tokens, the default budget
+     of GPUs under 70 GiB
+  7  8 layers; 32 decoding sequences at 4096 tokens plus the second
+     16,352-token chunk of a 32,704-token prompt: 16,384 tokens, the default
+     budget of GPUs with 160 GiB or more (MI355X has 288 GB)
 """
 from __future__ import annotations
 
@@ -85,6 +95,7 @@ class Workload:
     key_boost_prob: float = 0.0
     key_boost: float = 8.0
     fresh_tables_per_layer: bool = True
+    q_lens: np.ndarray | None = None     # int32 [batch]: new tokens per sequence (None: one each)
     description: str = ""
     _table_cache: dict = field(default_factory=dict, repr=False)
 
@@ -148,6 +159,12 @@ class Workload:
         """F16 [batch, num_q_heads, head_dim]."""
         return _normal_f16(_rng(self.seed, _Q, layer),
                            (self.batch, self.num_q_heads, self.head_dim))
+
+    @property
+    def query_start(self) -> np.ndarray:
+        """int32 [batch + 1]: first packed query row of each sequence."""
+        q = self.q_lens if self.q_lens is not None else np.ones(self.batch, np.int32)
+        return np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
 
     def q_rows(self, n_rows: int, layer: int = 0) -> np.ndarray:
         """F16 [n_rows, num_q_heads, head_dim]: the packed query rows of a step
@@ -233,7 +250,7 @@ def _uniform_ints(seed, purpose, lo, hi, n):
 
 
 def config(k: int, seed: int | None = None) -> Workload:
-    """The five workloads, numbered 1..5 as in the module docstring."""
+    """The workloads, numbered 1..7 as in the module docstring."""
     seed = k if seed is None else seed
     if k == 1:
         return Workload("paged decode, 1 layer, batch 1, ctx 256", seed, layers=1,
@@ -261,6 +278,14 @@ def config(k: int, seed: int | None = None) -> Workload:
         return Workload("paged decode, 1 layer, 256 sequences, 16 shared 2048-token prefixes",
                         seed, layers=1, ctx_lens=lens, pool_blocks=2 * need, max_blocks=512,
                         prefix_groups=(groups, gsize, pblocks))
+    if k in (6, 7):
+        chunk, hist, layers = (2016, 2016, 32) if k == 6 else (16352, 16352, 8)
+        lens = np.array([hist + chunk] + [4096] * 32, np.int32)
+        need = int((-(-lens.astype(np.int64) // 16)).sum())
+        return Workload(f"mixed step, {layers} layers, 32 decodes at ctx 4096 + a {chunk}-token "
+                        f"prompt chunk at position {hist}", seed, layers=layers, ctx_lens=lens,
+                        pool_blocks=2 * need, max_blocks=int(-(-lens.max() // 16)),
+                        q_lens=np.array([chunk] + [1] * 32, np.int32))
     raise ValueError(f"unknown workload {k}")
 
 
