@@ -207,11 +207,11 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
 //   into the score scale and V's into the output.
 // ---------------------------------------------------------------------------
 template <int NBUF, bool FP8>
-__global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_t bx, uint32_t by, uint32_t bz) {
     // Planned launches number work-groups item-major with the KV head fastest,
     // so the heads of one piece -- whose tiles share each 32 KiB block of
     // K and of V -- run side by side, as in the fixed-split grid.
-    const int g = a.items != nullptr ? static_cast<int>(blockIdx.x % a.num_kv_heads) : static_cast<int>(blockIdx.y);
+    const int g = a.items != nullptr ? static_cast<int>(bx % a.num_kv_heads) : static_cast<int>(by);
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     const int lane = tid & 63;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     if (a.items != nullptr) {
         // Plan entries are clamped so a damaged plan cannot index outside
         // q, out, the tables or the workspace.
-        const int32_t *it = a.items + kItemInts * static_cast<size_t>(blockIdx.x / a.num_kv_heads);
+        const int32_t *it = a.items + kItemInts * static_cast<size_t>(bx / a.num_kv_heads);
         s = min(max(it[0], 0), a.batch - 1);
         qrow = min(max(it[5], 0), a.num_q_rows - 1);
         ctx = min(max(it[3], 0), a.max_blocks * kBlockSize);
@@ -245,8 +245,8 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
         rec_base = static_cast<int64_t>(slot) * a.num_q_heads;
         rec_stride = 1;
     } else {
-        const int split = blockIdx.x;
-        s = blockIdx.z;
+        const int split = static_cast<int>(bx);
+        s = static_cast<int>(bz);
         qrow = s;
         ctx = clamp_ctx(a.ctx_lens[s], a.max_ctx, a.max_blocks);
         t_begin = split * a.split_tokens;
@@ -611,6 +611,11 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     }
 }
 
+template <int NBUF, bool FP8>
+__global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
+    decode_partial_body<NBUF, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
 // ---------------------------------------------------------------------------
 // decode_merge: 256 threads = two (sequence, query head) rows of 128 dims.
 //   M = max_i m_i,  L = sum_i 2^(m_i - M) l_i,  out = sum_i 2^(m_i - M) o_i / L
@@ -869,11 +874,11 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
 // query t sees keys 0 .. pos0 + t (causal).  Wave w owns query tokens
 // 16(w/2) .. +15 and query heads 4g + 2(w%2) + rt, rt < 2: two 16-row tiles
 // whose row n is token 16(w/2) + n.
-// Key blocks come two at a time: the work-group copies the pair's K and V
-// tiles (16 KiB) into LDS once -- each wave a quarter, 1 KiB per load
-// instruction -- double-buffered, one barrier per pair, and each wave reads
-// its MFMA operands from there once per pair (rows padded to 136 halves:
-// conflict-free).
+// Key blocks come kStageBlocks at a time: the work-group copies the stage's
+// K and V tiles into LDS once -- each wave a quarter, 1 KiB per load
+// instruction -- double-buffered, one barrier per stage; each wave then works
+// through the stage two blocks at a time, reading its MFMA operands once per
+// pair (rows padded to 136 halves: conflict-free).
 //   S^T = K . Q^T  v_mfma_f32_16x16x32_f16 per 32 dims and block:
 //                  A = K   (lane l: token pi(l%16) of the block, 8 dims)
 //                  B = Q^T (lane l: row l%16, the same 8 dims)
@@ -895,17 +900,22 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
 // rows.
 // ---------------------------------------------------------------------------
 constexpr int kKvRow = kHeadDim + 8;  // padded LDS row (halves)
+#ifndef PA_PREFILL_STAGE_BLOCKS
+#define PA_PREFILL_STAGE_BLOCKS 2
+#endif
+constexpr int kStageBlocks = PA_PREFILL_STAGE_BLOCKS;  // key blocks per LDS stage (even)
+static_assert(kStageBlocks % 2 == 0 && kStageBlocks >= 2, "stages hold whole pairs");
 
-__global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) {
-    const int g = static_cast<int>(blockIdx.x % a.num_kv_heads);
-    const int32_t *it = a.prefill_items + kPrefillItemInts * static_cast<size_t>(blockIdx.x / a.num_kv_heads);
+__device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
+    const int g = static_cast<int>(bx % a.num_kv_heads);
+    const int32_t *it = a.prefill_items + kPrefillItemInts * static_cast<size_t>(bx / a.num_kv_heads);
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int n = lane & 15, r = lane >> 4;
 
     __shared__ int tbl_lds[kMaxPrefillPieceBlocks];
-    __shared__ _Float16 kv_lds[2][2][2][kBlockSize][kKvRow];  // [buffer][K, V][block of the pair][row][dim]
+    __shared__ _Float16 kv_lds[2][2][kStageBlocks][kBlockSize][kKvRow];  // [buffer][K, V][block][row][dim]
     __shared__ float alpha_lds[kWaves][2][16];
     __shared__ float ml_lds[kWaves][2][16][2];
 
@@ -970,34 +980,40 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) {
     // dims 8(l%16) .. +7
     const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
     const size_t tile_bytes = tile_elems() * sizeof(uint16_t);
-    const int cp_tensor = w >> 1, cp_blk = w & 1;
+    constexpr int kCopyBlocks = kStageBlocks / 2;  // blocks of one tensor each wave copies per stage
+    const int cp_tensor = w >> 1, cp_blk0 = (w & 1) * kCopyBlocks;
     const char *cp_layer = cp_tensor ? a.v_layer : a.k_layer;
-    h8 stg[4];
-    auto fetch = [&](int b) {  // pair starting at block b
-        const int bb = b + cp_blk;
-        const bool live = bb < b_hi;
-        uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tbl_lds[live ? bb - b_lo : 0]));
-        phys = phys > last_block ? last_block : phys;
-        const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(cp_layer + base, live ? static_cast<int>(tile_bytes) : 0);
+    h8 stg[kCopyBlocks][4];
+    auto fetch = [&](int b) {  // stage starting at block b
 #pragma unroll
-        for (int i = 0; i < 4; ++i) stg[i] = load_tile16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
+        for (int x = 0; x < kCopyBlocks; ++x) {
+            const int bb = b + cp_blk0 + x;
+            const bool live = bb < b_hi;
+            uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tbl_lds[live ? bb - b_lo : 0]));
+            phys = phys > last_block ? last_block : phys;
+            const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(cp_layer + base, live ? static_cast<int>(tile_bytes) : 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) stg[x][i] = load_tile16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
+        }
     };
     auto commit = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<h8 *>(&kv_lds[buf][cp_tensor][cp_blk][(lane >> 4) + 4 * i][8 * n]) = stg[i];
+        for (int x = 0; x < kCopyBlocks; ++x)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<h8 *>(&kv_lds[buf][cp_tensor][cp_blk0 + x][(lane >> 4) + 4 * i][8 * n]) = stg[x][i];
     };
 
     const int kpi = 4 * (n & 3) + (n >> 2);  // pi(n)
-    auto compute = [&](int buf, int b) {
+    auto compute = [&](int buf, int sb, int b) {  // blocks sb, sb+1 of the stage = key blocks b, b+1
         // the pair's K operands, read once for both row tiles
         h8 kx[2][4];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                kx[blk][kk] = *reinterpret_cast<const h8 *>(&kv_lds[buf][0][blk][kpi][32 * kk + 8 * r]);
+                kx[blk][kk] = *reinterpret_cast<const h8 *>(&kv_lds[buf][0][sb + blk][kpi][32 * kk + 8 * r]);
         f4 st[2][2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -1015,7 +1031,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) vr[blk][c] = *reinterpret_cast<const h8 *>(&kv_lds[buf][1][blk][4 * c + r][8 * n]);
+            for (int c = 0; c < 4; ++c) vr[blk][c] = *reinterpret_cast<const h8 *>(&kv_lds[buf][1][sb + blk][4 * c + r][8 * n]);
         // masks, only where the pair reaches past the first row's position or
         // the last key this wave sees (keys there may be stale: zero their values)
         const int k_last = b * kBlockSize + 2 * kBlockSize - 1;
@@ -1086,18 +1102,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) {
 
     // the work-group walks every pair of the piece; a wave computes the pairs
     // below its last query's position
-    const int n_pairs = (b_hi - b_lo + 1) / 2;
-    const int w_pairs = w_end > t_lo ? ((w_end + kBlockSize - 1) / kBlockSize - b_lo + 1) / 2 : 0;
-    if (n_pairs > 0) {
+    const int n_stages = (b_hi - b_lo + kStageBlocks - 1) / kStageBlocks;
+    const int w_blocks = w_end > t_lo ? (w_end + kBlockSize - 1) / kBlockSize - b_lo : 0;  // blocks this wave needs
+    if (n_stages > 0) {
         fetch(b_lo);
         commit(0);
         __syncthreads();
     }
-    for (int p = 0; p < n_pairs; ++p) {
-        const int buf = p & 1;
-        if (p + 1 < n_pairs) fetch(b_lo + 2 * (p + 1));
-        if (p < w_pairs) compute(buf, b_lo + 2 * p);
-        if (p + 1 < n_pairs) commit(buf ^ 1);
+    for (int st = 0; st < n_stages; ++st) {
+        const int buf = st & 1;
+        const int b0 = b_lo + kStageBlocks * st;
+        if (st + 1 < n_stages) fetch(b0 + kStageBlocks);
+#pragma unroll
+        for (int sb = 0; sb < kStageBlocks; sb += 2)
+            if (kStageBlocks * st + sb < w_blocks) compute(buf, sb, b0 + sb);
+        if (st + 1 < n_stages) commit(buf ^ 1);
         __syncthreads();
     }
     if (rows_w <= 0) return;
@@ -1143,7 +1162,29 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) {
     }
 }
 
+__global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) { prefill_body(a, blockIdx.x); }
+
+// A mixed step's decode pieces and prefill pieces in one launch, so that the
+// bandwidth-bound decode work-groups and the matrix-core-bound prefill
+// work-groups share the compute units instead of running one after the
+// other.  Work-groups [0, decode items x Hkv) are decode pieces (F16 pools),
+// the rest prefill pieces.
+__global__ __launch_bounds__(256, 2) void mixed_kernel(DecodeArgs a) {
+    const uint32_t nd = static_cast<uint32_t>(a.num_items) * static_cast<uint32_t>(a.num_kv_heads);
+    if (blockIdx.x < nd)
+        decode_partial_body<PA_DECODE_NBUF, false>(a, blockIdx.x, 0, 0);
+    else
+        prefill_body(a, blockIdx.x - nd);
+}
+
 }  // namespace
+
+hipError_t launch_mixed(const DecodeArgs &a, hipStream_t stream) {
+    const uint32_t groups =
+        static_cast<uint32_t>((static_cast<int64_t>(a.num_items) + a.num_prefill_items) * a.num_kv_heads);
+    hipLaunchKernelGGL(mixed_kernel, dim3(groups), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream) {
     const int64_t total = static_cast<int64_t>(a.n_tokens) * a.num_kv_heads * (kHeadDim / 8);
