@@ -50,7 +50,12 @@ def kernel_source_hash():
 def read_counters(kv_dtype):
     """HBM traffic per decode_partial launch from the committed rocprofv3 summary,
     or None when it is missing or was taken on other kernel source."""
-    path = COUNTERS_FILES[kv_dtype]
+    return read_counter_file(COUNTERS_FILES[kv_dtype])
+
+
+def read_counter_file(path):
+    """fetch + write bytes per launch from a committed counter summary, or None
+    when it is missing or was taken on other kernel source."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -430,6 +435,7 @@ def main():
 
 
 MIXED_METRIC = "mixed step (chunked prefill + decode): query tokens/s"
+PREFILL_COUNTERS = {6: os.path.join(ROOT, "profiles", "prefill_c6_counters.txt")}
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
@@ -624,7 +630,9 @@ def bench_mixed(args, w, dev):
                    "schedule": {"decode_pieces": info.num_items, "prefill_pieces": info.num_prefill_items,
                                 "merges": info.num_merges}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": read_counter_file(PREFILL_COUNTERS[args.config])
+                     if args.config in PREFILL_COUNTERS and pf_info.num_merges == 0 else None,
                      "kernel": "prefill_kernel" + (" + decode_merge_planned_kernel" if pf_info.num_merges else ""),
                      "flops_per_layer": pf_flops, "mean_layer_us": round(pf_us, 3)},
         "decode_rows_us_per_layer": round(dec_us, 3),

@@ -414,8 +414,13 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
             int32_t f[pa::kPrefillItemInts];
         };
         std::vector<PrefillItem> pitems;
-        const int64_t ppiece = std::min<int64_t>(pa::kMaxPrefillPieceBlocks,
-                                                 std::max<int64_t>(8, cut(tile_blocks, items_target)));
+        int64_t ppiece = std::min<int64_t>(pa::kMaxPrefillPieceBlocks,
+                                           std::max<int64_t>(8, cut(tile_blocks, items_target)));
+        if (const char *env = std::getenv("PA_PREFILL_PIECE_BLOCKS")) {  // tuning override
+            char *end = nullptr;
+            const long v = std::strtol(env, &end, 10);
+            if (end != env && v >= 2 && v <= pa::kMaxPrefillPieceBlocks) ppiece = v;
+        }
         for (int32_t s = 0; s < batch; ++s) {
             const int64_t q_len = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
             if (q_len < 2) continue;
