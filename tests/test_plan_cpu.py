@@ -226,7 +226,7 @@ def _check_mixed(q_lens, lens, info, plan):
             records[slot] = records.get(slot, 0) + 1
     tiles = {}
     for s, row0, n_q, pos0, t0, t1, base, np_, p, *rest in pf:
-        assert q_lens[s] >= 2 and 1 <= n_q <= 32 and rest == [0, 0, 0]
+        assert q_lens[s] >= 2 and 1 <= n_q <= 64 and rest == [0, 0, 0]
         assert starts[s] <= row0 and row0 + n_q <= starts[s + 1]
         assert pos0 == lens[s] - q_lens[s] + (row0 - starts[s])
         assert t0 % 16 == 0 and 0 <= t0 < t1 <= pos0 + n_q and 0 <= p < np_
