@@ -133,8 +133,8 @@ def main():
     B, HQ, HKV, D = w.block_size, w.num_q_heads, w.num_kv_heads, w.head_dim
     log(f"workload: {w.name}; pool {w.layers} layers x {w.pool_blocks} blocks")
     if w.q_lens is not None:
-        if args.kv_dtype != "f16" or args.cascade or args.graph:
-            print("mixed steps run on F16 pools, without --cascade or --graph", file=sys.stderr)
+        if args.cascade or args.graph:
+            print("mixed steps run without --cascade or --graph", file=sys.stderr)
             sys.exit(2)
         return bench_mixed(args, w, dev)
 
@@ -456,11 +456,15 @@ def bench_mixed(args, w, dev):
     dec_seqs = [s for s in range(w.batch) if w.q_lens[s] == 1]
 
     t_stage = time.time()
-    pool = pa.Pool(w.layers, w.pool_blocks, HKV, D, B, device=dev, fill=0.0)
+    fp8 = args.kv_dtype == "fp8"
+    pool = pa.Pool(w.layers, w.pool_blocks, HKV, D, B, device=dev, fill=0.0,
+                   dtype=pa.PA_FP8_E4M3 if fp8 else pa.PA_F16)
     q_dev, tables_dev = [], []
     host0 = None
     for layer in range(w.layers):
         ids, k, v = w.kv_blocks(layer)
+        if fp8:
+            pool.set_scales(layer, FP8_SCALE, FP8_SCALE)
         pool.write_blocks(layer, torch.from_numpy(ids).to(dev), torch.from_numpy(k).to(dev),
                           torch.from_numpy(v).to(dev))
         q = w.q_rows(total_q, layer)
@@ -572,7 +576,7 @@ def bench_mixed(args, w, dev):
         vis += n * hist + n * (n + 1) // 2
     pf_flops = 4 * D * HQ * vis
     achieved = pf_flops / (pf_us * 1e-6) / 1e12
-    dec_bytes = int(lens_host[dec_seqs].astype(np.int64).sum()) * HKV * D * 2 * 2
+    dec_bytes = int(lens_host[dec_seqs].astype(np.int64).sum()) * HKV * D * 2 * (1 if fp8 else 2)
     log(f"step {ms_per_step:.4f} ms; prefill part {pf_us:.2f} us/layer ({achieved:.1f} TFLOP/s); "
         f"decode part {dec_us:.2f} us/layer ({dec_bytes / (dec_us * 1e-6) / 1e9:.0f} GB/s)")
 
@@ -585,6 +589,9 @@ def bench_mixed(args, w, dev):
         threads = len(os.sched_getaffinity(0))
         q, tables, ids, k, v = host0
         kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, w.ctx_lens, B)
+        if fp8:   # the codes the pool holds, computed by the oracle from the F16 values
+            kc = oracle.quantize_e4m3(kc, FP8_SCALE)
+            vc = oracle.quantize_e4m3(vc, FP8_SCALE)
         gpu = outs[0].cpu().numpy().astype(np.float64)
         owner = np.searchsorted(qs, np.arange(total_q), side="right") - 1
         rng = np.random.default_rng(0)
@@ -595,8 +602,12 @@ def bench_mixed(args, w, dev):
             own = owner[rows]
             visn = (lens_host[own] - w.q_lens[own] + (rows - qs[own]) + 1).astype(np.int32)
             t_cpu = time.perf_counter()
-            ref = oracle.prefill(q[rows], kc, vc, t2[own], np.arange(len(rows) + 1, dtype=np.int32), visn,
-                                 w.scale, B, threads=threads)
+            one_each = np.arange(len(rows) + 1, dtype=np.int32)
+            if fp8:
+                ref = oracle.prefill_e4m3(q[rows], kc, vc, t2[own], one_each, visn, w.scale, B, FP8_SCALE,
+                                          FP8_SCALE, threads=threads)
+            else:
+                ref = oracle.prefill(q[rows], kc, vc, t2[own], one_each, visn, w.scale, B, threads=threads)
             cpu_s += time.perf_counter() - t_cpu
             errs.append(float(np.abs(gpu[rows] - ref).max()))
             refs.append(float((ref ** 2).sum()))
@@ -621,9 +632,9 @@ def bench_mixed(args, w, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "fp8_e4m3" if fp8 else "f16",
         "data": "synthetic",
-        "config": {"workload": w.name, "layers": w.layers, "sequences": w.batch,
+        "config": {"workload": w.name, "kv_dtype": args.kv_dtype, "layers": w.layers, "sequences": w.batch,
                    "query_tokens": total_q, "prompt_chunk_tokens": int(sum(w.q_lens[chunk_seqs])),
                    "decode_rows": len(dec_seqs), "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
                    "block_size": B,
@@ -632,7 +643,7 @@ def bench_mixed(args, w, dev):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": read_counter_file(PREFILL_COUNTERS[args.config])
-                     if args.config in PREFILL_COUNTERS and pf_info.num_merges == 0 else None,
+                     if args.config in PREFILL_COUNTERS and pf_info.num_merges == 0 and not fp8 else None,
                      "kernel": "prefill_kernel" + (" + decode_merge_planned_kernel" if pf_info.num_merges else ""),
                      "flops_per_layer": pf_flops, "mean_layer_us": round(pf_us, 3)},
         "decode_rows_us_per_layer": round(dec_us, 3),

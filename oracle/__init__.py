@@ -218,3 +218,27 @@ def decode_e4m3(q, k_codes, v_codes, block_tables, ctx_lens, scale, block_size, 
     if rc != 0:
         raise ValueError(f"oracle rejected its inputs (code {rc})")
     return out
+
+
+def prefill_e4m3(q, k_codes, v_codes, block_tables, query_start, seq_lens, scale, block_size,
+                 k_scale, v_scale, threads=0):
+    """fp64 output of a chunked-prefill / mixed step over FP8 (E4M3) slot caches.
+
+    Query j of sequence s's q_len-token chunk attends exactly as a one-token
+    decode whose context is the positions it sees, 0 .. seq_len - q_len + j
+    (the identity the F16 prefill oracle is pinned to), so every packed row is
+    handed to decode_e4m3 with its own context length and its sequence's table.
+    """
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    starts = np.asarray(query_start, dtype=np.int64)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    batch = lens.shape[0]
+    assert starts.shape == (batch + 1,) and starts[0] == 0
+    q_lens = np.diff(starts)
+    if np.any(q_lens < 0) or np.any(lens < q_lens):
+        raise ValueError("query offsets do not fit the sequence lengths")
+    owner = np.repeat(np.arange(batch), q_lens)
+    j = np.arange(int(starts[-1])) - starts[owner]
+    ctx = (lens[owner] - q_lens[owner] + j + 1).astype(np.int32)
+    return decode_e4m3(q, k_codes, v_codes, tables[owner], ctx, scale, block_size, k_scale,
+                       v_scale, threads)

@@ -561,7 +561,7 @@ pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const
     a.num_members = info->num_members;
     a.prefill_items = a.members + static_cast<size_t>(pa::kMemberInts) * info->num_members;
     a.num_prefill_items = info->num_prefill_items;
-    if (info->num_items > 0 && info->num_prefill_items > 0 && pool->elem_bytes() == 2 &&
+    if (info->num_items > 0 && info->num_prefill_items > 0 &&
         static_cast<int64_t>(info->num_items + info->num_prefill_items) * pool->desc.num_kv_heads <= 0x7fffffff) {
         // decode and prefill pieces share one launch
         if (pa::launch_mixed(a, stream) != hipSuccess) return PA_ERR_HIP;
@@ -613,7 +613,6 @@ pa_status pa_prefill_run(pa_pool *pool, int32_t layer, const pa_plan_info *info,
                          int32_t max_blocks_per_seq, float scale, void *workspace_dev, size_t workspace_bytes,
                          hipStream_t stream) {
     if (info && (info->num_prefix_items != 0 || info->num_members != 0)) return PA_ERR_INVALID_ARG;
-    if (pool && info && info->num_prefill_items > 0 && pool->elem_bytes() != 2) return PA_ERR_UNSUPPORTED;
     return run_plan(pool, layer, info, plan_dev, q_dev, nullptr, nullptr, out_dev, block_tables_dev,
                     max_blocks_per_seq, scale, workspace_dev, workspace_bytes, stream);
 }

@@ -868,7 +868,7 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // prefill: chunked-prefill pieces of a mixed step ("Batching and Scheduling",
-// Example 5), F16 pools.  One work-group per (piece, KV head); a piece is a
+// Example 5).  One work-group per (piece, KV head); a piece is a
 // tile of up to kPrefillTile query tokens of one sequence against a range of
 // its key blocks.  The tile's queries sit at positions pos0 .. pos0+n_q-1 and
 // query t sees keys 0 .. pos0 + t (causal).  Wave w owns query tokens
@@ -876,7 +876,10 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
 // whose row n is token 16(w/2) + n.
 // Key blocks come kStageBlocks at a time: the work-group copies the stage's
 // K and V tiles into LDS once -- each wave a quarter, 1 KiB per load
-// instruction -- double-buffered, one barrier per stage; each wave then works
+// instruction -- double-buffered, one barrier per stage (FP8 pools: the
+// codes are widened to F16 on the way into LDS, so the arithmetic below is
+// the F16 path's; K's scale is folded into the score scale and V's applied
+// to the result); each wave then works
 // through the stage two blocks at a time, reading its MFMA operands once per
 // pair (rows padded to 136 halves: conflict-free).
 //   S^T = K . Q^T  v_mfma_f32_16x16x32_f16 per 32 dims and block:
@@ -906,6 +909,7 @@ constexpr int kKvRow = kHeadDim + 8;  // padded LDS row (halves)
 constexpr int kStageBlocks = PA_PREFILL_STAGE_BLOCKS;  // key blocks per LDS stage (even)
 static_assert(kStageBlocks % 2 == 0 && kStageBlocks >= 2, "stages hold whole pairs");
 
+template <bool FP8>
 __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     const int g = static_cast<int>(bx % a.num_kv_heads);
     const int32_t *it = a.prefill_items + kPrefillItemInts * static_cast<size_t>(bx / a.num_kv_heads);
@@ -976,14 +980,17 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     const h2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 
     // copies: wave w moves tensor w/2 (K, V) of block w%2 of the pair, 1 KiB per
-    // load instruction: lane l takes bytes 16 l + 1024 i, i.e. row l/16 + 4i,
-    // dims 8(l%16) .. +7
+    // load instruction: lane l takes bytes 16 l + 1024 i, i.e. for F16 row
+    // l/16 + 4i, dims 8(l%16) .. +7, and for FP8 row l/8 + 8i, dims
+    // 16(l%8) .. +15
     const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
-    const size_t tile_bytes = tile_elems() * sizeof(uint16_t);
+    const size_t tile_bytes = tile_elems() * (FP8 ? 1 : sizeof(uint16_t));
     constexpr int kCopyBlocks = kStageBlocks / 2;  // blocks of one tensor each wave copies per stage
+    constexpr int kLoads = FP8 ? 2 : 4;            // 16-byte loads per lane and tile
     const int cp_tensor = w >> 1, cp_blk0 = (w & 1) * kCopyBlocks;
     const char *cp_layer = cp_tensor ? a.v_layer : a.k_layer;
-    h8 stg[kCopyBlocks][4];
+    h8 stg[kCopyBlocks][kLoads];   // F16 pools
+    u4 stg8[kCopyBlocks][kLoads];  // FP8 pools: raw codes, widened at commit
     auto fetch = [&](int b) {  // stage starting at block b
 #pragma unroll
         for (int x = 0; x < kCopyBlocks; ++x) {
@@ -994,15 +1001,29 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
             const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
             const __amdgpu_buffer_rsrc_t rs = tile_rsrc(cp_layer + base, live ? static_cast<int>(tile_bytes) : 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) stg[x][i] = load_tile16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
+            for (int i = 0; i < kLoads; ++i) {
+                if constexpr (FP8)
+                    stg8[x][i] = load_raw16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
+                else
+                    stg[x][i] = load_tile16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
+            }
         }
     };
     auto commit = [&](int buf) {
 #pragma unroll
         for (int x = 0; x < kCopyBlocks; ++x)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<h8 *>(&kv_lds[buf][cp_tensor][cp_blk0 + x][(lane >> 4) + 4 * i][8 * n]) = stg[x][i];
+            for (int i = 0; i < kLoads; ++i) {
+                if constexpr (FP8) {
+                    _Float16 *dst = &kv_lds[buf][cp_tensor][cp_blk0 + x][(lane >> 3) + 8 * i][16 * (lane & 7)];
+                    const u4 c = stg8[x][i];
+                    *reinterpret_cast<h8 *>(dst) = fp8_decode8_h(c.x, c.y);
+                    *reinterpret_cast<h8 *>(dst + 8) = fp8_decode8_h(c.z, c.w);
+                } else {
+                    *reinterpret_cast<h8 *>(&kv_lds[buf][cp_tensor][cp_blk0 + x][(lane >> 4) + 4 * i][8 * n]) =
+                        stg[x][i];
+                }
+            }
     };
 
     const int kpi = 4 * (n & 3) + (n >> 2);  // pi(n)
@@ -1144,7 +1165,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
             const float m = ml_lds[w][rt][t][0], l = ml_lds[w][rt][t][1];
             if (direct) {
                 const size_t qrow = static_cast<size_t>(min(row0 + tok, a.num_q_rows - 1));
-                const float inv = 1.0f / l;
+                const float inv = (FP8 ? a.v_scale : 1.0f) / l;  // FP8: V's scale
                 h8 o;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) o[j] = static_cast<_Float16>(oacc[rt][j][c] * inv);
@@ -1154,27 +1175,34 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
                 const size_t slot = static_cast<size_t>(min<int64_t>(slot64, a.num_slots - 1));
                 const size_t rec = slot * a.num_q_heads + head;
                 float4 *dst = reinterpret_cast<float4 *>(a.o_part + rec * kHeadDim + 8 * n);
-                dst[0] = make_float4(oacc[rt][0][c], oacc[rt][1][c], oacc[rt][2][c], oacc[rt][3][c]);
-                dst[1] = make_float4(oacc[rt][4][c], oacc[rt][5][c], oacc[rt][6][c], oacc[rt][7][c]);
+                const float vs = FP8 ? a.v_scale : 1.0f;  // records hold values, as the decode pieces' do
+                dst[0] = make_float4(oacc[rt][0][c] * vs, oacc[rt][1][c] * vs, oacc[rt][2][c] * vs,
+                                     oacc[rt][3][c] * vs);
+                dst[1] = make_float4(oacc[rt][4][c] * vs, oacc[rt][5][c] * vs, oacc[rt][6][c] * vs,
+                                     oacc[rt][7][c] * vs);
                 if (n == 0) *reinterpret_cast<float2 *>(a.ml_part + rec * 2) = make_float2(m, l);
             }
         }
     }
 }
 
-__global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) { prefill_body(a, blockIdx.x); }
+template <bool FP8>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) {
+    prefill_body<FP8>(a, blockIdx.x);
+}
 
 // A mixed step's decode pieces and prefill pieces in one launch, so that the
 // bandwidth-bound decode work-groups and the matrix-core-bound prefill
 // work-groups share the compute units instead of running one after the
-// other.  Work-groups [0, decode items x Hkv) are decode pieces (F16 pools),
-// the rest prefill pieces.
+// other.  Work-groups [0, decode items x Hkv) are decode pieces, the rest
+// prefill pieces.
+template <bool FP8>
 __global__ __launch_bounds__(256, 2) void mixed_kernel(DecodeArgs a) {
     const uint32_t nd = static_cast<uint32_t>(a.num_items) * static_cast<uint32_t>(a.num_kv_heads);
     if (blockIdx.x < nd)
-        decode_partial_body<PA_DECODE_NBUF, false>(a, blockIdx.x, 0, 0);
+        decode_partial_body<FP8 ? PA_DECODE_NBUF_FP8 : PA_DECODE_NBUF, FP8>(a, blockIdx.x, 0, 0);
     else
-        prefill_body(a, blockIdx.x - nd);
+        prefill_body<FP8>(a, blockIdx.x - nd);
 }
 
 }  // namespace
@@ -1182,7 +1210,10 @@ __global__ __launch_bounds__(256, 2) void mixed_kernel(DecodeArgs a) {
 hipError_t launch_mixed(const DecodeArgs &a, hipStream_t stream) {
     const uint32_t groups =
         static_cast<uint32_t>((static_cast<int64_t>(a.num_items) + a.num_prefill_items) * a.num_kv_heads);
-    hipLaunchKernelGGL(mixed_kernel, dim3(groups), dim3(256), 0, stream, a);
+    if (a.elem_bytes == 1)
+        hipLaunchKernelGGL(mixed_kernel<true>, dim3(groups), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(mixed_kernel<false>, dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1218,7 +1249,10 @@ hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream) 
 
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
     const uint32_t groups = static_cast<uint32_t>(static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads);
-    hipLaunchKernelGGL(prefill_kernel, dim3(groups), dim3(256), 0, stream, a);
+    if (a.elem_bytes == 1)
+        hipLaunchKernelGGL(prefill_kernel<true>, dim3(groups), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(prefill_kernel<false>, dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -143,7 +143,7 @@ def test_fp8_value_scale_is_linear():
     st.pool.set_scales(0, SCALES[0], 2 * SCALES[1])
     b = st.decode(0).float()
     a2 = 2 * a.float()
-    normal = a.float().abs() >= 2.0 ** -14      # F16 subnormals round on their own grid
+    normal = a.float().abs() > 2.0 ** -14       # values at 2^-14 may be rounded subnormals
     assert torch.equal(b[normal], a2[normal])
     assert float((b - a2).abs().max()) <= 2.0 ** -24
     st.close()

@@ -4,6 +4,7 @@ float8_e4m3fn (CPU), round trips, tie cases, and the pinned F16 decode."""
 import math
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -84,3 +85,30 @@ def test_fp8_decode_reduces_to_the_f16_decode_on_dequantised_values():
     a = oracle.decode_e4m3(q, kc, vc, tables, lens, 0.3, bs, ks, vs)
     b = oracle.decode(q, kf, vf, tables, lens, 0.3, bs)
     np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_fp8_prefill_reduces_to_the_f16_prefill_on_dequantised_values():
+    """A chunked-prefill step over FP8 codes with power-of-two scales equals
+    the pinned F16 prefill oracle fed with the dequantised values (chunks of
+    0, 1 and several tokens, with and without history)."""
+    rng = np.random.default_rng(8)
+    hq, hkv, d, bs, nb = 8, 2, 16, 4, 32
+    q_lens = [3, 1, 0, 7, 5]
+    lens = np.array([3, 9, 6, 16, 12], np.int32)
+    starts = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    kc = rng.integers(0, 256, (nb * bs, hkv, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, (nb * bs, hkv, d)).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x21                   # no NaN codes
+    vc[(vc & 0x7F) == 0x7F] = 0x21
+    tables = rng.permutation(nb)[:20].reshape(5, 4).astype(np.int32)
+    q = rng.standard_normal((int(starts[-1]), hq, d)).astype(np.float16)
+    ks, vs = 0.125, 4.0
+    lut = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    kf = (lut[kc] * ks).astype(np.float16)
+    vf = (lut[vc] * vs).astype(np.float16)
+    assert np.array_equal(vf.astype(np.float64), lut[vc] * vs)   # exact in F16
+    a = oracle.prefill_e4m3(q, kc, vc, tables, starts, lens, 0.4, bs, ks, vs)
+    b = oracle.prefill(q, kf, vf, tables, starts, lens, 0.4, bs)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):                   # a chunk longer than its sequence
+        oracle.prefill_e4m3(q[:4], kc, vc, tables[:2], [0, 1, 4], [8, 2], 0.4, bs, ks, vs)

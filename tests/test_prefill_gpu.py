@@ -62,18 +62,25 @@ class Mixed:
         torch.cuda.synchronize()
         return out, plan
 
+    def _oracle(self, q, kc, vc, tables, starts, lens):
+        if self.st.fp8:
+            ks, vs = self.st.kv_scales
+            return oracle.prefill_e4m3(q, oracle.quantize_e4m3(kc, ks), oracle.quantize_e4m3(vc, vs), tables,
+                                       starts, lens, self.w.scale, 16, ks, vs)
+        return oracle.prefill(q, kc, vc, tables, starts, lens, self.w.scale, 16)
+
     def reference(self, rows=None):
         q, tables, ids, k, v = self.st.host[0]
         kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, self.w.ctx_lens, 16)
         if rows is None:
-            return oracle.prefill(self.q, kc, vc, t2, self.starts, self.lens, self.w.scale, 16)
+            return self._oracle(self.q, kc, vc, t2, self.starts, self.lens)
         # sampled rows: each as a one-token step over its own visible prefix
         owner = np.searchsorted(self.starts, rows, side="right") - 1
         q_lens = np.array(self.q_lens)
         seq_of = owner
         vis = np.array(self.lens)[seq_of] - q_lens[seq_of] + (rows - self.starts[seq_of]) + 1
-        return oracle.prefill(self.q[rows], kc, vc, t2[seq_of], np.arange(len(rows) + 1, dtype=np.int32),
-                              vis.astype(np.int32), self.w.scale, 16)
+        return self._oracle(self.q[rows], kc, vc, t2[seq_of], np.arange(len(rows) + 1, dtype=np.int32),
+                            vis.astype(np.int32))
 
     def close(self):
         self.st.close()
@@ -166,17 +173,75 @@ def test_mixed_step_under_a_2048_token_budget_sampled():
     m.close()
 
 
-def test_fp8_pool_runs_decode_rows_but_not_prefill_tiles():
-    m = Mixed([1, 1, 40], [30, 300, 10], seed=103, dtype=pa.PA_FP8_E4M3, kv_scales=(0.1, 0.02))
-    with pytest.raises(pa.PaError) as e:
-        m.run()
-    assert e.value.status == pa.PA_ERR_UNSUPPORTED
+FP8 = pa.PA_FP8_E4M3
+# non-power-of-two scales: fl32(1/scale) is inexact and the codes span most
+# of the format's range
+FP8_SCALES = (0.1, 0.0173)
+
+
+@pytest.mark.parametrize("q_lens,hist", [
+    ([1, 2, 15, 16, 17, 63, 64, 65, 100, 1, 0, 255], [100, 0, 17, 5, 0, 64, 1, 33, 4000, 4095, 9, 2000]),
+    ([40, 1, 1], [10, 30, 300]),
+])
+def test_fp8_mixed_step_ragged(q_lens, hist):
+    """FP8 pools: decode rows and prefill tiles in one launch; slots past each
+    sequence's length hold NaN codes."""
+    m = Mixed(q_lens, hist, seed=110 + len(q_lens), dtype=FP8, kv_scales=FP8_SCALES)
+    out, plan = m.run()
+    report("fp8 mixed ragged", rows=len(m.q), decode_items=plan.info.num_items,
+           prefill_items=plan.info.num_prefill_items, merges=plan.info.num_merges, poisoned=m.poisoned)
+    compare("fp8 mixed ragged", out, m.reference())
     m.close()
-    m = Mixed([1, 1], [30, 300], seed=104, dtype=pa.PA_FP8_E4M3, kv_scales=(0.1, 0.02))
+
+
+@pytest.mark.parametrize("n", [1, 17, 300])
+def test_fp8_whole_prompt_prefill(n):
+    m = Mixed([n], [0], seed=120 + n, dtype=FP8, kv_scales=FP8_SCALES)
     out, _ = m.run()
-    q, tables, ids, k, v = m.st.host[0]
-    kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, m.w.ctx_lens, 16)
-    ref = oracle.decode_e4m3(m.q, oracle.quantize_e4m3(kc, 0.1), oracle.quantize_e4m3(vc, 0.02), t2,
-                             np.array(m.lens, np.int32), m.w.scale, 16, 0.1, 0.02)
-    compare("fp8 decode rows via prefill_run", out, ref)
+    compare(f"fp8 whole prompt {n}", out, m.reference())
+    # the first token sees only itself: its value codes times V's scale,
+    # rounded once to fp32 and once to F16
+    codes = m.st.pool.v[0, int(m.st.host[0][1][0, 0]), :, 0, :].cpu().numpy()
+    lut = np.array([oracle.e4m3_to_f64(c) for c in range(256)], np.float32)
+    want = (lut[codes] * np.float32(FP8_SCALES[1])).astype(np.float16)
+    assert np.array_equal(out[0].cpu().numpy(), np.repeat(want, 4, axis=0))
+    m.close()
+
+
+def test_fp8_long_chunk_split_into_merged_pieces():
+    """Cut tiles write value-domain records (V's scale applied) that the
+    merge combines with each other."""
+    m = Mixed([300, 1, 1], [3000, 5000, 10], seed=130, dtype=FP8, kv_scales=FP8_SCALES)
+    out, plan = m.run()
+    report("fp8 split pieces", prefill_items=plan.info.num_prefill_items, merges=plan.info.num_merges)
+    assert plan.info.num_merges > 0 and plan.info.num_prefill_items > 5
+    compare("fp8 split pieces", out, m.reference())
+    m.close()
+
+
+def test_fp8_one_token_rows_equal_the_planned_decode_bitwise():
+    lens = [1, 17, 300, 4097, 64]
+    m = Mixed([1] * len(lens), [x - 1 for x in lens], seed=131, dtype=FP8, kv_scales=FP8_SCALES)
+    out, _ = m.run()
+    plan = m.st.pool.plan(np.array(lens, np.int32))
+    out2 = torch.empty_like(m.qd)
+    m.st.pool.run(0, plan, m.qd, out2, m.st.dev[0][1], m.w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    compare("fp8 decode rows", out, m.reference())
+    m.close()
+
+
+def test_fp8_value_scale_is_linear_in_prefill_rows():
+    """Doubling V's scale (codes unchanged) doubles every prefill row exactly,
+    for whole tiles and for cut (merged) tiles."""
+    m = Mixed([50, 200], [0, 4000], seed=132, dtype=FP8, kv_scales=FP8_SCALES)
+    a, plan = m.run()
+    assert plan.info.num_merges > 0
+    m.st.pool.set_scales(0, FP8_SCALES[0], 2 * FP8_SCALES[1])
+    b, _ = m.run()
+    a2, b = 2 * a.float(), b.float()
+    normal = a.float().abs() > 2.0 ** -14       # values at 2^-14 may be rounded subnormals
+    assert torch.equal(b[normal], a2[normal])
+    assert float((b - a2).abs().max()) <= 2.0 ** -24
     m.close()
