@@ -125,10 +125,6 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
         return
-    if args.cascade and args.kv_dtype == "fp8":
-        print("--cascade needs an F16 pool (the shared-prefix kernel reads F16 tiles)",
-              file=sys.stderr)
-        sys.exit(2)
     w = workloads.config(args.config, args.seed)
     B, HQ, HKV, D = w.block_size, w.num_q_heads, w.num_kv_heads, w.head_dim
     log(f"workload: {w.name}; pool {w.layers} layers x {w.pool_blocks} blocks")
@@ -314,7 +310,14 @@ def main():
     tokens_per_s = w.batch / (ms_per_step * 1e-3)
     kb = roofline.split_kernel_bytes(w.ctx_lens, HQ, HKV, D, B, kv_elem_bytes=eb)
     part_mean_s = float(np.mean(part_us)) * 1e-6
-    achieved = kb["total"] / part_mean_s / 1e9
+    # shared prefix blocks: HBM need deliver each distinct slot only once, so
+    # the roofline counts unique K/V bytes (the logical rate is "value")
+    basis = "logical"
+    launch_bytes = kb["total"]
+    if w.prefix_groups is not None:
+        basis = "unique"
+        launch_bytes = kb["total"] - kb["kv"] + w.kv_unique_bytes(eb) // w.layers
+    achieved = launch_bytes / part_mean_s / 1e9
     traffic = read_counters(args.kv_dtype) if args.config == COUNTERS_CONFIG else None
 
     # ---- HBM read probe: the bandwidth this GPU reaches on a plain stream ----
@@ -421,8 +424,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic if info.num_merges == 0 else None,
                      "kernel": "decode_partial_kernel" if info.num_merges == 0
-                     else "decode_partial_kernel + decode_merge_planned_kernel",
-                     "bytes_per_launch": kb["total"],
+                     else "decode_partial_kernel + " + ("decode_prefix_kernel + " if info.num_prefix_items else "")
+                     + "decode_merge_planned_kernel",
+                     "bytes_per_launch": launch_bytes, "kv_bytes_basis": basis,
                      "mean_launch_us": round(part_mean_s * 1e6, 3)},
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
         "hbm_read_probe_GBps": round(probe, 1) if probe else None,

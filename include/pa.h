@@ -40,8 +40,9 @@
  *
  * Geometry supported by this build: head_dim 128, block_size 16, F16 or FP8
  * (E4M3) keys and values, F16 queries and outputs, and num_q_heads = 4 *
- * num_kv_heads.  Other values return PA_ERR_UNSUPPORTED.  The shared-prefix
- * schedule (pa_cascade_plan) runs on F16 pools only.
+ * num_kv_heads.  Other values return PA_ERR_UNSUPPORTED.  Every schedule
+ * (decode, shared-prefix cascade, chunked prefill / mixed) runs on both pool
+ * types.
  */
 #ifndef PA_H
 #define PA_H
@@ -298,9 +299,8 @@ pa_status pa_prefill_plan(const pa_pool *pool, const int32_t *query_start_host,
                           void *plan_host, size_t plan_host_bytes, pa_plan_info *info);
 
 /* One layer of a chunked-prefill / mixed step on a pa_prefill_plan schedule.
- * q_dev and out_dev hold info->num_q_rows packed rows.  F16 pools only
- * (PA_ERR_UNSUPPORTED for an FP8 pool when the plan has prefill pieces).
- * Tables, scale, workspace and stream as pa_decode_run. */
+ * q_dev and out_dev hold info->num_q_rows packed rows (F16, for F16 and FP8
+ * pools alike).  Tables, scale, workspace and stream as pa_decode_run. */
 pa_status pa_prefill_run(pa_pool *pool, int32_t layer, const pa_plan_info *info,
                          const void *plan_dev, const void *q_dev, void *out_dev,
                          const int32_t *block_tables_dev, int32_t max_blocks_per_seq, float scale,

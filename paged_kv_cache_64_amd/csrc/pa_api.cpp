@@ -527,7 +527,6 @@ pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const
     const size_t need = planned_workspace(info->num_slots, info->num_q_heads, &o_bytes);
     if (need > 0 && (!workspace_dev || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace_dev, 256)) return PA_ERR_INVALID_ARG;
-    if (info->num_prefix_items > 0 && pool->elem_bytes() != 2) return PA_ERR_UNSUPPORTED;  // cascade: F16 pools
     pa::DecodeArgs a{};
     a.k_layer = static_cast<const char *>(pool->k) + pool->layer_offset(layer);
     a.v_layer = static_cast<const char *>(pool->v) + pool->layer_offset(layer);

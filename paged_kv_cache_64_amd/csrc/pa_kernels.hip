@@ -694,7 +694,10 @@ __global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a)
 //                                 from a per-wave LDS copy of the V tile
 //                   D = O        (lane: rows 4r + c, dim 16 dt + n)
 // Each member's result is a partial record (o, m, l), merged with the
-// member's own suffix pieces by decode_merge_planned.
+// member's own suffix pieces by decode_merge_planned.  FP8 pools: each lane
+// loads the same tokens and dims as 8-byte code groups and widens them to
+// F16 in registers; K's scale is folded into the score scale and V's
+// multiplies the records, which then hold values like every other piece's.
 // ---------------------------------------------------------------------------
 struct h4x2 {
     h4 v[2];
@@ -703,6 +706,7 @@ __device__ __forceinline__ h4x2 quads(h8 x) { return __builtin_bit_cast(h4x2, x)
 
 constexpr int kVRow = kHeadDim + 8;  // padded LDS row of the staged V tile (halves)
 
+template <bool FP8>
 __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
     const int g = static_cast<int>(blockIdx.x % a.num_kv_heads);
     const int32_t *it = a.prefix_items + kPrefixItemInts * static_cast<size_t>(blockIdx.x / a.num_kv_heads);
@@ -746,11 +750,13 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
     __syncthreads();
 
     const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
-    const size_t tile_bytes = tile_elems() * sizeof(uint16_t);  // F16 pools only
+    constexpr int kElem = FP8 ? 1 : 2;
+    const size_t tile_bytes = tile_elems() * kElem;
     const char *k_layer = a.k_layer;
     const char *v_layer = a.v_layer;
-    const uint32_t k_off = static_cast<uint32_t>(n * kHeadDim * 2 + 16 * r);  // + 64 i
-    const uint32_t v_off = static_cast<uint32_t>(lane * 16);                  // + 1024 c
+    // K: token n, dims 32i + 8r .. +7;  V: token 4c + r, dims 8n .. +7
+    const uint32_t k_off = static_cast<uint32_t>((n * kHeadDim + 8 * r) * kElem);  // + 32 i elements
+    const uint32_t v_off = static_cast<uint32_t>((r * kHeadDim + 8 * n) * kElem);  // + 4 c rows
 
     float m_run = -INFINITY;  // running max of row n (log2 units)
     float l_run = 0.0f;       // this lane's share of row n's running sum
@@ -759,6 +765,7 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
     for (int dt = 0; dt < 8; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
 
     h8 kb[2][4], vb[2][4];
+    u2 kr8[2][4], vr8[2][4];  // FP8 pools: raw codes until consumed
     auto issue = [&](int buf, int b) {
         const bool live = b < b_end;
         uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tbl_lds[live ? b - b_begin : 0]));
@@ -767,13 +774,29 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
         const int bytes = live ? static_cast<int>(tile_bytes) : 0;
         const __amdgpu_buffer_rsrc_t kr = tile_rsrc(k_layer + base, bytes);
         const __amdgpu_buffer_rsrc_t vr = tile_rsrc(v_layer + base, bytes);
+        if constexpr (FP8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kb[buf][i] = load_tile16(kr, k_off + 64u * i);
+            for (int i = 0; i < 4; ++i) kr8[buf][i] = load_raw8(kr, k_off + 32u * i);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) vb[buf][c] = load_tile16(vr, v_off + 1024u * c);
+            for (int c = 0; c < 4; ++c) vr8[buf][c] = load_raw8(vr, v_off + 512u * c);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kb[buf][i] = load_tile16(kr, k_off + 64u * i);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) vb[buf][c] = load_tile16(vr, v_off + 1024u * c);
+        }
+    };
+    auto widen = [&](int buf) {  // FP8: the buffer's codes to F16
+        if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kb[buf][i] = fp8_decode8_h(kr8[buf][i].x, kr8[buf][i].y);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) vb[buf][c] = fp8_decode8_h(vr8[buf][c].x, vr8[buf][c].y);
+        }
     };
 
     auto consume = [&](int buf, int b) {
+        widen(buf);
         // S^T for this wave's 16 rows
         f4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -856,8 +879,9 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const size_t rec = static_cast<size_t>(slot) * a.num_q_heads + g * kGroup + c;
+            const float vs = FP8 ? a.v_scale : 1.0f;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) a.o_part[rec * kHeadDim + 16 * dt + n] = acc[dt][c];
+            for (int dt = 0; dt < 8; ++dt) a.o_part[rec * kHeadDim + 16 * dt + n] = acc[dt][c] * vs;
             if (n == 0) {
                 a.ml_part[rec * 2] = ml_lds[w][4 * r + c][0];
                 a.ml_part[rec * 2 + 1] = ml_lds[w][4 * r + c][1];
@@ -1258,7 +1282,10 @@ hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
 
 hipError_t launch_decode_prefix(const DecodeArgs &a, hipStream_t stream) {
     const uint32_t groups = static_cast<uint32_t>(static_cast<int64_t>(a.num_prefix_items) * a.num_kv_heads);
-    hipLaunchKernelGGL(decode_prefix_kernel, dim3(groups), dim3(256), 0, stream, a);
+    if (a.elem_bytes == 1)
+        hipLaunchKernelGGL(decode_prefix_kernel<true>, dim3(groups), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(decode_prefix_kernel<false>, dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -212,13 +212,82 @@ def test_fp8_append_encodes_the_newest_token_and_attends_to_it(planned):
     st.close()
 
 
-def test_fp8_cascade_is_unsupported():
-    w = workloads.custom([40, 50], seed=67, prefix_groups=(1, 2, 2))
-    st = Staged(w, dtype=FP8, kv_scales=SCALES)
-    plan = st.pool.plan(w.ctx_lens, prefix_group=np.zeros(2, np.int32),
-                        prefix_len=np.array([32], np.int32))
+def _cascade(st, group, plen, k_new=None, v_new=None):
+    plan = st.pool.plan(st.w.ctx_lens, prefix_group=group, prefix_len=plen)
     q, tables = st.dev[0]
-    with pytest.raises(pa.PaError) as e:
-        st.pool.run(0, plan, q, torch.empty_like(q), tables, w.scale)
-    assert e.value.status == -2
+    out = torch.empty_like(q)
+    st.pool.run(0, plan, q, out, tables, st.w.scale, k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    return out, plan
+
+
+@pytest.mark.parametrize("groups,gsize,pblocks,extra", [(2, 3, 3, [0, 5, 16, 40, 77, 1]),
+                                                        (1, 20, 5, list(range(0, 200, 10))),
+                                                        (3, 16, 40, [int(x) for x in np.arange(48) * 37 % 900])])
+def test_fp8_cascade_matches_oracle(groups, gsize, pblocks, extra):
+    """Shared-prefix pieces over FP8 tiles: value-domain records merged with
+    the members' own suffix pieces; NaN codes past every context."""
+    lens = [pblocks * 16 + e for e in extra]
+    w = workloads.custom(lens, seed=140 + groups, prefix_groups=(groups, gsize, pblocks))
+    st = Staged(w, dtype=FP8, kv_scales=SCALES)
+    _poison_tails(st)
+    group = np.repeat(np.arange(groups), gsize).astype(np.int32)
+    plen = np.full(groups, pblocks * 16, np.int32)
+    out, plan = _cascade(st, group, plen)
+    report("fp8 cascade", groups=groups, members=gsize, prefix_items=plan.info.num_prefix_items,
+           merges=plan.info.num_merges)
+    assert plan.info.num_prefix_items > 0
+    compare(f"fp8 cascade g{groups}x{gsize}", out, st.reference(0))
+    plain, _ = _planned(st)
+    compare(f"fp8 cascade vs planned g{groups}x{gsize}", out, plain.cpu().numpy().astype(np.float64))
+    st.close()
+
+
+def test_fp8_cascade_with_ungrouped_sequences_and_append():
+    lens = [64 + 3, 64 + 100, 64 + 17, 64 + 1, 500, 0]
+    w = workloads.custom(lens, seed=150, prefix_groups=(1, 4, 4))
+    st = Staged(w, dtype=FP8, kv_scales=SCALES)
+    _poison_tails(st)
+    group = np.array([0, 0, 0, 0, -1, -1], np.int32)
+    plen = np.array([64], np.int32)
+    q, tables, ids, k, v = st.host[0]
+    rng = np.random.default_rng(12)
+    k_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+    v_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+    out, plan = _cascade(st, group, plen, torch.from_numpy(k_new).cuda(), torch.from_numpy(v_new).cuda())
+    assert plan.info.shared_newest == 0 and plan.info.num_prefix_items > 0
+    k2, v2 = k.copy(), v.copy()
+    for s, c in enumerate(w.ctx_lens):
+        if c:
+            r = np.searchsorted(ids, tables[s, (c - 1) // 16])
+            k2[r, (c - 1) % 16] = k_new[s]
+            v2[r, (c - 1) % 16] = v_new[s]
+    st.host[0] = (q, tables, ids, k2, v2)
+    compare("fp8 cascade append", out, st.reference(0))
+    st.close()
+
+
+def test_fp8_cascade_value_scale_is_linear():
+    w = workloads.custom([80 + e for e in (0, 7, 30, 100)], seed=151, prefix_groups=(1, 4, 5))
+    st = Staged(w, dtype=FP8, kv_scales=SCALES)
+    group, plen = np.zeros(4, np.int32), np.array([80], np.int32)
+    a, _ = _cascade(st, group, plen)
+    st.pool.set_scales(0, SCALES[0], 2 * SCALES[1])
+    b, _ = _cascade(st, group, plen)
+    a2, b = 2 * a.float(), b.float()
+    normal = a.float().abs() > 2.0 ** -14       # values at 2^-14 may be rounded subnormals
+    assert torch.equal(b[normal], a2[normal])
+    assert float((b - a2).abs().max()) <= 2.0 ** -24
+    st.close()
+
+
+def test_fp8_cascade_prefix_workload_full():
+    w = workloads.config(5)
+    st = Staged(w, dtype=FP8, kv_scales=SCALES)
+    group = np.repeat(np.arange(16), 16).astype(np.int32)
+    plen = np.full(16, 2048, np.int32)
+    out, plan = _cascade(st, group, plen)
+    report("fp8 cascade config5", prefix_items=plan.info.num_prefix_items, items=plan.info.num_items,
+           merges=plan.info.num_merges)
+    compare("fp8 cascade config5", out, st.reference(0))
     st.close()
