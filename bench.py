@@ -42,6 +42,17 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def kernel_source_hash():
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -385,7 +396,7 @@ def main():
                     break
             layer += 1
         cpu = {"value": round(done_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": host_cpu_model(),
                "sample": f"{done_seqs} (sequence, layer) rows of the same step over layers "
                          f"0..{layer - 1} ({done_bytes} B of K/V), fp64, {cpu_s:.1f} s of oracle time",
                "tokens_per_s_equiv": round(done_bytes / (kv_bytes_step / w.batch) / cpu_s, 4)}
@@ -401,6 +412,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_median": round(float(np.median(step_ms)), 5),
+        "ms_per_step_min": round(float(np.min(step_ms)), 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -536,7 +549,8 @@ def bench_mixed(args, w, dev):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = float(np.mean(step_ms))
 
     # Timed regions 2 and 3: the prompt chunk alone (the prefill kernel and its
     # merge) and the decode rows alone, each as its own plan over all layers
@@ -619,7 +633,7 @@ def bench_mixed(args, w, dev):
             done += len(rows)
         # a step is every row of every layer; the sample is uniform over the rows
         cpu = {"value": round(done / (cpu_s * w.layers), 4), "unit": "tokens/s", "cores": threads,
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": host_cpu_model(),
                "sample": f"{done} of the {total_q} query rows of layer 0 drawn uniformly, fp64, "
                          f"{cpu_s:.1f} s of oracle time, scaled to the {w.layers}-layer step"}
         parity = {"rows": done, "max_abs_err": max(errs), "rel_l2": (sum(diffs) / sum(refs)) ** 0.5}
@@ -633,6 +647,8 @@ def bench_mixed(args, w, dev):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_median": round(float(np.median(step_ms)), 5),
+        "ms_per_step_min": round(float(np.min(step_ms)), 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

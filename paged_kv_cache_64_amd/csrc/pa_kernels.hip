@@ -37,6 +37,7 @@ typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
 struct h2x4 {
     h2 v[4];
 };
@@ -905,18 +906,18 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
 // the F16 path's; K's scale is folded into the score scale and V's applied
 // to the result); each wave then works
 // through the stage two blocks at a time, reading its MFMA operands once per
-// pair (rows padded to 136 halves: conflict-free).
+// pair.
 //   S^T = K . Q^T  v_mfma_f32_16x16x32_f16 per 32 dims and block:
-//                  A = K   (lane l: token pi(l%16) of the block, 8 dims)
+//                  A = K   (lane l: token l%16 of the block, 8 dims)
 //                  B = Q^T (lane l: row l%16, the same 8 dims)
-//                  D = S^T (lane l: tokens 4c + l/16, c < 4, of row l%16),
-//                  pi(m) = 4 (m%4) + m/4 making D's token order that of the
-//                  value operand
-//   O  += P . V    v_mfma_f32_16x16x32_f16 per dim j < 8 and block pair:
-//                  A = P   (lane l: row l%16, tokens 4c + l/16 of both
+//                  D = S^T (lane l: tokens 4(l/16) + c, c < 4, of row l%16)
+//   O  += P . V    v_mfma_f32_16x16x32_f16 per 16 dims 16j .. 16j+15 and
+//                  block pair:
+//                  A = P   (lane l: row l%16, tokens 4(l/16) + c of both
 //                           blocks -- D of S^T as is, rounded to F16)
-//                  B = V   (lane l: the same 8 tokens, dim 8(l%16) + j)
-//                  D = O   (lane l: rows 4(l/16) + c, dim 8(l%16) + j)
+//                  B = V   (lane l: the same 8 tokens at dim 16j + l%16, two
+//                           LDS transpose reads, one per block)
+//                  D = O   (lane l: rows 4(l/16) + c, dim 16j + l%16)
 // Each wave computes only up to its last query's position, and masks only
 // the pairs that reach past its first query's position or its last key.
 // The softmax max is raised lazily as in the decode kernel (the comparison
@@ -926,7 +927,15 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
 // base + k * pieces + p) for decode_merge_planned; a single piece writes F16
 // rows.
 // ---------------------------------------------------------------------------
-constexpr int kKvRow = kHeadDim + 8;  // padded LDS row (halves)
+constexpr int kKvRow = kHeadDim + 8;  // padded K and V rows in LDS (halves): 68 dwords, 4 mod 32
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4a + b receives half b
+// of the 8-byte chunks addressed by lanes a, a + 4, a + 8, a + 12 (in that
+// order); p must point into LDS
+typedef __attribute__((address_space(3))) s4 lds_s4;
+__device__ __forceinline__ h4 lds_read_tr16(const _Float16 *p) {
+    return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(p)));
+}
 #ifndef PA_PREFILL_STAGE_BLOCKS
 #define PA_PREFILL_STAGE_BLOCKS 2
 #endif
@@ -943,7 +952,12 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     const int n = lane & 15, r = lane >> 4;
 
     __shared__ int tbl_lds[kMaxPrefillPieceBlocks];
-    __shared__ _Float16 kv_lds[2][2][kStageBlocks][kBlockSize][kKvRow];  // [buffer][K, V][block][row][dim]
+    __shared__ _Float16 k_lds[2][kStageBlocks][kBlockSize][kKvRow];  // [buffer][block][row][dim]
+    __shared__ _Float16 v_lds[2][kStageBlocks][kBlockSize][kKvRow];
+    // the tile row r of tensor t (0: K, 1: V) in stage buffer buf
+    auto kv_row = [&](int buf, int t, int blk, int row) -> _Float16 * {
+        return t ? &v_lds[buf][blk][row][0] : &k_lds[buf][blk][row][0];
+    };
     __shared__ float alpha_lds[kWaves][2][16];
     __shared__ float ml_lds[kWaves][2][16][2];
 
@@ -1015,6 +1029,11 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     const char *cp_layer = cp_tensor ? a.v_layer : a.k_layer;
     h8 stg[kCopyBlocks][kLoads];   // F16 pools
     u4 stg8[kCopyBlocks][kLoads];  // FP8 pools: raw codes, widened at commit
+    // Value rows at or past the piece's last key (t_hi) may hold anything
+    // (slots past the sequence in its last block): the V resource ends at the
+    // last row below t_hi, so those rows load as zeros and their zero weights
+    // cannot meet a NaN.  Keys below t_hi are stored tokens, finite like every
+    // key the rows see.
     auto fetch = [&](int b) {  // stage starting at block b
 #pragma unroll
         for (int x = 0; x < kCopyBlocks; ++x) {
@@ -1023,7 +1042,10 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
             uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tbl_lds[live ? bb - b_lo : 0]));
             phys = phys > last_block ? last_block : phys;
             const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
-            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(cp_layer + base, live ? static_cast<int>(tile_bytes) : 0);
+            const int rows = cp_tensor ? min(max(t_hi - bb * kBlockSize, 0), kBlockSize) : kBlockSize;
+            // (wave-uniform; said so, or the compiler wraps each load in a waterfall loop)
+            const int bytes = __builtin_amdgcn_readfirstlane(live ? rows * kHeadDim * (FP8 ? 1 : 2) : 0);
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(cp_layer + base, bytes);
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
                 if constexpr (FP8)
@@ -1039,18 +1061,20 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
                 if constexpr (FP8) {
-                    _Float16 *dst = &kv_lds[buf][cp_tensor][cp_blk0 + x][(lane >> 3) + 8 * i][16 * (lane & 7)];
+                    _Float16 *dst = kv_row(buf, cp_tensor, cp_blk0 + x, (lane >> 3) + 8 * i) + 16 * (lane & 7);
                     const u4 c = stg8[x][i];
                     *reinterpret_cast<h8 *>(dst) = fp8_decode8_h(c.x, c.y);
                     *reinterpret_cast<h8 *>(dst + 8) = fp8_decode8_h(c.z, c.w);
                 } else {
-                    *reinterpret_cast<h8 *>(&kv_lds[buf][cp_tensor][cp_blk0 + x][(lane >> 4) + 4 * i][8 * n]) =
+                    *reinterpret_cast<h8 *>(kv_row(buf, cp_tensor, cp_blk0 + x, (lane >> 4) + 4 * i) + 8 * n) =
                         stg[x][i];
                 }
             }
     };
 
-    const int kpi = 4 * (n & 3) + (n >> 2);  // pi(n)
+    // transpose reads: lane l addresses token 4(l/16) + (l/4)%4, dims 4(l%4) .. +3
+    // of a 16-dim slice, so that lane (r, n) receives tokens 4r .. 4r+3 at dim n
+    const int tr_row = 4 * r + ((lane >> 2) & 3), tr_col = 4 * (lane & 3);
     auto compute = [&](int buf, int sb, int b) {  // blocks sb, sb+1 of the stage = key blocks b, b+1
         // the pair's K operands, read once for both row tiles
         h8 kx[2][4];
@@ -1058,7 +1082,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                kx[blk][kk] = *reinterpret_cast<const h8 *>(&kv_lds[buf][0][sb + blk][kpi][32 * kk + 8 * r]);
+                kx[blk][kk] = *reinterpret_cast<const h8 *>(&k_lds[buf][sb + blk][n][32 * kk + 8 * r]);
         f4 st[2][2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -1071,14 +1095,8 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk)
                     st[rt][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kx[blk][kk], qv[rt][kk], st[rt][blk], 0, 0, 0);
-        // the value rows (tokens 4c + r of both blocks, dims 8n .. +7)
-        h8 vr[2][4];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) vr[blk][c] = *reinterpret_cast<const h8 *>(&kv_lds[buf][1][sb + blk][4 * c + r][8 * n]);
         // masks, only where the pair reaches past the first row's position or
-        // the last key this wave sees (keys there may be stale: zero their values)
+        // the last key this wave sees
         const int k_last = b * kBlockSize + 2 * kBlockSize - 1;
         const bool tail = k_last >= w_end;
         if (k_last > pos0 + tok0 || tail) {
@@ -1086,11 +1104,10 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const int kp = (b + blk) * kBlockSize + 4 * c + r;
+                    const int kp = (b + blk) * kBlockSize + 4 * r + c;
                     const bool vis = kp < w_end && kp <= qp;
 #pragma unroll
                     for (int rt = 0; rt < 2; ++rt) st[rt][blk][c] = vis ? st[rt][blk][c] : -INFINITY;
-                    if (tail && kp >= w_end) vr[blk][c] = h8(0);
                 }
         }
         h8 pw[2];
@@ -1134,11 +1151,14 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
                     l_run[rt] = __builtin_amdgcn_fdot2(pp, ones, l_run[rt], false);
                 }
         }
-        // P V: dim j of the lane's eight value rows
+        // P V over dims 16j .. 16j+15: lane (r, n) gets tokens 4r .. 4r+3 of
+        // each block at dim 16j + n straight from the transpose reads
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const h8 bv = {vr[0][0][j], vr[0][1][j], vr[0][2][j], vr[0][3][j],
-                           vr[1][0][j], vr[1][1][j], vr[1][2][j], vr[1][3][j]};
+            h4 t[2];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) t[blk] = lds_read_tr16(&v_lds[buf][sb + blk][tr_row][16 * j + tr_col]);
+            const h8 bv = {t[0][0], t[0][1], t[0][2], t[0][3], t[1][0], t[1][1], t[1][2], t[1][3]};
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
                 oacc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[rt], bv, oacc[rt][j], 0, 0, 0);
@@ -1190,20 +1210,16 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
             if (direct) {
                 const size_t qrow = static_cast<size_t>(min(row0 + tok, a.num_q_rows - 1));
                 const float inv = (FP8 ? a.v_scale : 1.0f) / l;  // FP8: V's scale
-                h8 o;
+                _Float16 *orow = reinterpret_cast<_Float16 *>(a.out + (qrow * a.num_q_heads + head) * kHeadDim);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) o[j] = static_cast<_Float16>(oacc[rt][j][c] * inv);
-                *reinterpret_cast<h8 *>(a.out + (qrow * a.num_q_heads + head) * kHeadDim + 8 * n) = o;
+                for (int j = 0; j < 8; ++j) orow[16 * j + n] = static_cast<_Float16>(oacc[rt][j][c] * inv);  // dim 16j + n
             } else {
                 const int64_t slot64 = static_cast<int64_t>(base_slot) + static_cast<int64_t>(tok) * np + piece;
                 const size_t slot = static_cast<size_t>(min<int64_t>(slot64, a.num_slots - 1));
                 const size_t rec = slot * a.num_q_heads + head;
-                float4 *dst = reinterpret_cast<float4 *>(a.o_part + rec * kHeadDim + 8 * n);
                 const float vs = FP8 ? a.v_scale : 1.0f;  // records hold values, as the decode pieces' do
-                dst[0] = make_float4(oacc[rt][0][c] * vs, oacc[rt][1][c] * vs, oacc[rt][2][c] * vs,
-                                     oacc[rt][3][c] * vs);
-                dst[1] = make_float4(oacc[rt][4][c] * vs, oacc[rt][5][c] * vs, oacc[rt][6][c] * vs,
-                                     oacc[rt][7][c] * vs);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a.o_part[rec * kHeadDim + 16 * j + n] = oacc[rt][j][c] * vs;
                 if (n == 0) *reinterpret_cast<float2 *>(a.ml_part + rec * 2) = make_float2(m, l);
             }
         }
