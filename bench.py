@@ -350,6 +350,35 @@ def main():
         del buf
         log(f"HBM read probe: {probe:.0f} GB/s")
 
+    # ---- gather probe: whole K tiles of the pool (the kernel's tile size) in a
+    # random order, 4 GiB per launch: the rate this access pattern allows ----
+    gather = None
+    if not args.no_probe:
+        plib.pa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        plib.pa_probe_gather.restype = ctypes.c_int32
+        tile = 16 * D * eb
+        src_bytes = pool.k.numel() * pool.k.element_size()
+        groups = plib.pa_probe_read_groups()
+        n_tiles = min(src_bytes // tile, (4 << 30) // tile) // groups * groups
+        if n_tiles > 0:
+            ids = np.random.default_rng(7).choice(src_bytes // tile, size=n_tiles, replace=False).astype(np.int32)
+            ids_dev = torch.from_numpy(ids).to(dev)
+            go = lambda: plib.pa_probe_gather(pool.k.data_ptr(), src_bytes, tile, ids_dev.data_ptr(), n_tiles,
+                                              sink.data_ptr(), sptr)
+            for _ in range(2):
+                assert go() == 0
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5
+            a.record(stream)
+            for _ in range(reps):
+                go()
+            b.record(stream)
+            torch.cuda.synchronize()
+            gather = n_tiles * tile * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+            del ids_dev
+            log(f"HBM gather probe ({tile} B tiles, random order): {gather:.0f} GB/s")
+
     # ---- oracle on the host: baseline timing and a parity sample ----
     cpu = None
     parity = None
@@ -444,6 +473,8 @@ def main():
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
         "hbm_read_probe_GBps": round(probe, 1) if probe else None,
         "pct_of_probe": round(100 * kv_gbps / probe, 2) if probe else None,
+        "hbm_gather_probe_GBps": round(gather, 1) if gather else None,
+        "kernel_pct_of_gather_probe": round(100 * achieved / gather, 2) if gather else None,
         "cpu_baseline": cpu,
         "parity_sample": parity,
     }

@@ -215,8 +215,13 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
                 total_blocks += static_cast<int64_t>(prefix_len[gi] / kBlockSize) *
                                 ((members[gi].size() + pa::kMaxMembers - 1) / pa::kMaxMembers);
         const int64_t items_target = std::max<int64_t>(1, kTargetWorkGroups / pool->desc.num_kv_heads);
-        const int64_t piece = std::min<int64_t>(kMaxSplitTokens / kBlockSize,
-                                                std::max<int64_t>(pa::kWaves, (total_blocks + items_target - 1) / items_target));
+        int64_t piece = std::min<int64_t>(kMaxSplitTokens / kBlockSize,
+                                          std::max<int64_t>(pa::kWaves, (total_blocks + items_target - 1) / items_target));
+        if (const char *env = std::getenv("PA_DECODE_PIECE_BLOCKS")) {  // tuning override
+            char *end = nullptr;
+            const long v = std::strtol(env, &end, 10);
+            if (end != env && v >= pa::kWaves && v <= kMaxSplitTokens / kBlockSize) piece = v;
+        }
         auto cut = [](int64_t nb, int64_t maxp) { return nb == 0 ? int64_t{0} : (nb + maxp - 1) / maxp; };
 
         // records: each member owns a contiguous run (prefix pieces, then its

@@ -3,6 +3,8 @@
 //   pa_probe_read  streams a buffer with 16-byte loads and folds it into one
 //                  word per work-group; gives the HBM read bandwidth this GPU
 //                  reaches, a second denominator next to the published peak
+//   pa_probe_gather reads whole tiles of a buffer in a given (random) order:
+//                  the bandwidth of the access pattern a paged cache imposes
 //   pa_probe_copy  plain 16-byte copy of a known size; its FETCH_SIZE and
 //                  WRITE_SIZE counter readings calibrate those counters
 
@@ -15,7 +17,9 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;       // 16-byte loads in flight per thread (streaming read)
+constexpr int kProbeGroups = 4096;
+constexpr int kGatherUnroll = 4;
 
 __global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4 *src, size_t n16, uint32_t *sink) {
     const size_t stride = static_cast<size_t>(gridDim.x) * kThreads * kUnroll;
@@ -39,6 +43,28 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4 *src, 
         __syncthreads();
     }
     if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
+// Work-group w reads tiles idx[w * per .. w * per + per - 1] (tile ids
+// clamped to the buffer), kThreads x kGatherUnroll 16-byte loads per step.
+__global__ __launch_bounds__(kThreads) void probe_gather_kernel(const u32x4 *src, int32_t max_tile, int32_t tile16,
+                                                                const int32_t *idx, int32_t per, uint32_t *sink) {
+    const int32_t *my = idx + static_cast<size_t>(blockIdx.x) * per;
+    const size_t total16 = static_cast<size_t>(per) * tile16;
+    uint32_t acc = 0;
+    for (size_t base = threadIdx.x; base < total16; base += kThreads * kGatherUnroll) {
+        u32x4 v[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const size_t e = base + static_cast<size_t>(u) * kThreads;
+            const bool in = e < total16;
+            const int32_t t = in ? min(max(my[e / tile16], 0), max_tile) : 0;
+            v[u] = in ? __builtin_nontemporal_load(src + static_cast<size_t>(t) * tile16 + e % tile16) : u32x4(0);
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;  // keeps the loads; practically never written
 }
 
 __global__ __launch_bounds__(kThreads) void probe_copy_kernel(uint4 *dst, const uint4 *src, size_t n16) {
@@ -132,8 +158,26 @@ int32_t pa_probe_mfma_16x16x16(const void *a, const void *b, void *d, hipStream_
 }
 
 
-// Work-groups used by pa_probe_read; `sink` must hold this many uint32.
-int32_t pa_probe_read_groups(void) { return 256 * 8; }
+// Work-groups used by pa_probe_read and pa_probe_gather; `sink` must hold
+// this many uint32.
+int32_t pa_probe_read_groups(void) { return kProbeGroups; }
+
+// Reads n_tiles tiles of tile_bytes each from src (src_bytes long), tile i at
+// src + idx[i] * tile_bytes (idx: device int32 [n_tiles]; ids outside the
+// buffer are clamped).  tile_bytes: a multiple of 16; n_tiles: a multiple of
+// pa_probe_read_groups().  Returns a hipError_t.
+int32_t pa_probe_gather(const void *src, size_t src_bytes, int32_t tile_bytes, const int32_t *idx, int32_t n_tiles,
+                        void *sink, hipStream_t stream) {
+    if (!src || !idx || !sink || tile_bytes <= 0 || tile_bytes % 16 != 0 || n_tiles <= 0 ||
+        n_tiles % kProbeGroups != 0 || src_bytes < static_cast<size_t>(tile_bytes))
+        return static_cast<int32_t>(hipErrorInvalidValue);
+    const size_t tiles = src_bytes / static_cast<size_t>(tile_bytes);
+    const int32_t max_tile = static_cast<int32_t>(tiles > 0x7fffffffu ? 0x7fffffff : tiles - 1);
+    hipLaunchKernelGGL(probe_gather_kernel, dim3(kProbeGroups), dim3(kThreads), 0, stream,
+                       static_cast<const u32x4 *>(src), max_tile, tile_bytes / 16, idx, n_tiles / kProbeGroups,
+                       static_cast<uint32_t *>(sink));
+    return static_cast<int32_t>(hipGetLastError());
+}
 
 // bytes must be a multiple of 16; src 16-byte aligned.  Returns a hipError_t.
 int32_t pa_probe_read(const void *src, size_t bytes, void *sink, hipStream_t stream) {
