@@ -57,3 +57,62 @@ def test_graph_replays_equal_the_eager_step():
     torch.cuda.synchronize()
     assert torch.equal(again.view(torch.int16), eager[2].view(torch.int16))
     st.close()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_graph_replays_of_a_mixed_step_equal_the_eager_step(fp8):
+    """A chunked-prefill / mixed step over two layers (decode rows, whole and
+    cut prompt tiles, merges) captured once and replayed: every replay gives
+    the eager bits, and the eager step matches the oracle."""
+    import oracle
+    import paged_kv_cache_64_amd as pa
+
+    q_lens = [1, 40, 1, 300, 7]
+    hist = [700, 0, 4095, 3000, 20]
+    lens = [h + n for h, n in zip(hist, q_lens)]
+    w = workloads.custom(lens, seed=52 + fp8, layers=2)
+    scales = (0.1, 0.0173)
+    st = Staged(w, layers=(0, 1), dtype=pa.PA_FP8_E4M3 if fp8 else pa.PA_F16, kv_scales=scales)
+    starts = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    rows = int(starts[-1])
+    qs = [torch.from_numpy(w.q_rows(rows, L)).cuda() for L in range(2)]
+    plan = st.pool.prefill_plan(starts, lens)
+    assert plan.info.num_merges > 0 and plan.info.num_items > 0 and plan.info.num_prefill_items > 0
+    pinned = torch.from_numpy(plan.host.copy()).pin_memory()
+    outs = [torch.zeros_like(q) for q in qs]
+
+    def step():
+        plan.dev.copy_(pinned, non_blocking=True)
+        for L in range(2):
+            st.pool.prefill_run(L, plan, qs[L], outs[L], st.dev[L][1], w.scale)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for L in range(2):
+            assert torch.equal(outs[L].view(torch.int16), eager[L].view(torch.int16)), (rep, L)
+    # layer 1 of the eager step against the oracle
+    q, tables, ids, k, v = st.host[1]
+    kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, w.ctx_lens, 16)
+    qh = w.q_rows(rows, 1)
+    if fp8:
+        ref = oracle.prefill_e4m3(qh, oracle.quantize_e4m3(kc, scales[0]), oracle.quantize_e4m3(vc, scales[1]),
+                                  t2, starts, lens, w.scale, 16, *scales)
+    else:
+        ref = oracle.prefill(qh, kc, vc, t2, starts, lens, w.scale, 16)
+    compare(f"graph mixed fp8={fp8}", eager[1], ref)
+    st.close()
