@@ -17,8 +17,10 @@
  *     out[s][h] = sum_t softmax(z)_t * V[slot(s,t)][g]
  * with the max-shifted softmax ("Reading Inference Engine Codebases",
  * Example 6) and scale usually 1/sqrt(head_dim) ("Reading Inference Engine
- * Codebases", Example 2).  Values are F16; accumulation is fp32; the output
- * is rounded once to F16 (round to nearest even).  ctx == 0 gives zeros.
+ * Codebases", Example 2).  Queries are F16; keys and values are F16, or FP8
+ * E4M3 codes times a per-layer scale (pa_pool_set_scales); accumulation is
+ * fp32; the output is rounded once to F16 (round to nearest even).  ctx == 0
+ * gives zeros.
  *
  * Memory.  Every pointer argument named *_dev is a device pointer owned by
  * the caller (for example a torch tensor's data_ptr()).  The library never
@@ -72,8 +74,9 @@ typedef enum {
 /* Geometry of one KV pool.  The pool holds num_layers independent layers of
  * num_blocks physical blocks each; one block holds block_size tokens of every
  * KV head.  Page size per block per layer is block_size x num_kv_heads x
- * (2 x head_dim) x 2 bytes ("vLLM Architecture and Installation", Example 6):
- * 65,536 B for block_size 16, 8 KV heads and head_dim 128. */
+ * (2 x head_dim) x bytes per value ("vLLM Architecture and Installation",
+ * Example 6): 65,536 B for block_size 16, 8 KV heads, head_dim 128 and F16
+ * values; half that for FP8. */
 typedef struct {
     int32_t num_layers;
     int32_t num_blocks;   /* per layer */
@@ -91,10 +94,11 @@ typedef struct pa_pool pa_pool;
  * size (2 for PA_F16, 1 for PA_FP8_E4M3: an FP8 cache halves the page,
  * "vLLM Architecture and Installation", Example 6).
  * Both buffers have this size; 256-byte alignment is required.  Device layout
- * of each buffer (row-major, F16):
+ * of each buffer (row-major; F16 values or FP8 codes):
  *     [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
  * so the block_size x head_dim tile of one (block, KV head) is contiguous
- * (4 KiB for the supported geometry).  Returns 0 for a null or invalid desc. */
+ * (4 KiB F16, 2 KiB FP8 for the supported geometry).  Returns 0 for a null
+ * or invalid desc. */
 size_t pa_pool_bytes(const pa_pool_desc *desc);
 
 /* Wraps two caller-allocated device buffers of pa_pool_bytes(desc) bytes each
@@ -123,7 +127,8 @@ pa_status pa_pool_destroy(pa_pool *pool);
 /* Scatters n_tokens new keys and values into the pool of one layer:
  * token i goes to slot slot_mapping_dev[i], i.e. block slot / block_size,
  * offset slot % block_size ("vLLM Architecture and Installation", Example 3).
- *   k_new_dev, v_new_dev: F16 [n_tokens][num_kv_heads][head_dim]
+ *   k_new_dev, v_new_dev: F16 [n_tokens][num_kv_heads][head_dim] (an FP8 pool
+ *                         stores their codes, see pa_pool_set_scales)
  *   slot_mapping_dev:     int32 [n_tokens]; a negative slot skips that token,
  *                         a slot >= num_blocks * block_size is skipped too.
  * n_tokens == 0 is a no-op.  Two tokens with the same slot race. */
@@ -290,7 +295,7 @@ pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info,
  * pa_prefill_plan builds the schedule on the host from query_start_host
  * (int32 [batch + 1], query_start_host[0] == 0, nondecreasing) and
  * seq_lens_host (int32 [batch]): one-token rows become decode pieces as in
- * pa_decode_plan; longer chunks are cut into tiles of 64 query tokens whose
+ * pa_decode_plan; longer chunks are cut into tiles of 32 query tokens whose
  * causal key ranges are cut into near-equal pieces for the matrix-core
  * prefill kernel; rows cut into several pieces are merged.  Sizing, the
  * two-call protocol and the device copy as pa_decode_plan. */
