@@ -41,8 +41,9 @@
  * pool or the tables; the numbers produced from such a value are unspecified.
  *
  * Geometry supported by this build: head_dim 128, block_size 16, F16 or FP8
- * (E4M3) keys and values, F16 queries and outputs, and num_q_heads = 4 *
- * num_kv_heads.  Other values return PA_ERR_UNSUPPORTED.  Every schedule
+ * (E4M3) keys and values, F16 queries and outputs, num_q_heads = 4 *
+ * num_kv_heads, and contexts (max_context_len, host lengths) of at most 2^30
+ * tokens.  Other values return PA_ERR_UNSUPPORTED.  Every schedule
  * (decode, shared-prefix cascade, chunked prefill / mixed) runs on both pool
  * types.
  */

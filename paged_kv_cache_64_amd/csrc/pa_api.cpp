@@ -105,6 +105,7 @@ pa_status check_decode_shape(const pa_pool *pool, int32_t batch, int32_t num_q_h
     if (static_cast<int64_t>(max_ctx) > static_cast<int64_t>(max_blocks) * pool->desc.block_size)
         return PA_ERR_INVALID_ARG;
     if (num_q_heads != kGroup * pool->desc.num_kv_heads) return PA_ERR_UNSUPPORTED;
+    if (max_ctx > pa::kMaxContextTokens) return PA_ERR_UNSUPPORTED;
     if (batch > 65535 || pool->desc.num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
@@ -198,6 +199,7 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
         int32_t max_ctx = 0;
         for (int32_t s = 0; s < batch; ++s) {
             if (lens[s] < 0) return PA_ERR_INVALID_ARG;
+            if (lens[s] > pa::kMaxContextTokens) return PA_ERR_UNSUPPORTED;
             max_ctx = std::max(max_ctx, lens[s]);
             if (group_of) {
                 const int32_t gi = group_of[s];
@@ -208,7 +210,7 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
                     members[gi].push_back(s);
                 }
             }
-            total_blocks += (lens[s] - plen[s] + kBlockSize - 1) / kBlockSize;
+            total_blocks += (static_cast<int64_t>(lens[s]) - plen[s] + kBlockSize - 1) / kBlockSize;
         }
         for (int32_t gi = 0; gi < num_groups; ++gi)
             if (!members[gi].empty())
@@ -227,30 +229,31 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
         // records: each member owns a contiguous run (prefix pieces, then its
         // suffix pieces); a sequence without prefix owns one only when cut
         std::vector<int32_t> first(batch, -1), n_prefix(batch, 0);
-        int32_t slots = 0;
+        int64_t slots = 0;  // records per query head; kept below 2^31
         int32_t shared_newest = 0;
         std::vector<int32_t> merges;
         for (int32_t s = 0; s < batch; ++s) {
-            const int64_t suffix_blocks = (lens[s] - plen[s] + kBlockSize - 1) / kBlockSize;
+            const int64_t suffix_blocks = (static_cast<int64_t>(lens[s]) - plen[s] + kBlockSize - 1) / kBlockSize;
             const int64_t np_suffix = cut(suffix_blocks, piece);
+            int64_t n = 0;
             if (plen[s] > 0) {
                 n_prefix[s] = static_cast<int32_t>(cut(plen[s] / kBlockSize, pa::kMaxPrefixPieceBlocks));
-                const int64_t n = n_prefix[s] + np_suffix;
-                first[s] = slots;
-                slots += static_cast<int32_t>(n);
-                merges.insert(merges.end(), {s, first[s], static_cast<int32_t>(n), s});
+                n = n_prefix[s] + np_suffix;
                 if (lens[s] == plen[s]) ++shared_newest;
             } else if (np_suffix > 1) {
-                first[s] = slots;
-                slots += static_cast<int32_t>(np_suffix);
-                merges.insert(merges.end(), {s, first[s], static_cast<int32_t>(np_suffix), s});
+                n = np_suffix;
             }
+            if (n == 0) continue;
+            if (slots + n > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+            first[s] = static_cast<int32_t>(slots);
+            slots += n;
+            merges.insert(merges.end(), {s, first[s], static_cast<int32_t>(n), s});
         }
         // ordinary pieces (whole contexts, or the suffixes of members)
         std::vector<PlanItem> items;
         for (int32_t s = 0; s < batch; ++s) {
             const int32_t ctx = lens[s];
-            const int64_t nb = (ctx - plen[s] + kBlockSize - 1) / kBlockSize;
+            const int64_t nb = (static_cast<int64_t>(ctx) - plen[s] + kBlockSize - 1) / kBlockSize;
             const int64_t np = cut(nb, piece);
             if (np == 0) {
                 if (plen[s] == 0) items.push_back({s, 0, 0, 0, -1});  // empty context: zero output
@@ -311,7 +314,7 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
         inf.max_context_len = max_ctx;
         inf.num_items = static_cast<int32_t>(n_items);
         inf.num_merges = static_cast<int32_t>(n_merges);
-        inf.num_slots = slots;
+        inf.num_slots = static_cast<int32_t>(slots);
         inf.max_piece_tokens = longest;
         inf.num_prefix_items = static_cast<int32_t>(n_pitems);
         inf.num_members = static_cast<int32_t>(n_members);
@@ -327,7 +330,7 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
         if (plan_host_bytes < inf.plan_bytes) return PA_ERR_WORKSPACE;
         int32_t *p = static_cast<int32_t *>(plan_host);
         const int32_t header[pa::kPlanHeader] = {pa::kPlanMagic, batch, num_q_heads, inf.num_items,
-                                                 inf.num_merges, slots, max_ctx, inf.num_prefix_items};
+                                                 inf.num_merges, inf.num_slots, max_ctx, inf.num_prefix_items};
         p = std::copy(header, header + pa::kPlanHeader, p);
         for (const PlanItem &it : items) {
             const int32_t rec[pa::kItemInts] = {it.s, it.t_begin, it.t_end, it.ctx, it.slot, it.s, 0, 0};
@@ -366,8 +369,9 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
         for (int32_t s = 0; s < batch; ++s) {
             const int64_t q_len = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
             if (q_len < 0 || lens[s] < q_len) return PA_ERR_INVALID_ARG;
+            if (lens[s] > pa::kMaxContextTokens) return PA_ERR_UNSUPPORTED;
             max_ctx = std::max(max_ctx, lens[s]);
-            if (q_len == 1) dec_blocks += (lens[s] + kBlockSize - 1) / kBlockSize;
+            if (q_len == 1) dec_blocks += (static_cast<int64_t>(lens[s]) + kBlockSize - 1) / kBlockSize;
             for (int64_t j0 = 0; j0 < q_len; j0 += pa::kPrefillTile) {
                 if (q_len == 1) break;
                 const int64_t kend = lens[s] - q_len + std::min<int64_t>(q_len, j0 + pa::kPrefillTile);
@@ -389,13 +393,14 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
         for (int32_t s = 0; s < batch; ++s) {
             if (query_start[s + 1] - query_start[s] != 1) continue;
             const int32_t ctx = lens[s], row = query_start[s];
-            const int64_t nb = (ctx + kBlockSize - 1) / kBlockSize;
+            const int64_t nb = (static_cast<int64_t>(ctx) + kBlockSize - 1) / kBlockSize;
             const int64_t np = cut(nb, piece);
             if (np <= 1) {
                 items.push_back({s, 0, ctx, ctx, -1});
                 item_row.push_back(row);
                 continue;
             }
+            if (slots + np > 0x7fffffff) return PA_ERR_UNSUPPORTED;
             merges.insert(merges.end(), {s, static_cast<int32_t>(slots), static_cast<int32_t>(np), row});
             const int64_t base = nb / np, extra = nb % np;
             int64_t b0 = 0;
@@ -527,6 +532,7 @@ pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const
     if (max_blocks_per_seq < 0 ||
         static_cast<int64_t>(info->max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlockSize)
         return PA_ERR_INVALID_ARG;
+    if (info->max_context_len > pa::kMaxContextTokens) return PA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
     size_t o_bytes = 0;
     const size_t need = planned_workspace(info->num_slots, info->num_q_heads, &o_bytes);

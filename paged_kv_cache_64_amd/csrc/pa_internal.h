@@ -16,6 +16,7 @@ constexpr int kGroup = 4;         // query heads per KV head
 constexpr int kWaves = 4;         // waves per work-group of the split kernel
 constexpr int kSplitQuantum = kWaves * kBlockSize;  // split lengths are multiples of this
 constexpr int kMaxSplitTokens = kWaves * 64 * kBlockSize;  // a wave owns at most 64 blocks
+constexpr int kMaxContextTokens = 1 << 30;  // longest context: token and block arithmetic stays in int32
 
 // Device layout of one pool buffer (K or V), F16, row-major:
 //   [num_layers][num_blocks][num_kv_heads][kBlockSize][kHeadDim]

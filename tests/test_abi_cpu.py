@@ -130,6 +130,7 @@ def test_decode_validation(lib, pool):
     assert _decode(lib, pool, q=FAKE + 4) == pa.PA_ERR_INVALID_ARG          # misaligned
     assert _decode(lib, pool, scale=float("nan")) == pa.PA_ERR_INVALID_ARG
     assert _decode(lib, pool, batch=70000) == pa.PA_ERR_UNSUPPORTED
+    assert _decode(lib, pool, width=(1 << 26) + 1, max_ctx=(1 << 30) + 1) == pa.PA_ERR_UNSUPPORTED  # > 2^30 tokens
     need = pa.pa_decode_workspace_bytes(pool, 4, 32, 256)
     assert need > 0
     assert _decode(lib, pool, ws_bytes=need - 1) == pa.PA_ERR_WORKSPACE

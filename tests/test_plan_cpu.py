@@ -312,3 +312,25 @@ def test_decode_plans_carry_their_rows(pool):
     assert np.array_equal(items[:, 5], items[:, 0])
     assert np.array_equal(merges[:, 3], merges[:, 0]) and info.num_q_rows == 3
     assert info.num_prefill_items == 0
+
+
+def test_longest_context_plans_and_longer_ones_are_unsupported(pool):
+    """Contexts of up to 2^30 tokens are cut into 4096-token pieces that cover
+    them exactly, for decode and mixed plans; longer ones (up to the int32
+    limit) are rejected as unsupported."""
+    for too_long in ((1 << 30) + 1, (1 << 31) - 1):
+        with pytest.raises(pa.PaError) as e:
+            pa.pa_decode_plan(pool, [too_long, 5], 32)
+        assert e.value.status == pa.PA_ERR_UNSUPPORTED
+        with pytest.raises(pa.PaError) as e:
+            pa.pa_prefill_plan(pool, np.array([0, 1, 2], np.int32), np.array([too_long, 5], np.int32), 32)
+        assert e.value.status == pa.PA_ERR_UNSUPPORTED
+    big = (1 << 30) - 3
+    lens = [big, 5]
+    info, plan = pa.pa_decode_plan(pool, lens, 32)
+    items, merges = _check_cover(lens, info, plan)
+    assert info.num_merges == 1 and info.max_context_len == big
+    assert info.num_items == -(-big // 4096) + 1
+    starts = np.array([0, 1, 2], np.int32)
+    info2, plan2 = pa.pa_prefill_plan(pool, starts, np.array(lens, np.int32), 32)
+    assert info2.num_items == info.num_items and info2.num_merges == 1 and info2.max_context_len == big
