@@ -22,6 +22,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,9 +54,14 @@ def host_cpu_model():
     return None
 
 
-def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_code_hash():
+    """sha256 of the kernel source with comments and whitespace removed: it
+    changes with the code, not with its comments."""
+    with open(KERNEL_SOURCE) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()
 
 
 def read_counters(kv_dtype):
@@ -75,7 +81,7 @@ def read_counter_file(path):
             if ":" in line:
                 key, val = line.split(":", 1)
                 kv[key.strip()] = val.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_code_sha256") != kernel_code_hash():
         return None
     try:
         return int(float(kv["fetch_bytes_per_launch"])) + int(float(kv["write_bytes_per_launch"]))
