@@ -95,7 +95,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3,
-                    help="workload 1..7 (default 3); 6 and 7 are mixed steps (chunked prefill)")
+                    help="workload 1..8 (default 3); 6 and 7 are mixed steps (chunked prefill); "
+                         "8 is a launch-bound 32-layer batch-1 step (see --graph)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
@@ -298,9 +299,22 @@ def main():
     log(f"timed {args.steps} steps: mean {ms_per_step:.4f} ms, min {min(step_ms):.4f} ms, "
         f"wall {1e3 * wall / args.steps:.4f} ms/step; decode_partial mean {np.mean(part_us):.2f} us")
 
-    # optional: the same step captured once in a HIP graph and replayed
+    # optional: the same step captured once in a HIP graph and replayed, against
+    # the eager step run back to back the same way (no flush between steps, the
+    # host enqueueing as fast as it can: where launches dominate, this is the
+    # cost a graph removes)
     graph_ms = None
+    eager_b2b_ms = None
     if args.graph:
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a_ev.record(stream)
+        for _ in range(args.steps):
+            step()
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        eager_b2b_ms = a_ev.elapsed_time(b_ev) / args.steps
+        log(f"eager steps back to back: {eager_b2b_ms:.4f} ms/step")
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -477,6 +491,7 @@ def main():
                      "bytes_per_launch": launch_bytes, "kv_bytes_basis": basis,
                      "mean_launch_us": round(part_mean_s * 1e6, 3)},
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
+        "eager_back_to_back_ms_per_step": round(eager_b2b_ms, 5) if eager_b2b_ms else None,
         "hbm_read_probe_GBps": round(probe, 1) if probe else None,
         "pct_of_probe": round(100 * kv_gbps / probe, 2) if probe else None,
         "hbm_gather_probe_GBps": round(gather, 1) if gather else None,

@@ -75,14 +75,20 @@ def test_ragged_batch_is_cut_into_near_equal_pieces(pool):
     assert info.workspace_bytes >= info.num_slots * 32 * 130 * 4
 
 
-def test_small_batches_get_small_pieces(pool):
+def test_small_batches_get_pieces_of_at_least_16_blocks(pool):
     lens = [256]
     info, plan = pa.pa_decode_plan(pool, lens, 32)
     _check_cover(lens, info, plan)
-    assert info.num_items == 4 and info.num_merges == 1      # 4 pieces of 64 tokens
+    assert info.num_items == 1 and info.num_merges == 0      # one piece, no merge
+    lens = [2048]
+    info, plan = pa.pa_decode_plan(pool, lens, 32)
+    items, _ = _check_cover(lens, info, plan)
+    assert info.num_items == 8 and info.num_merges == 1      # 8 pieces of 16 blocks
+    assert np.all(items[:, 2] - items[:, 1] == 256)
     lens = [1, 0, 17, 4097, 0]
     info, plan = pa.pa_decode_plan(pool, lens, 32)
-    _check_cover(lens, info, plan)
+    items, _ = _check_cover(lens, info, plan)
+    assert info.max_piece_tokens == 256
 
 
 def test_prefix_workload_plan(pool):

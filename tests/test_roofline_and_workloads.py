@@ -47,6 +47,10 @@ def test_configs_are_deterministic_and_shaped():
     assert np.any(c4.ctx_lens % 16 != 0)
     c5 = workloads.config(5)
     assert c5.batch == 256 and c5.ctx_lens.min() >= 2048 and c5.ctx_lens.max() <= 2048 + 6144
+    c8 = workloads.config(8)
+    assert c8.layers == 32 and c8.batch == 1 and c8.max_context_len == 256 and c8.pool_blocks == 64
+    assert not np.array_equal(c8.tables(0), c8.tables(1))       # a fresh table per layer
+    assert all(len(np.unique(c8.tables(L)[0])) == 16 for L in (0, 31))
 
 
 def test_tables_are_distinct_non_contiguous_and_inside_the_pool():

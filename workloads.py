@@ -34,6 +34,9 @@ every token in the cache.
   7  8 layers; 32 decoding sequences at 4096 tokens plus the second
      16,352-token chunk of a 32,704-token prompt: 16,384 tokens, the default
      budget of GPUs with 160 GiB or more (MI355X has 288 GB)
+One launch-bound step (the case a captured whole-step graph is for):
+  8  32 layers, batch 1, context 256; per layer the table is the first 16
+     ids of a random permutation of a 64-block pool (workload 1 on every layer)
 """
 from __future__ import annotations
 
@@ -250,7 +253,7 @@ def _uniform_ints(seed, purpose, lo, hi, n):
 
 
 def config(k: int, seed: int | None = None) -> Workload:
-    """The workloads, numbered 1..7 as in the module docstring."""
+    """The workloads, numbered 1..8 as in the module docstring."""
     seed = k if seed is None else seed
     if k == 1:
         return Workload("paged decode, 1 layer, batch 1, ctx 256", seed, layers=1,
@@ -278,6 +281,11 @@ def config(k: int, seed: int | None = None) -> Workload:
         return Workload("paged decode, 1 layer, 256 sequences, 16 shared 2048-token prefixes",
                         seed, layers=1, ctx_lens=lens, pool_blocks=2 * need, max_blocks=512,
                         prefix_groups=(groups, gsize, pblocks))
+    if k == 8:
+        return Workload("paged decode step, 32 layers, batch 1, ctx 256 (launch-bound)", seed, layers=32,
+                        ctx_lens=np.array([256], np.int32), pool_blocks=64, max_blocks=16,
+                        fresh_tables_per_layer=True,
+                        description="per layer: first 16 ids of a random permutation of 64 blocks")
     if k in (6, 7):
         chunk, hist, layers = (2016, 2016, 32) if k == 6 else (16352, 16352, 8)
         lens = np.array([hist + chunk] + [4096] * 32, np.int32)
