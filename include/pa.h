@@ -139,7 +139,7 @@ pa_status pa_write_kv(pa_pool *pool, int32_t layer, const void *k_new_dev, const
 /* Length in tokens of one context split of pa_decode for this launch shape
  * (a multiple of block_size; a sequence of ctx tokens is handled by
  * ceil(ctx / split) work-groups per KV head).  Returns 0 on invalid input.
- * Splits never exceed 4096 tokens.  The environment variable
+ * Splits are 256 to 4096 tokens long.  The environment variable
  * PA_SPLIT_TOKENS, when set to a multiple of 64 in [64, 4096], overrides the
  * choice (tuning only). */
 int32_t pa_decode_split_tokens(const pa_pool *pool, int32_t batch, int32_t num_q_heads,

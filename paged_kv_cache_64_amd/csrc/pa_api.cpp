@@ -80,7 +80,8 @@ int32_t plan_split(int32_t batch, int32_t num_kv_heads, int32_t max_ctx) {
     const int64_t pairs = static_cast<int64_t>(batch) * num_kv_heads;
     const int64_t splits = std::max<int64_t>(1, (kTargetWorkGroups + pairs - 1) / pairs);
     const int64_t per = (max_ctx + splits - 1) / splits;
-    const int64_t tokens = std::max<int64_t>(kSplitQuantum, round_up(per, kSplitQuantum));
+    // at least 4 blocks per wave, as for planned pieces (kMinPieceBlocks)
+    const int64_t tokens = std::max<int64_t>(kMinPieceBlocks * kBlockSize, round_up(per, kSplitQuantum));
     return static_cast<int32_t>(std::min<int64_t>(tokens, kMaxSplitTokens));
 }
 

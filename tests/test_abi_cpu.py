@@ -131,12 +131,14 @@ def test_decode_validation(lib, pool):
     assert _decode(lib, pool, scale=float("nan")) == pa.PA_ERR_INVALID_ARG
     assert _decode(lib, pool, batch=70000) == pa.PA_ERR_UNSUPPORTED
     assert _decode(lib, pool, width=(1 << 26) + 1, max_ctx=(1 << 30) + 1) == pa.PA_ERR_UNSUPPORTED  # > 2^30 tokens
-    need = pa.pa_decode_workspace_bytes(pool, 4, 32, 256)
+    assert pa.pa_decode_workspace_bytes(pool, 4, 32, 256) == 0               # one split: no workspace
+    need = pa.pa_decode_workspace_bytes(pool, 4, 32, 4096)
     assert need > 0
-    assert _decode(lib, pool, ws_bytes=need - 1) == pa.PA_ERR_WORKSPACE
-    assert _decode(lib, pool, ws=None) == pa.PA_ERR_WORKSPACE
-    assert _decode(lib, pool, ws=FAKE + 16) == pa.PA_ERR_INVALID_ARG        # workspace alignment
-    assert lib.pa_decode_merge(pool, FAKE, FAKE, 4, 32, 256, FAKE, need - 1, None) == pa.PA_ERR_WORKSPACE
+    split = dict(width=256, max_ctx=4096)
+    assert _decode(lib, pool, ws_bytes=need - 1, **split) == pa.PA_ERR_WORKSPACE
+    assert _decode(lib, pool, ws=None, **split) == pa.PA_ERR_WORKSPACE
+    assert _decode(lib, pool, ws=FAKE + 16, **split) == pa.PA_ERR_INVALID_ARG   # workspace alignment
+    assert lib.pa_decode_merge(pool, FAKE, FAKE, 4, 32, 4096, FAKE, need - 1, None) == pa.PA_ERR_WORKSPACE
     # the appending variant needs both new-token tensors, aligned
     assert lib.pa_append_decode(pool, 0, FAKE, None, FAKE, FAKE, FAKE, 16, FAKE, 4, 32, 256, 0.088,
                                 FAKE, 1 << 30, None) == pa.PA_ERR_INVALID_ARG
@@ -150,7 +152,7 @@ def test_split_plan_and_workspace(lib, pool, monkeypatch):
     monkeypatch.delenv("PA_SPLIT_TOKENS", raising=False)
     for batch, max_ctx in [(1, 256), (8, 4096), (32, 4096), (64, 8192), (256, 8192), (3, 1)]:
         s = pa.pa_decode_split_tokens(pool, batch, 32, max_ctx)
-        assert s % 64 == 0 and 64 <= s <= 4096
+        assert s % 64 == 0 and 256 <= s <= 4096      # at least 4 blocks per wave
         splits = -(-max_ctx // s)
         ws = pa.pa_decode_workspace_bytes(pool, batch, 32, max_ctx)
         if splits == 1:
@@ -158,6 +160,9 @@ def test_split_plan_and_workspace(lib, pool, monkeypatch):
         else:
             rows = batch * 32 * splits
             assert ws >= rows * (128 + 2) * 4
+    assert pa.pa_decode_split_tokens(pool, 1, 32, 256) == 256     # one split, no merge
+    assert pa.pa_decode_split_tokens(pool, 8, 32, 4096) == 1024
+    assert pa.pa_decode_split_tokens(pool, 32, 32, 4096) == 4096
     monkeypatch.setenv("PA_SPLIT_TOKENS", "128")
     assert pa.pa_decode_split_tokens(pool, 32, 32, 4096) == 128
     monkeypatch.setenv("PA_SPLIT_TOKENS", "100")     # not a multiple of 64: ignored
