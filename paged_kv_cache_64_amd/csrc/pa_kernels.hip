@@ -30,6 +30,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "pa_internal.h"
 
@@ -1035,14 +1036,18 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     constexpr int kLoads = FP8 ? 2 : 4;            // 16-byte loads per lane and tile
     const int cp_tensor = w >> 1, cp_blk0 = (w & 1) * kCopyBlocks;
     const char *cp_layer = cp_tensor ? a.v_layer : a.k_layer;
-    h8 stg[kCopyBlocks][kLoads];   // F16 pools
-    u4 stg8[kCopyBlocks][kLoads];  // FP8 pools: raw codes, widened at commit
+    // two register sets: the loads of stage k go to set k % 2 two stages
+    // before that stage is consumed, so a stage's copy has a whole stage of
+    // compute to arrive before it is written to LDS
+    h8 stg[2][kCopyBlocks][kLoads];   // F16 pools
+    u4 stg8[2][kCopyBlocks][kLoads];  // FP8 pools: raw codes, widened at commit
     // Value rows at or past the piece's last key (t_hi) may hold anything
     // (slots past the sequence in its last block): the V resource ends at the
     // last row below t_hi, so those rows load as zeros and their zero weights
     // cannot meet a NaN.  Keys below t_hi are stored tokens, finite like every
     // key the rows see.
-    auto fetch = [&](int b) {  // stage starting at block b
+    auto fetch = [&](int b, auto set) {  // stage starting at block b, into register set `set`
+        constexpr int S = decltype(set)::value;
 #pragma unroll
         for (int x = 0; x < kCopyBlocks; ++x) {
             const int bb = b + cp_blk0 + x;
@@ -1057,25 +1062,26 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
                 if constexpr (FP8)
-                    stg8[x][i] = load_raw16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
+                    stg8[S][x][i] = load_raw16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
                 else
-                    stg[x][i] = load_tile16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
+                    stg[S][x][i] = load_tile16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
             }
         }
     };
-    auto commit = [&](int buf) {
+    auto commit = [&](int buf, auto set) {  // register set `set` into LDS buffer buf
+        constexpr int S = decltype(set)::value;
 #pragma unroll
         for (int x = 0; x < kCopyBlocks; ++x)
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
                 if constexpr (FP8) {
                     _Float16 *dst = kv_row(buf, cp_tensor, cp_blk0 + x, (lane >> 3) + 8 * i) + 16 * (lane & 7);
-                    const u4 c = stg8[x][i];
+                    const u4 c = stg8[S][x][i];
                     *reinterpret_cast<h8 *>(dst) = fp8_decode8_h(c.x, c.y);
                     *reinterpret_cast<h8 *>(dst + 8) = fp8_decode8_h(c.z, c.w);
                 } else {
                     *reinterpret_cast<h8 *>(kv_row(buf, cp_tensor, cp_blk0 + x, (lane >> 4) + 4 * i) + 8 * n) =
-                        stg[x][i];
+                        stg[S][x][i];
                 }
             }
     };
@@ -1177,20 +1183,31 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     // below its last query's position
     const int n_stages = (b_hi - b_lo + kStageBlocks - 1) / kStageBlocks;
     const int w_blocks = w_end > t_lo ? (w_end + kBlockSize - 1) / kBlockSize - b_lo : 0;  // blocks this wave needs
+    using Set0 = std::integral_constant<int, 0>;
+    using Set1 = std::integral_constant<int, 1>;
     if (n_stages > 0) {
-        fetch(b_lo);
-        commit(0);
+        fetch(b_lo, Set0{});
+        commit(0, Set0{});
+        if (n_stages > 1) fetch(b_lo + kStageBlocks, Set1{});
         __syncthreads();
     }
-    for (int st = 0; st < n_stages; ++st) {
-        const int buf = st & 1;
+    // stage st reads LDS buffer st % 2; meanwhile stage st+2 is loaded into
+    // register set st % 2 and, at the end, stage st+1 goes from register set
+    // (st+1) % 2 into LDS buffer (st+1) % 2, which stage st-1 read before the
+    // last barrier
+    auto stage = [&](int st, auto set) {
+        constexpr int S = decltype(set)::value;  // == st % 2
         const int b0 = b_lo + kStageBlocks * st;
-        if (st + 1 < n_stages) fetch(b0 + kStageBlocks);
+        if (st + 2 < n_stages) fetch(b0 + 2 * kStageBlocks, std::integral_constant<int, S>{});
 #pragma unroll
         for (int sb = 0; sb < kStageBlocks; sb += 2)
-            if (kStageBlocks * st + sb < w_blocks) compute(buf, sb, b0 + sb);
-        if (st + 1 < n_stages) commit(buf ^ 1);
+            if (kStageBlocks * st + sb < w_blocks) compute(S, sb, b0 + sb);
+        if (st + 1 < n_stages) commit(S ^ 1, std::integral_constant<int, S ^ 1>{});
         __syncthreads();
+    };
+    for (int st = 0; st < n_stages; st += 2) {
+        stage(st, Set0{});
+        if (st + 1 < n_stages) stage(st + 1, Set1{});
     }
     if (rows_w <= 0) return;
 
