@@ -106,6 +106,13 @@ constexpr int kRsrcDword3 = 0x00020000;
 #ifndef PA_DECODE_NBUF_FP8
 #define PA_DECODE_NBUF_FP8 3
 #endif
+// QK^T of decode pieces on the matrix cores (1) or by v_dot2 (0), per pool type.
+#ifndef PA_QKM_F16
+#define PA_QKM_F16 1
+#endif
+#ifndef PA_QKM_FP8
+#define PA_QKM_FP8 1
+#endif
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *tile, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), static_cast<short>(0), bytes, kRsrcDword3);
 }
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
 //   reaches the A layout through 128 B of LDS as F16.  K's scale is folded
 //   into the score scale and V's into the output.
 // ---------------------------------------------------------------------------
-template <int NBUF, bool FP8>
+template <int NBUF, bool FP8, bool QKM>
 __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_t bx, uint32_t by, uint32_t bz) {
     // Planned launches number work-groups item-major with the KV head fastest,
     // so the heads of one piece -- whose tiles share each 32 KiB block of
@@ -227,6 +234,11 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     const int lane = tid & 63;
     const int kt = lane >> 2, kq = lane & 3;    // score layout
     const int vt = lane >> 4, vj = lane & 15;   // value layout
+    // MFMA score layout (QKM): MFMA row m of a block is token 4(m%4) + m/4, so
+    // the result gives lane (r = l/16, n = l%16) the scores of tokens 4c + r,
+    // c < 4, for query head n%4 -- the k-slots of the P V operand below.
+    const int ktok = QKM ? 4 * (vj & 3) + (vj >> 2) : kt;  // this lane's K token
+    const int kdl = QKM ? vt : kq;                         // which 16 bytes of each 64 it loads
 
     __shared__ float p_lds[kWaves][64];
     __shared__ float alpha_lds[kWaves][4];
@@ -285,15 +297,23 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
 
     // Query of the 4 heads in the score layout: chunk i of 8 dims starts at
     // dim 32i + 8kq (F16 pools) or 64(i/2) + 16kq + 8(i%2) (FP8 pools).
-    auto chunk_dim = [&](int i) { return FP8 ? 64 * (i >> 1) + 16 * kq + 8 * (i & 1) : 32 * i + 8 * kq; };
+    // QKM: qm[j] is MFMA j's B operand, head l%4 at the dims chunk_dim(j).
+    auto chunk_dim = [&](int i) { return FP8 ? 64 * (i >> 1) + 16 * kdl + 8 * (i & 1) : 32 * i + 8 * kdl; };
     h8 qv[kGroup][4];
+    h8 qm[4];
     {
         const uint16_t *qbase = a.q + (static_cast<size_t>(qrow) * a.num_q_heads + head0) * kHeadDim;
-#pragma unroll
-        for (int h = 0; h < kGroup; ++h)
+        if constexpr (QKM) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                qv[h][i] = *reinterpret_cast<const h8 *>(qbase + h * kHeadDim + chunk_dim(i));
+                qm[i] = *reinterpret_cast<const h8 *>(qbase + (lane & 3) * kHeadDim + chunk_dim(i));
+        } else {
+#pragma unroll
+            for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    qv[h][i] = *reinterpret_cast<const h8 *>(qbase + h * kHeadDim + chunk_dim(i));
+        }
     }
 
     // The newest token (position ctx-1) when this call also appends it: the
@@ -310,8 +330,8 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
         if (FP8) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const h8 lo = *reinterpret_cast<const h8 *>(a.k_new + row + 64 * i + 16 * kq);
-                const h8 hi = *reinterpret_cast<const h8 *>(a.k_new + row + 64 * i + 16 * kq + 8);
+                const h8 lo = *reinterpret_cast<const h8 *>(a.k_new + row + 64 * i + 16 * kdl);
+                const h8 hi = *reinterpret_cast<const h8 *>(a.k_new + row + 64 * i + 16 * kdl + 8);
                 const u2 cl = fp8_encode8(lo, a.inv_k_scale), ch = fp8_encode8(hi, a.inv_k_scale);
                 kn[i] = u4{cl.x, cl.y, ch.x, ch.y};
             }
@@ -320,7 +340,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
             vn = u4{cv.x, cv.y, 0u, 0u};
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kn[i] = *reinterpret_cast<const u4 *>(a.k_new + row + 32 * i + 8 * kq);
+            for (int i = 0; i < 4; ++i) kn[i] = *reinterpret_cast<const u4 *>(a.k_new + row + 32 * i + 8 * kdl);
             vn = *reinterpret_cast<const u4 *>(a.v_new + row + 8 * vj);
         }
         // store the row: F16 rows are 16 chunks of 16 B per tensor, FP8 rows 8
@@ -358,7 +378,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     const char *k_layer = a.k_layer;
     const char *v_layer = a.v_layer;
     // per-lane byte offsets inside a tile
-    const uint32_t k_off = static_cast<uint32_t>(kt * kHeadDim * kElem + 16 * kq);  // + 64 i
+    const uint32_t k_off = static_cast<uint32_t>(ktok * kHeadDim * kElem + 16 * kdl);  // + 64 i
     const uint32_t v_off = static_cast<uint32_t>(lane * 8 * kElem);                 // + 512 kElem c
 
     float m_run = -INFINITY;  // running max of head kq (log2 units), same in all lanes of that head
@@ -408,11 +428,99 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     auto consume = [&](int buf, int b) {
         if (owns_new && b == new_blk) {
             // the pool may still hold the previous content of the newest slot
-            const bool k_mine = kt == new_off;
+            const bool k_mine = ktok == new_off;
 #pragma unroll
             for (int i = 0; i < 4; ++i) kb[buf][i] = k_mine ? kn[i] : kb[buf][i];
 #pragma unroll
             for (int c = 0; c < 4; ++c) vb[buf][c] = (4 * c + vt == new_off) ? vn : vb[buf][c];
+        }
+        if constexpr (QKM) {
+            // ---- S^T = K Q^T on the matrix cores: four v_mfma_f32_16x16x32_f16 ----
+            h8 ka[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (FP8) {
+                    const u4 r = kb[buf][i >> 1];
+                    ka[i] = (i & 1) ? fp8_decode8_h(r.z, r.w) : fp8_decode8_h(r.x, r.y);
+                } else {
+                    ka[i] = __builtin_bit_cast(h8, kb[buf][i]);
+                }
+            }
+            f4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[i], qm[i], st, 0, 0, 0);
+            // st[c]: score of token 4c + vt for head vj%4 (the same in the lanes of
+            // one head: columns n and n + 4k of Q^T are equal)
+            const int valid = t_end - b * kBlockSize;  // >= 1; pieces end on block edges or at ctx
+            const bool partial = valid < kBlockSize;
+            float x[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                x[c] = st[c] * a.scale_log2e;
+                if (partial && 4 * c + vt >= valid) x[c] = -INFINITY;
+            }
+            float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            if (__builtin_amdgcn_ballot_w64(bm > m_run + kTau) != 0) {
+                bm = fmaxf(bm, shfl_xor(bm, 16));
+                bm = fmaxf(bm, shfl_xor(bm, 32));
+                const float m_new = fmaxf(m_run, bm);
+                const float alpha = fast_exp2(m_run - m_new);
+                l_run *= alpha;
+                m_run = m_new;
+                // lanes 0..3 hold heads 0..3; result element c is head c
+                const f4 a4 = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0)),
+                               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1)),
+                               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2)),
+                               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3))};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) oacc[j] *= a4;
+            }
+            // weights as F16 (at most 2^kTau); the running sum adds the same
+            // rounded values that enter P V
+            const h2 p01 = {static_cast<_Float16>(fast_exp2(x[0] - m_run)), static_cast<_Float16>(fast_exp2(x[1] - m_run))};
+            const h2 p23 = {static_cast<_Float16>(fast_exp2(x[2] - m_run)), static_cast<_Float16>(fast_exp2(x[3] - m_run))};
+            const h2 one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+            l_run = __builtin_amdgcn_fdot2(p01, one2, __builtin_amdgcn_fdot2(p23, one2, l_run, false), false);
+            const h4 pa = {p01.x, p01.y, p23.x, p23.y};  // A: row vj (head vj%4), k-slot 4 vt + c = token 4c + vt
+            // ---- P V: eight v_mfma_f32_16x16x16_f16, B = V at dim 8 vj + j ----
+            if (FP8) {
+                uint32_t vw[4][2];  // raw codes of token 4c + vt; stale slots may hold anything
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const bool dead = partial && 4 * c + vt >= valid;
+                    vw[c][0] = dead ? 0u : vb[buf][c].x;
+                    vw[c][1] = dead ? 0u : vb[buf][c].y;
+                }
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp) {
+                    // bytes {c0 dim j, c1 dim j, c0 dim j+1, c1 dim j+1}, j = 2 jp
+                    const uint32_t sel = (jp & 1) ? 0x07030602u : 0x05010400u;
+                    const int wd = jp >> 1;
+                    const uint32_t t01 = __builtin_amdgcn_perm(vw[1][wd], vw[0][wd], sel);
+                    const uint32_t t23 = __builtin_amdgcn_perm(vw[3][wd], vw[2][wd], sel);
+                    const h2 a01 = fp8_pair_f16<false>(t01), b01 = fp8_pair_f16<true>(t01);
+                    const h2 a23 = fp8_pair_f16<false>(t23), b23 = fp8_pair_f16<true>(t23);
+                    const h4 v0 = {a01.x, a01.y, a23.x, a23.y};  // dim 2jp of tokens c = 0..3
+                    const h4 v1 = {b01.x, b01.y, b23.x, b23.y};  // dim 2jp + 1
+                    oacc[2 * jp] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v0, oacc[2 * jp], 0, 0, 0);
+                    oacc[2 * jp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v1, oacc[2 * jp + 1], 0, 0, 0);
+                }
+            } else {
+                u4 vv[4];  // token 4c + vt, dims 8 vj .. +7; stale slots may hold anything
+#pragma unroll
+                for (int c = 0; c < 4; ++c) vv[c] = (partial && 4 * c + vt >= valid) ? u4(0u) : vb[buf][c];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    // halves j of tokens c = 0, 1 and c = 2, 3
+                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                    const int wd = j >> 1;
+                    const uint32_t t01 = __builtin_amdgcn_perm(vv[1][wd], vv[0][wd], sel);
+                    const uint32_t t23 = __builtin_amdgcn_perm(vv[3][wd], vv[2][wd], sel);
+                    const h4 vj4 = __builtin_bit_cast(h4, u2{t01, t23});
+                    oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vj4, oacc[j], 0, 0, 0);
+                }
+            }
+            return;
         }
         // K chunks as F16
         h8 kc[4];
@@ -552,15 +660,17 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     }
 
     // ---- per-wave totals ----
-    l_run += dpp_row_ror4(l_run);
-    l_run += dpp_row_ror8(l_run);
+    if (!QKM) {  // QKM: lanes n, n + 4, n + 8, n + 12 of a row hold the same sum
+        l_run += dpp_row_ror4(l_run);
+        l_run += dpp_row_ror8(l_run);
+    }
     l_run += shfl_xor(l_run, 16);
     l_run += shfl_xor(l_run, 32);
     if (lane < 4) {
         m_lds[w][lane] = m_run;
         l_lds[w][lane] = l_run;
     }
-    if (FP8) {
+    if (FP8 || QKM) {
         // every lane group holds all four heads: group vt stores head vt (row 0)
         float ov[8];
 #pragma unroll
@@ -593,7 +703,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     for (int x = 0; x < kWaves; ++x) {
         const float wgt = mw[x] == -INFINITY ? 0.0f : fast_exp2(mw[x] - M);
         float s0 = 0.0f, s1 = 0.0f;
-        constexpr int kRows = FP8 ? 1 : 4;  // FP8: the MFMA already summed the token rows
+        constexpr int kRows = (FP8 || QKM) ? 1 : 4;  // MFMA P V already summed the token rows
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             const float2 v = *reinterpret_cast<const float2 *>(&o_lds[x][r][h][d0]);
@@ -623,7 +733,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
 
 template <int NBUF, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
-    decode_partial_body<NBUF, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    decode_partial_body<NBUF, FP8, FP8 ? PA_QKM_FP8 : PA_QKM_F16>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // ---------------------------------------------------------------------------
@@ -1265,7 +1375,8 @@ template <bool FP8>
 __global__ __launch_bounds__(256, 2) void mixed_kernel(DecodeArgs a) {
     const uint32_t nd = static_cast<uint32_t>(a.num_items) * static_cast<uint32_t>(a.num_kv_heads);
     if (blockIdx.x < nd)
-        decode_partial_body<FP8 ? PA_DECODE_NBUF_FP8 : PA_DECODE_NBUF, FP8>(a, blockIdx.x, 0, 0);
+        decode_partial_body<FP8 ? PA_DECODE_NBUF_FP8 : PA_DECODE_NBUF, FP8, FP8 ? PA_QKM_FP8 : PA_QKM_F16>(a, blockIdx.x, 0,
+                                                                                                        0);
     else
         prefill_body<FP8>(a, blockIdx.x - nd);
 }
