@@ -46,10 +46,6 @@ typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef short s4 __attribute__((ext_vector_type(4)));
-struct h2x4 {
-    h2 v[4];
-};
-__device__ __forceinline__ h2x4 pairs(h8 x) { return __builtin_bit_cast(h2x4, x); }
 
 // Online-softmax bookkeeping: the running max m is only raised when a score
 // exceeds it by more than kTau (log2 units), so most blocks skip the
@@ -58,20 +54,6 @@ __device__ __forceinline__ h2x4 pairs(h8 x) { return __builtin_bit_cast(h2x4, x)
 // the common factor exactly.
 constexpr float kTau = 8.0f;
 
-__device__ __forceinline__ float dpp_quad_xor1(float v) {
-    // quad_perm [1,0,3,2]
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_quad_xor2(float v) {
-    // quad_perm [2,3,0,1]
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_row_ror4(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_row_ror8(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-}
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
     const int lane = __lane_id();
     return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
@@ -105,13 +87,6 @@ constexpr int kRsrcDword3 = 0x00020000;
 // 2 % of each other.
 #ifndef PA_DECODE_NBUF_FP8
 #define PA_DECODE_NBUF_FP8 3
-#endif
-// QK^T of decode pieces on the matrix cores (1) or by v_dot2 (0), per pool type.
-#ifndef PA_QKM_F16
-#define PA_QKM_F16 1
-#endif
-#ifndef PA_QKM_FP8
-#define PA_QKM_FP8 1
 #endif
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *tile, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), static_cast<short>(0), bytes, kRsrcDword3);
@@ -201,29 +176,37 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
 //
 // Each wave walks its own contiguous run of the split's blocks and keeps its
 // own running max, sum and output accumulator; the four waves are merged
-// through LDS at the end.  Per block (16 tokens x 128 dims, 4 KiB of K and
-// 4 KiB of V for one KV head):
+// through LDS at the end.  A block is 16 tokens x 128 dims of one KV head:
+// 4 KiB of K and 4 KiB of V (2 KiB each for FP8 codes).  With lane
+// l = 16r + n (r = l/16, n = l%16), per block:
 //
-//   K layout in registers: lane l holds token kt = l/4, dims
-//     {32i + 8(l%4) + e : i < 4, e < 8}  -- four 16-byte loads; each load
-//     instruction covers 64 contiguous bytes of each of 16 token rows.
-//   Scores: 4 heads x 32 dims per lane by v_dot2, then a 4-lane transpose-
-//     reduction leaves lane l with the score of head l%4 for token l/4.
-//   V layout in registers: load c, lane l holds token 4c + l/16, dims
-//     8(l%16) .. +7 -- each load instruction is 1 KiB contiguous.
-//   Weights go from the score lanes to the value lanes through 256 B of LDS.
-// FP8 pools (2 KiB tiles): lane l holds token l/4, dims
-//   {64i + 16(l%4) + e : i < 2, e < 16} (two 16-byte loads) and, for V, token
-//   4c + l/16, dims 8(l%16) .. +7 (four 8-byte loads, 512 B contiguous each).
-//   Keys are converted to F16 for v_dot2.  P V runs on the matrix cores: per
-//   block, eight v_mfma_f32_16x16x16_f16 with A = P (rows = the 4 heads, k =
-//   the 16 tokens, k-slot 4(l/16) + c standing for token 4c + l/16) and B = V
-//   (n = l%16 standing for dim 8(l%16) + j in MFMA j), which is the V register
-//   layout once a byte permute gathers one dim of the lane's four tokens; P
-//   reaches the A layout through 128 B of LDS as F16.  K's scale is folded
-//   into the score scale and V's into the output.
+//   S^T = K Q^T   four v_mfma_f32_16x16x32_f16, 32 dims each:
+//                 A = K: lane l holds MFMA row n, which is token
+//                     4(n%4) + n/4 (the 4x4 transpose of the token index),
+//                     at 8 dims per MFMA -- F16 pools: dims 32i + 8r .. +7
+//                     of 16-byte load i < 4; FP8 pools: dims 64i + 16r .. +15
+//                     of 16-byte load i < 2, widened to F16 (exact).  Each
+//                     load instruction covers 64 contiguous bytes of each of
+//                     16 token rows.
+//                 B = Q^T: column n is query head n%4 of the group (columns
+//                     4..15 repeat heads 0..3) at the same dims.
+//                 D: lane l holds the scores of tokens 4c + r, c < 4, for
+//                    head n%4.
+//   softmax       on those four scores per lane (the lanes of one head hold
+//                 equal values), with the lazily raised max; the weights are
+//                 rounded to F16 (at most 2^kTau) and the running sum adds
+//                 the rounded values.
+//   O += P V      eight v_mfma_f32_16x16x16_f16, one per dim 8n + j, j < 8:
+//                 A = P: lane l's four weights at k-slots 4r + c = token
+//                     4c + r -- the D layout of S^T as it stands;
+//                 B = V: load c < 4 of lane l holds token 4c + r, dims
+//                     8n .. 8n+7 (each F16 load instruction is 1 KiB
+//                     contiguous, each FP8 one 512 B); byte permutes gather
+//                     dim 8n + j of the lane's four tokens;
+//                 D: result element c of lane l is head c at dim 8n + j.
+//   K's FP8 scale is folded into the score scale and V's into the output.
 // ---------------------------------------------------------------------------
-template <int NBUF, bool FP8, bool QKM>
+template <int NBUF, bool FP8>
 __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_t bx, uint32_t by, uint32_t bz) {
     // Planned launches number work-groups item-major with the KV head fastest,
     // so the heads of one piece -- whose tiles share each 32 KiB block of
@@ -232,19 +215,12 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     const int lane = tid & 63;
-    const int kt = lane >> 2, kq = lane & 3;    // score layout
-    const int vt = lane >> 4, vj = lane & 15;   // value layout
-    // MFMA score layout (QKM): MFMA row m of a block is token 4(m%4) + m/4, so
-    // the result gives lane (r = l/16, n = l%16) the scores of tokens 4c + r,
-    // c < 4, for query head n%4 -- the k-slots of the P V operand below.
-    const int ktok = QKM ? 4 * (vj & 3) + (vj >> 2) : kt;  // this lane's K token
-    const int kdl = QKM ? vt : kq;                         // which 16 bytes of each 64 it loads
+    const int r = lane >> 4, n = lane & 15;
+    const int ktok = 4 * (n & 3) + (n >> 2);  // the token of this lane's MFMA row of K
 
-    __shared__ float p_lds[kWaves][64];
-    __shared__ float alpha_lds[kWaves][4];
     __shared__ float m_lds[kWaves][4];
     __shared__ float l_lds[kWaves][4];
-    __shared__ float o_lds[kWaves][4][kGroup][kHeadDim];
+    __shared__ float o_lds[kWaves][kGroup][kHeadDim];
 
     // This work-group's piece of one sequence: tokens [t_begin, t_end) of
     // sequence s (context ctx), and where its result goes -- the final F16
@@ -295,107 +271,77 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     const int wb_begin = min(b_end, b_begin + w * per_wave);
     const int wb_end = min(b_end, wb_begin + per_wave);
 
-    // Query of the 4 heads in the score layout: chunk i of 8 dims starts at
-    // dim 32i + 8kq (F16 pools) or 64(i/2) + 16kq + 8(i%2) (FP8 pools).
-    // QKM: qm[j] is MFMA j's B operand, head l%4 at the dims chunk_dim(j).
-    auto chunk_dim = [&](int i) { return FP8 ? 64 * (i >> 1) + 16 * kdl + 8 * (i & 1) : 32 * i + 8 * kdl; };
-    h8 qv[kGroup][4];
+    // Block-table entries of this wave's blocks go to LDS up front (a wave
+    // never owns more than 64 blocks), so the loop reads them without a
+    // memory load that would have to wait behind the K/V loads in flight.
+    // Their load comes first: every K/V address depends on it.
+    const int32_t *table = a.tables + static_cast<size_t>(s) * a.max_blocks;
+    __shared__ int tbl_lds[kWaves][64];
+    if (lane < wb_end - wb_begin) tbl_lds[w][lane] = table[wb_begin + lane];
+    wave_lds_sync();
+
+    // Q^T operands: qm[i] holds query head l%4 at the 8 dims of MFMA i in this
+    // lane, chunk_dim(i) .. +7.
+    auto chunk_dim = [&](int i) { return FP8 ? 64 * (i >> 1) + 16 * r + 8 * (i & 1) : 32 * i + 8 * r; };
     h8 qm[4];
     {
-        const uint16_t *qbase = a.q + (static_cast<size_t>(qrow) * a.num_q_heads + head0) * kHeadDim;
-        if constexpr (QKM) {
+        const uint16_t *qh = a.q + (static_cast<size_t>(qrow) * a.num_q_heads + head0 + (lane & 3)) * kHeadDim;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                qm[i] = *reinterpret_cast<const h8 *>(qbase + (lane & 3) * kHeadDim + chunk_dim(i));
-        } else {
-#pragma unroll
-            for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    qv[h][i] = *reinterpret_cast<const h8 *>(qbase + h * kHeadDim + chunk_dim(i));
-        }
+        for (int i = 0; i < 4; ++i) qm[i] = *reinterpret_cast<const h8 *>(qh + chunk_dim(i));
     }
 
     // The newest token (position ctx-1) when this call also appends it: the
     // work-group whose split holds it stores its K/V row into the pool (for
     // later steps) and uses the new values straight from registers, so no
-    // load in this launch depends on that store.
+    // load in this launch depends on that store.  The values are loaded here
+    // (F16, in this lane's K and V layout), encoded where they are used, and
+    // the row is stored after the loop, so nothing waits for them before the
+    // first K/V loads are issued.
     const int new_tok = ctx - 1;
     const bool owns_new = a.k_new != nullptr && new_tok >= t_begin && new_tok < t_end;
     const int new_blk = new_tok / kBlockSize;
     const int new_off = new_tok % kBlockSize;
-    u4 kn[4], vn;  // the newest token's K (this lane's dims) and V, in the pool's encoding
+    constexpr int kChunks = FP8 ? 8 : 16;  // 16-byte chunks of a stored K or V row
+    const bool stores_new = owns_new && w == 0 && lane < 2 * kChunks;
+    u4 kn_raw[4], vn_raw;  // K: dims chunk_dim(i) .. +7; V: dims 8n .. 8n+7
+    u4 st_raw[2];          // the stored row's chunk as F16: 16 values (FP8 pools) or 8
+    uint32_t new_phys = 0;
     if (owns_new) {
         const size_t row = (static_cast<size_t>(s) * a.num_kv_heads + g) * kHeadDim;
-        if (FP8) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const h8 lo = *reinterpret_cast<const h8 *>(a.k_new + row + 64 * i + 16 * kdl);
-                const h8 hi = *reinterpret_cast<const h8 *>(a.k_new + row + 64 * i + 16 * kdl + 8);
-                const u2 cl = fp8_encode8(lo, a.inv_k_scale), ch = fp8_encode8(hi, a.inv_k_scale);
-                kn[i] = u4{cl.x, cl.y, ch.x, ch.y};
-            }
-            kn[2] = kn[3] = u4(0u);
-            const u2 cv = fp8_encode8(*reinterpret_cast<const h8 *>(a.v_new + row + 8 * vj), a.inv_v_scale);
-            vn = u4{cv.x, cv.y, 0u, 0u};
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) kn[i] = *reinterpret_cast<const u4 *>(a.k_new + row + 32 * i + 8 * kdl);
-            vn = *reinterpret_cast<const u4 *>(a.v_new + row + 8 * vj);
-        }
-        // store the row: F16 rows are 16 chunks of 16 B per tensor, FP8 rows 8
-        const int chunks = FP8 ? 8 : 16;
-        if (w == 0 && lane < 2 * chunks) {
-            uint32_t phys = static_cast<uint32_t>(a.tables[static_cast<size_t>(s) * a.max_blocks + new_blk]);
-            phys = phys > static_cast<uint32_t>(a.num_blocks - 1) ? static_cast<uint32_t>(a.num_blocks - 1) : phys;
-            const bool is_k = lane < chunks;
-            const int c = is_k ? lane : lane - chunks;
-            const size_t elems = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_elems() +
-                                 static_cast<size_t>(new_off) * kHeadDim;
-            char *pool = const_cast<char *>(is_k ? a.k_layer : a.v_layer);
-            const uint16_t *src = (is_k ? a.k_new : a.v_new) + row;
-            if (FP8) {
-                const float inv = is_k ? a.inv_k_scale : a.inv_v_scale;
-                const u2 lo = fp8_encode8(*reinterpret_cast<const h8 *>(src + 16 * c), inv);
-                const u2 hi = fp8_encode8(*reinterpret_cast<const h8 *>(src + 16 * c + 8), inv);
-                *reinterpret_cast<u4 *>(pool + elems + 16 * c) = u4{lo.x, lo.y, hi.x, hi.y};
-            } else {
-                *reinterpret_cast<u4 *>(pool + 2 * elems + 16 * c) = *reinterpret_cast<const u4 *>(src + 8 * c);
-            }
+        for (int i = 0; i < 4; ++i) kn_raw[i] = *reinterpret_cast<const u4 *>(a.k_new + row + chunk_dim(i));
+        vn_raw = *reinterpret_cast<const u4 *>(a.v_new + row + 8 * n);
+        if (stores_new) {
+            const bool is_k = lane < kChunks;
+            const int c = is_k ? lane : lane - kChunks;
+            const uint16_t *src = (is_k ? a.k_new : a.v_new) + row + (FP8 ? 16 : 8) * c;
+            st_raw[0] = *reinterpret_cast<const u4 *>(src);
+            if (FP8) st_raw[1] = *reinterpret_cast<const u4 *>(src + 8);
+            new_phys = static_cast<uint32_t>(table[new_blk]);
         }
     }
 
-    // Block-table entries of this wave's blocks go to LDS up front (a wave
-    // never owns more than 64 blocks), so the loop reads them without a
-    // memory load that would have to wait behind the K/V loads in flight.
-    const int32_t *table = a.tables + static_cast<size_t>(s) * a.max_blocks;
-    __shared__ int tbl_lds[kWaves][64];
-    if (lane < wb_end - wb_begin) tbl_lds[w][lane] = table[wb_begin + lane];
-    wave_lds_sync();
     const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
     constexpr int kElem = FP8 ? 1 : 2;
     const size_t tile_bytes = tile_elems() * kElem;
     const char *k_layer = a.k_layer;
     const char *v_layer = a.v_layer;
     // per-lane byte offsets inside a tile
-    const uint32_t k_off = static_cast<uint32_t>(ktok * kHeadDim * kElem + 16 * kdl);  // + 64 i
+    const uint32_t k_off = static_cast<uint32_t>(ktok * kHeadDim * kElem + 16 * r);  // + 64 i
     const uint32_t v_off = static_cast<uint32_t>(lane * 8 * kElem);                 // + 512 kElem c
 
-    float m_run = -INFINITY;  // running max of head kq (log2 units), same in all lanes of that head
-    float l_run = 0.0f;       // this lane's share of the running sum of head kq
-    float o[kGroup][8];       // F16 pools, value layout: o[h][e] for dim 8vj+e over tokens of row vt
-    f4 oacc[8];               // FP8 pools, MFMA j's result: oacc[j][r] = head r, dim 8(l%16) + j
-#pragma unroll
-    for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
+    float m_run = -INFINITY;  // running max of head n%4 (log2 units), equal in the lanes of that head
+    float l_run = 0.0f;       // sum of this lane's weights (tokens 4c + r) of head n%4
+    f4 oacc[8];               // MFMA j's result: oacc[j][c] = head c at dim 8n + j
 #pragma unroll
     for (int j = 0; j < 8; ++j) oacc[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    // FP8: P of the current block as F16, [head][4 (t % 4) + t / 4], so that
-    // lane l's A operand (tokens 4c + l/16, c < 4) is 8 contiguous bytes
-    __shared__ _Float16 p16_lds[kWaves][kGroup * kBlockSize];
 
-    u4 kb[NBUF][4], vb[NBUF][4];  // raw tile data (FP8: K uses [0..1], V uses .x .y)
+    // Registers of one block: K as 16-byte loads, V as 16-byte (F16) or
+    // 8-byte (FP8) loads.
+    constexpr int kKLoads = FP8 ? 2 : 4;
+    using VReg = std::conditional_t<FP8, u2, u4>;
+    u4 kb[NBUF][kKLoads];  // raw tile data
+    VReg vb[NBUF][4];
 
     // Issues the loads of block b into register buffer buf.  Blocks past
     // the wave's run are issued through empty resources (no memory traffic),
@@ -409,203 +355,95 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
         const int bytes = live ? static_cast<int>(tile_bytes) : 0;
         const __amdgpu_buffer_rsrc_t kr = tile_rsrc(k_layer + base, bytes);
         const __amdgpu_buffer_rsrc_t vr = tile_rsrc(v_layer + base, bytes);
-        if (FP8) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) kb[buf][i] = load_raw16(kr, k_off + 64u * i);
+        for (int i = 0; i < kKLoads; ++i) kb[buf][i] = load_raw16(kr, k_off + 64u * i);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u2 v2 = load_raw8(vr, v_off + 512u * c);
-                vb[buf][c] = u4{v2.x, v2.y, 0u, 0u};
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) kb[buf][i] = load_raw16(kr, k_off + 64u * i);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) vb[buf][c] = load_raw16(vr, v_off + 1024u * c);
+        for (int c = 0; c < 4; ++c) {
+            if constexpr (FP8)
+                vb[buf][c] = load_raw8(vr, v_off + 512u * c);
+            else
+                vb[buf][c] = load_raw16(vr, v_off + 1024u * c);
         }
     };
 
     auto consume = [&](int buf, int b) {
         if (owns_new && b == new_blk) {
             // the pool may still hold the previous content of the newest slot
+            u4 kn[kKLoads];
+            VReg vn;
+            if constexpr (FP8) {
+#pragma unroll
+                for (int i = 0; i < kKLoads; ++i) {
+                    const u2 lo = fp8_encode8(__builtin_bit_cast(h8, kn_raw[2 * i]), a.inv_k_scale);
+                    const u2 hi = fp8_encode8(__builtin_bit_cast(h8, kn_raw[2 * i + 1]), a.inv_k_scale);
+                    kn[i] = u4{lo.x, lo.y, hi.x, hi.y};
+                }
+                vn = fp8_encode8(__builtin_bit_cast(h8, vn_raw), a.inv_v_scale);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kKLoads; ++i) kn[i] = kn_raw[i];
+                vn = vn_raw;
+            }
             const bool k_mine = ktok == new_off;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kb[buf][i] = k_mine ? kn[i] : kb[buf][i];
+            for (int i = 0; i < kKLoads; ++i) kb[buf][i] = k_mine ? kn[i] : kb[buf][i];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) vb[buf][c] = (4 * c + vt == new_off) ? vn : vb[buf][c];
+            for (int c = 0; c < 4; ++c) vb[buf][c] = (4 * c + r == new_off) ? vn : vb[buf][c];
         }
-        if constexpr (QKM) {
-            // ---- S^T = K Q^T on the matrix cores: four v_mfma_f32_16x16x32_f16 ----
-            h8 ka[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (FP8) {
-                    const u4 r = kb[buf][i >> 1];
-                    ka[i] = (i & 1) ? fp8_decode8_h(r.z, r.w) : fp8_decode8_h(r.x, r.y);
-                } else {
-                    ka[i] = __builtin_bit_cast(h8, kb[buf][i]);
-                }
-            }
-            f4 st = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[i], qm[i], st, 0, 0, 0);
-            // st[c]: score of token 4c + vt for head vj%4 (the same in the lanes of
-            // one head: columns n and n + 4k of Q^T are equal)
-            const int valid = t_end - b * kBlockSize;  // >= 1; pieces end on block edges or at ctx
-            const bool partial = valid < kBlockSize;
-            float x[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                x[c] = st[c] * a.scale_log2e;
-                if (partial && 4 * c + vt >= valid) x[c] = -INFINITY;
-            }
-            float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            if (__builtin_amdgcn_ballot_w64(bm > m_run + kTau) != 0) {
-                bm = fmaxf(bm, shfl_xor(bm, 16));
-                bm = fmaxf(bm, shfl_xor(bm, 32));
-                const float m_new = fmaxf(m_run, bm);
-                const float alpha = fast_exp2(m_run - m_new);
-                l_run *= alpha;
-                m_run = m_new;
-                // lanes 0..3 hold heads 0..3; result element c is head c
-                const f4 a4 = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0)),
-                               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1)),
-                               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2)),
-                               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3))};
-#pragma unroll
-                for (int j = 0; j < 8; ++j) oacc[j] *= a4;
-            }
-            // weights as F16 (at most 2^kTau); the running sum adds the same
-            // rounded values that enter P V
-            const h2 p01 = {static_cast<_Float16>(fast_exp2(x[0] - m_run)), static_cast<_Float16>(fast_exp2(x[1] - m_run))};
-            const h2 p23 = {static_cast<_Float16>(fast_exp2(x[2] - m_run)), static_cast<_Float16>(fast_exp2(x[3] - m_run))};
-            const h2 one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-            l_run = __builtin_amdgcn_fdot2(p01, one2, __builtin_amdgcn_fdot2(p23, one2, l_run, false), false);
-            const h4 pa = {p01.x, p01.y, p23.x, p23.y};  // A: row vj (head vj%4), k-slot 4 vt + c = token 4c + vt
-            // ---- P V: eight v_mfma_f32_16x16x16_f16, B = V at dim 8 vj + j ----
-            if (FP8) {
-                uint32_t vw[4][2];  // raw codes of token 4c + vt; stale slots may hold anything
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const bool dead = partial && 4 * c + vt >= valid;
-                    vw[c][0] = dead ? 0u : vb[buf][c].x;
-                    vw[c][1] = dead ? 0u : vb[buf][c].y;
-                }
-#pragma unroll
-                for (int jp = 0; jp < 4; ++jp) {
-                    // bytes {c0 dim j, c1 dim j, c0 dim j+1, c1 dim j+1}, j = 2 jp
-                    const uint32_t sel = (jp & 1) ? 0x07030602u : 0x05010400u;
-                    const int wd = jp >> 1;
-                    const uint32_t t01 = __builtin_amdgcn_perm(vw[1][wd], vw[0][wd], sel);
-                    const uint32_t t23 = __builtin_amdgcn_perm(vw[3][wd], vw[2][wd], sel);
-                    const h2 a01 = fp8_pair_f16<false>(t01), b01 = fp8_pair_f16<true>(t01);
-                    const h2 a23 = fp8_pair_f16<false>(t23), b23 = fp8_pair_f16<true>(t23);
-                    const h4 v0 = {a01.x, a01.y, a23.x, a23.y};  // dim 2jp of tokens c = 0..3
-                    const h4 v1 = {b01.x, b01.y, b23.x, b23.y};  // dim 2jp + 1
-                    oacc[2 * jp] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v0, oacc[2 * jp], 0, 0, 0);
-                    oacc[2 * jp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v1, oacc[2 * jp + 1], 0, 0, 0);
-                }
-            } else {
-                u4 vv[4];  // token 4c + vt, dims 8 vj .. +7; stale slots may hold anything
-#pragma unroll
-                for (int c = 0; c < 4; ++c) vv[c] = (partial && 4 * c + vt >= valid) ? u4(0u) : vb[buf][c];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    // halves j of tokens c = 0, 1 and c = 2, 3
-                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                    const int wd = j >> 1;
-                    const uint32_t t01 = __builtin_amdgcn_perm(vv[1][wd], vv[0][wd], sel);
-                    const uint32_t t23 = __builtin_amdgcn_perm(vv[3][wd], vv[2][wd], sel);
-                    const h4 vj4 = __builtin_bit_cast(h4, u2{t01, t23});
-                    oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vj4, oacc[j], 0, 0, 0);
-                }
-            }
-            return;
-        }
-        // K chunks as F16
-        h8 kc[4];
+        // ---- S^T = K Q^T ----
+        h8 ka[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (FP8) {
-                const u4 r = kb[buf][i >> 1];
-                kc[i] = (i & 1) ? fp8_decode8_h(r.z, r.w) : fp8_decode8_h(r.x, r.y);
+            if constexpr (FP8) {
+                const u4 k2 = kb[buf][i >> 1];
+                ka[i] = (i & 1) ? fp8_decode8_h(k2.z, k2.w) : fp8_decode8_h(k2.x, k2.y);
             } else {
-                kc[i] = __builtin_bit_cast(h8, kb[buf][i]);
+                ka[i] = __builtin_bit_cast(h8, kb[buf][i]);
             }
         }
-        // ---- scores: partial dots over this lane's 32 dims, 4 heads ----
-        float acc[kGroup];
+        f4 st = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int h = 0; h < kGroup; ++h) {
-            float x = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const h2x4 qq = pairs(qv[h][i]);
-                const h2x4 kk = pairs(kc[i]);
-#pragma unroll
-                for (int p = 0; p < 4; ++p) x = __builtin_amdgcn_fdot2(qq.v[p], kk.v[p], x, false);
-            }
-            acc[h] = x;
-        }
-        // ---- 4-lane transpose-reduce: lane keeps head kq ----
-        const bool hi2 = (kq & 2) != 0;
-        const bool hi1 = (kq & 1) != 0;
-        float keep0 = hi2 ? acc[2] : acc[0];
-        float keep1 = hi2 ? acc[3] : acc[1];
-        const float send0 = hi2 ? acc[0] : acc[2];
-        const float send1 = hi2 ? acc[1] : acc[3];
-        keep0 += dpp_quad_xor2(send0);
-        keep1 += dpp_quad_xor2(send1);
-        float sc = hi1 ? keep1 : keep0;
-        sc += dpp_quad_xor1(hi1 ? keep0 : keep1);
-        sc *= a.scale_log2e;
+        for (int i = 0; i < 4; ++i) st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[i], qm[i], st, 0, 0, 0);
 
         // ---- mask the tail of the sequence's last block ----
         const int valid = t_end - b * kBlockSize;  // >= 1; pieces end on block edges or at ctx
         const bool partial = valid < kBlockSize;
-        if (partial && kt >= valid) sc = -INFINITY;
+        float x[4];  // scores of tokens 4c + r in log2 units
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            x[c] = st[c] * a.scale_log2e;
+            if (partial && 4 * c + r >= valid) x[c] = -INFINITY;
+        }
 
         // ---- online softmax with a lazily raised max ----
-        if (__builtin_amdgcn_ballot_w64(sc > m_run + kTau) != 0) {
-            float bm = sc;
-            bm = fmaxf(bm, dpp_row_ror4(bm));
-            bm = fmaxf(bm, dpp_row_ror8(bm));
+        float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        if (__builtin_amdgcn_ballot_w64(bm > m_run + kTau) != 0) {
             bm = fmaxf(bm, shfl_xor(bm, 16));
             bm = fmaxf(bm, shfl_xor(bm, 32));
             const float m_new = fmaxf(m_run, bm);
             const float alpha = fast_exp2(m_run - m_new);
             l_run *= alpha;
             m_run = m_new;
-            if (lane < 4) alpha_lds[w][lane] = alpha;
-            wave_lds_sync();
-            const float4 al = *reinterpret_cast<const float4 *>(alpha_lds[w]);
-            if (FP8) {
-                const f4 a4 = {al.x, al.y, al.z, al.w};
+            // lanes 0..3 hold heads 0..3, result element c is head c
+            const f4 a4 = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0)),
+                           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1)),
+                           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2)),
+                           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3))};
 #pragma unroll
-                for (int j = 0; j < 8; ++j) oacc[j] *= a4;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    o[0][e] *= al.x;
-                    o[1][e] *= al.y;
-                    o[2][e] *= al.z;
-                    o[3][e] *= al.w;
-                }
-            }
+            for (int j = 0; j < 8; ++j) oacc[j] *= a4;
         }
-        const float p = fast_exp2(sc - m_run);
-        l_run += p;
-        if (FP8) {
-            p16_lds[w][kq * kBlockSize + 4 * (kt & 3) + (kt >> 2)] = static_cast<_Float16>(p);
-            wave_lds_sync();
-            // ---- P V on the matrix cores ----
-            // A: rows m = l%16 read head m%4 (rows 4..15 repeat heads 0..3, so every
-            // lane group of the result holds all four heads)
-            const h4 pa = *reinterpret_cast<const h4 *>(&p16_lds[w][(lane & 3) * kBlockSize + 4 * vt]);
-            uint32_t vw[4][2];  // raw codes of token 4c + vt; stale slots may hold anything
+        const h2 p01 = {static_cast<_Float16>(fast_exp2(x[0] - m_run)), static_cast<_Float16>(fast_exp2(x[1] - m_run))};
+        const h2 p23 = {static_cast<_Float16>(fast_exp2(x[2] - m_run)), static_cast<_Float16>(fast_exp2(x[3] - m_run))};
+        const h2 one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+        l_run = __builtin_amdgcn_fdot2(p01, one2, __builtin_amdgcn_fdot2(p23, one2, l_run, false), false);
+        const h4 pa = {p01.x, p01.y, p23.x, p23.y};
+
+        // ---- O += P V ----
+        if constexpr (FP8) {
+            uint32_t vw[4][2];  // codes of token 4c + r; stale slots may hold anything
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const bool dead = partial && 4 * c + vt >= valid;
+                const bool dead = partial && 4 * c + r >= valid;
                 vw[c][0] = dead ? 0u : vb[buf][c].x;
                 vw[c][1] = dead ? 0u : vb[buf][c].y;
             }
@@ -618,39 +456,38 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
                 const uint32_t t23 = __builtin_amdgcn_perm(vw[3][wd], vw[2][wd], sel);
                 const h2 a01 = fp8_pair_f16<false>(t01), b01 = fp8_pair_f16<true>(t01);
                 const h2 a23 = fp8_pair_f16<false>(t23), b23 = fp8_pair_f16<true>(t23);
-                const h4 v0 = {a01.x, a01.y, a23.x, a23.y};  // dim 2jp of tokens c = 0..3
-                const h4 v1 = {b01.x, b01.y, b23.x, b23.y};  // dim 2jp + 1
+                const h4 v0 = {a01.x, a01.y, a23.x, a23.y};  // dim 8n + 2jp of tokens c = 0..3
+                const h4 v1 = {b01.x, b01.y, b23.x, b23.y};  // dim 8n + 2jp + 1
                 oacc[2 * jp] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v0, oacc[2 * jp], 0, 0, 0);
                 oacc[2 * jp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v1, oacc[2 * jp + 1], 0, 0, 0);
             }
         } else {
-            p_lds[w][lane] = p;  // index 4*kt + kq == lane
-            wave_lds_sync();
-
-            // ---- P V ----
+            u4 vv[4];  // token 4c + r, dims 8n .. 8n+7; stale slots may hold anything
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float4 pc = *reinterpret_cast<const float4 *>(&p_lds[w][4 * (4 * c + vt)]);
-                u4 vr = vb[buf][c];
-                if (partial && 4 * c + vt >= valid) vr = u4(0u);  // stale slots may hold anything
-                const h8 vv = __builtin_bit_cast(h8, vr);
+            for (int c = 0; c < 4; ++c) vv[c] = (partial && 4 * c + r >= valid) ? u4(0u) : u4(vb[buf][c]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = static_cast<float>(vv[e]);
-                    o[0][e] = fmaf(pc.x, x, o[0][e]);
-                    o[1][e] = fmaf(pc.y, x, o[1][e]);
-                    o[2][e] = fmaf(pc.z, x, o[2][e]);
-                    o[3][e] = fmaf(pc.w, x, o[3][e]);
-                }
+            for (int j = 0; j < 8; ++j) {
+                // half j of tokens c = 0, 1 and of tokens c = 2, 3
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                const int wd = j >> 1;
+                const uint32_t t01 = __builtin_amdgcn_perm(vv[1][wd], vv[0][wd], sel);
+                const uint32_t t23 = __builtin_amdgcn_perm(vv[3][wd], vv[2][wd], sel);
+                oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{t01, t23}), oacc[j], 0,
+                                                                0, 0);
             }
         }
-        wave_lds_sync();  // p_lds is rewritten by the next block
     };
 
     // Software pipeline over this wave's blocks with NBUF register buffers:
-    // block b + NBUF - 1 is issued before block b is consumed.
+    // block b + NBUF - 1 is issued before block b is consumed.  The prologue
+    // keeps its loads in issue order (K then V, block by block) as in the
+    // loop: reordered, they left the loop entry with a merged wait count
+    // that waited for two blocks where one was due.
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) issue(i, wb_begin + i);
+    for (int i = 0; i < NBUF - 1; ++i) {
+        issue(i, wb_begin + i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int base = wb_begin; base < wb_end; base += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
@@ -659,33 +496,39 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
         }
     }
 
-    // ---- per-wave totals ----
-    if (!QKM) {  // QKM: lanes n, n + 4, n + 8, n + 12 of a row hold the same sum
-        l_run += dpp_row_ror4(l_run);
-        l_run += dpp_row_ror8(l_run);
+    // ---- store the newest token's K/V row ----
+    if (stores_new) {
+        const uint32_t phys = new_phys > last_block ? last_block : new_phys;
+        const bool is_k = lane < kChunks;
+        const int c = is_k ? lane : lane - kChunks;
+        const size_t elems = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_elems() +
+                             static_cast<size_t>(new_off) * kHeadDim;
+        char *pool = const_cast<char *>(is_k ? a.k_layer : a.v_layer);
+        if constexpr (FP8) {
+            const float inv = is_k ? a.inv_k_scale : a.inv_v_scale;
+            const u2 lo = fp8_encode8(__builtin_bit_cast(h8, st_raw[0]), inv);
+            const u2 hi = fp8_encode8(__builtin_bit_cast(h8, st_raw[1]), inv);
+            *reinterpret_cast<u4 *>(pool + elems + 16 * c) = u4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+            *reinterpret_cast<u4 *>(pool + 2 * elems + 16 * c) = st_raw[0];
+        }
     }
+
+    // ---- per-wave totals: sum over the four lane groups r ----
     l_run += shfl_xor(l_run, 16);
     l_run += shfl_xor(l_run, 32);
     if (lane < 4) {
         m_lds[w][lane] = m_run;
         l_lds[w][lane] = l_run;
     }
-    if (FP8 || QKM) {
-        // every lane group holds all four heads: group vt stores head vt (row 0)
+    {
+        // every lane group holds all four heads: group r stores head r
         float ov[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            ov[j] = vt == 0 ? oacc[j][0] : vt == 1 ? oacc[j][1] : vt == 2 ? oacc[j][2] : oacc[j][3];
-        float4 *dst = reinterpret_cast<float4 *>(&o_lds[w][0][vt][8 * vj]);
+        for (int j = 0; j < 8; ++j) ov[j] = r == 0 ? oacc[j][0] : r == 1 ? oacc[j][1] : r == 2 ? oacc[j][2] : oacc[j][3];
+        float4 *dst = reinterpret_cast<float4 *>(&o_lds[w][r][8 * n]);
         dst[0] = make_float4(ov[0], ov[1], ov[2], ov[3]);
         dst[1] = make_float4(ov[4], ov[5], ov[6], ov[7]);
-    } else {
-#pragma unroll
-        for (int h = 0; h < kGroup; ++h) {
-            float4 *dst = reinterpret_cast<float4 *>(&o_lds[w][vt][h][8 * vj]);
-            dst[0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-            dst[1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
-        }
     }
     __syncthreads();
 
@@ -702,17 +545,10 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
 #pragma unroll
     for (int x = 0; x < kWaves; ++x) {
         const float wgt = mw[x] == -INFINITY ? 0.0f : fast_exp2(mw[x] - M);
-        float s0 = 0.0f, s1 = 0.0f;
-        constexpr int kRows = (FP8 || QKM) ? 1 : 4;  // MFMA P V already summed the token rows
-#pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const float2 v = *reinterpret_cast<const float2 *>(&o_lds[x][r][h][d0]);
-            s0 += v.x;
-            s1 += v.y;
-        }
+        const float2 v = *reinterpret_cast<const float2 *>(&o_lds[x][h][d0]);
         L += wgt * l_lds[x][h];
-        O0 += wgt * s0;
-        O1 += wgt * s1;
+        O0 += wgt * v.x;
+        O1 += wgt * v.y;
     }
     if (FP8) {  // V's scale
         O0 *= a.v_scale;
@@ -733,7 +569,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
 
 template <int NBUF, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
-    decode_partial_body<NBUF, FP8, FP8 ? PA_QKM_FP8 : PA_QKM_F16>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    decode_partial_body<NBUF, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // ---------------------------------------------------------------------------
@@ -1375,8 +1211,7 @@ template <bool FP8>
 __global__ __launch_bounds__(256, 2) void mixed_kernel(DecodeArgs a) {
     const uint32_t nd = static_cast<uint32_t>(a.num_items) * static_cast<uint32_t>(a.num_kv_heads);
     if (blockIdx.x < nd)
-        decode_partial_body<FP8 ? PA_DECODE_NBUF_FP8 : PA_DECODE_NBUF, FP8, FP8 ? PA_QKM_FP8 : PA_QKM_F16>(a, blockIdx.x, 0,
-                                                                                                        0);
+        decode_partial_body<FP8 ? PA_DECODE_NBUF_FP8 : PA_DECODE_NBUF, FP8>(a, blockIdx.x, 0, 0);
     else
         prefill_body<FP8>(a, blockIdx.x - nd);
 }
