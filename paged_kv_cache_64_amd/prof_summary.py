@@ -1,0 +1,163 @@
+"""Short text summaries of rocprofv3 CSV output (kernel traces and counter
+runs), in the form kept under profiles/.
+
+    python -m paged_kv_cache_64_amd.prof_summary trace DIR --title T --command C [--note N ...]
+    python -m paged_kv_cache_64_amd.prof_summary counters --kernel K --fetch DIR --write DIR
+        --cal-fetch DIR --cal-write DIR --cal-bytes B --bytes B --title T --workload W
+        --command-fetch C --command-write C --command-cal C [--note N ...]
+    python -m paged_kv_cache_64_amd.prof_summary sq DIR --kernel K [--title T --command C]
+
+A counter summary records the kernel source hash of bench.py's
+kernel_code_hash(): bench.py reads the traffic figures only while the source
+is unchanged.
+"""
+import argparse
+import csv
+import glob
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _csv_files(path, suffix):
+    files = sorted(glob.glob(os.path.join(path, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {path}")
+    return files
+
+
+def kernel_stats(path):
+    """Rows (name, calls, average ns, min ns, max ns, total ns), largest total first."""
+    rows = []
+    for f in _csv_files(path, "kernel_stats.csv"):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                             float(r["MaxNs"]), float(r["TotalDurationNs"])))
+    rows.sort(key=lambda x: -x[5])
+    return rows
+
+
+def counter_means(path, counter):
+    """{kernel name: (mean value per dispatch, dispatches)} for one counter."""
+    acc = defaultdict(lambda: [0.0, 0])
+    for f in _csv_files(path, "counter_collection.csv"):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                a = acc[r["Kernel_Name"]]
+                a[0] += float(r["Counter_Value"])
+                a[1] += 1
+    return {k: (v[0] / v[1], v[1]) for k, v in acc.items() if v[1]}
+
+
+def _match(means, kernel):
+    hits = {k: v for k, v in means.items() if kernel in k}
+    if not hits:
+        raise SystemExit(f"kernel {kernel} not in the counter output")
+    if len(hits) > 1:  # several instantiations: weight by dispatches
+        tot = sum(v[1] for v in hits.values())
+        return sum(v[0] * v[1] for v in hits.values()) / tot, tot
+    return next(iter(hits.values()))
+
+
+def _short(name, width=88):
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def cmd_trace(args):
+    out = [f"# {args.title}", f"# command: {args.command}"]
+    out += [f"# {n}" for n in args.note or []]
+    out.append("# name | calls | average ns | min ns | max ns | total ns")
+    for name, calls, avg, mn, mx, tot in kernel_stats(args.dir)[: args.top]:
+        out.append(f"{_short(name)} | {calls} | {avg:.0f} | {mn:.0f} | {mx:.0f} | {tot:.0f}")
+    return "\n".join(out) + "\n"
+
+
+def cmd_counters(args):
+    sys.path.insert(0, ROOT)
+    import bench
+
+    cal_f = _match(counter_means(args.cal_fetch, "FETCH_SIZE"), "probe_copy_kernel")[0]
+    cal_w = _match(counter_means(args.cal_write, "WRITE_SIZE"), "probe_copy_kernel")[0]
+    fetch_scale = args.cal_bytes / (cal_f * 1024.0)
+    write_scale = args.cal_bytes / (cal_w * 1024.0)
+    f, nf = _match(counter_means(args.fetch, "FETCH_SIZE"), args.kernel)
+    w, nw = _match(counter_means(args.write, "WRITE_SIZE"), args.kernel)
+    fetch_bytes = f * 1024.0 * fetch_scale
+    write_bytes = w * 1024.0 * write_scale
+    out = [f"# {args.title}",
+           f"# FETCH_SIZE run:  {args.command_fetch}",
+           f"# WRITE_SIZE run:  {args.command_write}",
+           f"# calibration:     {args.command_cal}",
+           f"#   a plain copy of {args.cal_bytes} B read FETCH_SIZE = {cal_f:.1f} KiB and WRITE_SIZE = "
+           f"{cal_w:.1f} KiB per launch,",
+           f"#   so FETCH_SIZE is scaled by {fetch_scale:.4f} and WRITE_SIZE by {write_scale:.4f} to give bytes",
+           f"# {args.kernel}: FETCH_SIZE {f:.1f} KiB/launch over {nf} launches, WRITE_SIZE {w:.1f} KiB/launch "
+           f"over {nw} launches",
+           f"# algorithmic bytes per launch: {args.bytes}",
+           f"# traffic / algorithmic = {(fetch_bytes + write_bytes) / args.bytes:.4f}"]
+    out += [f"# {n}" for n in args.note or []]
+    out += [f"kernel: {args.kernel}",
+            f"workload: {args.workload}",
+            f"kernel_code_sha256: {bench.kernel_code_hash()}",
+            f"fetch_scale: {fetch_scale:.6f}",
+            f"write_scale: {write_scale:.6f}",
+            f"fetch_bytes_per_launch: {fetch_bytes:.0f}",
+            f"write_bytes_per_launch: {write_bytes:.0f}"]
+    return "\n".join(out) + "\n"
+
+
+def cmd_sq(args):
+    """Mean per-dispatch value of every counter in the run, for one kernel."""
+    names = set()
+    for f in _csv_files(args.dir, "counter_collection.csv"):
+        with open(f, newline="") as fh:
+            names.update(r["Counter_Name"] for r in csv.DictReader(fh))
+    out = []
+    if args.title:
+        out.append(f"# {args.title}")
+    if args.command:
+        out.append(f"# command: {args.command}")
+    for c in sorted(names):
+        v, n = _match(counter_means(args.dir, c), args.kernel)
+        out.append(f"{args.kernel} {c}: {v:.6g} per launch over {n} launches")
+    return "\n".join(out) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("--title", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--note", action="append")
+    t.add_argument("--top", type=int, default=12)
+    c = sub.add_parser("counters")
+    for k in ("kernel", "fetch", "write", "cal_fetch", "cal_write", "title", "workload", "command_fetch",
+              "command_write", "command_cal"):
+        c.add_argument("--" + k.replace("_", "-"), required=True)
+    c.add_argument("--cal-bytes", type=int, required=True)
+    c.add_argument("--bytes", type=int, required=True)
+    c.add_argument("--note", action="append")
+    q = sub.add_parser("sq")
+    q.add_argument("dir")
+    q.add_argument("--kernel", required=True)
+    q.add_argument("--title")
+    q.add_argument("--command")
+    ap.add_argument("-o", "--out")
+    args = ap.parse_args(argv)
+    text = {"trace": cmd_trace, "counters": cmd_counters, "sq": cmd_sq}[args.cmd](args)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    else:
+        sys.stdout.write(text)
+
+
+if __name__ == "__main__":
+    main()
