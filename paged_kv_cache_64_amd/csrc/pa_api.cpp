@@ -583,11 +583,16 @@ pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const
         static_cast<int64_t>(info->num_items + info->num_prefill_items) * pool->desc.num_kv_heads <= 0x7fffffff) {
         // decode and prefill pieces share one launch
         if (pa::launch_mixed(a, stream) != hipSuccess) return PA_ERR_HIP;
+    } else if (info->num_items > 0 && info->num_prefix_items > 0 &&
+               static_cast<int64_t>(info->num_items + info->num_prefix_items) * pool->desc.num_kv_heads <=
+                   0x7fffffff) {
+        // ordinary and shared-prefix pieces share one launch
+        if (pa::launch_cascade(a, stream) != hipSuccess) return PA_ERR_HIP;
     } else {
         if (info->num_items > 0 && pa::launch_decode_partial(a, stream) != hipSuccess) return PA_ERR_HIP;
         if (info->num_prefill_items > 0 && pa::launch_prefill(a, stream) != hipSuccess) return PA_ERR_HIP;
+        if (info->num_prefix_items > 0 && pa::launch_decode_prefix(a, stream) != hipSuccess) return PA_ERR_HIP;
     }
-    if (info->num_prefix_items > 0 && pa::launch_decode_prefix(a, stream) != hipSuccess) return PA_ERR_HIP;
     if (info->num_merges > 0 && pa::launch_decode_merge_planned(a, stream) != hipSuccess) return PA_ERR_HIP;
     return PA_OK;
 }

@@ -112,6 +112,7 @@ hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_prefix(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_cascade(const DecodeArgs &a, hipStream_t stream);  // decode + shared-prefix pieces
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_mixed(const DecodeArgs &a, hipStream_t stream);  // decode + prefill pieces (F16)
 

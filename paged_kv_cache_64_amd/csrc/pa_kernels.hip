@@ -19,6 +19,8 @@
 //                          Example 5)
 //   mixed_kernel           decode and prefill pieces of one step in one
 //                          launch
+//   cascade_kernel         decode and shared-prefix pieces of one step in one
+//                          launch
 //
 // A decode step is bound by HBM bandwidth: every sequence reads its own K/V
 // once per step and nothing is shared between sequences ("Batching and
@@ -78,6 +80,11 @@ constexpr int kRsrcDword3 = 0x00020000;
 // 12 % faster than the default policy on the 32-layer batch-32 step.
 #ifndef PA_KV_LOAD_AUX
 #define PA_KV_LOAD_AUX 2
+#endif
+// Register buffers of the shared-prefix pipeline (each wave reads every
+// block of its piece).
+#ifndef PA_PREFIX_NBUF
+#define PA_PREFIX_NBUF 2
 #endif
 // Register buffers of the decode pipeline (blocks in flight per wave).
 #ifndef PA_DECODE_NBUF
@@ -642,13 +649,16 @@ __global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a)
 //   wave w owns rows 16w .. 16w+15: row 16w + 4r + j is member 4w + r, query
 //   head 4g + j.  In the lane layout of the MFMA (lane l, n = l % 16,
 //   r = l / 16):
-//   S^T = K . Q^T   A = K tile   (lane: token n, dims {32i + 8r + 4u + c})
+//   S^T = K . Q^T   A = K tile   (lane: MFMA row n = token 4(n%4) + n/4,
+//                                 dims {32i + 8r + 4u + c})
 //                   B = Q^T      (lane: row n, the same dims)
-//                   D = S^T      (lane: tokens 4r + c of row n)
-//   O   = P . V     A = P        (lane: row n, tokens 4r + c) -- D of S^T as is
-//                   B = V        (lane: tokens 4r + c, dim 16 dt + n) read
-//                                 from a per-wave LDS copy of the V tile
-//                   D = O        (lane: rows 4r + c, dim 16 dt + n)
+//                   D = S^T      (lane: tokens 4c + r of row n)
+//   O   = P . V     A = P        (lane: row n, k-slot 4r + c = token 4c + r)
+//                                 -- D of S^T as is
+//                   B = V        (lane: tokens 4c + r at dim 8n + j, MFMA j:
+//                                 byte permutes of the lane's V registers,
+//                                 token 4c + r, dims 8n .. 8n+7)
+//                   D = O        (lane: rows 4r + c, dim 8n + j)
 // Each member's result is a partial record (o, m, l), merged with the
 // member's own suffix pieces by decode_merge_planned.  FP8 pools: each lane
 // loads the same tokens and dims as 8-byte code groups and widens them to
@@ -660,19 +670,17 @@ struct h4x2 {
 };
 __device__ __forceinline__ h4x2 quads(h8 x) { return __builtin_bit_cast(h4x2, x); }
 
-constexpr int kVRow = kHeadDim + 8;  // padded LDS row of the staged V tile (halves)
 
 template <bool FP8>
-__global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
-    const int g = static_cast<int>(blockIdx.x % a.num_kv_heads);
-    const int32_t *it = a.prefix_items + kPrefixItemInts * static_cast<size_t>(blockIdx.x / a.num_kv_heads);
+__device__ __forceinline__ void prefix_body(const DecodeArgs &a, uint32_t bx) {
+    const int g = static_cast<int>(bx % a.num_kv_heads);
+    const int32_t *it = a.prefix_items + kPrefixItemInts * static_cast<size_t>(bx / a.num_kv_heads);
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int n = lane & 15, r = lane >> 4;
 
     __shared__ int tbl_lds[kMaxPrefixPieceBlocks];
-    __shared__ _Float16 v_lds[kWaves][kBlockSize][kVRow];
     __shared__ float alpha_lds[kWaves][16];
     __shared__ float ml_lds[kWaves][16][2];
 
@@ -710,18 +718,21 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
     const size_t tile_bytes = tile_elems() * kElem;
     const char *k_layer = a.k_layer;
     const char *v_layer = a.v_layer;
-    // K: token n, dims 32i + 8r .. +7;  V: token 4c + r, dims 8n .. +7
-    const uint32_t k_off = static_cast<uint32_t>((n * kHeadDim + 8 * r) * kElem);  // + 32 i elements
+    // K: MFMA row n is token 4(n%4) + n/4, dims 32i + 8r .. +7, so S^T gives
+    // lane (r, n) the scores of tokens 4c + r -- the tokens of its V registers:
+    // V: token 4c + r, dims 8n .. +7
+    const int ktok = 4 * (n & 3) + (n >> 2);
+    const uint32_t k_off = static_cast<uint32_t>((ktok * kHeadDim + 8 * r) * kElem);  // + 32 i elements
     const uint32_t v_off = static_cast<uint32_t>((r * kHeadDim + 8 * n) * kElem);  // + 4 c rows
 
     float m_run = -INFINITY;  // running max of row n (log2 units)
     float l_run = 0.0f;       // this lane's share of row n's running sum
-    f4 acc[8];
+    f4 acc[8];  // MFMA j's result: acc[j][c] = row 4r + c at dim 8n + j
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
 
-    h8 kb[2][4], vb[2][4];
-    u2 kr8[2][4], vr8[2][4];  // FP8 pools: raw codes until consumed
+    h8 kb[PA_PREFIX_NBUF][4], vb[PA_PREFIX_NBUF][4];
+    u2 kr8[PA_PREFIX_NBUF][4], vr8[PA_PREFIX_NBUF][4];  // FP8 pools: raw codes until consumed
     auto issue = [&](int buf, int b) {
         const bool live = b < b_end;
         uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tbl_lds[live ? b - b_begin : 0]));
@@ -765,7 +776,7 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
         const int valid = min(kBlockSize, t_end - b * kBlockSize);
         float sc[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) sc[c] = (4 * r + c < valid) ? st[c] * a.scale_log2e : -INFINITY;
+        for (int c = 0; c < 4; ++c) sc[c] = (4 * c + r < valid) ? st[c] * a.scale_log2e : -INFINITY;
         const float bmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         if (__builtin_amdgcn_ballot_w64(bmax > m_run + kTau) != 0) {
             float bm = bmax;
@@ -794,30 +805,34 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
             pa[c] = static_cast<_Float16>(fast_exp2(sc[c] - m_run));
             l_run += static_cast<float>(pa[c]);
         }
-        // stage V (token 4c + r, dims 8n .. 8n+7 in this lane) into LDS
+        // P V, one MFMA per dim 8n + j: byte permutes gather dim 8n + j of the
+        // lane's four tokens (stale slots past the context are zeroed)
+        u4 vv[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            h8 vv = vb[buf][c];
-            if (4 * c + r >= valid) vv = h8(0);
-            *reinterpret_cast<h8 *>(&v_lds[w][4 * c + r][8 * n]) = vv;
+        for (int c = 0; c < 4; ++c) vv[c] = (4 * c + r >= valid) ? u4(0u) : __builtin_bit_cast(u4, vb[buf][c]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t t01 = __builtin_amdgcn_perm(vv[1][j >> 1], vv[0][j >> 1], sel);
+            const uint32_t t23 = __builtin_amdgcn_perm(vv[3][j >> 1], vv[2][j >> 1], sel);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{t01, t23}), acc[j], 0, 0, 0);
         }
-        wave_lds_sync();
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            h4 vbv;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) vbv[c] = v_lds[w][4 * r + c][16 * dt + n];
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vbv, acc[dt], 0, 0, 0);
-        }
-        wave_lds_sync();  // the next block restages V
     };
 
-    issue(0, b_begin);
-    for (int b = b_begin; b < b_end; b += 2) {
-        issue(1, b + 1);
-        consume(0, b);
-        issue(0, b + 2);
-        if (b + 1 < b_end) consume(1, b + 1);
+    // Software pipeline as in decode_partial: block b + NBUF - 1 is issued
+    // before block b is consumed, the prologue's loads in issue order.
+    constexpr int NBUF = PA_PREFIX_NBUF;
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) {
+        issue(i, b_begin + i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int base = b_begin; base < b_end; base += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+            issue((u + NBUF - 1) % NBUF, base + u + NBUF - 1);
+            if (base + u < b_end) consume(u, base + u);
+        }
     }
 
     // row sums over the four lane groups; (m, l) of rows 4r + c via LDS
@@ -836,14 +851,33 @@ __global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
         for (int c = 0; c < 4; ++c) {
             const size_t rec = static_cast<size_t>(slot) * a.num_q_heads + g * kGroup + c;
             const float vs = FP8 ? a.v_scale : 1.0f;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) a.o_part[rec * kHeadDim + 16 * dt + n] = acc[dt][c] * vs;
+            float4 *dst = reinterpret_cast<float4 *>(a.o_part + rec * kHeadDim + 8 * n);
+            dst[0] = make_float4(acc[0][c] * vs, acc[1][c] * vs, acc[2][c] * vs, acc[3][c] * vs);
+            dst[1] = make_float4(acc[4][c] * vs, acc[5][c] * vs, acc[6][c] * vs, acc[7][c] * vs);
             if (n == 0) {
                 a.ml_part[rec * 2] = ml_lds[w][4 * r + c][0];
                 a.ml_part[rec * 2 + 1] = ml_lds[w][4 * r + c][1];
             }
         }
     }
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(256) void decode_prefix_kernel(DecodeArgs a) {
+    prefix_body<FP8>(a, blockIdx.x);
+}
+
+// A shared-prefix (cascade) step in one launch: work-groups
+// [0, decode items x Hkv) run ordinary pieces (whole contexts and the
+// members' suffixes), the rest the shared-prefix pieces, so the prefix tiles
+// stream beside the suffixes instead of in a launch of their own.
+template <bool FP8>
+__global__ __launch_bounds__(256, 2) void cascade_kernel(DecodeArgs a) {
+    const uint32_t nd = static_cast<uint32_t>(a.num_items) * static_cast<uint32_t>(a.num_kv_heads);
+    if (blockIdx.x < nd)
+        decode_partial_body<FP8 ? PA_DECODE_NBUF_FP8 : PA_DECODE_NBUF, FP8>(a, blockIdx.x, 0, 0);
+    else
+        prefix_body<FP8>(a, blockIdx.x - nd);
 }
 
 // ---------------------------------------------------------------------------
@@ -1264,6 +1298,16 @@ hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL(prefill_kernel<true>, dim3(groups), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(prefill_kernel<false>, dim3(groups), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_cascade(const DecodeArgs &a, hipStream_t stream) {
+    const uint32_t groups =
+        static_cast<uint32_t>((static_cast<int64_t>(a.num_items) + a.num_prefix_items) * a.num_kv_heads);
+    if (a.elem_bytes == 1)
+        hipLaunchKernelGGL(cascade_kernel<true>, dim3(groups), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(cascade_kernel<false>, dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
