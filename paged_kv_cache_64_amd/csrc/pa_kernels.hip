@@ -579,6 +579,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     decode_partial_body<NBUF, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
+// Records a merge loads in one round (the merges are latency-bound).
+constexpr int kMergeBatch = 8;
+
 // ---------------------------------------------------------------------------
 // decode_merge: 256 threads = two (sequence, query head) rows of 128 dims.
 //   M = max_i m_i,  L = sum_i 2^(m_i - M) l_i,  out = sum_i 2^(m_i - M) o_i / L
@@ -597,13 +600,37 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     }
     const float *ml = a.ml_part + row * a.max_splits * 2;
     const float *op = a.o_part + row * a.max_splits * kHeadDim + d;
-    float M = -INFINITY;
-    for (int i = 0; i < ns; ++i) M = fmaxf(M, ml[2 * i]);
-    float L = 0.0f, O = 0.0f;
-    for (int i = 0; i < ns; ++i) {
-        const float wgt = fast_exp2(ml[2 * i] - M);
-        L += wgt * ml[2 * i + 1];
-        O += wgt * op[static_cast<int64_t>(i) * kHeadDim];
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    if (ns <= kMergeBatch) {
+        // every split's (m, l) and o in one round of loads, then the same
+        // arithmetic in the same order as below
+        float2 mlv[kMergeBatch];
+        float ov[kMergeBatch];
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            if (i < ns) {
+                mlv[i] = *reinterpret_cast<const float2 *>(ml + 2 * i);
+                ov[i] = op[static_cast<int64_t>(i) * kHeadDim];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i)
+            if (i < ns) M = fmaxf(M, mlv[i].x);
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            if (i < ns) {
+                const float wgt = fast_exp2(mlv[i].x - M);
+                L += wgt * mlv[i].y;
+                O += wgt * ov[i];
+            }
+        }
+    } else {
+        for (int i = 0; i < ns; ++i) M = fmaxf(M, ml[2 * i]);
+        for (int i = 0; i < ns; ++i) {
+            const float wgt = fast_exp2(ml[2 * i] - M);
+            L += wgt * ml[2 * i + 1];
+            O += wgt * op[static_cast<int64_t>(i) * kHeadDim];
+        }
     }
     const _Float16 r = static_cast<_Float16>(O / L);
     *reinterpret_cast<_Float16 *>(out) = r;
@@ -611,7 +638,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // decode_merge_planned: grid (merge entry, query-head pair); the pieces of
-// sequence s are records first .. first + n - 1.
+// sequence s are records first .. first + n - 1.  Up to kMergeBatch records
+// are loaded in one round (the merge is latency-bound: a few hundred KB).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a) {
     const int32_t *m = a.merges + kMergeInts * static_cast<size_t>(blockIdx.x);
@@ -626,14 +654,39 @@ __global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a)
         *out = 0;
         return;
     }
-    float M = -INFINITY;
-    for (int i = 0; i < n; ++i) M = fmaxf(M, a.ml_part[(static_cast<size_t>(first + i) * a.num_q_heads + h) * 2]);
-    float L = 0.0f, O = 0.0f;
-    for (int i = 0; i < n; ++i) {
-        const size_t rec = static_cast<size_t>(first + i) * a.num_q_heads + h;
-        const float wgt = fast_exp2(a.ml_part[rec * 2] - M);
-        L += wgt * a.ml_part[rec * 2 + 1];
-        O += wgt * a.o_part[rec * kHeadDim + d];
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    if (n <= kMergeBatch) {
+        // every record's (m, l) and o in one round of loads, then the same
+        // arithmetic in the same order as below
+        float2 ml[kMergeBatch];
+        float o[kMergeBatch];
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            if (i < n) {
+                const size_t rec = static_cast<size_t>(first + i) * a.num_q_heads + h;
+                ml[i] = *reinterpret_cast<const float2 *>(a.ml_part + rec * 2);
+                o[i] = a.o_part[rec * kHeadDim + d];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i)
+            if (i < n) M = fmaxf(M, ml[i].x);
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            if (i < n) {
+                const float wgt = fast_exp2(ml[i].x - M);
+                L += wgt * ml[i].y;
+                O += wgt * o[i];
+            }
+        }
+    } else {
+        for (int i = 0; i < n; ++i) M = fmaxf(M, a.ml_part[(static_cast<size_t>(first + i) * a.num_q_heads + h) * 2]);
+        for (int i = 0; i < n; ++i) {
+            const size_t rec = static_cast<size_t>(first + i) * a.num_q_heads + h;
+            const float wgt = fast_exp2(a.ml_part[rec * 2] - M);
+            L += wgt * a.ml_part[rec * 2 + 1];
+            O += wgt * a.o_part[rec * kHeadDim + d];
+        }
     }
     const _Float16 r = static_cast<_Float16>(O / L);
     *reinterpret_cast<_Float16 *>(out) = r;
