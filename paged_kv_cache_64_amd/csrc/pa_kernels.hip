@@ -86,12 +86,16 @@ constexpr int kRsrcDword3 = 0x00020000;
 #ifndef PA_PREFIX_NBUF
 #define PA_PREFIX_NBUF 2
 #endif
-// Register buffers of the decode pipeline (blocks in flight per wave).
+// Register buffers of the decode pipeline (blocks in flight per wave).  F16
+// at 2 / 3 / 4: 81.3 / 81.7 / 81.8 us per launch on the 32-layer batch-32
+// step, but depth 2 (158 VGPRs, three waves per SIMD) took the ragged
+// 64-sequence step from 184 to 191 us and the shared-prefix step from 580 to
+// 595 us, so 3 is kept.
 #ifndef PA_DECODE_NBUF
 #define PA_DECODE_NBUF 3
 #endif
-// The same depth for FP8 pools (tiles half the size): 3 to 6 measured within
-// 2 % of each other.
+// FP8 pools (tiles half the size): 2 / 3 / 4 / 5 measured 44.9 / 44.8 / 45.0
+// / 45.4 us.
 #ifndef PA_DECODE_NBUF_FP8
 #define PA_DECODE_NBUF_FP8 3
 #endif
