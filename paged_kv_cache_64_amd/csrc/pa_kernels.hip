@@ -102,9 +102,6 @@ constexpr int kRsrcDword3 = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *tile, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), static_cast<short>(0), bytes, kRsrcDword3);
 }
-__device__ __forceinline__ h8 load_tile16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, PA_KV_LOAD_AUX));
-}
 __device__ __forceinline__ u4 load_raw16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, PA_KV_LOAD_AUX));
 }
