@@ -343,7 +343,8 @@ def _cascade(st, group, plen, k_new=None, v_new=None):
 
 @pytest.mark.parametrize("groups,gsize,pblocks,extra", [(2, 3, 3, [0, 5, 16, 40, 77, 1]),
                                                         (1, 20, 5, list(range(0, 200, 10))),
-                                                        (3, 16, 40, [int(x) for x in np.arange(48) * 37 % 900])])
+                                                        (3, 16, 40, [int(x) for x in np.arange(48) * 37 % 900]),
+                                                        (2, 4, 6, [0] * 8)])
 def test_cascade_matches_oracle(groups, gsize, pblocks, extra):
     lens = [pblocks * 16 + e for e in extra]
     assert len(lens) == groups * gsize
@@ -353,8 +354,11 @@ def test_cascade_matches_oracle(groups, gsize, pblocks, extra):
     group = np.repeat(np.arange(groups), gsize).astype(np.int32)
     plen = np.full(groups, pblocks * 16, np.int32)
     out, plan = _cascade(st, group, plen)
-    report("cascade", groups=groups, members=gsize, prefix_items=plan.info.num_prefix_items,
-           merges=plan.info.num_merges)
+    report("cascade", groups=groups, members=gsize, items=plan.info.num_items,
+           prefix_items=plan.info.num_prefix_items, merges=plan.info.num_merges)
+    # contexts equal to the prefix leave no ordinary pieces: the prefix pieces
+    # then run in a launch of their own, otherwise beside the ordinary ones
+    assert (plan.info.num_items == 0) == all(e == 0 for e in extra)
     compare(f"cascade g{groups}x{gsize}", out, st.reference(0))
     # the same attention as the plain planned schedule
     plain, _ = _planned(st)
