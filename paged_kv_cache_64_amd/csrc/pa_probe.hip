@@ -94,6 +94,25 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(const _Float16 *a, const
     for (int c = 0; c < 4; ++c) d[(4 * r + c) * 16 + m] = acc[c];
 }
 
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+// One v_mfma_f32_16x16x32_f16 on row-major inputs (A 16x32, B 32x16, D 16x16),
+// with the lane layout the decode and prefill kernels rely on:
+//   A: lane l holds A[l % 16][8 (l / 16) + e], e < 8
+//   B: lane l holds B[8 (l / 16) + e][l % 16]
+//   D: lane l holds D[4 (l / 16) + c][l % 16]
+__global__ __launch_bounds__(64) void probe_mfma32_kernel(const _Float16 *a, const _Float16 *b, float *d) {
+    const int l = threadIdx.x, m = l % 16, r = l / 16;
+    h8 av, bv;
+    for (int e = 0; e < 8; ++e) {
+        av[e] = a[m * 32 + 8 * r + e];
+        bv[e] = b[(8 * r + e) * 16 + m];
+    }
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+    for (int c = 0; c < 4; ++c) d[(4 * r + c) * 16 + m] = acc[c];
+}
+
 // FP8 (OCP E4M3 on gfx950) conversions as the decode kernels use them.
 __global__ __launch_bounds__(256) void probe_fp8_decode_kernel(const uint8_t *codes, float *out) {
     const int i = threadIdx.x;  // 128 threads x 2 codes
@@ -157,6 +176,15 @@ int32_t pa_probe_mfma_16x16x16(const void *a, const void *b, void *d, hipStream_
     return static_cast<int32_t>(hipGetLastError());
 }
 
+
+// Lane-layout check of the 16x16x32 f16 MFMA: a F16 [16][32], b F16 [32][16],
+// d fp32 [16][16], one wave.  Returns a hipError_t.
+int32_t pa_probe_mfma_16x16x32(const void *a, const void *b, void *d, hipStream_t stream) {
+    if (!a || !b || !d) return static_cast<int32_t>(hipErrorInvalidValue);
+    hipLaunchKernelGGL(probe_mfma32_kernel, dim3(1), dim3(64), 0, stream, static_cast<const _Float16 *>(a),
+                       static_cast<const _Float16 *>(b), static_cast<float *>(d));
+    return static_cast<int32_t>(hipGetLastError());
+}
 
 // Work-groups used by pa_probe_read and pa_probe_gather; `sink` must hold
 // this many uint32.
