@@ -475,6 +475,22 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
         std::stable_sort(pitems.begin(), pitems.end(), [](const PrefillItem &x, const PrefillItem &y) {
             return (x.f[5] - x.f[4]) > (y.f[5] - y.f[4]);
         });
+        // A prefill-only launch that fits in one round of two work-groups per
+        // CU starts all its work-groups at once, so order decides only which
+        // two share a CU: the dispatcher's second round lands on the CUs in
+        // the first round's order.  The longest kTargetWorkGroups/Hkv tiles go
+        // first, longest first, and the rest follow shortest first, so the
+        // longest tile shares its CU with the shortest.  (A 2016-token chunk at
+        // position 2016, 63 tiles: 124.9 us per layer against 127.7-129.2 us
+        // longest-first; with decode pieces in the launch, or more tiles than
+        // one round holds, the plain longest-first order measured as fast or
+        // faster.)
+        {
+            const int64_t first = kTargetWorkGroups / pool->desc.num_kv_heads;
+            const int64_t wgs = static_cast<int64_t>(pitems.size()) * pool->desc.num_kv_heads;
+            if (items.empty() && first > 0 && wgs > kTargetWorkGroups && wgs <= 2 * kTargetWorkGroups)
+                std::reverse(pitems.begin() + first, pitems.end());
+        }
         int32_t longest = 0;
         for (const PlanItem &it : items) longest = std::max(longest, it.t_end - it.t_begin);
         const size_t n_items = items.size(), n_merges = merges.size() / pa::kMergeInts, n_pf = pitems.size();

@@ -173,6 +173,20 @@ def test_mixed_step_under_a_2048_token_budget_sampled():
     m.close()
 
 
+def test_prompt_chunk_alone_sampled():
+    """The 2016-token chunk of the step above on its own: 63 tiles, one round
+    of two work-groups per CU, dispatched longest half first and then
+    shortest first.  Rows are sampled."""
+    m = Mixed([2016], [2016], seed=102)
+    out, plan = m.run()
+    assert plan.info.num_items == 0 and plan.info.num_prefill_items == 63 and plan.info.num_merges == 0
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 1000, 1983, 1984, 2015],
+                                     rng.choice(2016, 24, replace=False)])).astype(np.int64)
+    compare("chunk alone sampled", out[torch.from_numpy(rows).cuda()], m.reference(rows))
+    m.close()
+
+
 FP8 = pa.PA_FP8_E4M3
 # non-power-of-two scales: fl32(1/scale) is inexact and the codes span most
 # of the format's range
