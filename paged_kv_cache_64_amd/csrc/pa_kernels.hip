@@ -1005,8 +1005,9 @@ __device__ __forceinline__ h4 lds_read_tr16(const _Float16 *p) {
 constexpr int kStageBlocks = PA_PREFILL_STAGE_BLOCKS;  // key blocks per LDS stage (even)
 static_assert(kStageBlocks % 2 == 0 && kStageBlocks >= 2, "stages hold whole pairs");
 
-template <bool FP8>
+template <bool FP8, int NSETS = 2>
 __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
+    static_assert(NSETS == 1 || NSETS == 2, "one or two copy register sets");
     const int g = static_cast<int>(bx % a.num_kv_heads);
     const int32_t *it = a.prefill_items + kPrefillItemInts * static_cast<size_t>(bx / a.num_kv_heads);
     const int tid = threadIdx.x;
@@ -1090,11 +1091,12 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     constexpr int kLoads = FP8 ? 2 : 4;            // 16-byte loads per lane and tile
     const int cp_tensor = w >> 1, cp_blk0 = (w & 1) * kCopyBlocks;
     const char *cp_layer = cp_tensor ? a.v_layer : a.k_layer;
-    // two register sets: the loads of stage k go to set k % 2 two stages
+    // NSETS = 2: the loads of stage k go to register set k % 2 two stages
     // before that stage is consumed, so a stage's copy has a whole stage of
-    // compute to arrive before it is written to LDS
-    h8 stg[2][kCopyBlocks][kLoads];   // F16 pools
-    u4 stg8[2][kCopyBlocks][kLoads];  // FP8 pools: raw codes, widened at commit
+    // compute to arrive before it is written to LDS.  NSETS = 1: one stage
+    // ahead, 16 VGPRs fewer (F16).
+    h8 stg[NSETS][kCopyBlocks][kLoads];   // F16 pools
+    u4 stg8[NSETS][kCopyBlocks][kLoads];  // FP8 pools: raw codes, widened at commit
     // Value rows at or past the piece's last key (t_hi) may hold anything
     // (slots past the sequence in its last block): the V resource ends at the
     // last row below t_hi, so those rows load as zeros and their zero weights
@@ -1242,21 +1244,22 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     if (n_stages > 0) {
         fetch(b_lo, Set0{});
         commit(0, Set0{});
-        if (n_stages > 1) fetch(b_lo + kStageBlocks, Set1{});
+        if (NSETS == 2 && n_stages > 1) fetch(b_lo + kStageBlocks, std::integral_constant<int, NSETS - 1>{});
         __syncthreads();
     }
-    // stage st reads LDS buffer st % 2; meanwhile stage st+2 is loaded into
-    // register set st % 2 and, at the end, stage st+1 goes from register set
-    // (st+1) % 2 into LDS buffer (st+1) % 2, which stage st-1 read before the
-    // last barrier
+    // stage st reads LDS buffer st % 2; meanwhile stage st+NSETS is loaded
+    // into register set st % NSETS and, at the end, stage st+1 goes from
+    // register set (st+1) % NSETS into LDS buffer (st+1) % 2, which stage
+    // st-1 read before the last barrier
     auto stage = [&](int st, auto set) {
         constexpr int S = decltype(set)::value;  // == st % 2
+        constexpr int kLoadSet = S % NSETS, kCommitSet = (S ^ 1) % NSETS;
         const int b0 = b_lo + kStageBlocks * st;
-        if (st + 2 < n_stages) fetch(b0 + 2 * kStageBlocks, std::integral_constant<int, S>{});
+        if (st + NSETS < n_stages) fetch(b0 + NSETS * kStageBlocks, std::integral_constant<int, kLoadSet>{});
 #pragma unroll
         for (int sb = 0; sb < kStageBlocks; sb += 2)
             if (kStageBlocks * st + sb < w_blocks) compute(S, sb, b0 + sb);
-        if (st + 1 < n_stages) commit(S ^ 1, std::integral_constant<int, S ^ 1>{});
+        if (st + 1 < n_stages) commit(S ^ 1, std::integral_constant<int, kCommitSet>{});
         __syncthreads();
     };
     for (int st = 0; st < n_stages; st += 2) {
@@ -1305,9 +1308,13 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     }
 }
 
-template <bool FP8>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) {
-    prefill_body<FP8>(a, blockIdx.x);
+// WGS work-groups per CU: 2 with the copy two stages ahead (184 VGPRs for
+// F16), 3 with it one stage ahead (at most 168 VGPRs; F16 spills 3 of them).
+// Which pays depends on the launch; launch_prefill chooses.
+template <bool FP8, int WGS>
+__global__ __launch_bounds__(256, WGS) void prefill_kernel(DecodeArgs a) {
+    static_assert(WGS == 2 || WGS == 3, "two or three work-groups per CU");
+    prefill_body<FP8, WGS == 3 ? 1 : 2>(a, blockIdx.x);
 }
 
 // A mixed step's decode pieces and prefill pieces in one launch, so that the
@@ -1315,24 +1322,45 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(DecodeArgs a) {
 // work-groups share the compute units instead of running one after the
 // other.  Work-groups [0, decode items x Hkv) are decode pieces, the rest
 // prefill pieces.
-template <bool FP8>
-__global__ __launch_bounds__(256, 2) void mixed_kernel(DecodeArgs a) {
+// As prefill_kernel, WGS work-groups per CU; at 3 the decode pieces keep two
+// blocks in flight instead of three (158 VGPRs for F16 on their own).
+template <bool FP8, int WGS>
+__global__ __launch_bounds__(256, WGS) void mixed_kernel(DecodeArgs a) {
+    static_assert(WGS == 2 || WGS == 3, "two or three work-groups per CU");
     const uint32_t nd = static_cast<uint32_t>(a.num_items) * static_cast<uint32_t>(a.num_kv_heads);
     if (blockIdx.x < nd)
-        decode_partial_body<FP8 ? PA_DECODE_NBUF_FP8 : PA_DECODE_NBUF, FP8>(a, blockIdx.x, 0, 0);
+        decode_partial_body<WGS == 3 ? 2 : (FP8 ? PA_DECODE_NBUF_FP8 : PA_DECODE_NBUF), FP8>(a, blockIdx.x, 0, 0);
     else
-        prefill_body<FP8>(a, blockIdx.x - nd);
+        prefill_body<FP8, WGS == 3 ? 1 : 2>(a, blockIdx.x - nd);
 }
 
+}  // namespace
+
+namespace {
+// Three prefill work-groups per CU (the copy one stage ahead) pay when the
+// launch holds more prefill work-groups than one round of two per CU: the
+// extra slot keeps a CU busy while its tiles finish unevenly.  Measured on
+// MI355X (256 CUs), F16 per layer: a 16,384-token chunk at position 16,384
+// (with 32 decodes beside it) 7.71 against 8.42 ms, the chunk alone 7.61
+// against 8.33 ms; a 2016-token chunk (504 work-groups) 131.8 against
+// 127.3 us alone and 210 against 204 us with 32 decodes.  FP8 pools gain or
+// tie in every case (their bodies fit 168 VGPRs without spilling): 155
+// against 164 us per layer for the 2016-token step.
+constexpr int64_t kPrefillRoundGroups = 2 * 256;
+bool prefill_three_per_cu(const DecodeArgs &a) {
+    return a.elem_bytes == 1 || static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads > kPrefillRoundGroups;
+}
 }  // namespace
 
 hipError_t launch_mixed(const DecodeArgs &a, hipStream_t stream) {
     const uint32_t groups =
         static_cast<uint32_t>((static_cast<int64_t>(a.num_items) + a.num_prefill_items) * a.num_kv_heads);
     if (a.elem_bytes == 1)
-        hipLaunchKernelGGL(mixed_kernel<true>, dim3(groups), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((mixed_kernel<true, 3>), dim3(groups), dim3(256), 0, stream, a);
+    else if (prefill_three_per_cu(a))
+        hipLaunchKernelGGL((mixed_kernel<false, 3>), dim3(groups), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(mixed_kernel<false>, dim3(groups), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((mixed_kernel<false, 2>), dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1369,9 +1397,11 @@ hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream) 
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
     const uint32_t groups = static_cast<uint32_t>(static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads);
     if (a.elem_bytes == 1)
-        hipLaunchKernelGGL(prefill_kernel<true>, dim3(groups), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((prefill_kernel<true, 3>), dim3(groups), dim3(256), 0, stream, a);
+    else if (prefill_three_per_cu(a))
+        hipLaunchKernelGGL((prefill_kernel<false, 3>), dim3(groups), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(prefill_kernel<false>, dim3(groups), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((prefill_kernel<false, 2>), dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -187,6 +187,21 @@ def test_prompt_chunk_alone_sampled():
     m.close()
 
 
+@pytest.mark.parametrize("q_lens,hist", [([2100], [0]), ([2100, 1, 1, 1], [0, 4000, 100, 2047])])
+def test_more_tiles_than_one_round_sampled(q_lens, hist):
+    """66 prompt tiles (528 work-groups, more than one round of two per CU):
+    the launch takes the three-per-CU kernels, alone and with decode rows.
+    Rows are sampled."""
+    m = Mixed(q_lens, hist, seed=103 + len(q_lens))
+    out, plan = m.run()
+    assert plan.info.num_prefill_items * 8 > 512
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 2067, 2068, 2099], rng.choice(2100, 24, replace=False),
+                                     np.arange(2100, len(m.q))])).astype(np.int64)
+    compare("66 tiles sampled", out[torch.from_numpy(rows).cuda()], m.reference(rows))
+    m.close()
+
+
 FP8 = pa.PA_FP8_E4M3
 # non-power-of-two scales: fl32(1/scale) is inexact and the codes span most
 # of the format's range
