@@ -216,6 +216,42 @@ def test_config3_sampled_layers_and_sequences():
     st.close()
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_config3_timed_launch_sampled(fp8):
+    """The timed step's launch configuration at full size: the 32-layer pool of
+    batch 32 x ctx 4096, one plan for the step, and pa_decode_run appending
+    each sequence's newest token, on layers 0 and 31 (the other layers hold
+    NaN and are never read).  Sampled sequences are checked against the oracle
+    with the appended rows in place."""
+    w = workloads.config(3)
+    layers = (0, 31)
+    kw = dict(dtype=pa.PA_FP8_E4M3, kv_scales=(0.1, 0.0173)) if fp8 else {}
+    st = Staged(w, layers=layers, pool_layers=32, **kw)
+    plan = st.pool.plan(w.ctx_lens)
+    assert plan.info.num_items == 32 and plan.info.num_merges == 0
+    rng = np.random.default_rng(12)
+    for layer in layers:
+        q, tables, ids, k, v = st.host[layer]
+        k_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+        v_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+        qd, td = st.dev[layer]
+        out = torch.empty_like(qd)
+        st.pool.run(layer, plan, qd, out, td, w.scale, k_new=torch.from_numpy(k_new).cuda(),
+                    v_new=torch.from_numpy(v_new).cuda())
+        torch.cuda.synchronize()
+        k2, v2 = k.copy(), v.copy()
+        for s, c in enumerate(w.ctx_lens):
+            r = np.searchsorted(ids, tables[s, (c - 1) // 16])
+            k2[r, (c - 1) % 16] = k_new[s]
+            v2[r, (c - 1) % 16] = v_new[s]
+        st.host[layer] = (q, tables, ids, k2, v2)
+        seqs = np.sort(rng.choice(w.batch, size=4, replace=False))
+        compare(f"config3 timed launch fp8={fp8} layer{layer} seqs{list(seqs)}", out.cpu().numpy()[seqs],
+                st.reference(layer, seqs))
+        del k2, v2
+    st.close()
+
+
 @pytest.mark.parametrize("split", [None, 64, 256])
 def test_append_decode_writes_the_newest_token_and_attends_to_it(monkeypatch, split):
     """pa_append_decode == pa_write_kv(newest slots) + pa_decode, with fresh K/V

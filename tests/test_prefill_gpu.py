@@ -187,6 +187,25 @@ def test_prompt_chunk_alone_sampled():
     m.close()
 
 
+def test_mixed_step_under_a_16384_token_budget_sampled():
+    """32 decoding sequences at 4096 tokens plus the second 16,352-token chunk
+    of a 32,704-token prompt: 16,384 tokens, the default budget of the largest
+    GPUs in the vLLM page, Example 5.  Tiles are cut into merged pieces and
+    the launch runs three work-groups per CU.  Rows are sampled."""
+    q_lens = [16352] + [1] * 32
+    hist = [16352] + [4095] * 32
+    m = Mixed(q_lens, hist, seed=104)
+    out, plan = m.run()
+    report("budget 16384", decode_items=plan.info.num_items, prefill_items=plan.info.num_prefill_items,
+           merges=plan.info.num_merges)
+    assert plan.info.num_prefill_items * 8 > 512 and plan.info.num_merges > 32
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 8191, 16351], rng.choice(16352, 24, replace=False),
+                                     16352 + np.arange(32)[::4]])).astype(np.int64)
+    compare("budget 16384 sampled", out[torch.from_numpy(rows).cuda()], m.reference(rows))
+    m.close()
+
+
 @pytest.mark.parametrize("q_lens,hist", [([2100], [0]), ([2100, 1, 1, 1], [0, 4000, 100, 2047])])
 def test_more_tiles_than_one_round_sampled(q_lens, hist):
     """66 prompt tiles (528 work-groups, more than one round of two per CU):
