@@ -14,9 +14,10 @@
 //   decode_merge_planned_kernel   weights and write F16
 //   decode_prefix_kernel   shared-prefix pieces: one read of a group's
 //                          prefix tiles serves every member (MFMA)
-//   prefill_kernel         chunked-prefill tiles of 32 query tokens, causal,
-//                          on the matrix cores ("Batching and Scheduling",
-//                          Example 5)
+//   prefill_dma_kernel,    chunked-prefill tiles of 32 query tokens, causal,
+//   prefill_kernel         on the matrix cores ("Batching and Scheduling",
+//                          Example 5); F16 pools copy K/V tiles straight
+//                          into LDS, FP8 pools widen them through registers
 //   mixed_kernel           decode and prefill pieces of one step in one
 //                          launch
 //   cascade_kernel         decode and shared-prefix pieces of one step in one
@@ -1016,6 +1017,9 @@ __device__ __forceinline__ h4 lds_read_tr16(const _Float16 *p) {
 constexpr int kStageBlocks = PA_PREFILL_STAGE_BLOCKS;  // key blocks per LDS stage (even)
 static_assert(kStageBlocks % 2 == 0 && kStageBlocks >= 2, "stages hold whole pairs");
 
+// The register-staged copy serves FP8 pools, whose codes are widened on the
+// way into LDS (one stage ahead in the kernels built); F16 pools take
+// prefill_body_dma below.
 template <bool FP8, int NSETS = 2>
 __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     static_assert(NSETS == 1 || NSETS == 2, "one or two copy register sets");
@@ -1321,59 +1325,391 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     }
 }
 
-// WGS work-groups per CU: 2 with the copy two stages ahead (184 VGPRs for
-// F16), 3 with it one stage ahead (at most 168 VGPRs; F16 spills 3 of them).
-// Which pays depends on the launch; launch_prefill chooses.
-template <bool FP8, int WGS>
-__global__ __launch_bounds__(256, WGS) void prefill_kernel(DecodeArgs a) {
-    static_assert(WGS == 2 || WGS == 3, "two or three work-groups per CU");
-    prefill_body<FP8, WGS == 3 ? 1 : 2>(a, blockIdx.x);
+// LDS-DMA prefill helpers: the compiler cannot see which LDS buffer an
+// intrinsic transpose read touches and would wait for every DMA in flight;
+// these reads and the barrier are plain instructions whose waits are explicit.
+__device__ __forceinline__ uint32_t lds_addr(const _Float16 *p) {
+    return (uint32_t)(size_t)((const __attribute__((address_space(3))) _Float16 *)p);
+}
+// eight transpose reads, complete when the statement ends
+__device__ __forceinline__ void lds_read_tr16_x8(u2 (&d)[8], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// prefill_body for F16 pools with the copy straight into LDS
+// (buffer_load ... lds, 16 bytes per lane): no staging registers, so three
+// work-groups fit a CU without spilling, or three LDS buffers keep the copy
+// two stages ahead at two per CU.  The K/V tiles sit in LDS unpadded, each
+// row's 16-byte chunks permuted by an XOR swizzle that keeps the operand
+// reads conflict-free: chunk c of key row t at c ^ (t & 7) (the 16-byte
+// reads of rows 0..7 hit 8 distinct bank quads), of value row t at
+// c ^ 2 (t & 3) (a transpose read's four rows hit disjoint bank pairs).  The
+// copy lane that fills a position loads the global chunk the swizzle puts
+// there; out-of-range lanes of a zero-size resource write zeros.  The
+// arithmetic from the scores on and the epilogue are prefill_body's.
+template <int NB>
+__device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t bx) {
+    static_assert(NB == 2 || NB == 3, "two or three LDS buffers");
+    const int g = static_cast<int>(bx % a.num_kv_heads);
+    const int32_t *it = a.prefill_items + kPrefillItemInts * static_cast<size_t>(bx / a.num_kv_heads);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int n = lane & 15, r = lane >> 4;
+
+    __shared__ int tbl_lds[kMaxPrefillPieceBlocks];
+    // unpadded rows; 16-byte chunk c of row t sits at chunk c ^ (t & 7) (K)
+    // or c ^ 2 (t & 3) (V)
+    __shared__ __attribute__((aligned(16))) _Float16 k_lds[NB][kStageBlocks][kBlockSize][kHeadDim];
+    __shared__ __attribute__((aligned(16))) _Float16 v_lds[NB][kStageBlocks][kBlockSize][kHeadDim];
+    __shared__ float alpha_lds[kWaves][2][16];
+    __shared__ float ml_lds[kWaves][2][16][2];
+
+    // Plan entries are clamped so a damaged plan cannot index outside q, out,
+    // the tables, the pool or the workspace.
+    const int s = min(max(it[0], 0), a.batch - 1);
+    const int row0 = max(it[1], 0);
+    const int n_q = min(max(it[2], 0), kPrefillTile);
+    const int pos0 = max(it[3], 0);
+    const int cap = a.max_blocks * kBlockSize;
+    const int t_lo = min(max(it[4], 0), cap) & ~(kBlockSize - 1);
+    const int t_hi = min(min(it[5], cap), pos0 + n_q);
+    const int base_slot = it[6];
+    const int np = max(it[7], 1);
+    const int piece = min(max(it[8], 0), np - 1);
+    const bool direct = base_slot < 0;
+    if (!direct && a.num_slots <= 0) return;
+    const int b_lo = t_lo / kBlockSize;
+    const int b_hi = max(b_lo, min((t_hi + kBlockSize - 1) / kBlockSize, b_lo + kMaxPrefillPieceBlocks));
+
+    const int32_t *table = a.tables + static_cast<size_t>(s) * a.max_blocks;
+    for (int i = tid; i < b_hi - b_lo; i += 256) tbl_lds[i] = table[b_lo + i];
+    __syncthreads();
+
+    // this wave's query tokens and heads, and the keys its rows can see
+    const int tok0 = 16 * (w >> 1);
+    const int head0 = g * kGroup + 2 * (w & 1);
+    const int rows_w = min(16, n_q - tok0);  // may be <= 0: the wave then only helps with the copies
+    const int w_end = rows_w > 0 ? min(t_hi, pos0 + tok0 + rows_w) : t_lo;
+    const int qp = pos0 + tok0 + n;  // position of row n
+
+    // Q of the two row tiles, as the B operand of S^T: dims 32kk + 8r .. +7
+    h8 qv[2][4];
+    {
+        const bool row_ok = n < rows_w;
+        const size_t qr = static_cast<size_t>(min(max(row0 + tok0 + n, 0), a.num_q_rows - 1));
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const uint16_t *qrow = a.q + (qr * a.num_q_heads + head0 + rt) * kHeadDim + 8 * r;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const h8 x = *reinterpret_cast<const h8 *>(qrow + 32 * kk);
+                qv[rt][kk] = row_ok ? x : h8(0);
+            }
+        }
+    }
+
+    f4 oacc[2][8];
+    float m_run[2], l_run[2];  // row n of each tile, log2 units (l: this lane's share)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        m_run[rt] = -INFINITY;
+        l_run[rt] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) oacc[rt][j] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float c_scale = a.scale_log2e;
+    const h2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+
+    // copies: wave w moves tensor w/2 (K, V) of block w%2 of the pair straight
+    // into LDS, 1 KiB per load instruction: lane l fills chunk l%16 of row
+    // 4i + l/16 with the global chunk that the swizzle puts there
+    const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
+    const size_t tile_bytes = tile_elems() * sizeof(uint16_t);
+    constexpr int kCopyBlocks = kStageBlocks / 2;
+    constexpr int kLoads = 4;
+    const int cp_tensor = w >> 1, cp_blk0 = (w & 1) * kCopyBlocks;
+    const char *cp_layer = cp_tensor ? a.v_layer : a.k_layer;
+    uint32_t cp_off[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int row = 4 * i + (lane >> 4), pos = lane & 15;
+        const int c = cp_tensor ? pos ^ (2 * (row & 3)) : pos ^ (row & 7);
+        cp_off[i] = static_cast<uint32_t>(row * (kHeadDim * 2) + 16 * c);
+    }
+    auto fetch = [&](int b, int buf) {  // stage starting at block b, into LDS buffer buf
+#pragma unroll
+        for (int x = 0; x < kCopyBlocks; ++x) {
+            const int bb = b + cp_blk0 + x;
+            const bool live = bb < b_hi;
+            uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tbl_lds[live ? bb - b_lo : 0]));
+            phys = phys > last_block ? last_block : phys;
+            const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
+            const int rows = cp_tensor ? min(max(t_hi - bb * kBlockSize, 0), kBlockSize) : kBlockSize;
+            const int bytes = __builtin_amdgcn_readfirstlane(live ? rows * kHeadDim * 2 : 0);
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(cp_layer + base, bytes);
+            _Float16 *tile = cp_tensor ? &v_lds[buf][cp_blk0 + x][0][0] : &k_lds[buf][cp_blk0 + x][0][0];
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void *)(tile + 4 * i * kHeadDim), 16, cp_off[i], 0, 0, 0);
+        }
+    };
+
+    // transpose reads: lane l addresses token 4(l/16) + (l/4)%4, dims 4(l%4) .. +3
+    // of a 16-dim slice, so that lane (r, n) receives tokens 4r .. 4r+3 at dim n
+    const int tr_row = 4 * r + ((lane >> 2) & 3), tr_col = 4 * (lane & 3);
+    const int tr_swz = 2 * (tr_row & 3);
+    auto compute = [&](int buf, int sb, int b) {  // blocks sb, sb+1 of the stage = key blocks b, b+1
+        // the pair's K operands, read once for both row tiles
+        h8 kx[2][4];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                kx[blk][kk] = *reinterpret_cast<const h8 *>(&k_lds[buf][sb + blk][n][8 * ((4 * kk + r) ^ (n & 7))]);
+        f4 st[2][2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) st[rt][blk] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+                    st[rt][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kx[blk][kk], qv[rt][kk], st[rt][blk], 0, 0, 0);
+        // masks, only where the pair reaches past the first row's position or
+        // the last key this wave sees
+        const int k_last = b * kBlockSize + 2 * kBlockSize - 1;
+        const bool tail = k_last >= w_end;
+        if (k_last > pos0 + tok0 || tail) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int kp = (b + blk) * kBlockSize + 4 * r + c;
+                    const bool vis = kp < w_end && kp <= qp;
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) st[rt][blk][c] = vis ? st[rt][blk][c] : -INFINITY;
+                }
+        }
+        h8 pw[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const float m1 = max3_raw(st[rt][0][0], st[rt][0][1], st[rt][0][2]);
+            const float m2 = max3_raw(st[rt][0][3], st[rt][1][0], st[rt][1][1]);
+            const float m3 = max3_raw(st[rt][1][2], st[rt][1][3], m1);
+            const float bmax = max3_raw(m2, m3, m3);
+            const float mb = bmax * c_scale;
+            if (__builtin_amdgcn_ballot_w64(mb > m_run[rt] + kTau) != 0) {
+                float bm = mb;
+                bm = fmaxf(bm, shfl_xor(bm, 16));
+                bm = fmaxf(bm, shfl_xor(bm, 32));
+                const float m_new = fmaxf(m_run[rt], bm);
+                // a row that has seen no key yet keeps m = -inf (and alpha 1)
+                const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run[rt] - m_new);
+                l_run[rt] *= alpha;
+                m_run[rt] = m_new;
+                if (r == 0) alpha_lds[w][rt][n] = alpha;
+                wave_lds_sync();
+                const float4 al = *reinterpret_cast<const float4 *>(&alpha_lds[w][rt][4 * r]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    oacc[rt][j][0] *= al.x;
+                    oacc[rt][j][1] *= al.y;
+                    oacc[rt][j][2] *= al.z;
+                    oacc[rt][j][3] *= al.w;
+                }
+            }
+            // weights exp2(s * scale - m) enter P V as F16; the running sum
+            // adds the same rounded values (masked scores give exp2(-inf) = 0)
+            const float neg_m = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int c = 0; c < 4; c += 2) {
+                    const float p0 = fast_exp2(fmaf(st[rt][blk][c], c_scale, neg_m));
+                    const float p1 = fast_exp2(fmaf(st[rt][blk][c + 1], c_scale, neg_m));
+                    const h2 pp = {static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
+                    pw[rt][4 * blk + c] = pp.x;
+                    pw[rt][4 * blk + c + 1] = pp.y;
+                    l_run[rt] = __builtin_amdgcn_fdot2(pp, ones, l_run[rt], false);
+                }
+        }
+        // P V over dims 16j .. 16j+15: lane (r, n) gets tokens 4r .. 4r+3 of
+        // each block at dim 16j + n straight from the transpose reads
+        u2 t[2][8];  // [half][4 j's x 2 blocks]
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            uint32_t ad[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int j = 4 * hf + (q >> 1), blk = q & 1;
+                ad[q] = lds_addr(&v_lds[buf][sb + blk][tr_row][8 * ((2 * j + (tr_col >> 3)) ^ tr_swz) + (tr_col & 7)]);
+            }
+            lds_read_tr16_x8(t[hf], ad);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const h4 t0 = __builtin_bit_cast(h4, t[j >> 2][2 * (j & 3)]);
+            const h4 t1 = __builtin_bit_cast(h4, t[j >> 2][2 * (j & 3) + 1]);
+            const h8 bv = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+                oacc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[rt], bv, oacc[rt][j], 0, 0, 0);
+        }
+    };
+
+    // the work-group walks every pair of the piece; a wave computes the pairs
+    // below its last query's position
+    const int n_stages = (b_hi - b_lo + kStageBlocks - 1) / kStageBlocks;
+    const int w_blocks = w_end > t_lo ? (w_end + kBlockSize - 1) / kBlockSize - b_lo : 0;  // blocks this wave needs
+    // stage st reads LDS buffer st % NB; its loads were issued NB - 1 stages
+    // earlier.  Each stage issues kLoads * kCopyBlocks loads per wave.
+    constexpr int kAhead = NB - 1;
+    constexpr int kStageLoads = kLoads * kCopyBlocks;
+#pragma unroll
+    for (int s0 = 0; s0 < kAhead; ++s0)
+        if (s0 < n_stages) fetch(b_lo + s0 * kStageBlocks, s0);
+    if (n_stages > 0) {
+        if (kAhead > 1 && n_stages > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (kStageLoads * (kAhead - 1)));
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        raw_barrier();
+    }
+    auto stage = [&](int st, auto bufc) {
+        constexpr int B = decltype(bufc)::value;  // == st % NB
+        const int b0 = b_lo + kStageBlocks * st;
+        const bool more = st + kAhead < n_stages;
+        if (more) fetch(b0 + kAhead * kStageBlocks, (B + kAhead) % NB);
+#pragma unroll
+        for (int sb = 0; sb < kStageBlocks; sb += 2)
+            if (kStageBlocks * st + sb < w_blocks) compute(B, sb, b0 + sb);
+        // stage st+1's loads must have landed: all but those of later stages
+        if (kAhead > 1 && more) __builtin_amdgcn_s_waitcnt(0x0F70 | (kStageLoads * (kAhead - 1)));
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        raw_barrier();
+    };
+    for (int st = 0; st < n_stages; st += NB) {
+        stage(st, std::integral_constant<int, 0>{});
+        if (st + 1 < n_stages) stage(st + 1, std::integral_constant<int, 1>{});
+        if constexpr (NB == 3)
+            if (st + 2 < n_stages) stage(st + 2, std::integral_constant<int, 2 % NB>{});
+    }
+    if (rows_w <= 0) return;
+
+    // (m, l) of every row to LDS; lane l then writes rows 4r + c of each tile
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        float l = l_run[rt];
+        l += shfl_xor(l, 16);
+        l += shfl_xor(l, 32);
+        if (r == 0) {
+            ml_lds[w][rt][n][0] = m_run[rt];
+            ml_lds[w][rt][n][1] = l;
+        }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int head = head0 + rt;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int t = 4 * r + c;  // row of the tile
+            if (t >= rows_w) continue;
+            const int tok = tok0 + t;
+            const float m = ml_lds[w][rt][t][0], l = ml_lds[w][rt][t][1];
+            if (direct) {
+                const size_t qrow = static_cast<size_t>(min(row0 + tok, a.num_q_rows - 1));
+                const float inv = 1.0f / l;
+                _Float16 *orow = reinterpret_cast<_Float16 *>(a.out + (qrow * a.num_q_heads + head) * kHeadDim);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) orow[16 * j + n] = static_cast<_Float16>(oacc[rt][j][c] * inv);  // dim 16j + n
+            } else {
+                const int64_t slot64 = static_cast<int64_t>(base_slot) + static_cast<int64_t>(tok) * np + piece;
+                const size_t slot = static_cast<size_t>(min<int64_t>(slot64, a.num_slots - 1));
+                const size_t rec = slot * a.num_q_heads + head;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a.o_part[rec * kHeadDim + 16 * j + n] = oacc[rt][j][c];
+                if (n == 0) *reinterpret_cast<float2 *>(a.ml_part + rec * 2) = make_float2(m, l);
+            }
+        }
+    }
 }
 
-// A mixed step's decode pieces and prefill pieces in one launch, so that the
-// bandwidth-bound decode work-groups and the matrix-core-bound prefill
-// work-groups share the compute units instead of running one after the
-// other.  Work-groups [0, decode items x Hkv) are decode pieces, the rest
-// prefill pieces.
-// As prefill_kernel, WGS work-groups per CU; at 3 the decode pieces keep two
-// blocks in flight instead of three (158 VGPRs for F16 on their own).
+
+// FP8 pools: codes are widened on their way into LDS, so the copy goes
+// through registers, one stage ahead, three work-groups per CU (160 VGPRs).
 template <bool FP8, int WGS>
-__global__ __launch_bounds__(256, WGS) void mixed_kernel(DecodeArgs a) {
-    static_assert(WGS == 2 || WGS == 3, "two or three work-groups per CU");
+__global__ __launch_bounds__(256, WGS) void prefill_kernel(DecodeArgs a) {
+    static_assert(FP8 && WGS == 3, "F16 pools take prefill_dma_kernel");
+    prefill_body<FP8, 1>(a, blockIdx.x);
+}
+
+// F16 pools: the copy goes straight to LDS, NB - 1 stages ahead; WGS
+// work-groups per CU.  launch_prefill chooses.
+template <int NB, int WGS>
+__global__ __launch_bounds__(256, WGS) void prefill_dma_kernel(DecodeArgs a) {
+    prefill_body_dma<NB>(a, blockIdx.x);
+}
+
+// A mixed step's decode and prefill pieces in one launch, three work-groups
+// per CU: the decode pieces keep two blocks in flight instead of three (158
+// VGPRs on their own), the F16 prefill pieces copy straight to LDS one stage
+// ahead, the FP8 ones through registers.
+template <bool FP8>
+__global__ __launch_bounds__(256, 3) void mixed_kernel(DecodeArgs a) {
     const uint32_t nd = static_cast<uint32_t>(a.num_items) * static_cast<uint32_t>(a.num_kv_heads);
     if (blockIdx.x < nd)
-        decode_partial_body<WGS == 3 ? 2 : (FP8 ? PA_DECODE_NBUF_FP8 : PA_DECODE_NBUF), FP8>(a, blockIdx.x, 0, 0);
+        decode_partial_body<2, FP8>(a, blockIdx.x, 0, 0);
+    else if constexpr (FP8)
+        prefill_body<true, 1>(a, blockIdx.x - nd);
     else
-        prefill_body<FP8, WGS == 3 ? 1 : 2>(a, blockIdx.x - nd);
+        prefill_body_dma<2>(a, blockIdx.x - nd);
 }
 
 }  // namespace
 
 namespace {
-// Three prefill work-groups per CU (the copy one stage ahead) pay when the
-// launch holds more prefill work-groups than one round of two per CU: the
-// extra slot keeps a CU busy while its tiles finish unevenly.  Measured on
-// MI355X (256 CUs), F16 per layer: a 16,384-token chunk at position 16,384
-// (with 32 decodes beside it) 7.71 against 8.42 ms, the chunk alone 7.61
-// against 8.33 ms; a 2016-token chunk (504 work-groups) 131.8 against
-// 127.3 us alone and 210 against 204 us with 32 decodes.  FP8 pools gain or
-// tie in every case (their bodies fit 168 VGPRs without spilling): 155
-// against 164 us per layer for the 2016-token step.
+// One round: every prefill work-group of the launch fits two per CU.
+// Measured on MI355X (256 CUs), F16 pools, per layer:
+//  - a 2016-token chunk at position 2016 (504 work-groups, one round): three
+//    LDS buffers at two work-groups per CU 117.3-118.2 us, one-stage-ahead
+//    copies at three per CU 122.3-122.5 us, register staging two stages
+//    ahead at two per CU 121.6-122.5 us;
+//  - a 16,384-token chunk at position 16,352 (4,088 work-groups): two LDS
+//    buffers at three per CU 6.85 ms, three buffers 6.90 ms, register staging
+//    at three per CU 7.07 ms.  Past one round the third slot keeps a CU busy
+//    while its tiles finish unevenly.
 constexpr int64_t kPrefillRoundGroups = 2 * 256;
-bool prefill_three_per_cu(const DecodeArgs &a) {
-    return a.elem_bytes == 1 || static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads > kPrefillRoundGroups;
+bool prefill_one_round(const DecodeArgs &a) {
+    return static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads <= kPrefillRoundGroups;
 }
 }  // namespace
 
+// Mixed steps: F16 16,384-token step 55.7 against 57.0 ms with register
+// staging; the 2016-token step 6.35-6.36 against 6.39-6.40 ms.
 hipError_t launch_mixed(const DecodeArgs &a, hipStream_t stream) {
     const uint32_t groups =
         static_cast<uint32_t>((static_cast<int64_t>(a.num_items) + a.num_prefill_items) * a.num_kv_heads);
     if (a.elem_bytes == 1)
-        hipLaunchKernelGGL((mixed_kernel<true, 3>), dim3(groups), dim3(256), 0, stream, a);
-    else if (prefill_three_per_cu(a))
-        hipLaunchKernelGGL((mixed_kernel<false, 3>), dim3(groups), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(mixed_kernel<true>, dim3(groups), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((mixed_kernel<false, 2>), dim3(groups), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(mixed_kernel<false>, dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1411,10 +1747,10 @@ hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
     const uint32_t groups = static_cast<uint32_t>(static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads);
     if (a.elem_bytes == 1)
         hipLaunchKernelGGL((prefill_kernel<true, 3>), dim3(groups), dim3(256), 0, stream, a);
-    else if (prefill_three_per_cu(a))
-        hipLaunchKernelGGL((prefill_kernel<false, 3>), dim3(groups), dim3(256), 0, stream, a);
+    else if (prefill_one_round(a))
+        hipLaunchKernelGGL((prefill_dma_kernel<3, 2>), dim3(groups), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<false, 2>), dim3(groups), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((prefill_dma_kernel<2, 3>), dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
