@@ -716,7 +716,8 @@ def bench_mixed(args, w, dev):
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": read_counter_file(PREFILL_COUNTERS[args.config])
                      if args.config in PREFILL_COUNTERS and pf_info.num_merges == 0 and not fp8 else None,
-                     "kernel": "prefill_kernel" + (" + decode_merge_planned_kernel" if pf_info.num_merges else ""),
+                     "kernel": ("prefill_kernel" if fp8 else "prefill_dma_kernel")
+                     + (" + decode_merge_planned_kernel" if pf_info.num_merges else ""),
                      "flops_per_layer": pf_flops, "mean_layer_us": round(pf_us, 3)},
         "decode_rows_us_per_layer": round(dec_us, 3),
         "decode_rows_GBps": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),
