@@ -89,6 +89,17 @@ def read_counter_file(path):
         return None
 
 
+def write_blocks(pool, layer, ids, k, v, dev):
+    """Stores whole physical blocks (host F16 [n, B, Hkv, d]) through pa_write_kv
+    with the caller-built slot list of those blocks."""
+    import torch
+    import workloads
+
+    rows = lambda x: torch.from_numpy(x.reshape(-1, pool.num_kv_heads, pool.head_dim)).to(dev)
+    pool.write(layer, rows(k), rows(v),
+               torch.from_numpy(workloads.block_slot_mapping(ids, pool.block_size)).to(dev))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,8 +176,7 @@ def main():
         ids, k, v = w.kv_blocks(layer)
         if fp8:
             pool.set_scales(layer, FP8_SCALE, FP8_SCALE)
-        pool.write_blocks(layer, torch.from_numpy(ids).to(dev), torch.from_numpy(k).to(dev),
-                          torch.from_numpy(v).to(dev))
+        write_blocks(pool, layer, ids, k, v, dev)
         q = w.q(layer)
         tables = w.tables(layer)
         q_dev.append(torch.from_numpy(q).to(dev))
@@ -225,7 +235,8 @@ def main():
     f_run = lib.pa_decode_run
     # a cascade plan whose newest tokens lie in shared blocks cannot append them
     append = info.shared_newest == 0
-    run_args = [(h, L, ctypes.byref(info), plan_dev.data_ptr(), q_dev[L].data_ptr(),
+    plan_dev_bytes = plan_dev.numel() * 4
+    run_args = [(h, L, ctypes.byref(info), plan_dev.data_ptr(), plan_dev_bytes, q_dev[L].data_ptr(),
                  knew[L].data_ptr() if append else None, vnew[L].data_ptr() if append else None,
                  outs[L].data_ptr(),
                  tables_dev[L].data_ptr(), width, scale, ws.data_ptr(), ws_bytes, sptr)
@@ -420,7 +431,7 @@ def main():
                 kc = oracle.quantize_e4m3(kc, FP8_SCALE)
                 vc = oracle.quantize_e4m3(vc, FP8_SCALE)
             # the GPU result of this layer (read-only decode of the staged pool)
-            rc = f_run(h, layer, ctypes.byref(info), plan_dev.data_ptr(), q_dev[layer].data_ptr(),
+            rc = f_run(h, layer, ctypes.byref(info), plan_dev.data_ptr(), plan_dev_bytes, q_dev[layer].data_ptr(),
                        None, None, outs[layer].data_ptr(), tables_dev[layer].data_ptr(), width,
                        scale, ws.data_ptr(), ws_bytes, sptr)
             assert rc == 0, rc
@@ -449,6 +460,28 @@ def main():
                "sample": f"{done_seqs} (sequence, layer) rows of the same step over layers "
                          f"0..{layer - 1} ({done_bytes} B of K/V), fp64, {cpu_s:.1f} s of oracle time",
                "tokens_per_s_equiv": round(done_bytes / (kv_bytes_step / w.batch) / cpu_s, 4)}
+        # the same oracle on one thread, over the first sequences of layer 0
+        q, tables, ids, k, v = host0
+        kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, w.ctx_lens, B)
+        if fp8:
+            kc = oracle.quantize_e4m3(kc, FP8_SCALE)
+            vc = oracle.quantize_e4m3(vc, FP8_SCALE)
+        one_s, one_bytes, one_seqs = 0.0, 0, 0
+        while one_seqs < w.batch and one_s < args.cpu_seconds / 4:
+            seqs = np.array([one_seqs])
+            t_cpu = time.perf_counter()
+            if fp8:
+                oracle.decode_e4m3(q[seqs], kc, vc, t2[seqs], w.ctx_lens[seqs], w.scale, B, FP8_SCALE,
+                                   FP8_SCALE, threads=1)
+            else:
+                oracle.decode(q[seqs], kc, vc, t2[seqs], w.ctx_lens[seqs], w.scale, B, threads=1)
+            one_s += time.perf_counter() - t_cpu
+            one_bytes += int(w.ctx_lens[one_seqs]) * HKV * D * 2 * eb
+            one_seqs += 1
+        del kc, vc
+        cpu["one_thread"] = {"value": round(one_bytes / one_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+                             "sample": f"{one_seqs} sequences of layer 0 ({one_bytes} B of K/V), fp64, "
+                                       f"{one_s:.1f} s"}
         parity = {"rows": done_seqs, "max_abs_err": max(errs),
                   "rel_l2": (sum(diffs) / sum(refs)) ** 0.5}
         log(f"oracle: {cpu['value']} GB/s on {threads} threads; parity {parity}")
@@ -498,6 +531,7 @@ def main():
         "kernel_pct_of_gather_probe": round(100 * achieved / gather, 2) if gather else None,
         "cpu_baseline": cpu,
         "parity_sample": parity,
+        "pages_context": roofline.pages_context(),
     }
     print(json.dumps(line), flush=True)
     pool.close()
@@ -534,8 +568,7 @@ def bench_mixed(args, w, dev):
         ids, k, v = w.kv_blocks(layer)
         if fp8:
             pool.set_scales(layer, FP8_SCALE, FP8_SCALE)
-        pool.write_blocks(layer, torch.from_numpy(ids).to(dev), torch.from_numpy(k).to(dev),
-                          torch.from_numpy(v).to(dev))
+        write_blocks(pool, layer, ids, k, v, dev)
         q = w.q_rows(total_q, layer)
         tables = w.tables(layer)
         q_dev.append(torch.from_numpy(q).to(dev))
@@ -578,7 +611,8 @@ def bench_mixed(args, w, dev):
             raise RuntimeError(f"pa_prefill_plan failed: {rc}")
         plan_dev.copy_(buf, non_blocking=True)
         for L in range(w.layers):
-            rc = lib.pa_prefill_run(h, L, ctypes.byref(info), plan_dev.data_ptr(), q_dev[L].data_ptr(),
+            rc = lib.pa_prefill_run(h, L, ctypes.byref(info), plan_dev.data_ptr(), plan_dev.numel() * 4,
+                                    q_dev[L].data_ptr(),
                                     outs[L].data_ptr(), tables_dev[L].data_ptr(), width, scale,
                                     ws.data_ptr(), info.workspace_bytes, sptr)
             if rc != 0:
@@ -623,7 +657,8 @@ def bench_mixed(args, w, dev):
 
         def go():
             for L in range(w.layers):
-                rc = lib.pa_prefill_run(h, L, ctypes.byref(inf), pd.data_ptr(), qp[L].data_ptr(), op[L].data_ptr(),
+                rc = lib.pa_prefill_run(h, L, ctypes.byref(inf), pd.data_ptr(), pd.numel() * 4, qp[L].data_ptr(),
+                                        op[L].data_ptr(),
                                         tp[L].data_ptr(), width, scale, wsp.data_ptr(), inf.workspace_bytes, sptr)
                 assert rc == 0, rc
         go()

@@ -42,8 +42,9 @@
  *
  * Geometry supported by this build: head_dim 128, block_size 16, F16 or FP8
  * (E4M3) keys and values, F16 queries and outputs, num_q_heads = 4 *
- * num_kv_heads, and contexts (max_context_len, host lengths) of at most 2^30
- * tokens.  Other values return PA_ERR_UNSUPPORTED.  Every schedule
+ * num_kv_heads, contexts (max_context_len, host lengths) of at most 2^30
+ * tokens and block tables at most 2^26 entries wide.  Other values return
+ * PA_ERR_UNSUPPORTED.  Every schedule
  * (decode, shared-prefix cascade, chunked prefill / mixed) runs on both pool
  * types.
  */
@@ -178,9 +179,9 @@ pa_status pa_decode(pa_pool *pool, int32_t layer, const void *q_dev, void *out_d
  * attention then runs over positions [0, ctx) exactly as pa_decode does.
  * The result equals pa_write_kv of those slots followed by pa_decode, in one
  * launch fewer: the new values are used from registers, and the pool write
- * only serves later calls.  The pages describe the attention kernel as doing
- * both: it "writes new keys and values to the right places and reads a
- * request's history through its block table" ("vLLM Architecture and
+ * only serves later calls.  On the pages the attention kernel does both jobs
+ * in one step: it stores the step's keys and values in their slots and reads
+ * the earlier ones through the block table ("vLLM Architecture and
  * Installation", Example 3).
  *   k_new_dev, v_new_dev: F16 [batch][num_kv_heads][head_dim], 16-byte aligned
  * Other arguments as pa_decode.  The newest position's block must not be
@@ -268,15 +269,22 @@ pa_status pa_cascade_plan(const pa_pool *pool, const int32_t *context_lens_host,
  * append the newest token as pa_append_decode does (rejected with
  * PA_ERR_INVALID_ARG when info->shared_newest > 0: that token would land in
  * a shared block).  q, out, tables, scale and
- * stream as pa_decode; the context lengths come from the plan, whose device
- * copy plan_dev must stay unchanged until the work completes.  A damaged plan
- * cannot make the kernels access memory outside the given buffers, but its
- * results are unspecified. */
+ * stream as pa_decode; the context lengths come from the plan.
+ *   info:           the pa_plan_info the plan builder filled in; its counts
+ *                   must give exactly info->plan_bytes (else
+ *                   PA_ERR_INVALID_ARG)
+ *   plan_dev:       16-byte aligned device copy of the plan's bytes; it must
+ *                   stay unchanged until the work completes
+ *   plan_dev_bytes: size of the buffer at plan_dev; PA_ERR_WORKSPACE when it
+ *                   is smaller than info->plan_bytes
+ * A plan whose device bytes were damaged cannot make the kernels access
+ * memory outside the given buffers (every entry is clamped), but its results
+ * are unspecified. */
 pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info,
-                        const void *plan_dev, const void *q_dev, const void *k_new_dev,
-                        const void *v_new_dev, void *out_dev, const int32_t *block_tables_dev,
-                        int32_t max_blocks_per_seq, float scale, void *workspace_dev,
-                        size_t workspace_bytes, hipStream_t stream);
+                        const void *plan_dev, size_t plan_dev_bytes, const void *q_dev,
+                        const void *k_new_dev, const void *v_new_dev, void *out_dev,
+                        const int32_t *block_tables_dev, int32_t max_blocks_per_seq, float scale,
+                        void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
 
 /* ---- Chunked prefill / mixed step -------------------------------------
  * A step gives every scheduled request some number of new tokens under a
@@ -306,11 +314,13 @@ pa_status pa_prefill_plan(const pa_pool *pool, const int32_t *query_start_host,
 
 /* One layer of a chunked-prefill / mixed step on a pa_prefill_plan schedule.
  * q_dev and out_dev hold info->num_q_rows packed rows (F16, for F16 and FP8
- * pools alike).  Tables, scale, workspace and stream as pa_decode_run. */
+ * pools alike).  The plan (info, plan_dev, plan_dev_bytes), tables, scale,
+ * workspace and stream as pa_decode_run. */
 pa_status pa_prefill_run(pa_pool *pool, int32_t layer, const pa_plan_info *info,
-                         const void *plan_dev, const void *q_dev, void *out_dev,
-                         const int32_t *block_tables_dev, int32_t max_blocks_per_seq, float scale,
-                         void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+                         const void *plan_dev, size_t plan_dev_bytes, const void *q_dev,
+                         void *out_dev, const int32_t *block_tables_dev, int32_t max_blocks_per_seq,
+                         float scale, void *workspace_dev, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* Static English text for a status code. */
 const char *pa_status_string(pa_status status);

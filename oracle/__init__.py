@@ -21,9 +21,10 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        lib = ctypes.CDLL(_build.LIB)
+        path = os.environ.get("PA_ORACLE_LIB") or _build.LIB
+        if os.path.abspath(path) == _build.DEFAULT_LIB and not _build.is_current(path):
+            _build.build(lib=path)   # missing, or built from other sources
+        lib = ctypes.CDLL(path)
         lib.pa_oracle_f16_to_f64.restype = ctypes.c_double
         lib.pa_oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.pa_oracle_slot.restype = ctypes.c_int64
@@ -163,15 +164,18 @@ def relabelled_cache(ids, k_blocks, v_blocks, tables, ctx_lens, block_size):
     change the result (a pinned invariance).  Table entries past a sequence's
     context are left as 0.
     """
-    ids = np.asarray(ids)
+    ids = np.asarray(ids, dtype=np.int64)
     tables = np.asarray(tables)
     held = -(-np.asarray(ctx_lens, dtype=np.int64) // block_size)
+    order = np.argsort(ids, kind="stable")
+    sorted_ids = ids[order]
     out_tables = np.zeros_like(tables, dtype=np.int32)
     for s in range(tables.shape[0]):
         row = tables[s, :held[s]]
-        pos = np.searchsorted(ids, row)
-        assert np.all(ids[pos] == row)
-        out_tables[s, :held[s]] = pos
+        pos = np.minimum(np.searchsorted(sorted_ids, row), max(len(ids) - 1, 0))
+        if row.size and not np.all(sorted_ids[pos] == row):
+            raise ValueError(f"sequence {s} names a block that is not among ids")
+        out_tables[s, :held[s]] = order[pos]
     n, b, hkv, d = k_blocks.shape
     return k_blocks.reshape(n * b, hkv, d), v_blocks.reshape(n * b, hkv, d), out_tables
 

@@ -54,6 +54,14 @@
 #include <omp.h>
 #endif
 
+#ifndef PA_ORACLE_SOURCE_SHA256
+#define PA_ORACLE_SOURCE_SHA256 "unknown"
+#endif
+/* sha256 of this file and the build flags (oracle/build.py); the loader reads
+ * it from the library file and rebuilds a library made from other sources. */
+__attribute__((used, visibility("default"))) const char pa_oracle_build_source[] =
+    "pa-oracle-source-sha256:" PA_ORACLE_SOURCE_SHA256;
+
 /* IEEE 754 binary16 -> double, written from the format's definition:
  * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
  *   e == 0      : subnormal, value = frac * 2^-24

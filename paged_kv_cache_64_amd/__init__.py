@@ -4,7 +4,8 @@ The functions below carry the C entry points' names and only marshal
 arguments: torch tensors supply device pointers, and the current torch stream
 supplies the HIP stream.  Every step of the computation runs in the library's
 HIP kernels; there is no fallback.  If libpa.so has not been built, importing
-works but every call raises RuntimeError.
+works but every call raises RuntimeError; so does a libpa.so built from
+sources other than the ones beside it (build.py embeds their hash).
 """
 from __future__ import annotations
 
@@ -64,8 +65,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+    from . import build as _build
+
+    _build.check_current(path)
     lib = ctypes.CDLL(path)
     lib.pa_pool_bytes.restype = ctypes.c_size_t
     lib.pa_pool_bytes.argtypes = [ctypes.POINTER(PoolDesc)]
@@ -99,11 +101,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_prefill_plan.restype = _I
     lib.pa_prefill_plan.argtypes = [_P, _P, _P, _I, _I, _P, ctypes.c_size_t, ctypes.POINTER(PlanInfo)]
     lib.pa_prefill_run.restype = _I
-    lib.pa_prefill_run.argtypes = [_P, _I, ctypes.POINTER(PlanInfo), _P, _P, _P, _P, _I,
-                                   ctypes.c_float, _P, ctypes.c_size_t, _P]
+    lib.pa_prefill_run.argtypes = [_P, _I, ctypes.POINTER(PlanInfo), _P, ctypes.c_size_t, _P, _P,
+                                   _P, _I, ctypes.c_float, _P, ctypes.c_size_t, _P]
     lib.pa_decode_run.restype = _I
-    lib.pa_decode_run.argtypes = [_P, _I, ctypes.POINTER(PlanInfo), _P, _P, _P, _P, _P, _P, _I,
-                                  ctypes.c_float, _P, ctypes.c_size_t, _P]
+    lib.pa_decode_run.argtypes = [_P, _I, ctypes.POINTER(PlanInfo), _P, ctypes.c_size_t, _P, _P,
+                                  _P, _P, _P, _I, ctypes.c_float, _P, ctypes.c_size_t, _P]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [_I]
     _lib = lib
@@ -261,10 +263,19 @@ def pa_cascade_plan(handle, context_lens_host, prefix_group_host, prefix_len_hos
     return info, plan
 
 
+def _nbytes(t, nbytes):
+    if nbytes is not None:
+        return int(nbytes)
+    return t.numel() * t.element_size() if isinstance(t, torch.Tensor) else 0
+
+
 def pa_decode_run(handle, layer, info, plan_dev, q, k_new, v_new, out, block_tables,
-                  max_blocks_per_seq, scale, workspace, workspace_bytes, stream=None):
-    _check(load_library().pa_decode_run(handle, layer, ctypes.byref(info), _ptr(plan_dev), _ptr(q),
-                                        _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(block_tables),
+                  max_blocks_per_seq, scale, workspace, workspace_bytes, stream=None,
+                  plan_dev_bytes=None):
+    """plan_dev_bytes defaults to the size of plan_dev when it is a tensor."""
+    _check(load_library().pa_decode_run(handle, layer, ctypes.byref(info), _ptr(plan_dev),
+                                        _nbytes(plan_dev, plan_dev_bytes), _ptr(q), _ptr(k_new),
+                                        _ptr(v_new), _ptr(out), _ptr(block_tables),
                                         max_blocks_per_seq, float(scale), _ptr(workspace),
                                         int(workspace_bytes), _stream(stream)), "pa_decode_run")
 
@@ -289,11 +300,13 @@ def pa_prefill_plan(handle, query_start_host, seq_lens_host, num_q_heads):
 
 
 def pa_prefill_run(handle, layer, info, plan_dev, q, out, block_tables, max_blocks_per_seq, scale,
-                   workspace, workspace_bytes, stream=None):
-    _check(load_library().pa_prefill_run(handle, layer, ctypes.byref(info), _ptr(plan_dev), _ptr(q),
-                                         _ptr(out), _ptr(block_tables), max_blocks_per_seq,
-                                         float(scale), _ptr(workspace), int(workspace_bytes),
-                                         _stream(stream)), "pa_prefill_run")
+                   workspace, workspace_bytes, stream=None, plan_dev_bytes=None):
+    """plan_dev_bytes defaults to the size of plan_dev when it is a tensor."""
+    _check(load_library().pa_prefill_run(handle, layer, ctypes.byref(info), _ptr(plan_dev),
+                                         _nbytes(plan_dev, plan_dev_bytes), _ptr(q), _ptr(out),
+                                         _ptr(block_tables), max_blocks_per_seq, float(scale),
+                                         _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "pa_prefill_run")
 
 
 class Plan:
@@ -373,17 +386,6 @@ class Pool:
         _expect(v_new, torch.float16, shape, "v_new")
         _expect(slot_mapping, torch.int32, (n,), "slot_mapping")
         pa_write_kv(self.handle, layer, k_new, v_new, slot_mapping, n, stream)
-
-    def write_blocks(self, layer, block_ids, k_blocks, v_blocks, stream=None):
-        """Writes whole physical blocks: k_blocks[i] ([block_size, Hkv, d]) is
-        stored in block block_ids[i], i.e. slots block_ids[i]*B + 0..B-1."""
-        bs = self.block_size
-        ids = torch.as_tensor(block_ids, dtype=torch.int64, device=k_blocks.device)
-        slots = (ids[:, None] * bs + torch.arange(bs, device=ids.device)[None, :]).reshape(-1)
-        n = slots.shape[0]
-        self.write(layer, k_blocks.reshape(n, self.num_kv_heads, self.head_dim).contiguous(),
-                   v_blocks.reshape(n, self.num_kv_heads, self.head_dim).contiguous(),
-                   slots.to(torch.int32).contiguous(), stream)
 
     def plan(self, context_lens_host, num_q_heads=None, prefix_group=None, prefix_len=None):
         return Plan(self.handle, context_lens_host, num_q_heads or 4 * self.num_kv_heads,

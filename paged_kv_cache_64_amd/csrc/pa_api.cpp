@@ -13,6 +13,15 @@
 
 #include "pa_internal.h"
 
+#ifndef PA_SOURCE_SHA256
+#define PA_SOURCE_SHA256 "unknown"
+#endif
+// A sha256 of the sources and flags this library was built from (computed by
+// the build script); the Python loader reads it from the file to refuse a
+// stale build.  Nothing calls it.
+extern "C" __attribute__((used, visibility("default"))) const char pa_build_source[] =
+    "pa-source-sha256:" PA_SOURCE_SHA256;
+
 struct pa_pool {
     pa_pool_desc desc;
     void *k;
@@ -113,7 +122,7 @@ pa_status check_decode_shape(const pa_pool *pool, int32_t batch, int32_t num_q_h
     if (static_cast<int64_t>(max_ctx) > static_cast<int64_t>(max_blocks) * pool->desc.block_size)
         return PA_ERR_INVALID_ARG;
     if (num_q_heads != kGroup * pool->desc.num_kv_heads) return PA_ERR_UNSUPPORTED;
-    if (max_ctx > pa::kMaxContextTokens) return PA_ERR_UNSUPPORTED;
+    if (max_ctx > pa::kMaxContextTokens || max_blocks > pa::kMaxContextTokens / kBlockSize) return PA_ERR_UNSUPPORTED;
     if (batch > 65535 || pool->desc.num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
@@ -225,13 +234,8 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
                 total_blocks += static_cast<int64_t>(prefix_len[gi] / kBlockSize) *
                                 ((members[gi].size() + pa::kMaxMembers - 1) / pa::kMaxMembers);
         const int64_t items_target = std::max<int64_t>(1, kTargetWorkGroups / pool->desc.num_kv_heads);
-        int64_t piece = std::min<int64_t>(kMaxSplitTokens / kBlockSize,
-                                          std::max<int64_t>(kMinPieceBlocks, (total_blocks + items_target - 1) / items_target));
-        if (const char *env = std::getenv("PA_DECODE_PIECE_BLOCKS")) {  // tuning override
-            char *end = nullptr;
-            const long v = std::strtol(env, &end, 10);
-            if (end != env && v >= pa::kWaves && v <= kMaxSplitTokens / kBlockSize) piece = v;
-        }
+        const int64_t piece = std::min<int64_t>(
+            kMaxSplitTokens / kBlockSize, std::max<int64_t>(kMinPieceBlocks, (total_blocks + items_target - 1) / items_target));
         auto cut = [](int64_t nb, int64_t maxp) { return nb == 0 ? int64_t{0} : (nb + maxp - 1) / maxp; };
 
         // records: each member owns a contiguous run (prefix pieces, then its
@@ -432,13 +436,8 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
             int32_t f[pa::kPrefillItemInts];
         };
         std::vector<PrefillItem> pitems;
-        int64_t ppiece = std::min<int64_t>(pa::kMaxPrefillPieceBlocks,
-                                           std::max<int64_t>(8, cut(tile_blocks, items_target)));
-        if (const char *env = std::getenv("PA_PREFILL_PIECE_BLOCKS")) {  // tuning override
-            char *end = nullptr;
-            const long v = std::strtol(env, &end, 10);
-            if (end != env && v >= 2 && v <= pa::kMaxPrefillPieceBlocks) ppiece = v;
-        }
+        const int64_t ppiece = std::min<int64_t>(pa::kMaxPrefillPieceBlocks,
+                                                 std::max<int64_t>(8, cut(tile_blocks, items_target)));
         for (int32_t s = 0; s < batch; ++s) {
             const int64_t q_len = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
             if (q_len < 2) continue;
@@ -534,8 +533,8 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
 // One layer on a serialised schedule (pa_decode_plan, pa_cascade_plan or
 // pa_prefill_plan): decode pieces, shared-prefix pieces, prefill pieces, then
 // the merges.
-pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const void *plan_dev, const void *q_dev,
-                   const void *k_new_dev, const void *v_new_dev, void *out_dev, const int32_t *block_tables_dev,
+pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const void *plan_dev,
+                   size_t plan_dev_bytes, const void *q_dev, const void *k_new_dev, const void *v_new_dev, void *out_dev, const int32_t *block_tables_dev,
                    int32_t max_blocks_per_seq, float scale, void *workspace_dev, size_t workspace_bytes,
                    hipStream_t stream) {
     if (!pool || !info || layer < 0 || layer >= pool->desc.num_layers) return PA_ERR_INVALID_ARG;
@@ -543,8 +542,18 @@ pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const
     if (info->num_items < 0 || info->num_prefix_items < 0 || info->num_prefill_items < 0 || info->num_merges < 0 ||
         info->num_slots < 0 || info->num_members < 0 || info->num_q_rows < 0)
         return PA_ERR_INVALID_ARG;
+    // The kernels index the plan's sections by these counts, so the plan must
+    // be exactly the serialised size they imply and fit the device buffer.
+    const uint64_t plan_ints = static_cast<uint64_t>(pa::kPlanHeader) +
+                               static_cast<uint64_t>(pa::kItemInts) * info->num_items +
+                               static_cast<uint64_t>(pa::kMergeInts) * info->num_merges +
+                               static_cast<uint64_t>(pa::kPrefixItemInts) * info->num_prefix_items +
+                               static_cast<uint64_t>(pa::kMemberInts) * info->num_members +
+                               static_cast<uint64_t>(pa::kPrefillItemInts) * info->num_prefill_items;
+    if (info->plan_bytes != plan_ints * sizeof(int32_t)) return PA_ERR_INVALID_ARG;
     if (info->batch == 0 || (info->num_items == 0 && info->num_prefix_items == 0 && info->num_prefill_items == 0))
         return PA_OK;
+    if (plan_dev_bytes < info->plan_bytes) return PA_ERR_WORKSPACE;
     if (info->num_q_rows == 0) return PA_ERR_INVALID_ARG;
     if (k_new_dev && info->num_q_rows != info->batch) return PA_ERR_INVALID_ARG;
     if (!plan_dev || !q_dev || !out_dev || !aligned(plan_dev, 16) || !aligned(q_dev, 16) || !aligned(out_dev, 16))
@@ -556,7 +565,8 @@ pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const
     if (max_blocks_per_seq < 0 ||
         static_cast<int64_t>(info->max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlockSize)
         return PA_ERR_INVALID_ARG;
-    if (info->max_context_len > pa::kMaxContextTokens) return PA_ERR_UNSUPPORTED;
+    if (info->max_context_len > pa::kMaxContextTokens || max_blocks_per_seq > pa::kMaxContextTokens / kBlockSize)
+        return PA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
     size_t o_bytes = 0;
     const size_t need = planned_workspace(info->num_slots, info->num_q_heads, &o_bytes);
@@ -632,12 +642,12 @@ pa_status pa_cascade_plan(const pa_pool *pool, const int32_t *context_lens_host,
 }
 
 pa_status pa_decode_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, const void *plan_dev,
-                        const void *q_dev, const void *k_new_dev, const void *v_new_dev, void *out_dev,
-                        const int32_t *block_tables_dev, int32_t max_blocks_per_seq, float scale,
+                        size_t plan_dev_bytes, const void *q_dev, const void *k_new_dev, const void *v_new_dev,
+                        void *out_dev, const int32_t *block_tables_dev, int32_t max_blocks_per_seq, float scale,
                         void *workspace_dev, size_t workspace_bytes, hipStream_t stream) {
     if (info && info->num_prefill_items != 0) return PA_ERR_INVALID_ARG;  // a pa_prefill_plan schedule
-    return run_plan(pool, layer, info, plan_dev, q_dev, k_new_dev, v_new_dev, out_dev, block_tables_dev,
-                    max_blocks_per_seq, scale, workspace_dev, workspace_bytes, stream);
+    return run_plan(pool, layer, info, plan_dev, plan_dev_bytes, q_dev, k_new_dev, v_new_dev, out_dev,
+                    block_tables_dev, max_blocks_per_seq, scale, workspace_dev, workspace_bytes, stream);
 }
 
 pa_status pa_prefill_plan(const pa_pool *pool, const int32_t *query_start_host, const int32_t *seq_lens_host,
@@ -648,12 +658,12 @@ pa_status pa_prefill_plan(const pa_pool *pool, const int32_t *query_start_host, 
 }
 
 pa_status pa_prefill_run(pa_pool *pool, int32_t layer, const pa_plan_info *info, const void *plan_dev,
-                         const void *q_dev, void *out_dev, const int32_t *block_tables_dev,
+                         size_t plan_dev_bytes, const void *q_dev, void *out_dev, const int32_t *block_tables_dev,
                          int32_t max_blocks_per_seq, float scale, void *workspace_dev, size_t workspace_bytes,
                          hipStream_t stream) {
     if (info && (info->num_prefix_items != 0 || info->num_members != 0)) return PA_ERR_INVALID_ARG;
-    return run_plan(pool, layer, info, plan_dev, q_dev, nullptr, nullptr, out_dev, block_tables_dev,
-                    max_blocks_per_seq, scale, workspace_dev, workspace_bytes, stream);
+    return run_plan(pool, layer, info, plan_dev, plan_dev_bytes, q_dev, nullptr, nullptr, out_dev,
+                    block_tables_dev, max_blocks_per_seq, scale, workspace_dev, workspace_bytes, stream);
 }
 
 size_t pa_pool_bytes(const pa_pool_desc *desc) {

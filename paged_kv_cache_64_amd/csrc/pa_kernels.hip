@@ -289,7 +289,11 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
         return;
     }
     const int b_begin = t_begin / kBlockSize;
-    const int b_end = (t_end + kBlockSize - 1) / kBlockSize;
+    // A piece never spans more than kMaxSplitTokens / kBlockSize blocks (64 per
+    // wave, the size of a wave's row of tbl_lds); a damaged plan entry is cut
+    // there too.
+    const int b_end = min((t_end + kBlockSize - 1) / kBlockSize, b_begin + kMaxSplitTokens / kBlockSize);
+    t_end = min(t_end, b_end * kBlockSize);
     const int per_wave = (b_end - b_begin + kWaves - 1) / kWaves;
     const int wb_begin = min(b_end, b_begin + w * per_wave);
     const int wb_end = min(b_end, wb_begin + per_wave);

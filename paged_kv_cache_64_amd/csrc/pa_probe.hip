@@ -12,6 +12,13 @@
 
 #include <cstdint>
 
+#ifndef PA_SOURCE_SHA256
+#define PA_SOURCE_SHA256 "unknown"
+#endif
+// sha256 of this file and the build flags, read from the file by the loader
+extern "C" __attribute__((used, visibility("default"))) const char pa_probe_build_source[] =
+    "pa-source-sha256:" PA_SOURCE_SHA256;
+
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

@@ -2,6 +2,7 @@
 runs), in the form kept under profiles/.
 
     python -m paged_kv_cache_64_amd.prof_summary trace DIR --title T --command C [--note N ...]
+        [--skip KERNEL=N ...]
     python -m paged_kv_cache_64_amd.prof_summary counters --kernel K --fetch DIR --write DIR
         --cal-fetch DIR --cal-write DIR --cal-bytes B --bytes B --title T --workload W
         --command-fetch C --command-write C --command-cal C [--note N ...]
@@ -40,6 +41,40 @@ def kernel_stats(path):
     return rows
 
 
+def dispatch_stats(path, skip=None):
+    """Per-kernel rows from the per-dispatch kernel trace: (name, calls, mean ns,
+    median ns, min ns, max ns, total ns, skipped), largest total first.
+
+    skip maps a kernel-name substring to a number of that kernel's first
+    dispatches (in dispatch order) to leave out, e.g. a bench's warm-up
+    launches.  Returns None when the directory holds no kernel_trace.csv."""
+    files = sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        return None
+    per = defaultdict(list)
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                key = int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)
+                per[r["Kernel_Name"]].append((key, int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows = []
+    for name, ds in per.items():
+        ds.sort()
+        n_skip = 0
+        for sub, n in (skip or {}).items():
+            if sub in name:
+                n_skip = min(len(ds), n)
+        kept = [end - start for _, start, end in ds[n_skip:]]
+        if not kept:
+            continue
+        kept.sort()
+        mid = len(kept) // 2
+        median = kept[mid] if len(kept) % 2 else (kept[mid - 1] + kept[mid]) / 2
+        rows.append((name, len(kept), sum(kept) / len(kept), median, kept[0], kept[-1], sum(kept), n_skip))
+    rows.sort(key=lambda x: -x[6])
+    return rows
+
+
 def counter_means(path, counter):
     """{kernel name: (mean value per dispatch, dispatches)} for one counter."""
     acc = defaultdict(lambda: [0.0, 0])
@@ -68,12 +103,33 @@ def _short(name, width=88):
     return name if len(name) <= width else name[:width - 3] + "..."
 
 
+def _skips(items):
+    skip = {}
+    for it in items or []:
+        sub, _, n = it.rpartition("=")
+        if not sub:
+            raise SystemExit(f"--skip wants KERNEL=N, got {it!r}")
+        skip[sub] = int(n)
+    return skip
+
+
 def cmd_trace(args):
     out = [f"# {args.title}", f"# command: {args.command}"]
     out += [f"# {n}" for n in args.note or []]
-    out.append("# name | calls | average ns | min ns | max ns | total ns")
-    for name, calls, avg, mn, mx, tot in kernel_stats(args.dir)[: args.top]:
-        out.append(f"{_short(name)} | {calls} | {avg:.0f} | {mn:.0f} | {mx:.0f} | {tot:.0f}")
+    rows = dispatch_stats(args.dir, _skips(args.skip))
+    if rows is None:
+        if args.skip:
+            raise SystemExit("--skip needs the per-dispatch kernel_trace.csv")
+        out.append("# name | calls | average ns | min ns | max ns | total ns")
+        for name, calls, avg, mn, mx, tot in kernel_stats(args.dir)[: args.top]:
+            out.append(f"{_short(name)} | {calls} | {avg:.0f} | {mn:.0f} | {mx:.0f} | {tot:.0f}")
+        return "\n".join(out) + "\n"
+    for name, calls, *_rest, skipped in rows:
+        if skipped:
+            out.append(f"# {_short(name, 60)}: its first {skipped} dispatches (warm-up) are left out")
+    out.append("# name | calls | average ns | median ns | min ns | max ns | total ns")
+    for name, calls, avg, med, mn, mx, tot, _ in rows[: args.top]:
+        out.append(f"{_short(name)} | {calls} | {avg:.0f} | {med:.0f} | {mn:.0f} | {mx:.0f} | {tot:.0f}")
     return "\n".join(out) + "\n"
 
 
@@ -137,6 +193,8 @@ def main(argv=None):
     t.add_argument("--command", required=True)
     t.add_argument("--note", action="append")
     t.add_argument("--top", type=int, default=12)
+    t.add_argument("--skip", action="append", metavar="KERNEL=N",
+                   help="leave out the first N dispatches of kernels whose name contains KERNEL")
     c = sub.add_parser("counters")
     for k in ("kernel", "fetch", "write", "cal_fetch", "cal_write", "title", "workload", "command_fetch",
               "command_write", "command_cal"):

@@ -8,3 +8,10 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    # tests/test_sanitize_cpu.py runs CPU suites against a sanitized host build
+    # of the library, named here; load_library() then returns that build
+    lib = os.environ.get("PA_TEST_LIBRARY")
+    if lib:
+        import paged_kv_cache_64_amd as pa
+
+        pa.load_library(lib)

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 import paged_kv_cache_64_amd as pa
+import workloads
 
 # Tolerance for F16 outputs against the fp64 oracle.
 MAX_ABS = 2e-3
@@ -41,8 +42,7 @@ class Staged:
             if self.fp8:
                 self.pool.set_scales(layer, *self.kv_scales)
             ids, k, v = w.kv_blocks(layer)
-            self.pool.write_blocks(layer, torch.from_numpy(ids).cuda(), torch.from_numpy(k).cuda(),
-                                   torch.from_numpy(v).cuda())
+            write_blocks(self.pool, layer, ids, k, v)
             q = w.q(layer)
             tables = w.tables(layer)
             self.dev[layer] = (torch.from_numpy(q).cuda(), torch.from_numpy(tables).cuda())
@@ -76,6 +76,16 @@ class Staged:
 
     def close(self):
         self.pool.close()
+
+
+def write_blocks(pool, layer, ids, k_blocks, v_blocks):
+    """Stores whole physical blocks through pa_write_kv: k_blocks[i] ([B, Hkv, d],
+    host F16) goes to block ids[i]."""
+    n = int(np.asarray(ids).shape[0]) * pool.block_size
+    slots = workloads.block_slot_mapping(ids, pool.block_size)
+    rows = lambda x: torch.from_numpy(np.ascontiguousarray(x).reshape(n, pool.num_kv_heads,
+                                                                     pool.head_dim)).cuda()
+    pool.write(layer, rows(k_blocks), rows(v_blocks), torch.from_numpy(slots).cuda())
 
 
 def compare(name, gpu_out, ref, max_abs=MAX_ABS, rel_l2=REL_L2):

@@ -168,3 +168,40 @@ def test_split_plan_and_workspace(lib, pool, monkeypatch):
     monkeypatch.setenv("PA_SPLIT_TOKENS", "100")     # not a multiple of 64: ignored
     assert pa.pa_decode_split_tokens(pool, 32, 32, 4096) % 64 == 0
     assert pa.pa_decode_split_tokens(pool, 32, 32, 4096) != 100
+
+
+def test_a_library_built_from_other_sources_is_refused(tmp_path):
+    """load_library checks the source hash the build embeds: a copy of the
+    library whose recorded hash differs from the sources is refused, and so is
+    a library without one."""
+    from paged_kv_cache_64_amd import build
+
+    data = open(pa.LIB_PATH, "rb").read()
+    have = build.built_hash(pa.LIB_PATH)
+    assert have == build.source_hash()
+    stale = tmp_path / "libpa_stale.so"
+    stale.write_bytes(data.replace(have.encode(), b"0" * 64))
+    with pytest.raises(RuntimeError, match="other sources"):
+        build.check_current(str(stale))
+    bare = tmp_path / "libpa_bare.so"
+    bare.write_bytes(data.replace(b"pa-source-sha256:", b"xx-source-sha256:"))
+    with pytest.raises(RuntimeError, match="other sources"):
+        build.check_current(str(bare))
+    with pytest.raises(RuntimeError, match="missing"):
+        build.check_current(str(tmp_path / "nothing.so"))
+    # an edited source changes the hash the loader expects
+    src = tmp_path / "pa_kernels.hip"
+    src.write_bytes(open(build.SOURCES[-1], "rb").read() + b"\n// edit\n")
+    assert build.source_hash(build.SOURCES[:-1] + [str(src)]) != have
+
+
+def test_the_oracle_rebuilds_a_library_made_from_other_sources(tmp_path):
+    from oracle import build as obuild
+
+    lib = str(tmp_path / "liboracle.so")
+    obuild.build(lib=lib)
+    assert obuild.is_current(lib)
+    data = open(lib, "rb").read()
+    open(lib, "wb").write(data.replace(obuild.source_hash().encode(), b"f" * 64))
+    assert not obuild.is_current(lib)
+    assert obuild.is_current(obuild.DEFAULT_LIB) or not os.path.exists(obuild.DEFAULT_LIB)

@@ -23,7 +23,6 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(autouse=True)
 def _no_overrides(monkeypatch):
     monkeypatch.delenv("PA_SPLIT_TOKENS", raising=False)
-    monkeypatch.delenv("PA_DECODE_PIECE_BLOCKS", raising=False)
 
 
 def _planned(st, layer=0):

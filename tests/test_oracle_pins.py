@@ -303,3 +303,49 @@ def test_shared_blocks_and_nan_outside_context_are_harmless():
     assert np.all(np.isfinite(got))
     for s in range(2):
         np.testing.assert_allclose(got[s], _brute(q[s], lk[0], lv[0], 0.3), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# the compact relabelled cache the GPU tests hand to the oracle
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_relabelled_cache_matches_the_uncompacted_slot_cache(shuffle):
+    """oracle.relabelled_cache compacts the referenced blocks into blocks
+    0..n-1 and rewrites the tables.  Against the full slot-indexed cache of the
+    pool (host_cache: every referenced block at its own id, NaN elsewhere) and
+    the original tables it must give the same gathered rows and the same
+    decode, bit for bit -- also with block ids listed out of order and with
+    blocks shared by several tables."""
+    import workloads
+
+    for w in (workloads.custom([1, 15, 16, 17, 0, 40, 33], seed=41),
+              workloads.custom([40, 48, 35, 64], seed=42, prefix_groups=(2, 2, 2))):
+        B = w.block_size
+        ids, k, v = w.kv_blocks(0)
+        if shuffle:
+            p = np.random.default_rng(5).permutation(len(ids))
+            ids, k, v = ids[p], k[p], v[p]
+        tables, lens, q = w.tables(0), w.ctx_lens, w.q(0)
+        full_k = oracle.host_cache(w.pool_blocks, B, ids, k)
+        full_v = oracle.host_cache(w.pool_blocks, B, ids, v)
+        kc, vc, t2 = oracle.relabelled_cache(ids, k, v, tables, lens, B)
+        held = w.blocks_held()
+        for s in range(w.batch):
+            for j in range(int(held[s])):
+                a, b = int(tables[s, j]) * B, int(t2[s, j]) * B
+                assert np.array_equal(kc[b:b + B].view(np.uint16), full_k[a:a + B].view(np.uint16))
+                assert np.array_equal(vc[b:b + B].view(np.uint16), full_v[a:a + B].view(np.uint16))
+            assert np.all(t2[s, int(held[s]):] == 0)
+        ref = oracle.decode(q, full_k, full_v, tables, lens, w.scale, B)
+        got = oracle.decode(q, kc, vc, t2, lens, w.scale, B)
+        assert np.array_equal(ref.view(np.uint64), got.view(np.uint64))
+        assert np.all(np.isfinite(ref))
+
+
+def test_relabelled_cache_rejects_tables_naming_missing_blocks():
+    import workloads
+
+    w = workloads.custom([20, 40], seed=43)
+    ids, k, v = w.kv_blocks(0)
+    with pytest.raises(ValueError):
+        oracle.relabelled_cache(ids[1:], k[1:], v[1:], w.tables(0), w.ctx_lens, w.block_size)

@@ -111,18 +111,53 @@ def test_plan_validation(pool):
     info0, plan0 = pa.pa_decode_plan(pool, [], 32)
     assert info0.num_items == 0
     # run with an empty plan is a no-op; a bad layer is rejected before any launch
-    assert lib.pa_decode_run(pool, 0, info0, FAKE, FAKE, None, None, FAKE, FAKE, 1, 0.1, None, 0,
-                             None) == pa.PA_OK
+    assert lib.pa_decode_run(pool, 0, info0, FAKE, info0.plan_bytes, FAKE, None, None, FAKE, FAKE, 1,
+                             0.1, None, 0, None) == pa.PA_OK
     info1, _ = pa.pa_decode_plan(pool, [100], 32)
-    assert lib.pa_decode_run(pool, 3, info1, FAKE, FAKE, None, None, FAKE, FAKE, 7, 0.1, FAKE,
+    pb = info1.plan_bytes
+    assert lib.pa_decode_run(pool, 3, info1, FAKE, pb, FAKE, None, None, FAKE, FAKE, 7, 0.1, FAKE,
                              1 << 20, None) == pa.PA_ERR_INVALID_ARG
-    assert lib.pa_decode_run(pool, 0, info1, FAKE, FAKE, None, None, FAKE, FAKE, 6, 0.1, FAKE,
+    assert lib.pa_decode_run(pool, 0, info1, FAKE, pb, FAKE, None, None, FAKE, FAKE, 6, 0.1, FAKE,
                              1 << 20, None) == pa.PA_ERR_INVALID_ARG      # table too narrow
-    assert lib.pa_decode_run(pool, 0, info1, FAKE, FAKE, FAKE, None, FAKE, FAKE, 7, 0.1, FAKE,
+    assert lib.pa_decode_run(pool, 0, info1, FAKE, pb, FAKE, FAKE, None, FAKE, FAKE, 7, 0.1, FAKE,
                              1 << 20, None) == pa.PA_ERR_INVALID_ARG      # k_new without v_new
+    assert lib.pa_decode_run(pool, 0, info1, FAKE, pb, FAKE, None, None, FAKE, FAKE, (1 << 26) + 1,
+                             0.1, FAKE, 1 << 20, None) == pa.PA_ERR_UNSUPPORTED  # table wider than 2^26
     if info1.workspace_bytes:
-        assert lib.pa_decode_run(pool, 0, info1, FAKE, FAKE, None, None, FAKE, FAKE, 7, 0.1, FAKE,
+        assert lib.pa_decode_run(pool, 0, info1, FAKE, pb, FAKE, None, None, FAKE, FAKE, 7, 0.1, FAKE,
                                  info1.workspace_bytes - 1, None) == pa.PA_ERR_WORKSPACE
+
+
+def test_run_checks_the_plan_against_its_info_and_buffer(pool):
+    """The kernels index the plan's sections by the counts in the info, so a run
+    whose info does not describe the plan, or whose device buffer is smaller than
+    the plan, is refused before anything is enqueued."""
+    lib = pa.load_library()
+    lens = list(workloads.config(4).ctx_lens)
+    info, _ = pa.pa_decode_plan(pool, lens, 32)
+    assert info.num_merges > 0
+    ws = info.workspace_bytes
+    run = lambda inf, nbytes: lib.pa_decode_run(pool, 0, inf, FAKE, nbytes, FAKE, None, None, FAKE,
+                                                FAKE, 512, 0.1, FAKE, ws, None)
+    assert run(info, info.plan_bytes - 4) == pa.PA_ERR_WORKSPACE     # buffer one word short
+    # an info kept from a larger step: more items than its plan_bytes hold
+    big = pa.PlanInfo.from_buffer_copy(info)
+    big.num_items += 1
+    assert run(big, 1 << 30) == pa.PA_ERR_INVALID_ARG
+    big = pa.PlanInfo.from_buffer_copy(info)
+    big.num_merges += 3
+    assert run(big, 1 << 30) == pa.PA_ERR_INVALID_ARG
+    big = pa.PlanInfo.from_buffer_copy(info)
+    big.plan_bytes += 4
+    assert run(big, 1 << 30) == pa.PA_ERR_INVALID_ARG
+    # the same checks guard the prefill entry point
+    pinfo, _ = pa.pa_prefill_plan(pool, np.array([0, 40, 41], np.int32), np.array([100, 60], np.int32), 32)
+    prun = lambda inf, nbytes: lib.pa_prefill_run(pool, 0, inf, FAKE, nbytes, FAKE, FAKE, FAKE, 16, 0.1,
+                                                  FAKE, 1 << 30, None)
+    assert prun(pinfo, pinfo.plan_bytes - 1) == pa.PA_ERR_WORKSPACE
+    bad = pa.PlanInfo.from_buffer_copy(pinfo)
+    bad.num_prefill_items += 1
+    assert prun(bad, 1 << 30) == pa.PA_ERR_INVALID_ARG
 
 
 def _decode_cascade(info, plan):
@@ -202,8 +237,8 @@ def test_cascade_run_rejects_appending_into_a_shared_block(pool):
     info, _ = pa.pa_cascade_plan(pool, lens, np.array([0, 0], np.int32), np.array([64], np.int32), 32)
     assert info.shared_newest == 1
     lib = pa.load_library()
-    assert lib.pa_decode_run(pool, 0, info, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, 0.1, FAKE,
-                             1 << 30, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_run(pool, 0, info, FAKE, info.plan_bytes, FAKE, FAKE, FAKE, FAKE, FAKE, 5, 0.1,
+                             FAKE, 1 << 30, None) == pa.PA_ERR_INVALID_ARG
 
 
 # ---- chunked-prefill / mixed-step schedule (pa_prefill_plan) ----------------

@@ -8,11 +8,14 @@ from paged_kv_cache_64_amd import prof_summary as ps
 
 
 def _write(path, header, rows):
+    """A CSV file as rocprofv3 writes them (fields with commas quoted)."""
+    import csv
+
     os.makedirs(os.path.dirname(path), exist_ok=True)
-    with open(path, "w") as f:
-        f.write(",".join(header) + "\n")
-        for r in rows:
-            f.write(",".join(str(x) for x in r) + "\n")
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(header)
+        wr.writerows(rows)
 
 
 def _counters(d, counter, per_kernel):
@@ -64,3 +67,26 @@ def test_sq_lists_every_counter_of_the_kernel(tmp_path):
         (tmp_path / "sq.txt").read_text().splitlines()
     assert "k( SQ_BUSY_CYCLES: 100 per launch over 1 launches" in lines
     assert "k( SQ_WAVES: 6 per launch over 2 launches" in lines
+
+
+def test_dispatch_trace_skips_warmup_and_reports_the_median(tmp_path):
+    hdr = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    t = 0
+    # decode: 3 slow warm-up dispatches, then 5 timed ones (100, 102, 98, 101, 99 ns)
+    for i, dur in enumerate([500, 400, 300, 100, 102, 98, 101, 99]):
+        rows.append(("KERNEL_DISPATCH", 10 + 2 * i, "decode_partial_kernel<3, false>", t, t + dur))
+        t += 1000
+    rows.append(("KERNEL_DISPATCH", 11, "write_kv_kernel", 5, 25))
+    # out of order in the file: sorted by dispatch id
+    _write(str(tmp_path / "tr" / "x_kernel_trace.csv"), hdr, rows[::-1])
+    got = ps.dispatch_stats(str(tmp_path / "tr"), {"decode_partial": 3})
+    by = {r[0]: r for r in got}
+    d = by["decode_partial_kernel<3, false>"]
+    assert d[1] == 5 and d[2] == 100.0 and d[3] == 100 and d[4] == 98 and d[5] == 102 and d[7] == 3
+    assert by["write_kv_kernel"][1:4] == (1, 20.0, 20)
+    ps.main(["-o", str(tmp_path / "out.txt"), "trace", str(tmp_path / "tr"), "--title", "T", "--command", "C",
+             "--skip", "decode_partial=3"])
+    out = open(tmp_path / "out.txt").read()
+    assert "first 3 dispatches" in out and "median ns" in out
+    assert ps.dispatch_stats(str(tmp_path / "none")) is None

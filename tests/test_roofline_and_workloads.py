@@ -105,3 +105,23 @@ def test_key_boost_hits_about_one_percent_of_key_vectors():
     assert 0.007 < frac < 0.013
     vn = np.linalg.norm(v.astype(np.float32), axis=-1)
     assert float((vn > 4 * np.sqrt(128)).mean()) == 0.0
+
+
+def test_pages_context_rows_are_the_printed_table():
+    with open(os.path.join(GOLDEN, "roofline_rtx4090.json")) as f:
+        g = json.load(f)
+    ctx = roofline.pages_context()
+    for row, want in zip(ctx["rows"], g["rows"]):
+        assert row["batch"] == want[0]
+        assert "%.2f" % row["bytes_per_step_GB"] == want[1] and "%.2f" % row["rtx4090_step_ms"] == want[2]
+    assert "%.2f" % ctx["rows"][-1]["kv_GB"] == g["kv_gb_at_batch_32"]
+    # at MI355X's 8 TB/s the batch-32 step is bandwidth-bound too: 21.70 GB / 8 TB/s
+    assert abs(ctx["rows"][-1]["mi355x_peak_step_ms"] - 21.70e9 / 8e12 * 1e3) < 0.01
+
+
+def test_split_kernel_bytes_counts_every_stream_once():
+    b = roofline.split_kernel_bytes([4096] * 32, 32, 8, 128, 16)
+    assert b["kv"] == 32 * 4096 * 4096
+    assert b["q"] == b["out"] == 32 * 32 * 128 * 2
+    assert b["table"] == 32 * 256 * 4
+    assert b["total"] == 537165824 + 32 * 8192      # 537,427,968 B per launch

@@ -248,6 +248,22 @@ class Workload:
         return int(self.ctx_lens.astype(np.int64).sum()) * per_token * (layers or self.layers)
 
 
+def block_slot_mapping(block_ids, block_size: int = 16) -> np.ndarray:
+    """int32 slot list that writes whole physical blocks: block_ids[i]'s tokens
+    go to slots block_ids[i] * block_size + 0 .. block_size - 1, in that order.
+
+    This is the caller's side of the pool write: an engine's model runner
+    builds slot_mapping from its block tables ("vLLM Architecture and
+    Installation", Example 3) and hands it to the write entry point, which only
+    scatters rows to the slots it is given.  Rows of a [n, block_size, Hkv, d]
+    block array reshaped to [n * block_size, Hkv, d] line up with these slots.
+    """
+    ids = np.asarray(block_ids, dtype=np.int64).reshape(-1)
+    slots = ids[:, None] * block_size + np.arange(block_size, dtype=np.int64)[None, :]
+    assert slots.size == 0 or int(slots.max()) < 2 ** 31
+    return slots.reshape(-1).astype(np.int32)
+
+
 def _uniform_ints(seed, purpose, lo, hi, n):
     return _rng(seed, _META, purpose).integers(lo, hi + 1, size=n).astype(np.int32)
 
