@@ -322,6 +322,24 @@ pa_status pa_prefill_run(pa_pool *pool, int32_t layer, const pa_plan_info *info,
                          float scale, void *workspace_dev, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* pa_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments and result as pa_decode.  When the split
+ * plan needs a workspace (pa_decode_workspace_bytes > 0) the partials go to
+ * one fixed array of 32 MiB that the library keeps in each GPU's memory until
+ * the process ends; a launch shape that would need more returns
+ * PA_ERR_WORKSPACE.  The call itself allocates nothing: the array's address is
+ * looked up once per device, on the first call on that device (the device of
+ * `stream`).  Every call on one GPU shares that GPU's array, which keeps the
+ * last call's partials (nothing in it has to start at zero: each call writes
+ * every record it reads), so calls that overlap in time on one GPU -- on
+ * different streams, or from different threads -- race and must be ordered
+ * by the caller. */
+pa_status pa_decode_noalloc(pa_pool *pool, int32_t layer, const void *q_dev, void *out_dev,
+                            const int32_t *block_tables_dev, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens_dev, int32_t batch, int32_t num_q_heads,
+                            int32_t max_context_len, float scale, hipStream_t stream);
+
 /* Static English text for a status code. */
 const char *pa_status_string(pa_status status);
 

@@ -29,7 +29,7 @@ EXPORTS = ("pa_pool_bytes", "pa_pool_create", "pa_pool_set_scales", "pa_pool_des
            "pa_decode_split_tokens", "pa_decode_workspace_bytes", "pa_decode",
            "pa_append_decode", "pa_decode_partial", "pa_decode_merge", "pa_decode_plan",
            "pa_cascade_plan", "pa_decode_run", "pa_prefill_plan", "pa_prefill_run",
-           "pa_status_string")
+           "pa_decode_noalloc", "pa_status_string")
 
 
 class PaError(RuntimeError):
@@ -106,6 +106,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_run.restype = _I
     lib.pa_decode_run.argtypes = [_P, _I, ctypes.POINTER(PlanInfo), _P, ctypes.c_size_t, _P, _P,
                                   _P, _P, _P, _I, ctypes.c_float, _P, ctypes.c_size_t, _P]
+    lib.pa_decode_noalloc.restype = _I
+    lib.pa_decode_noalloc.argtypes = [_P, _I, _P, _P, _P, _I, _P, _I, _I, _I, ctypes.c_float, _P]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [_I]
     _lib = lib
@@ -190,6 +192,14 @@ def pa_decode(handle, layer, q, out, block_tables, max_blocks_per_seq, context_l
                                     max_blocks_per_seq, _ptr(context_lens), batch, num_q_heads,
                                     max_context_len, float(scale), _ptr(workspace),
                                     int(workspace_bytes), _stream(stream)), "pa_decode")
+
+
+def pa_decode_noalloc(handle, layer, q, out, block_tables, max_blocks_per_seq, context_lens, batch,
+                      num_q_heads, max_context_len, scale, stream=None):
+    _check(load_library().pa_decode_noalloc(handle, layer, _ptr(q), _ptr(out), _ptr(block_tables),
+                                            max_blocks_per_seq, _ptr(context_lens), batch,
+                                            num_q_heads, max_context_len, float(scale),
+                                            _stream(stream)), "pa_decode_noalloc")
 
 
 def _new_kv_call(name, handle, layer, q, k_new, v_new, out, block_tables, max_blocks_per_seq,

@@ -809,6 +809,23 @@ pa_status pa_decode(pa_pool *pool, int32_t layer, const void *q_dev, void *out_d
                            workspace_bytes, stream);
 }
 
+pa_status pa_decode_noalloc(pa_pool *pool, int32_t layer, const void *q_dev, void *out_dev,
+                            const int32_t *block_tables_dev, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens_dev, int32_t batch, int32_t num_q_heads,
+                            int32_t max_context_len, float scale, hipStream_t stream) {
+    const pa_status st = check_decode_shape(pool, batch, num_q_heads, max_blocks_per_seq, max_context_len);
+    if (st != PA_OK) return st;
+    if (batch == 0)
+        return pa_decode(pool, layer, q_dev, out_dev, block_tables_dev, max_blocks_per_seq, context_lens_dev,
+                         batch, num_q_heads, max_context_len, scale, nullptr, 0, stream);
+    const Plan plan = make_plan(pool, batch, num_q_heads, max_context_len);
+    if (plan.workspace > pa::kNoAllocScratchBytes) return PA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (plan.workspace > 0 && pa::noalloc_scratch(stream, &ws) != hipSuccess) return PA_ERR_HIP;
+    return pa_decode(pool, layer, q_dev, out_dev, block_tables_dev, max_blocks_per_seq, context_lens_dev, batch,
+                     num_q_heads, max_context_len, scale, ws, plan.workspace, stream);
+}
+
 const char *pa_status_string(pa_status status) {
     switch (status) {
         case PA_OK: return "ok";

@@ -107,6 +107,14 @@ constexpr int kMaxPrefixPieceBlocks = 32;
 constexpr int32_t kPlanMagic = 0x50414e31;  // "PAN1"
 
 
+// The allocation-free decode (pa_decode_noalloc) keeps its split partials in
+// one fixed device array of this many bytes per GPU.
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+
+// Device address of that array on the GPU that `stream` belongs to, looked
+// up once per device (hipGetSymbolAddress) and kept.
+hipError_t noalloc_scratch(hipStream_t stream, void **ptr);
+
 hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream);

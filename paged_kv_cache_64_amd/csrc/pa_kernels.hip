@@ -33,6 +33,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "pa_internal.h"
@@ -1766,6 +1767,42 @@ hipError_t launch_cascade(const DecodeArgs &a, hipStream_t stream) {
     else
         hipLaunchKernelGGL(cascade_kernel<false>, dim3(groups), dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+// ---- scratch of the allocation-free decode ---------------------------------
+// pa_decode_noalloc keeps its split partials here instead of in a caller's
+// workspace, for callers that cannot allocate.  Each GPU holds its own copy at
+// its own address until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol: its device address comes from hipGetSymbolAddress,
+// once per device, and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(hipStream_t stream, void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        // the lookup runs with the stream's device current
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode_prefix(const DecodeArgs &a, hipStream_t stream) {

@@ -16,5 +16,9 @@ hipError_t launch_decode_prefix(const DecodeArgs &, hipStream_t) { return hipSuc
 hipError_t launch_cascade(const DecodeArgs &, hipStream_t) { return hipSuccess; }
 hipError_t launch_prefill(const DecodeArgs &, hipStream_t) { return hipSuccess; }
 hipError_t launch_mixed(const DecodeArgs &, hipStream_t) { return hipSuccess; }
+hipError_t noalloc_scratch(hipStream_t, void **ptr) {
+    *ptr = reinterpret_cast<void *>(uintptr_t{1} << 20);  // never dereferenced: nothing is launched
+    return hipSuccess;
+}
 
 }  // namespace pa

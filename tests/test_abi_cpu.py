@@ -205,3 +205,16 @@ def test_the_oracle_rebuilds_a_library_made_from_other_sources(tmp_path):
     open(lib, "wb").write(data.replace(obuild.source_hash().encode(), b"f" * 64))
     assert not obuild.is_current(lib)
     assert obuild.is_current(obuild.DEFAULT_LIB) or not os.path.exists(obuild.DEFAULT_LIB)
+
+
+def test_noalloc_decode_validation(lib, pool):
+    """pa_decode_noalloc rejects what pa_decode rejects, and a launch shape whose
+    partials would not fit its fixed 32 MiB array, before any device work."""
+    f = lib.pa_decode_noalloc
+    assert f(pool, 0, FAKE, FAKE, FAKE, 16, FAKE, 0, 32, 0, 0.1, None) == pa.PA_OK      # empty batch
+    assert f(None, 0, FAKE, FAKE, FAKE, 16, FAKE, 2, 32, 256, 0.1, None) == pa.PA_ERR_INVALID_ARG
+    assert f(pool, 0, FAKE, FAKE, FAKE, 16, FAKE, 2, 30, 256, 0.1, None) == pa.PA_ERR_INVALID_ARG
+    assert f(pool, 0, FAKE, FAKE, FAKE, 15, FAKE, 2, 32, 256, 0.1, None) == pa.PA_ERR_INVALID_ARG
+    # 1000 sequences of up to 2^20 tokens: 256 splits each, 4.3 GB of partials
+    assert lib.pa_decode_workspace_bytes(pool, 1000, 32, 1 << 20) > 32 << 20
+    assert f(pool, 0, FAKE, FAKE, FAKE, 1 << 16, FAKE, 1000, 32, 1 << 20, 0.1, None) == pa.PA_ERR_WORKSPACE
