@@ -8,7 +8,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <functional>
 #include <new>
+#include <queue>
 #include <vector>
 
 #include "pa_internal.h"
@@ -186,6 +188,115 @@ struct PlanItem {
     int32_t s, t_begin, t_end, ctx, slot;
 };
 
+// ---- piece size by a model of the dispatch ----------------------------------
+// Measured on MI355X: a compute unit pulls K/V at about 26 GB/s however few
+// others are busy, so a decode launch lasts as long as its most loaded unit.
+// The dispatcher hands work-group j of a launch to unit j mod 256 while each
+// unit has room for two (j < 512), and each later one to the unit that frees
+// a slot first.  The model charges a unit the blocks of every work-group it
+// gets, plus kWgOverheadBlocks each for the work-group's fixed work (query,
+// table, the four-wave merge), and a plan that cuts a sequence one launch of
+// the merge kernel (kMergeBlocks of F16 blocks: about 5 us at that rate).
+// Measured against it, per layer: batch 8 / 16 / 24 / 32 at 4096 tokens took
+// 29 / 50 / 86 / 82 us, modelled 26 / 46 / 88 / 82 us; the ragged 64-sequence
+// step 185 us, modelled 186 us.
+constexpr int kDispatchUnits = 256;
+constexpr int kSlotsPerUnit = 2;
+constexpr int64_t kWgOverheadBlocks = 3;
+constexpr int64_t kMergeBlocks = 16;
+
+// Blocks of each piece when every context is cut into near-equal pieces of
+// at most max_piece blocks (an empty context gives an empty piece), longest
+// first (a counting sort: pieces are at most kMaxSplitTokens / kBlockSize
+// blocks).
+void piece_blocks(const int32_t *lens, const std::vector<int32_t> &plen, int32_t batch, int64_t max_piece,
+                  std::vector<int64_t> *out, bool *cuts) {
+    constexpr int64_t kMaxPiece = kMaxSplitTokens / kBlockSize;
+    std::vector<int64_t> count(kMaxPiece + 1, 0);
+    *cuts = false;
+    for (int32_t s = 0; s < batch; ++s) {
+        const int64_t nb = (static_cast<int64_t>(lens[s]) - plen[s] + kBlockSize - 1) / kBlockSize;
+        if (nb == 0) {
+            if (plen[s] == 0) ++count[0];
+            continue;
+        }
+        const int64_t np = (nb + max_piece - 1) / max_piece;
+        *cuts = *cuts || np > 1;
+        // near-equal: nb % np pieces one block longer (never past max_piece)
+        if (nb % np != 0) count[nb / np + 1] += nb % np;
+        count[nb / np] += np - nb % np;
+    }
+    out->clear();
+    for (int64_t b = kMaxPiece; b >= 0; --b) out->insert(out->end(), static_cast<size_t>(count[b]), b);
+}
+
+// The modelled time of a launch of these pieces, longest first, each run by
+// `heads` consecutive work-groups, in blocks of the most loaded unit.  When
+// `heads` divides the unit count, a piece's work-groups land on `heads`
+// units whose loads stay equal, so the model tracks groups of units.
+int64_t modelled_makespan(const std::vector<int64_t> &pieces, int32_t heads) {
+    const bool grouped = heads > 0 && kDispatchUnits % heads == 0;
+    const int units = grouped ? kDispatchUnits / heads : kDispatchUnits;  // tracked units (or groups)
+    const int per = grouped ? 1 : heads;                                  // work-groups per piece and unit
+    const int64_t first_round = static_cast<int64_t>(units) * kSlotsPerUnit;
+    std::vector<int64_t> load(units, 0);
+    std::priority_queue<std::pair<int64_t, int>, std::vector<std::pair<int64_t, int>>, std::greater<>> later;
+    int64_t j = 0;
+    for (const int64_t p : pieces) {
+        for (int h = 0; h < per; ++h, ++j) {
+            const int64_t w = p + kWgOverheadBlocks;
+            if (j < first_round) {
+                load[j % units] += w;
+                if (j + 1 == first_round)
+                    for (int u = 0; u < units; ++u) later.push({load[u], u});
+            } else {
+                const int u = later.top().second;
+                later.pop();
+                load[u] += w;
+                later.push({load[u], u});
+            }
+        }
+    }
+    return *std::max_element(load.begin(), load.end());
+}
+
+// Piece size (in blocks) from a ladder of candidates, largest first, from
+// kMaxSplitTokens / kBlockSize down to kMinPieceBlocks: a smaller piece is
+// taken only when its modelled launch time beats the best so far by more
+// than 1/32 (3 %).  The model knows nothing of tiles that several sequences
+// share and the caches serve (the 256-sequence shared-prefix step took 808 us
+// with 256-block pieces and 834 us with the 128-block pieces the model rated
+// 2 % faster), so small modelled gains do not change the plan.
+// merge_blocks: the charge for a plan that cuts a sequence.  A candidate
+// whose lower bound (its work spread evenly, or its longest piece) cannot
+// beat the best so far is not simulated.
+int64_t balanced_piece(const int32_t *lens, const std::vector<int32_t> &plen, int32_t batch, int32_t heads,
+                       int64_t merge_blocks) {
+    static const int64_t kLadder[] = {256, 224, 192, 160, 128, 112, 96, 80, 64, 56, 48, 40, 32, 28, 24, 20, 16};
+    const bool grouped = heads > 0 && kDispatchUnits % heads == 0;
+    const int64_t units = grouped ? kDispatchUnits / heads : kDispatchUnits;
+    const int64_t per = grouped ? 1 : heads;
+    int64_t best = kMaxSplitTokens / kBlockSize, best_cost = -1;
+    std::vector<int64_t> pieces;
+    for (const int64_t p : kLadder) {
+        if (p < kMinPieceBlocks || p > kMaxSplitTokens / kBlockSize) continue;
+        bool cuts = false;
+        piece_blocks(lens, plen, batch, p, &pieces, &cuts);
+        int64_t work = 0;
+        for (const int64_t b : pieces) work += (b + kWgOverheadBlocks) * per;
+        const int64_t bound = std::max<int64_t>((work + units - 1) / units,
+                                                pieces.empty() ? 0 : pieces[0] + kWgOverheadBlocks) +
+                              (cuts ? merge_blocks : 0);
+        if (best_cost >= 0 && bound >= best_cost - best_cost / 32) continue;
+        const int64_t cost = modelled_makespan(pieces, heads) + (cuts ? merge_blocks : 0);
+        if (best_cost < 0 || cost < best_cost - best_cost / 32) {
+            best_cost = cost;
+            best = p;
+        }
+    }
+    return best;
+}
+
 size_t planned_workspace(int64_t slots, int32_t num_q_heads, size_t *o_bytes) {
     const size_t recs = static_cast<size_t>(slots) * num_q_heads;
     *o_bytes = round_up(static_cast<int64_t>(recs * kHeadDim * sizeof(float)), 256);
@@ -234,8 +345,14 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
                 total_blocks += static_cast<int64_t>(prefix_len[gi] / kBlockSize) *
                                 ((members[gi].size() + pa::kMaxMembers - 1) / pa::kMaxMembers);
         const int64_t items_target = std::max<int64_t>(1, kTargetWorkGroups / pool->desc.num_kv_heads);
-        const int64_t piece = std::min<int64_t>(
-            kMaxSplitTokens / kBlockSize, std::max<int64_t>(kMinPieceBlocks, (total_blocks + items_target - 1) / items_target));
+        // Without shared prefixes the piece size comes from the dispatch model
+        // (F16 blocks cost twice an FP8 block's time, so the merge charge
+        // doubles in FP8 blocks); with them, from the work-group target.
+        const int64_t piece =
+            group_of == nullptr
+                ? balanced_piece(lens, plen, batch, pool->desc.num_kv_heads, kMergeBlocks * 2 / pool->elem_bytes())
+                : std::min<int64_t>(kMaxSplitTokens / kBlockSize,
+                                    std::max<int64_t>(kMinPieceBlocks, (total_blocks + items_target - 1) / items_target));
         auto cut = [](int64_t nb, int64_t maxp) { return nb == 0 ? int64_t{0} : (nb + maxp - 1) / maxp; };
 
         // records: each member owns a contiguous run (prefix pieces, then its

@@ -291,22 +291,21 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     }
     const int b_begin = t_begin / kBlockSize;
     // A piece never spans more than kMaxSplitTokens / kBlockSize blocks (64 per
-    // wave, the size of a wave's row of tbl_lds); a damaged plan entry is cut
-    // there too.
+    // wave, one per lane of a wave's table register); a damaged plan entry is
+    // cut there too.
     const int b_end = min((t_end + kBlockSize - 1) / kBlockSize, b_begin + kMaxSplitTokens / kBlockSize);
     t_end = min(t_end, b_end * kBlockSize);
     const int per_wave = (b_end - b_begin + kWaves - 1) / kWaves;
     const int wb_begin = min(b_end, b_begin + w * per_wave);
     const int wb_end = min(b_end, wb_begin + per_wave);
 
-    // Block-table entries of this wave's blocks go to LDS up front (a wave
-    // never owns more than 64 blocks), so the loop reads them without a
-    // memory load that would have to wait behind the K/V loads in flight.
-    // Their load comes first: every K/V address depends on it.
+    // Block-table entries of this wave's blocks are loaded up front, entry
+    // wb_begin + i into lane i (a wave never owns more than 64 blocks), and
+    // each block's entry is then read with v_readlane: no memory or LDS
+    // access has to complete between a block's turn and the issue of its
+    // K/V loads.  This load comes first: every K/V address depends on it.
     const int32_t *table = a.tables + static_cast<size_t>(s) * a.max_blocks;
-    __shared__ int tbl_lds[kWaves][64];
-    if (lane < wb_end - wb_begin) tbl_lds[w][lane] = table[wb_begin + lane];
-    wave_lds_sync();
+    const int tbl_v = lane < wb_end - wb_begin ? table[wb_begin + lane] : 0;
 
     // Q^T operands: qm[i] holds query head l%4 at the 8 dims of MFMA i in this
     // lane, chunk_dim(i) .. +7.
@@ -376,13 +375,17 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     // so every pipeline step issues the same number of loads.
     auto issue = [&](int buf, int b) {
         const bool live = b < wb_end;
-        uint32_t phys = static_cast<uint32_t>(
-            __builtin_amdgcn_readfirstlane(tbl_lds[w][live ? b - wb_begin : 0]));
+        uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readlane(tbl_v, live ? b - wb_begin : 0));
         phys = phys > last_block ? last_block : phys;
         const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
         const int bytes = live ? static_cast<int>(tile_bytes) : 0;
+        // The V resource ends at the piece's last token: value rows past it
+        // (slots past the sequence in its last block, which may hold
+        // anything) load as zeros, so their zero weights cannot meet a NaN,
+        // at no VALU cost.  Keys past it are masked to -inf in consume.
+        const int vbytes = live ? min(t_end - b * kBlockSize, kBlockSize) * kHeadDim * kElem : 0;
         const __amdgpu_buffer_rsrc_t kr = tile_rsrc(k_layer + base, bytes);
-        const __amdgpu_buffer_rsrc_t vr = tile_rsrc(v_layer + base, bytes);
+        const __amdgpu_buffer_rsrc_t vr = tile_rsrc(v_layer + base, vbytes);
 #pragma unroll
         for (int i = 0; i < kKLoads; ++i) kb[buf][i] = load_raw16(kr, k_off + 64u * i);
 #pragma unroll
@@ -434,6 +437,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
         for (int i = 0; i < 4; ++i) st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[i], qm[i], st, 0, 0, 0);
 
         // ---- mask the tail of the sequence's last block ----
+        // (its value rows past the end already loaded as zeros, see issue)
         const int valid = t_end - b * kBlockSize;  // >= 1; pieces end on block edges or at ctx
         const bool partial = valid < kBlockSize;
         float x[4];  // scores of tokens 4c + r in log2 units
@@ -468,12 +472,11 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
 
         // ---- O += P V ----
         if constexpr (FP8) {
-            uint32_t vw[4][2];  // codes of token 4c + r; stale slots may hold anything
+            uint32_t vw[4][2];  // codes of token 4c + r (zero past the piece's end)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const bool dead = partial && 4 * c + r >= valid;
-                vw[c][0] = dead ? 0u : vb[buf][c].x;
-                vw[c][1] = dead ? 0u : vb[buf][c].y;
+                vw[c][0] = vb[buf][c].x;
+                vw[c][1] = vb[buf][c].y;
             }
 #pragma unroll
             for (int jp = 0; jp < 4; ++jp) {
@@ -490,9 +493,9 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
                 oacc[2 * jp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v1, oacc[2 * jp + 1], 0, 0, 0);
             }
         } else {
-            u4 vv[4];  // token 4c + r, dims 8n .. 8n+7; stale slots may hold anything
+            u4 vv[4];  // token 4c + r, dims 8n .. 8n+7 (zero past the piece's end)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) vv[c] = (partial && 4 * c + r >= valid) ? u4(0u) : u4(vb[buf][c]);
+            for (int c = 0; c < 4; ++c) vv[c] = vb[buf][c];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 // half j of tokens c = 0, 1 and of tokens c = 2, 3
@@ -603,9 +606,47 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
 // Records a merge loads in one round (the merges are latency-bound).
 constexpr int kMergeBatch = 8;
 
+// Log-sum-exp merge of n partial records at one output element:
+//   M = max_i m_i,  L = sum_i 2^(m_i - M) l_i,  O = sum_i 2^(m_i - M) o_i
+// load(i, ml, o) fetches record i's (m, l) and o.  Records come kMergeBatch
+// at a time with all their loads in flight together; a later round that
+// raises M rescales the running sums once.  For n <= kMergeBatch this is one
+// round: M over all records, then the sums in record order.  A record with
+// m = -inf (a piece that saw no key) adds nothing.  Returns O / L.
+template <class Load>
+__device__ __forceinline__ float merge_records(int n, Load load) {
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
+        float2 ml[kMergeBatch];
+        float o[kMergeBatch];
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i)
+            if (i0 + i < n) load(i0 + i, ml[i], o[i]);
+        float Mc = M;
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i)
+            if (i0 + i < n) Mc = fmaxf(Mc, ml[i].x);
+        if (Mc != M) {
+            const float sc = M == -INFINITY ? 0.0f : fast_exp2(M - Mc);
+            L *= sc;
+            O *= sc;
+            M = Mc;
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            if (i0 + i < n) {
+                const float wgt = ml[i].x == -INFINITY ? 0.0f : fast_exp2(ml[i].x - M);
+                L += wgt * ml[i].y;
+                O += wgt * o[i];
+            }
+        }
+    }
+    return O / L;
+}
+
 // ---------------------------------------------------------------------------
-// decode_merge: 256 threads = two (sequence, query head) rows of 128 dims.
-//   M = max_i m_i,  L = sum_i 2^(m_i - M) l_i,  out = sum_i 2^(m_i - M) o_i / L
+// decode_merge: 256 threads = two (sequence, query head) rows of 128 dims;
+// merges the row's split records and writes F16.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     const int64_t row = static_cast<int64_t>(blockIdx.x) * 2 + (threadIdx.x >> 7);
@@ -621,46 +662,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     }
     const float *ml = a.ml_part + row * a.max_splits * 2;
     const float *op = a.o_part + row * a.max_splits * kHeadDim + d;
-    float M = -INFINITY, L = 0.0f, O = 0.0f;
-    if (ns <= kMergeBatch) {
-        // every split's (m, l) and o in one round of loads, then the same
-        // arithmetic in the same order as below
-        float2 mlv[kMergeBatch];
-        float ov[kMergeBatch];
-#pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i) {
-            if (i < ns) {
-                mlv[i] = *reinterpret_cast<const float2 *>(ml + 2 * i);
-                ov[i] = op[static_cast<int64_t>(i) * kHeadDim];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i)
-            if (i < ns) M = fmaxf(M, mlv[i].x);
-#pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i) {
-            if (i < ns) {
-                const float wgt = fast_exp2(mlv[i].x - M);
-                L += wgt * mlv[i].y;
-                O += wgt * ov[i];
-            }
-        }
-    } else {
-        for (int i = 0; i < ns; ++i) M = fmaxf(M, ml[2 * i]);
-        for (int i = 0; i < ns; ++i) {
-            const float wgt = fast_exp2(ml[2 * i] - M);
-            L += wgt * ml[2 * i + 1];
-            O += wgt * op[static_cast<int64_t>(i) * kHeadDim];
-        }
-    }
-    const _Float16 r = static_cast<_Float16>(O / L);
-    *reinterpret_cast<_Float16 *>(out) = r;
+    const float r = merge_records(ns, [&](int i, float2 &mlv, float &ov) {
+        mlv = *reinterpret_cast<const float2 *>(ml + 2 * i);
+        ov = op[static_cast<int64_t>(i) * kHeadDim];
+    });
+    *reinterpret_cast<_Float16 *>(out) = static_cast<_Float16>(r);
 }
 
 // ---------------------------------------------------------------------------
 // decode_merge_planned: grid (merge entry, query-head pair); the pieces of
-// sequence s are records first .. first + n - 1.  Up to kMergeBatch records
-// are loaded in one round (the merge is latency-bound: a few hundred KB).
+// sequence s are records first .. first + n - 1.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a) {
     const int32_t *m = a.merges + kMergeInts * static_cast<size_t>(blockIdx.x);
@@ -675,42 +686,12 @@ __global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a)
         *out = 0;
         return;
     }
-    float M = -INFINITY, L = 0.0f, O = 0.0f;
-    if (n <= kMergeBatch) {
-        // every record's (m, l) and o in one round of loads, then the same
-        // arithmetic in the same order as below
-        float2 ml[kMergeBatch];
-        float o[kMergeBatch];
-#pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i) {
-            if (i < n) {
-                const size_t rec = static_cast<size_t>(first + i) * a.num_q_heads + h;
-                ml[i] = *reinterpret_cast<const float2 *>(a.ml_part + rec * 2);
-                o[i] = a.o_part[rec * kHeadDim + d];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i)
-            if (i < n) M = fmaxf(M, ml[i].x);
-#pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i) {
-            if (i < n) {
-                const float wgt = fast_exp2(ml[i].x - M);
-                L += wgt * ml[i].y;
-                O += wgt * o[i];
-            }
-        }
-    } else {
-        for (int i = 0; i < n; ++i) M = fmaxf(M, a.ml_part[(static_cast<size_t>(first + i) * a.num_q_heads + h) * 2]);
-        for (int i = 0; i < n; ++i) {
-            const size_t rec = static_cast<size_t>(first + i) * a.num_q_heads + h;
-            const float wgt = fast_exp2(a.ml_part[rec * 2] - M);
-            L += wgt * a.ml_part[rec * 2 + 1];
-            O += wgt * a.o_part[rec * kHeadDim + d];
-        }
-    }
-    const _Float16 r = static_cast<_Float16>(O / L);
-    *reinterpret_cast<_Float16 *>(out) = r;
+    const float r = merge_records(n, [&](int i, float2 &mlv, float &ov) {
+        const size_t rec = static_cast<size_t>(first + i) * a.num_q_heads + h;
+        mlv = *reinterpret_cast<const float2 *>(a.ml_part + rec * 2);
+        ov = a.o_part[rec * kHeadDim + d];
+    });
+    *reinterpret_cast<_Float16 *>(out) = static_cast<_Float16>(r);
 }
 
 // ---------------------------------------------------------------------------

@@ -27,8 +27,8 @@ def _decode_plan(info, plan):
 def _check_cover(lens, info, plan):
     items, merges = _decode_plan(info, plan)
     pieces = {}
-    for s, t0, t1, ctx, slot, *_ in items:
-        assert ctx == lens[s] and 0 <= t0 <= t1 <= ctx
+    for s, t0, t1, ctx, slot, row, hsel, _ in items:
+        assert ctx == lens[s] and 0 <= t0 <= t1 <= ctx and row == s and hsel == 0
         assert t0 % 16 == 0 and (t1 % 16 == 0 or t1 == ctx)
         pieces.setdefault(s, []).append((t0, t1, slot))
     assert sorted(pieces) == list(range(len(lens)))
@@ -383,3 +383,22 @@ def test_longest_context_plans_and_longer_ones_are_unsupported(pool):
     starts = np.array([0, 1, 2], np.int32)
     info2, plan2 = pa.pa_prefill_plan(pool, starts, np.array(lens, np.int32), 32)
     assert info2.num_items == info.num_items and info2.num_merges == 1 and info2.max_context_len == big
+
+
+def test_piece_size_balances_the_compute_units(pool):
+    """Without shared prefixes the piece size comes from a model of the
+    dispatch (each compute unit pulls K/V at a bounded rate, so the most loaded
+    unit sets the launch time): uniform batches whose one-piece plans would
+    leave some units with twice the work of others are cut so that every unit
+    gets the same, and batches that fill the chip evenly are not cut."""
+    cases = {  # lengths: (pieces, merged sequences, longest piece in tokens)
+        (4096,) * 32: (32, 0, 4096),     # 256 work-groups of 256 blocks: even
+        (4096,) * 24: (96, 24, 1024),    # 768 work-groups of 64 blocks: 3 per unit
+        (4096,) * 48: (96, 48, 2048),    # 768 work-groups of 128 blocks
+        (1024,) * 24: (24, 0, 1024),     # 192 work-groups, no merge
+        (4096,) * 8: (32, 8, 1024),
+    }
+    for lens, (n_items, n_merges, longest) in cases.items():
+        info, plan = pa.pa_decode_plan(pool, list(lens), 32)
+        _check_cover(list(lens), info, plan)
+        assert (info.num_items, info.num_merges, info.max_piece_tokens) == (n_items, n_merges, longest), lens

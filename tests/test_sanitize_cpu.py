@@ -58,7 +58,12 @@ def test_host_code_and_oracle_under_asan_and_ubsan(tmp_path):
     })
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "-m", "not gpu"]
                        + SUITES, cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
-    tail = (r.stdout + r.stderr)[-4000:]
+    report = r.stderr
+    for mark in ("ERROR: AddressSanitizer", "runtime error:"):
+        if mark in report:
+            report = report[report.index(mark):]
+            break
+    tail = r.stdout[-2000:] + "\n" + report[:6000]
     assert r.returncode == 0, tail
     assert "ERROR: AddressSanitizer" not in r.stderr and "runtime error:" not in r.stderr, tail
     assert " passed" in r.stdout, tail
