@@ -234,6 +234,10 @@ typedef struct {
     int32_t shared_newest;    /* members whose newest token lies in the shared prefix */
     int32_t num_prefill_items; /* chunked-prefill pieces (pa_prefill_plan) */
     int32_t num_q_rows;       /* rows of q and out: batch, or the step's query tokens */
+    int32_t mixed_decode_waves; /* pa_prefill_plan with both kinds of pieces: waves per
+                                   work-group that walk a decode piece (2 when the prompt
+                                   tiles are the longer part, so they progress beside the
+                                   decode streams; else 4); 4 in every other plan */
     size_t plan_bytes;        /* bytes of the serialised plan */
     size_t workspace_bytes;   /* device workspace pa_decode_run needs (0: none) */
 } pa_plan_info;

@@ -450,6 +450,7 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
         inf.shared_newest = shared_newest;
         inf.num_prefill_items = 0;
         inf.num_q_rows = batch;
+        inf.mixed_decode_waves = pa::kWaves;
         inf.plan_bytes = sizeof(int32_t) * (pa::kPlanHeader + pa::kItemInts * n_items + merges.size() +
                                             pitems.size() + mlist.size());
         size_t o_bytes = 0;
@@ -509,6 +510,29 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
         }
         const int32_t num_q_rows = query_start[batch];
         if (num_q_rows > (1 << 24)) return PA_ERR_UNSUPPORTED;
+        // A launch with both kinds of pieces: when the prompt tiles take longer
+        // than the decode pieces, the decode pieces are walked by 2 of their
+        // work-group's 4 waves.  Decode streams with all 4 waves fill each CU's
+        // memory path, and the prompt tiles sharing the CU barely progress until
+        // they end (the launch then costs the sum of its parts); with 2, both
+        // kinds run side by side and the decode pieces, at about half their
+        // rate, end about when the tiles do.  Config 6's geometry (32 decodes at
+        // 4096 tokens + a 2016-token chunk at 2016), per layer: decode alone
+        // 89 us, chunk alone 142-150 us, fused 228-234 us with 4 waves and
+        // 190-198 us with 2 (1 wave: 188 us; 3: 220 us).  The estimate: decode
+        // bytes at 6.5 TB/s against the tiles' flops at 0.85 PFLOP/s (their
+        // rates measured alone).
+        double tile_flops = 0.0;
+        for (int32_t s = 0; s < batch; ++s) {
+            const int64_t q_len = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
+            if (q_len < 2) continue;
+            const double hist = static_cast<double>(lens[s]) - static_cast<double>(q_len);
+            tile_flops += 4.0 * kHeadDim * num_q_heads *
+                          (static_cast<double>(q_len) * hist + static_cast<double>(q_len) * (q_len + 1) / 2.0);
+        }
+        const double dec_bytes = static_cast<double>(dec_blocks) * kBlockSize * pool->desc.num_kv_heads * kHeadDim *
+                                 2.0 * pool->elem_bytes();
+        const int32_t mixed_waves = tile_flops / 0.85e15 > dec_bytes / 6.5e12 ? 2 : pa::kWaves;
         const int64_t items_target = std::max<int64_t>(1, kTargetWorkGroups / pool->desc.num_kv_heads);
         auto cut = [](int64_t nb, int64_t maxp) { return nb == 0 ? int64_t{0} : (nb + maxp - 1) / maxp; };
 
@@ -623,6 +647,7 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
         inf.max_piece_tokens = longest;
         inf.num_prefill_items = static_cast<int32_t>(n_pf);
         inf.num_q_rows = num_q_rows;
+        inf.mixed_decode_waves = mixed_waves;
         inf.plan_bytes = sizeof(int32_t) * (pa::kPlanHeader + pa::kItemInts * n_items + merges.size() +
                                             pa::kPrefillItemInts * n_pf);
         size_t o_bytes = 0;
@@ -722,6 +747,7 @@ pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const
     a.num_members = info->num_members;
     a.prefill_items = a.members + static_cast<size_t>(pa::kMemberInts) * info->num_members;
     a.num_prefill_items = info->num_prefill_items;
+    a.mixed_decode_waves = info->mixed_decode_waves == 2 ? 2 : pa::kWaves;
     if (info->num_items > 0 && info->num_prefill_items > 0 &&
         static_cast<int64_t>(info->num_items + info->num_prefill_items) * pool->desc.num_kv_heads <= 0x7fffffff) {
         // decode and prefill pieces share one launch

@@ -85,6 +85,8 @@ struct DecodeArgs {
     const int32_t *prefill_items;
     int32_t num_prefill_items;
     int32_t num_q_rows;  // rows of q / out: batch for a decode step, total query tokens for a mixed one
+    // waves of a work-group that walk a decode piece in a mixed launch (2 or 4)
+    int32_t mixed_decode_waves;
 };
 
 // Serialised host plan: a header of kPlanHeader int32, then the decode items,

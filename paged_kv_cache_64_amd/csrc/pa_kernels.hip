@@ -230,7 +230,10 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
 //                 D: result element c of lane l is head c at dim 8n + j.
 //   K's FP8 scale is folded into the score scale and V's into the output.
 // ---------------------------------------------------------------------------
-template <int NBUF, bool FP8>
+// MIXED: the decode pieces of a mixed launch, walked by a.mixed_decode_waves
+// (2 or 4) of the work-group's waves; a wave then owns up to 128 blocks, its
+// table entries in two registers.
+template <int NBUF, bool FP8, bool MIXED = false>
 __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_t bx, uint32_t by, uint32_t bz) {
     // Planned launches number work-groups item-major with the KV head fastest,
     // so the heads of one piece -- whose tiles share each 32 KiB block of
@@ -291,12 +294,13 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     }
     const int b_begin = t_begin / kBlockSize;
     // A piece never spans more than kMaxSplitTokens / kBlockSize blocks (64 per
-    // wave, one per lane of a wave's table register); a damaged plan entry is
-    // cut there too.
+    // wave when four walk it, one per lane of a wave's table register); a
+    // damaged plan entry is cut there too.
     const int b_end = min((t_end + kBlockSize - 1) / kBlockSize, b_begin + kMaxSplitTokens / kBlockSize);
     t_end = min(t_end, b_end * kBlockSize);
-    const int per_wave = (b_end - b_begin + kWaves - 1) / kWaves;
-    const int wb_begin = min(b_end, b_begin + w * per_wave);
+    const int nw = MIXED && a.mixed_decode_waves == 2 ? 2 : kWaves;  // waves that walk blocks
+    const int per_wave = (b_end - b_begin + nw - 1) / nw;
+    const int wb_begin = w < nw ? min(b_end, b_begin + w * per_wave) : b_end;
     const int wb_end = min(b_end, wb_begin + per_wave);
 
     // Block-table entries of this wave's blocks are loaded up front, entry
@@ -306,6 +310,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     // K/V loads.  This load comes first: every K/V address depends on it.
     const int32_t *table = a.tables + static_cast<size_t>(s) * a.max_blocks;
     const int tbl_v = lane < wb_end - wb_begin ? table[wb_begin + lane] : 0;
+    const int tbl_v1 = MIXED && lane + 64 < wb_end - wb_begin ? table[wb_begin + 64 + lane] : 0;
 
     // Q^T operands: qm[i] holds query head l%4 at the 8 dims of MFMA i in this
     // lane, chunk_dim(i) .. +7.
@@ -375,7 +380,9 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     // so every pipeline step issues the same number of loads.
     auto issue = [&](int buf, int b) {
         const bool live = b < wb_end;
-        uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readlane(tbl_v, live ? b - wb_begin : 0));
+        const int ti = live ? b - wb_begin : 0;
+        uint32_t phys = static_cast<uint32_t>(MIXED && ti >= 64 ? __builtin_amdgcn_readlane(tbl_v1, ti - 64)
+                                                                : __builtin_amdgcn_readlane(tbl_v, ti));
         phys = phys > last_block ? last_block : phys;
         const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
         const int bytes = live ? static_cast<int>(tile_bytes) : 0;
@@ -1655,13 +1662,14 @@ __global__ __launch_bounds__(256, WGS) void prefill_dma_kernel(DecodeArgs a) {
 
 // A mixed step's decode and prefill pieces in one launch, three work-groups
 // per CU: the decode pieces keep two blocks in flight instead of three (158
-// VGPRs on their own), the F16 prefill pieces copy straight to LDS one stage
-// ahead, the FP8 ones through registers.
+// VGPRs on their own) and are walked by a.mixed_decode_waves of the four
+// waves, the F16 prefill pieces copy straight to LDS one stage ahead, the FP8
+// ones through registers.
 template <bool FP8>
 __global__ __launch_bounds__(256, 3) void mixed_kernel(DecodeArgs a) {
     const uint32_t nd = static_cast<uint32_t>(a.num_items) * static_cast<uint32_t>(a.num_kv_heads);
     if (blockIdx.x < nd)
-        decode_partial_body<2, FP8>(a, blockIdx.x, 0, 0);
+        decode_partial_body<2, FP8, true>(a, blockIdx.x, 0, 0);
     else if constexpr (FP8)
         prefill_body<true, 1>(a, blockIdx.x - nd);
     else

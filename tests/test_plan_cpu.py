@@ -402,3 +402,24 @@ def test_piece_size_balances_the_compute_units(pool):
         info, plan = pa.pa_decode_plan(pool, list(lens), 32)
         _check_cover(list(lens), info, plan)
         assert (info.num_items, info.num_merges, info.max_piece_tokens) == (n_items, n_merges, longest), lens
+
+
+def test_mixed_launch_walks_decode_pieces_with_two_waves_when_the_tiles_dominate(pool):
+    """pa_plan_info.mixed_decode_waves: a mixed step whose prompt tiles take longer
+    than its decode pieces (config 6's geometry) walks the decode pieces with 2
+    of 4 waves so both kinds progress side by side; a step dominated by its
+    decode rows keeps 4, and so does every plan without both kinds."""
+    cfg6_q = [2016] + [1] * 32
+    cfg6_lens = [4032] + [4096] * 32
+    starts = np.concatenate([[0], np.cumsum(cfg6_q)]).astype(np.int32)
+    info, plan = pa.pa_prefill_plan(pool, starts, cfg6_lens, 32)
+    _check_mixed(cfg6_q, cfg6_lens, info, plan)
+    assert info.num_items > 0 and info.num_prefill_items > 0 and info.mixed_decode_waves == 2
+    small_q = [17] + [1] * 32
+    small_lens = [117] + [4096] * 32
+    starts = np.concatenate([[0], np.cumsum(small_q)]).astype(np.int32)
+    info, plan = pa.pa_prefill_plan(pool, starts, small_lens, 32)
+    _check_mixed(small_q, small_lens, info, plan)
+    assert info.num_items > 0 and info.num_prefill_items > 0 and info.mixed_decode_waves == 4
+    assert pa.pa_decode_plan(pool, [4096] * 32, 32)[0].mixed_decode_waves == 4
+    assert pa.pa_prefill_plan(pool, np.array([0, 1, 2], np.int32), [50, 60], 32)[0].mixed_decode_waves == 4
