@@ -64,6 +64,20 @@ def kernel_code_hash():
     return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()
 
 
+def launch_kernels(info):
+    """The kernels one pa_decode_run launch of this plan runs, as the library
+    picks them: ordinary and shared-prefix pieces share cascade_kernel, and a
+    plan that cuts sequences adds the merge."""
+    if info.num_items > 0 and info.num_prefix_items > 0:
+        names = ["cascade_kernel"]
+    else:
+        names = ["decode_partial_kernel"] if info.num_items > 0 else []
+        names += ["decode_prefix_kernel"] if info.num_prefix_items > 0 else []
+    if info.num_merges > 0:
+        names.append("decode_merge_planned_kernel")
+    return " + ".join(names)
+
+
 def read_counters(kv_dtype):
     """HBM traffic per decode_partial launch from the committed rocprofv3 summary,
     or None when it is missing or was taken on other kernel source."""
@@ -518,9 +532,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic if info.num_merges == 0 else None,
-                     "kernel": "decode_partial_kernel" if info.num_merges == 0
-                     else "decode_partial_kernel + " + ("decode_prefix_kernel + " if info.num_prefix_items else "")
-                     + "decode_merge_planned_kernel",
+                     "kernel": launch_kernels(info),
                      "bytes_per_launch": launch_bytes, "kv_bytes_basis": basis,
                      "mean_launch_us": round(part_mean_s * 1e6, 3)},
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,

@@ -6,7 +6,7 @@ runs), in the form kept under profiles/.
     python -m paged_kv_cache_64_amd.prof_summary counters --kernel K --fetch DIR --write DIR
         --cal-fetch DIR --cal-write DIR --cal-bytes B --bytes B --title T --workload W
         --command-fetch C --command-write C --command-cal C [--note N ...]
-    python -m paged_kv_cache_64_amd.prof_summary sq DIR --kernel K [--title T --command C]
+    python -m paged_kv_cache_64_amd.prof_summary sq DIR --kernel K [--title T --command C ... --note N ...]
 
 A counter summary records the kernel source hash of bench.py's
 kernel_code_hash(): bench.py reads the traffic figures only while the source
@@ -176,8 +176,9 @@ def cmd_sq(args):
     out = []
     if args.title:
         out.append(f"# {args.title}")
-    if args.command:
-        out.append(f"# command: {args.command}")
+    for cmd in args.command or []:
+        out.append(f"# command: {cmd}")
+    out += [f"# {n}" for n in args.note or []]
     for c in sorted(names):
         v, n = _match(counter_means(args.dir, c), args.kernel)
         out.append(f"{args.kernel} {c}: {v:.6g} per launch over {n} launches")
@@ -206,7 +207,8 @@ def main(argv=None):
     q.add_argument("dir")
     q.add_argument("--kernel", required=True)
     q.add_argument("--title")
-    q.add_argument("--command")
+    q.add_argument("--command", action="append", help="one per counter pass whose output lies under DIR")
+    q.add_argument("--note", action="append")
     ap.add_argument("-o", "--out")
     args = ap.parse_args(argv)
     text = {"trace": cmd_trace, "counters": cmd_counters, "sq": cmd_sq}[args.cmd](args)

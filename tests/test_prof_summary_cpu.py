@@ -90,3 +90,15 @@ def test_dispatch_trace_skips_warmup_and_reports_the_median(tmp_path):
     out = open(tmp_path / "out.txt").read()
     assert "first 3 dispatches" in out and "median ns" in out
     assert ps.dispatch_stats(str(tmp_path / "none")) is None
+
+
+def test_bench_names_the_kernels_a_decode_launch_runs():
+    from types import SimpleNamespace as NS
+    assert bench.launch_kernels(NS(num_items=32, num_prefix_items=0, num_merges=0)) == "decode_partial_kernel"
+    assert bench.launch_kernels(NS(num_items=40, num_prefix_items=0, num_merges=3)) == \
+        "decode_partial_kernel + decode_merge_planned_kernel"
+    # ordinary and shared-prefix pieces run in one cascade launch, then the merge
+    assert bench.launch_kernels(NS(num_items=340, num_prefix_items=64, num_merges=256)) == \
+        "cascade_kernel + decode_merge_planned_kernel"
+    assert bench.launch_kernels(NS(num_items=0, num_prefix_items=8, num_merges=4)) == \
+        "decode_prefix_kernel + decode_merge_planned_kernel"
