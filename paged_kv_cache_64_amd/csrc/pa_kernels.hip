@@ -989,13 +989,24 @@ __device__ __forceinline__ float max3_raw(float a, float b, float c) {
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
     return d;
 }
-constexpr int kKvRow = kHeadDim + 8;  // padded K rows in LDS (halves): 68 dwords, 4 mod 32 banks
-// Padded V rows (halves): 72 dwords, 8 mod 32, so the four rows a 16-lane
-// group of a transpose read addresses (8 banks each) fall on disjoint banks.
-// With the K stride the rows overlapped by 4 banks: SQ_LDS_BANK_CONFLICT
-// halved (12.3 M -> 6.1 M per launch) and the 2016-token chunk went from
-// 131.0-131.4 to 129.7-129.8 us per layer.
-constexpr int kVRow = kHeadDim + 16;
+// LDS layouts of the K/V tiles, chosen by measuring SQ_LDS_BANK_CONFLICT
+// for each access pattern alone on gfx950.  A key operand read takes one
+// 16-byte chunk of each of 16 rows per 16-lane group; a value transpose read
+// takes 32 bytes of each of 4 rows per 16-lane group; the register-staged
+// copy writes one whole row per 16 lanes.
+//  - Padded rows (register-staged copy): a row stride that is an odd
+//    multiple of 8 dwords (72, 88, 104, 120) is conflict-free for both
+//    reads; 68, 76, 80 or 84 dwords conflicted 2-way, 96 dwords 4-way.  The
+//    reads keep one base address per lane and immediate offsets.  Writes of
+//    one row per 16 lanes are conflict-free; two rows per 16 lanes were not.
+//  - Unpadded 256-byte rows (copy straight into LDS, 1 KiB per
+//    instruction): 16-byte chunk c of key row t at c ^ k_swz(t), of value
+//    row t at c ^ v_swz(t), conflict-free; XORs over 8 (K) and 4 (V) rows
+//    conflicted 2-way, unswizzled K rows 8-way.
+// The F16 prompt chunk went from 12.3 M conflict cycles per launch to none.
+constexpr int kPadRow = kHeadDim + 16;  // halves: 72 dwords
+__device__ __forceinline__ int k_swz(int t) { return t & 15; }
+__device__ __forceinline__ int v_swz(int t) { return 2 * (t & 7); }
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane 4a + b receives half b
 // of the 8-byte chunks addressed by lanes a, a + 4, a + 8, a + 12 (in that
@@ -1024,8 +1035,8 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     const int n = lane & 15, r = lane >> 4;
 
     __shared__ int tbl_lds[kMaxPrefillPieceBlocks];
-    __shared__ _Float16 k_lds[2][kStageBlocks][kBlockSize][kKvRow];  // [buffer][block][row][dim]
-    __shared__ _Float16 v_lds[2][kStageBlocks][kBlockSize][kVRow];
+    __shared__ __attribute__((aligned(16))) _Float16 k_lds[2][kStageBlocks][kBlockSize][kPadRow];  // [buffer][block][row][dim]
+    __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][kStageBlocks][kBlockSize][kPadRow];
     // the tile row r of tensor t (0: K, 1: V) in stage buffer buf
     auto kv_row = [&](int buf, int t, int blk, int row) -> _Float16 * {
         return t ? &v_lds[buf][blk][row][0] : &k_lds[buf][blk][row][0];
@@ -1089,14 +1100,13 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     const float c_scale = a.scale_log2e;
     const h2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 
-    // copies: wave w moves tensor w/2 (K, V) of block w%2 of the pair, 1 KiB per
-    // load instruction: lane l takes bytes 16 l + 1024 i, i.e. for F16 row
-    // l/16 + 4i, dims 8(l%16) .. +7, and for FP8 row l/8 + 8i, dims
-    // 16(l%8) .. +15
+    // copies: wave w moves tensor w/2 (K, V) of block w%2 of the pair: lane l
+    // takes row l/16 + 4i, dims 8(l%16) .. +7 (16 bytes of F16, 8 of FP8
+    // codes), so each 16-lane pass of the LDS writes covers one whole row
     const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
     const size_t tile_bytes = tile_elems() * (FP8 ? 1 : sizeof(uint16_t));
     constexpr int kCopyBlocks = kStageBlocks / 2;  // blocks of one tensor each wave copies per stage
-    constexpr int kLoads = FP8 ? 2 : 4;            // 16-byte loads per lane and tile
+    constexpr int kLoads = 4;                      // loads per lane and tile
     const int cp_tensor = w >> 1, cp_blk0 = (w & 1) * kCopyBlocks;
     const char *cp_layer = cp_tensor ? a.v_layer : a.k_layer;
     // NSETS = 2: the loads of stage k go to register set k % 2 two stages
@@ -1104,7 +1114,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     // compute to arrive before it is written to LDS.  NSETS = 1: one stage
     // ahead, 16 VGPRs fewer (F16).
     h8 stg[NSETS][kCopyBlocks][kLoads];   // F16 pools
-    u4 stg8[NSETS][kCopyBlocks][kLoads];  // FP8 pools: raw codes, widened at commit
+    u2 stg8[NSETS][kCopyBlocks][kLoads];  // FP8 pools: raw codes, widened at commit
     // Value rows at or past the piece's last key (t_hi) may hold anything
     // (slots past the sequence in its last block): the V resource ends at the
     // last row below t_hi, so those rows load as zeros and their zero weights
@@ -1126,7 +1136,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
                 if constexpr (FP8)
-                    stg8[S][x][i] = __builtin_bit_cast(u4, load_shared16(rs, static_cast<uint32_t>(16 * lane + 1024 * i)));
+                    stg8[S][x][i] = load_shared8(rs, static_cast<uint32_t>(8 * lane + 512 * i));
                 else
                     stg[S][x][i] = load_shared16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
             }
@@ -1138,15 +1148,11 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
         for (int x = 0; x < kCopyBlocks; ++x)
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
-                if constexpr (FP8) {
-                    _Float16 *dst = kv_row(buf, cp_tensor, cp_blk0 + x, (lane >> 3) + 8 * i) + 16 * (lane & 7);
-                    const u4 c = stg8[S][x][i];
-                    *reinterpret_cast<h8 *>(dst) = fp8_decode8_h(c.x, c.y);
-                    *reinterpret_cast<h8 *>(dst + 8) = fp8_decode8_h(c.z, c.w);
-                } else {
-                    *reinterpret_cast<h8 *>(kv_row(buf, cp_tensor, cp_blk0 + x, (lane >> 4) + 4 * i) + 8 * n) =
-                        stg[S][x][i];
-                }
+                _Float16 *dst = kv_row(buf, cp_tensor, cp_blk0 + x, (lane >> 4) + 4 * i) + 8 * n;
+                if constexpr (FP8)
+                    *reinterpret_cast<h8 *>(dst) = fp8_decode8_h(stg8[S][x][i].x, stg8[S][x][i].y);
+                else
+                    *reinterpret_cast<h8 *>(dst) = stg[S][x][i];
             }
     };
 
@@ -1345,14 +1351,11 @@ __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "me
 // prefill_body for F16 pools with the copy straight into LDS
 // (buffer_load ... lds, 16 bytes per lane): no staging registers, so three
 // work-groups fit a CU without spilling, or three LDS buffers keep the copy
-// two stages ahead at two per CU.  The K/V tiles sit in LDS unpadded, each
-// row's 16-byte chunks permuted by an XOR swizzle that keeps the operand
-// reads conflict-free: chunk c of key row t at c ^ (t & 7) (the 16-byte
-// reads of rows 0..7 hit 8 distinct bank quads), of value row t at
-// c ^ 2 (t & 3) (a transpose read's four rows hit disjoint bank pairs).  The
-// copy lane that fills a position loads the global chunk the swizzle puts
-// there; out-of-range lanes of a zero-size resource write zeros.  The
-// arithmetic from the scores on and the epilogue are prefill_body's.
+// two stages ahead at two per CU.  The tiles sit in unpadded swizzled rows
+// (k_swz, v_swz); the copy lane that fills a position loads the global chunk
+// the swizzle puts there, and out-of-range lanes of a zero-size resource
+// write zeros.  The arithmetic from the scores on and the epilogue are
+// prefill_body's.
 template <int NB>
 __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t bx) {
     static_assert(NB == 2 || NB == 3, "two or three LDS buffers");
@@ -1364,8 +1367,8 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
     const int n = lane & 15, r = lane >> 4;
 
     __shared__ int tbl_lds[kMaxPrefillPieceBlocks];
-    // unpadded rows; 16-byte chunk c of row t sits at chunk c ^ (t & 7) (K)
-    // or c ^ 2 (t & 3) (V)
+    // unpadded rows; 16-byte chunk c of row t sits at chunk c ^ k_swz(t) (K)
+    // or c ^ v_swz(t) (V)
     __shared__ __attribute__((aligned(16))) _Float16 k_lds[NB][kStageBlocks][kBlockSize][kHeadDim];
     __shared__ __attribute__((aligned(16))) _Float16 v_lds[NB][kStageBlocks][kBlockSize][kHeadDim];
     __shared__ float alpha_lds[kWaves][2][16];
@@ -1440,7 +1443,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
         const int row = 4 * i + (lane >> 4), pos = lane & 15;
-        const int c = cp_tensor ? pos ^ (2 * (row & 3)) : pos ^ (row & 7);
+        const int c = pos ^ (cp_tensor ? v_swz(row) : k_swz(row));
         cp_off[i] = static_cast<uint32_t>(row * (kHeadDim * 2) + 16 * c);
     }
     auto fetch = [&](int b, int buf) {  // stage starting at block b, into LDS buffer buf
@@ -1465,7 +1468,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
     // transpose reads: lane l addresses token 4(l/16) + (l/4)%4, dims 4(l%4) .. +3
     // of a 16-dim slice, so that lane (r, n) receives tokens 4r .. 4r+3 at dim n
     const int tr_row = 4 * r + ((lane >> 2) & 3), tr_col = 4 * (lane & 3);
-    const int tr_swz = 2 * (tr_row & 3);
+    const int tr_swz = v_swz(tr_row);
     auto compute = [&](int buf, int sb, int b) {  // blocks sb, sb+1 of the stage = key blocks b, b+1
         // the pair's K operands, read once for both row tiles
         h8 kx[2][4];
@@ -1473,7 +1476,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                kx[blk][kk] = *reinterpret_cast<const h8 *>(&k_lds[buf][sb + blk][n][8 * ((4 * kk + r) ^ (n & 7))]);
+                kx[blk][kk] = *reinterpret_cast<const h8 *>(&k_lds[buf][sb + blk][n][8 * ((4 * kk + r) ^ k_swz(n))]);
         f4 st[2][2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
