@@ -1021,12 +1021,10 @@ __device__ __forceinline__ h4 lds_read_tr16(const _Float16 *p) {
 constexpr int kStageBlocks = PA_PREFILL_STAGE_BLOCKS;  // key blocks per LDS stage (even)
 static_assert(kStageBlocks % 2 == 0 && kStageBlocks >= 2, "stages hold whole pairs");
 
-// The register-staged copy serves FP8 pools, whose codes are widened on the
-// way into LDS (one stage ahead in the kernels built); F16 pools take
-// prefill_body_dma below.
-template <bool FP8, int NSETS = 2>
-__device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
-    static_assert(NSETS == 1 || NSETS == 2, "one or two copy register sets");
+// Prompt-chunk pieces over an FP8 pool: the codes go through registers, one
+// stage ahead, and are widened to F16 on their way into LDS (F16 pools take
+// prefill_body_dma below, which copies straight into LDS).
+__device__ __forceinline__ void prefill_body_fp8(const DecodeArgs &a, uint32_t bx) {
     const int g = static_cast<int>(bx % a.num_kv_heads);
     const int32_t *it = a.prefill_items + kPrefillItemInts * static_cast<size_t>(bx / a.num_kv_heads);
     const int tid = threadIdx.x;
@@ -1101,27 +1099,21 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     const h2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 
     // copies: wave w moves tensor w/2 (K, V) of block w%2 of the pair: lane l
-    // takes row l/16 + 4i, dims 8(l%16) .. +7 (16 bytes of F16, 8 of FP8
-    // codes), so each 16-lane pass of the LDS writes covers one whole row
+    // takes row l/16 + 4i, codes 8(l%16) .. +7, so each 16-lane pass of the
+    // LDS writes covers one whole row
     const uint32_t last_block = static_cast<uint32_t>(a.num_blocks - 1);
-    const size_t tile_bytes = tile_elems() * (FP8 ? 1 : sizeof(uint16_t));
+    const size_t tile_bytes = tile_elems();        // one byte per code
     constexpr int kCopyBlocks = kStageBlocks / 2;  // blocks of one tensor each wave copies per stage
-    constexpr int kLoads = 4;                      // loads per lane and tile
+    constexpr int kLoads = 4;                      // 8-byte loads per lane and tile
     const int cp_tensor = w >> 1, cp_blk0 = (w & 1) * kCopyBlocks;
     const char *cp_layer = cp_tensor ? a.v_layer : a.k_layer;
-    // NSETS = 2: the loads of stage k go to register set k % 2 two stages
-    // before that stage is consumed, so a stage's copy has a whole stage of
-    // compute to arrive before it is written to LDS.  NSETS = 1: one stage
-    // ahead, 16 VGPRs fewer (F16).
-    h8 stg[NSETS][kCopyBlocks][kLoads];   // F16 pools
-    u2 stg8[NSETS][kCopyBlocks][kLoads];  // FP8 pools: raw codes, widened at commit
+    u2 stg8[kCopyBlocks][kLoads];  // raw codes of the next stage, widened at commit
     // Value rows at or past the piece's last key (t_hi) may hold anything
     // (slots past the sequence in its last block): the V resource ends at the
     // last row below t_hi, so those rows load as zeros and their zero weights
     // cannot meet a NaN.  Keys below t_hi are stored tokens, finite like every
     // key the rows see.
-    auto fetch = [&](int b, auto set) {  // stage starting at block b, into register set `set`
-        constexpr int S = decltype(set)::value;
+    auto fetch = [&](int b) {  // stage starting at block b, into the staging registers
 #pragma unroll
         for (int x = 0; x < kCopyBlocks; ++x) {
             const int bb = b + cp_blk0 + x;
@@ -1131,28 +1123,19 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
             const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
             const int rows = cp_tensor ? min(max(t_hi - bb * kBlockSize, 0), kBlockSize) : kBlockSize;
             // (wave-uniform; said so, or the compiler wraps each load in a waterfall loop)
-            const int bytes = __builtin_amdgcn_readfirstlane(live ? rows * kHeadDim * (FP8 ? 1 : 2) : 0);
+            const int bytes = __builtin_amdgcn_readfirstlane(live ? rows * kHeadDim : 0);
             const __amdgpu_buffer_rsrc_t rs = tile_rsrc(cp_layer + base, bytes);
 #pragma unroll
-            for (int i = 0; i < kLoads; ++i) {
-                if constexpr (FP8)
-                    stg8[S][x][i] = load_shared8(rs, static_cast<uint32_t>(8 * lane + 512 * i));
-                else
-                    stg[S][x][i] = load_shared16(rs, static_cast<uint32_t>(16 * lane + 1024 * i));
-            }
+            for (int i = 0; i < kLoads; ++i) stg8[x][i] = load_shared8(rs, static_cast<uint32_t>(8 * lane + 512 * i));
         }
     };
-    auto commit = [&](int buf, auto set) {  // register set `set` into LDS buffer buf
-        constexpr int S = decltype(set)::value;
+    auto commit = [&](int buf) {  // the staging registers, widened, into LDS buffer buf
 #pragma unroll
         for (int x = 0; x < kCopyBlocks; ++x)
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
                 _Float16 *dst = kv_row(buf, cp_tensor, cp_blk0 + x, (lane >> 4) + 4 * i) + 8 * n;
-                if constexpr (FP8)
-                    *reinterpret_cast<h8 *>(dst) = fp8_decode8_h(stg8[S][x][i].x, stg8[S][x][i].y);
-                else
-                    *reinterpret_cast<h8 *>(dst) = stg[S][x][i];
+                *reinterpret_cast<h8 *>(dst) = fp8_decode8_h(stg8[x][i].x, stg8[x][i].y);
             }
     };
 
@@ -1255,32 +1238,27 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
     // below its last query's position
     const int n_stages = (b_hi - b_lo + kStageBlocks - 1) / kStageBlocks;
     const int w_blocks = w_end > t_lo ? (w_end + kBlockSize - 1) / kBlockSize - b_lo : 0;  // blocks this wave needs
-    using Set0 = std::integral_constant<int, 0>;
-    using Set1 = std::integral_constant<int, 1>;
     if (n_stages > 0) {
-        fetch(b_lo, Set0{});
-        commit(0, Set0{});
-        if (NSETS == 2 && n_stages > 1) fetch(b_lo + kStageBlocks, std::integral_constant<int, NSETS - 1>{});
+        fetch(b_lo);
+        commit(0);
         __syncthreads();
     }
-    // stage st reads LDS buffer st % 2; meanwhile stage st+NSETS is loaded
-    // into register set st % NSETS and, at the end, stage st+1 goes from
-    // register set (st+1) % NSETS into LDS buffer (st+1) % 2, which stage
-    // st-1 read before the last barrier
-    auto stage = [&](int st, auto set) {
-        constexpr int S = decltype(set)::value;  // == st % 2
-        constexpr int kLoadSet = S % NSETS, kCommitSet = (S ^ 1) % NSETS;
+    // stage st reads LDS buffer st % 2; meanwhile stage st+1 is loaded into
+    // the staging registers and, at the end, goes into LDS buffer (st+1) % 2,
+    // which stage st-1 read before the last barrier
+    auto stage = [&](int st, auto bufc) {
+        constexpr int S = decltype(bufc)::value;  // == st % 2
         const int b0 = b_lo + kStageBlocks * st;
-        if (st + NSETS < n_stages) fetch(b0 + NSETS * kStageBlocks, std::integral_constant<int, kLoadSet>{});
+        if (st + 1 < n_stages) fetch(b0 + kStageBlocks);
 #pragma unroll
         for (int sb = 0; sb < kStageBlocks; sb += 2)
             if (kStageBlocks * st + sb < w_blocks) compute(S, sb, b0 + sb);
-        if (st + 1 < n_stages) commit(S ^ 1, std::integral_constant<int, kCommitSet>{});
+        if (st + 1 < n_stages) commit(S ^ 1);
         __syncthreads();
     };
     for (int st = 0; st < n_stages; st += 2) {
-        stage(st, Set0{});
-        if (st + 1 < n_stages) stage(st + 1, Set1{});
+        stage(st, std::integral_constant<int, 0>{});
+        if (st + 1 < n_stages) stage(st + 1, std::integral_constant<int, 1>{});
     }
     if (rows_w <= 0) return;
 
@@ -1307,7 +1285,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
             const float m = ml_lds[w][rt][t][0], l = ml_lds[w][rt][t][1];
             if (direct) {
                 const size_t qrow = static_cast<size_t>(min(row0 + tok, a.num_q_rows - 1));
-                const float inv = (FP8 ? a.v_scale : 1.0f) / l;  // FP8: V's scale
+                const float inv = a.v_scale / l;  // V's scale
                 _Float16 *orow = reinterpret_cast<_Float16 *>(a.out + (qrow * a.num_q_heads + head) * kHeadDim);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) orow[16 * j + n] = static_cast<_Float16>(oacc[rt][j][c] * inv);  // dim 16j + n
@@ -1315,9 +1293,9 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs &a, uint32_t bx) {
                 const int64_t slot64 = static_cast<int64_t>(base_slot) + static_cast<int64_t>(tok) * np + piece;
                 const size_t slot = static_cast<size_t>(min<int64_t>(slot64, a.num_slots - 1));
                 const size_t rec = slot * a.num_q_heads + head;
-                const float vs = FP8 ? a.v_scale : 1.0f;  // records hold values, as the decode pieces' do
+                // records hold values (V's scale applied), as the decode pieces' do
 #pragma unroll
-                for (int j = 0; j < 8; ++j) a.o_part[rec * kHeadDim + 16 * j + n] = oacc[rt][j][c] * vs;
+                for (int j = 0; j < 8; ++j) a.o_part[rec * kHeadDim + 16 * j + n] = oacc[rt][j][c] * a.v_scale;
                 if (n == 0) *reinterpret_cast<float2 *>(a.ml_part + rec * 2) = make_float2(m, l);
             }
         }
@@ -1348,14 +1326,14 @@ __device__ __forceinline__ void lds_read_tr16_x8(u2 (&d)[8], const uint32_t (&a)
 }
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// prefill_body for F16 pools with the copy straight into LDS
+// The prompt-chunk body for F16 pools, with the copy straight into LDS
 // (buffer_load ... lds, 16 bytes per lane): no staging registers, so three
 // work-groups fit a CU without spilling, or three LDS buffers keep the copy
 // two stages ahead at two per CU.  The tiles sit in unpadded swizzled rows
 // (k_swz, v_swz); the copy lane that fills a position loads the global chunk
 // the swizzle puts there, and out-of-range lanes of a zero-size resource
 // write zeros.  The arithmetic from the scores on and the epilogue are
-// prefill_body's.
+// prefill_body_fp8's.
 template <int NB>
 __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t bx) {
     static_assert(NB == 2 || NB == 3, "two or three LDS buffers");
@@ -1653,7 +1631,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
 template <bool FP8, int WGS>
 __global__ __launch_bounds__(256, WGS) void prefill_kernel(DecodeArgs a) {
     static_assert(FP8 && WGS == 3, "F16 pools take prefill_dma_kernel");
-    prefill_body<FP8, 1>(a, blockIdx.x);
+    prefill_body_fp8(a, blockIdx.x);
 }
 
 // F16 pools: the copy goes straight to LDS, NB - 1 stages ahead; WGS
@@ -1674,7 +1652,7 @@ __global__ __launch_bounds__(256, 3) void mixed_kernel(DecodeArgs a) {
     if (blockIdx.x < nd)
         decode_partial_body<2, FP8, true>(a, blockIdx.x, 0, 0);
     else if constexpr (FP8)
-        prefill_body<true, 1>(a, blockIdx.x - nd);
+        prefill_body_fp8(a, blockIdx.x - nd);
     else
         prefill_body_dma<2>(a, blockIdx.x - nd);
 }
