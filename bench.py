@@ -32,7 +32,9 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: achieved KV GB/s (% HBM peak) and decode tokens/s"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_64_amd", "csrc", "pa_kernels.hip")
+# the kernels and the header whose constants and argument layout they compile with
+KERNEL_SOURCES = (os.path.join(ROOT, "paged_kv_cache_64_amd", "csrc", "pa_internal.h"),
+                  os.path.join(ROOT, "paged_kv_cache_64_amd", "csrc", "pa_kernels.hip"))
 COUNTERS_FILES = {"f16": os.path.join(ROOT, "profiles", "decode_partial_c3_counters.txt"),
                   "fp8": os.path.join(ROOT, "profiles", "decode_partial_fp8_c3_counters.txt")}
 COUNTERS_CONFIG = 3          # the workload the counter files were taken on
@@ -55,10 +57,12 @@ def host_cpu_model():
 
 
 def kernel_code_hash():
-    """sha256 of the kernel source with comments and whitespace removed: it
+    """sha256 of the kernel sources with comments and whitespace removed: it
     changes with the code, not with its comments."""
-    with open(KERNEL_SOURCE) as f:
-        text = f.read()
+    text = ""
+    for path in KERNEL_SOURCES:
+        with open(path) as f:
+            text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()

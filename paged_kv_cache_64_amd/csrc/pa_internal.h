@@ -101,7 +101,13 @@ constexpr int kItemInts = 8;
 constexpr int kMergeInts = 4;
 constexpr int kPrefillItemInts = 12;
 constexpr int kPrefillTile = 32;             // query tokens per prefill work-group (16 per wave pair)
-constexpr int kMaxPrefillPieceBlocks = 256;  // key blocks per prefill piece
+// Key blocks per prefill piece (the piece's table row is staged in LDS, 6 KiB).
+// A 16,352-token chunk at position 16,352 has tiles of 1,022-2,044 blocks: cut
+// into pieces of at most 256 blocks they wrote 1.8 GB of fp32 partial records
+// per layer and the merge launch took 0.48 ms.  At most 1,024 blocks (0.5 GB)
+// the chunk took 6.28-6.36 ms per layer, at most 1,536 (0.3 GB, the longer
+// half of the tiles cut in two) 6.10 ms.
+constexpr int kMaxPrefillPieceBlocks = 1536;
 constexpr int kPrefixItemInts = 8;
 constexpr int kMemberInts = 2;
 constexpr int kMaxMembers = 16;        // 16 members x 4 query heads = 64 stacked rows

@@ -328,12 +328,22 @@ def test_mixed_plan_produces_every_row_once(pool, q_lens, hist):
 
 
 def test_mixed_plan_long_chunk_is_cut_and_merged(pool):
+    # tiles of 1,877-2,004 key blocks: longer than a piece may be (1,536 blocks)
+    q_lens, lens = [2048], [32048]
+    info, plan = pa.pa_prefill_plan(pool, [0, 2048], lens, 32)
+    items, merges, pf = _check_mixed(q_lens, lens, info, plan)
+    assert info.num_items == 0 and info.num_prefill_items == 2 * 64
+    assert info.num_merges == 2048 and info.workspace_bytes > 0
+    assert (pf[:, 5] - pf[:, 4]).max() <= 1536 * 16
+
+
+def test_mixed_plan_keeps_tiles_whole_when_they_fit_a_piece(pool):
+    # 2048 queries after 6144 tokens of history: tiles of 386-512 blocks fill
+    # 64 x 8 work-groups, so none is cut and nothing is merged
     q_lens, lens = [2048], [8192]
     info, plan = pa.pa_prefill_plan(pool, [0, 2048], lens, 32)
     items, merges, pf = _check_mixed(q_lens, lens, info, plan)
-    assert info.num_items == 0 and info.num_prefill_items > 32
-    assert info.num_merges > 0 and info.workspace_bytes > 0
-    assert (pf[:, 5] - pf[:, 4]).max() <= 256 * 16
+    assert info.num_prefill_items == 64 and info.num_merges == 0 and info.num_slots == 0
 
 
 def test_mixed_plan_rejects_bad_offsets(pool):
