@@ -677,28 +677,85 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// decode_merge_planned: grid (merge entry, query-head pair); the pieces of
-// sequence s are records first .. first + n - 1.
+// decode_merge_planned: grid (merge entry, group of HPW query heads); the
+// pieces of sequence s are records first .. first + n - 1.  A merge's records
+// of HPW consecutive heads are HPW x 128 contiguous floats; thread t merges
+// elements t, t + 256, ... of them (HPW / 2 each).  Few merges (decode
+// steps) keep two heads per work-group for parallelism; many (cut prompt
+// tiles, one merge per query token) take more heads per work-group rather
+// than launch tens of thousands of tiny ones.
 // ---------------------------------------------------------------------------
+// N records (N <= kMergeBatch) of E elements per thread, every load issued
+// before any arithmetic: the same sums in the same order as merge_records.
+template <int N, int E, typename Ptr>
+__device__ __forceinline__ void merge_records_n(const Ptr &ptrs, float (&res)[E]) {
+    float2 ml[E][N];
+    float o[E][N];
+#pragma unroll
+    for (int k = 0; k < E; ++k)
+#pragma unroll
+        for (int i = 0; i < N; ++i) ptrs(k, i, ml[k][i], o[k][i]);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < N; ++i) M = fmaxf(M, ml[k][i].x);
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float wgt = ml[k][i].x == -INFINITY ? 0.0f : fast_exp2(ml[k][i].x - M);
+            L += wgt * ml[k][i].y;
+            O += wgt * o[k][i];
+        }
+        res[k] = O / L;
+    }
+}
+
+template <int HPW>
 __global__ __launch_bounds__(256) void decode_merge_planned_kernel(DecodeArgs a) {
+    static_assert(HPW % 2 == 0 && HPW <= 32, "heads per work-group");
+    constexpr int E = HPW / 2;  // elements per thread
     const int32_t *m = a.merges + kMergeInts * static_cast<size_t>(blockIdx.x);
     const int row = min(max(m[3], 0), a.num_q_rows - 1);  // the output row
     const int first = max(m[1], 0);
     const int n = min(m[2], a.num_slots - first);
-    const int h = blockIdx.y * 2 + (threadIdx.x >> 7);
-    const int d = threadIdx.x & 127;
-    if (h >= a.num_q_heads) return;
-    uint16_t *out = a.out + (static_cast<size_t>(row) * a.num_q_heads + h) * kHeadDim + d;
-    if (n <= 0) {
-        *out = 0;
+    const int d = static_cast<int>(threadIdx.x) % kHeadDim;
+    const int h0 = static_cast<int>(blockIdx.y) * HPW + static_cast<int>(threadIdx.x) / kHeadDim;  // + 2k
+    // 2 to 4 records (cut prompt tiles, most decode merges): straight-line
+    if (n >= 2 && n <= 4 && static_cast<int>(blockIdx.y) * HPW + HPW <= a.num_q_heads) {
+        auto ptrs = [&](int k, int i, float2 &mlv, float &ov) {
+            const size_t rec = static_cast<size_t>(first + i) * a.num_q_heads + h0 + 2 * k;
+            mlv = *reinterpret_cast<const float2 *>(a.ml_part + rec * 2);
+            ov = a.o_part[rec * kHeadDim + d];
+        };
+        float res[E];
+        if (n == 2) merge_records_n<2, E>(ptrs, res);
+        else if (n == 3) merge_records_n<3, E>(ptrs, res);
+        else merge_records_n<4, E>(ptrs, res);
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            *reinterpret_cast<_Float16 *>(a.out + (static_cast<size_t>(row) * a.num_q_heads + h0 + 2 * k) * kHeadDim +
+                                          d) = static_cast<_Float16>(res[k]);
         return;
     }
-    const float r = merge_records(n, [&](int i, float2 &mlv, float &ov) {
-        const size_t rec = static_cast<size_t>(first + i) * a.num_q_heads + h;
-        mlv = *reinterpret_cast<const float2 *>(a.ml_part + rec * 2);
-        ov = a.o_part[rec * kHeadDim + d];
-    });
-    *reinterpret_cast<_Float16 *>(out) = static_cast<_Float16>(r);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const int e = static_cast<int>(threadIdx.x) + 256 * k;
+        const int h = static_cast<int>(blockIdx.y) * HPW + e / kHeadDim;
+        const int d = e % kHeadDim;
+        if (h >= a.num_q_heads) break;
+        uint16_t *out = a.out + (static_cast<size_t>(row) * a.num_q_heads + h) * kHeadDim + d;
+        if (n <= 0) {
+            *out = 0;
+            continue;
+        }
+        const float r = merge_records(n, [&](int i, float2 &mlv, float &ov) {
+            const size_t rec = static_cast<size_t>(first + i) * a.num_q_heads + h;
+            mlv = *reinterpret_cast<const float2 *>(a.ml_part + rec * 2);
+            ov = a.o_part[rec * kHeadDim + d];
+        });
+        *reinterpret_cast<_Float16 *>(out) = static_cast<_Float16>(r);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1713,8 +1770,17 @@ hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_merge_planned_kernel, dim3(a.num_merges, (a.num_q_heads + 1) / 2), dim3(256), 0, stream,
-                       a);
+    // about 2,048 or more work-groups either way: a 32-head step's 8 merges
+    // take 128 of two heads; a prompt chunk's 8,000 take 16,000 of 16
+    if (a.num_merges >= 2048)
+        hipLaunchKernelGGL(decode_merge_planned_kernel<16>, dim3(a.num_merges, (a.num_q_heads + 15) / 16), dim3(256), 0,
+                           stream, a);
+    else if (a.num_merges >= 512)
+        hipLaunchKernelGGL(decode_merge_planned_kernel<8>, dim3(a.num_merges, (a.num_q_heads + 7) / 8), dim3(256), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(decode_merge_planned_kernel<2>, dim3(a.num_merges, (a.num_q_heads + 1) / 2), dim3(256), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -206,6 +206,21 @@ def test_mixed_step_under_a_16384_token_budget_sampled():
     m.close()
 
 
+def test_long_history_chunk_merges_with_eight_heads_per_work_group_sampled():
+    """A 1,024-token chunk after 26,000 tokens of history: its 32 tiles of
+    1,627-1,689 key blocks exceed a piece (1,536 blocks) and are cut in two,
+    so 1,024 query tokens are merged, with the merge launch's eight-head
+    work-groups (512-2,047 merges).  Rows are sampled."""
+    m = Mixed([1024], [26000], seed=105)
+    out, plan = m.run()
+    report("1024 after 26000", prefill_items=plan.info.num_prefill_items, merges=plan.info.num_merges)
+    assert plan.info.num_prefill_items == 64 and plan.info.num_merges == 1024
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 511, 1023], rng.choice(1024, 10, replace=False)])).astype(np.int64)
+    compare("1024 after 26000 sampled", out[torch.from_numpy(rows).cuda()], m.reference(rows))
+    m.close()
+
+
 @pytest.mark.parametrize("q_lens,hist", [([2100], [0]), ([2100, 1, 1, 1], [0, 4000, 100, 2047])])
 def test_more_tiles_than_one_round_sampled(q_lens, hist):
     """66 prompt tiles (528 work-groups, more than one round of two per CU):
