@@ -51,7 +51,7 @@ class PlanInfo(ctypes.Structure):
                 ("max_piece_tokens", ctypes.c_int32), ("num_prefix_items", ctypes.c_int32),
                 ("num_members", ctypes.c_int32), ("shared_newest", ctypes.c_int32),
                 ("num_prefill_items", ctypes.c_int32), ("num_q_rows", ctypes.c_int32),
-                ("mixed_decode_waves", ctypes.c_int32),
+                ("mixed_decode_waves", ctypes.c_int32), ("decode_wave_heads", ctypes.c_int32),
                 ("plan_bytes", ctypes.c_size_t),
                 ("workspace_bytes", ctypes.c_size_t)]
 

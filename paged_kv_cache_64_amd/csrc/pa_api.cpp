@@ -204,6 +204,17 @@ constexpr int kDispatchUnits = 256;
 constexpr int kSlotsPerUnit = 2;
 constexpr int64_t kWgOverheadBlocks = 3;
 constexpr int64_t kMergeBlocks = 16;
+// Per-wave KV heads (decode_wave_heads): each wave walks a whole piece for
+// its own KV head, so a work-group's fixed work (query, table, pipeline
+// start, epilogue) is spread over four times the blocks and no partial sums
+// cross waves.  Pieces are then at most one table register of blocks, and the
+// mode is chosen when it still leaves a work-group per dispatch unit.
+// Measured on one-layer cold decodes (F16 / FP8 us, four-wave split -> wave
+// heads): 1024 x 128 tokens 117.5 -> 96.7 / 81.5 -> 55.6; 512 x 256
+// 100.6 -> 90.1 / 62.4 -> 49.6; 256 x 1024 170.1 -> 161.7 / 91.9 -> 89.1;
+// 128 x 512 (256 work-groups) 46.7 -> 44.6 / 28.5 -> 26.5; but 64 x 1024
+// (128 work-groups) 45.7 -> 67.0 / 27.6 -> 39.9.
+constexpr int kWaveHeadsMaxBlocks = 64;
 
 // Blocks of each piece when every context is cut into near-equal pieces of
 // at most max_piece blocks (an empty context gives an empty piece), longest
@@ -451,6 +462,11 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
         inf.num_prefill_items = 0;
         inf.num_q_rows = batch;
         inf.mixed_decode_waves = pa::kWaves;
+        inf.decode_wave_heads = pool->desc.num_kv_heads % pa::kWaves == 0 && longest <= kWaveHeadsMaxBlocks * kBlockSize &&
+                                        static_cast<int64_t>(n_items) * (pool->desc.num_kv_heads / pa::kWaves) >=
+                                            kDispatchUnits
+                                    ? 1
+                                    : 0;
         inf.plan_bytes = sizeof(int32_t) * (pa::kPlanHeader + pa::kItemInts * n_items + merges.size() +
                                             pitems.size() + mlist.size());
         size_t o_bytes = 0;
@@ -748,6 +764,10 @@ pa_status run_plan(pa_pool *pool, int32_t layer, const pa_plan_info *info, const
     a.prefill_items = a.members + static_cast<size_t>(pa::kMemberInts) * info->num_members;
     a.num_prefill_items = info->num_prefill_items;
     a.mixed_decode_waves = info->mixed_decode_waves == 2 ? 2 : pa::kWaves;
+    a.decode_wave_heads = info->decode_wave_heads == 1 && a.num_kv_heads % pa::kWaves == 0 &&
+                                  info->max_piece_tokens <= kWaveHeadsMaxBlocks * kBlockSize
+                              ? 1
+                              : 0;
     if (info->num_items > 0 && info->num_prefill_items > 0 &&
         static_cast<int64_t>(info->num_items + info->num_prefill_items) * pool->desc.num_kv_heads <= 0x7fffffff) {
         // decode and prefill pieces share one launch

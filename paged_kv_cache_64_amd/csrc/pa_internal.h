@@ -87,6 +87,9 @@ struct DecodeArgs {
     int32_t num_q_rows;  // rows of q / out: batch for a decode step, total query tokens for a mixed one
     // waves of a work-group that walk a decode piece in a mixed launch (2 or 4)
     int32_t mixed_decode_waves;
+    // decode launches: 1 = four KV heads per work-group, one per wave, each
+    // wave walking its head's whole piece (short pieces; Hkv a multiple of 4)
+    int32_t decode_wave_heads;
 };
 
 // Serialised host plan: a header of kPlanHeader int32, then the decode items,

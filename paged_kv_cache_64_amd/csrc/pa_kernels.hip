@@ -233,14 +233,22 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
 // MIXED: the decode pieces of a mixed launch, walked by a.mixed_decode_waves
 // (2 or 4) of the work-group's waves; a wave then owns up to 128 blocks, its
 // table entries in two registers.
-template <int NBUF, bool FP8, bool MIXED = false>
+// WH: each of the four waves takes its own KV head of the piece and walks all
+// of the piece's blocks (at most 64), so no partial sums cross waves; the
+// plan asks for this when its pieces are short (a work-group's fixed work is
+// then spread over four times the blocks).
+template <int NBUF, bool FP8, bool MIXED = false, bool WH = false>
 __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_t bx, uint32_t by, uint32_t bz) {
+    static_assert(!(WH && MIXED), "a mixed launch keeps one KV head per work-group");
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     // Planned launches number work-groups item-major with the KV head fastest,
     // so the heads of one piece -- whose tiles share each 32 KiB block of
     // K and of V -- run side by side, as in the fixed-split grid.
-    const int g = a.items != nullptr ? static_cast<int>(bx % a.num_kv_heads) : static_cast<int>(by);
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
+    const int wg_heads = WH ? a.num_kv_heads / kWaves : a.num_kv_heads;  // work-groups per item
+    const int g = a.items == nullptr ? static_cast<int>(by)
+                  : WH               ? static_cast<int>(bx % wg_heads) * kWaves + w
+                                     : static_cast<int>(bx % a.num_kv_heads);
     const int lane = tid & 63;
     const int r = lane >> 4, n = lane & 15;
     const int ktok = 4 * (n & 3) + (n >> 2);  // the token of this lane's MFMA row of K
@@ -259,7 +267,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     if (a.items != nullptr) {
         // Plan entries are clamped so a damaged plan cannot index outside
         // q, out, the tables or the workspace.
-        const int32_t *it = a.items + kItemInts * static_cast<size_t>(bx / a.num_kv_heads);
+        const int32_t *it = a.items + kItemInts * static_cast<size_t>(bx / wg_heads);
         s = min(max(it[0], 0), a.batch - 1);
         qrow = min(max(it[5], 0), a.num_q_rows - 1);
         ctx = min(max(it[3], 0), a.max_blocks * kBlockSize);
@@ -286,9 +294,18 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
         // Nothing to attend to.  A direct piece that starts at 0 owns an
         // empty context, whose output row is zero.
         if (direct && t_begin == 0) {
-            const int h = tid >> 6, d0 = (tid & 63) * 2;
-            uint16_t *o = a.out + (static_cast<size_t>(qrow) * a.num_q_heads + head0 + h) * kHeadDim + d0;
-            *reinterpret_cast<uint32_t *>(o) = 0u;
+            const int d0 = (tid & 63) * 2;
+            if constexpr (WH) {  // the wave's own four heads
+#pragma unroll
+                for (int h = 0; h < kGroup; ++h) {
+                    uint16_t *o = a.out + (static_cast<size_t>(qrow) * a.num_q_heads + head0 + h) * kHeadDim + d0;
+                    *reinterpret_cast<uint32_t *>(o) = 0u;
+                }
+            } else {
+                const int h = tid >> 6;
+                uint16_t *o = a.out + (static_cast<size_t>(qrow) * a.num_q_heads + head0 + h) * kHeadDim + d0;
+                *reinterpret_cast<uint32_t *>(o) = 0u;
+            }
         }
         return;
     }
@@ -296,11 +313,12 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     // A piece never spans more than kMaxSplitTokens / kBlockSize blocks (64 per
     // wave when four walk it, one per lane of a wave's table register); a
     // damaged plan entry is cut there too.
-    const int b_end = min((t_end + kBlockSize - 1) / kBlockSize, b_begin + kMaxSplitTokens / kBlockSize);
+    // (WH: 64 blocks, as each wave walks the whole piece)
+    const int b_end = min((t_end + kBlockSize - 1) / kBlockSize, b_begin + (WH ? 64 : kMaxSplitTokens / kBlockSize));
     t_end = min(t_end, b_end * kBlockSize);
     const int nw = MIXED && a.mixed_decode_waves == 2 ? 2 : kWaves;  // waves that walk blocks
-    const int per_wave = (b_end - b_begin + nw - 1) / nw;
-    const int wb_begin = w < nw ? min(b_end, b_begin + w * per_wave) : b_end;
+    const int per_wave = WH ? b_end - b_begin : (b_end - b_begin + nw - 1) / nw;
+    const int wb_begin = WH ? b_begin : w < nw ? min(b_end, b_begin + w * per_wave) : b_end;
     const int wb_end = min(b_end, wb_begin + per_wave);
 
     // Block-table entries of this wave's blocks are loaded up front, entry
@@ -334,7 +352,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     const int new_blk = new_tok / kBlockSize;
     const int new_off = new_tok % kBlockSize;
     constexpr int kChunks = FP8 ? 8 : 16;  // 16-byte chunks of a stored K or V row
-    const bool stores_new = owns_new && w == 0 && lane < 2 * kChunks;
+    const bool stores_new = owns_new && (WH || w == 0) && lane < 2 * kChunks;  // WH: each wave its own head
     u4 kn_raw[4], vn_raw;  // K: dims chunk_dim(i) .. +7; V: dims 8n .. 8n+7
     u4 st_raw[2];          // the stored row's chunk as F16: 16 values (FP8 pools) or 8
     uint32_t new_phys = 0;
@@ -568,6 +586,27 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
         dst[0] = make_float4(ov[0], ov[1], ov[2], ov[3]);
         dst[1] = make_float4(ov[4], ov[5], ov[6], ov[7]);
     }
+    if constexpr (WH) {
+        // the wave's own four heads, each finished by this wave alone
+        wave_lds_sync();
+        const int d0 = lane * 2;
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) {
+            const float M = m_lds[w][h], L = l_lds[w][h];
+            const float2 v = *reinterpret_cast<const float2 *>(&o_lds[w][h][d0]);
+            const float O0 = FP8 ? v.x * a.v_scale : v.x, O1 = FP8 ? v.y * a.v_scale : v.y;
+            const size_t row = static_cast<size_t>(qrow) * a.num_q_heads + head0 + h;
+            if (direct) {
+                h2 pr = {static_cast<_Float16>(O0 / L), static_cast<_Float16>(O1 / L)};
+                *reinterpret_cast<h2 *>(a.out + row * kHeadDim + d0) = pr;
+            } else {
+                const size_t slot = static_cast<size_t>(rec_base + static_cast<int64_t>(head0 + h) * rec_stride);
+                *reinterpret_cast<float2 *>(a.o_part + slot * kHeadDim + d0) = make_float2(O0, O1);
+                if (d0 == 0) *reinterpret_cast<float2 *>(a.ml_part + slot * 2) = make_float2(M, L);
+            }
+        }
+        return;
+    }
     __syncthreads();
 
     // ---- merge the four waves: thread -> (head, 2 dims) ----
@@ -605,9 +644,9 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs &a, uint32_
     }
 }
 
-template <int NBUF, bool FP8>
+template <int NBUF, bool FP8, bool WH = false>
 __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
-    decode_partial_body<NBUF, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    decode_partial_body<NBUF, FP8, false, WH>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Records a merge loads in one round (the merges are latency-bound).
@@ -1753,6 +1792,14 @@ hipError_t launch_write_kv(const WriteKvArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
+    if (a.items && a.decode_wave_heads) {  // four KV heads per work-group, one per wave
+        const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_items) * (a.num_kv_heads / kWaves)), 1, 1);
+        if (a.elem_bytes == 1)
+            hipLaunchKernelGGL((decode_partial_kernel<PA_DECODE_NBUF_FP8, true, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_partial_kernel<PA_DECODE_NBUF, false, true>), grid, dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     const dim3 grid = a.items ? dim3(static_cast<uint32_t>(static_cast<int64_t>(a.num_items) * a.num_kv_heads), 1, 1)
                               : dim3(a.max_splits, a.num_kv_heads, a.batch);
     if (a.elem_bytes == 1)

@@ -50,8 +50,10 @@ def _poison_tails(st, layer=0):
     return n
 
 
-def _planned(st, layer=0, k_new=None, v_new=None):
+def _planned(st, layer=0, k_new=None, v_new=None, wave_heads=None):
     plan = st.pool.plan(st.w.ctx_lens)
+    if wave_heads is not None:  # override the planner's choice of per-wave KV heads
+        plan.info.decode_wave_heads = wave_heads
     q, tables = st.dev[layer]
     out = torch.empty_like(q)
     st.pool.run(layer, plan, q, out, tables, st.w.scale, k_new=k_new, v_new=v_new)
@@ -112,6 +114,8 @@ def test_fp8_ragged_batch_fixed_phases_and_planned():
     planned, plan = _planned(st)
     report("fp8 planned", items=plan.info.num_items, merges=plan.info.num_merges)
     compare("fp8 ragged planned", planned, ref)
+    assert plan.info.max_piece_tokens <= 1024
+    compare("fp8 ragged planned, wave heads", _planned(st, wave_heads=1)[0], ref)
     st.close()
 
 
@@ -171,7 +175,7 @@ def test_fp8_config_full_parity(k):
     st.close()
 
 
-@pytest.mark.parametrize("planned", [False, True])
+@pytest.mark.parametrize("planned", [False, True, "wave_heads"])
 def test_fp8_append_encodes_the_newest_token_and_attends_to_it(planned):
     lens = [1, 16, 17, 100, 257, 1000, 0, 4097]
     w = workloads.custom(lens, seed=66)
@@ -183,8 +187,10 @@ def test_fp8_append_encodes_the_newest_token_and_attends_to_it(planned):
     v_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
     kd, vd = torch.from_numpy(k_new).cuda(), torch.from_numpy(v_new).cuda()
     qd, td = st.dev[0]
+    wh = 1 if planned == "wave_heads" else None
     if planned:
-        out, _ = _planned(st, k_new=kd, v_new=vd)
+        out, plan = _planned(st, k_new=kd, v_new=vd, wave_heads=wh)
+        assert plan.info.max_piece_tokens <= 1024
     else:
         out = torch.empty_like(qd)
         st.pool.decode(0, qd, out, td, st.lens, w.max_context_len, w.scale, k_new=kd, v_new=vd)
@@ -207,7 +213,7 @@ def test_fp8_append_encodes_the_newest_token_and_attends_to_it(planned):
         assert np.array_equal(kp[blk, :, off, :], qk[s])
         assert np.array_equal(vp[blk, :, off, :], qv[s])
     # a read-only decode of the same schedule afterwards gives the same bits
-    again = _planned(st)[0] if planned else st.decode(0)
+    again = _planned(st, wave_heads=wh)[0] if planned else st.decode(0)
     assert torch.equal(again.view(torch.int16), out.view(torch.int16))
     st.close()
 

@@ -298,8 +298,10 @@ def test_append_decode_writes_the_newest_token_and_attends_to_it(monkeypatch, sp
     st.close()
 
 
-def _planned(st, layer=0, k_new=None, v_new=None):
+def _planned(st, layer=0, k_new=None, v_new=None, wave_heads=None):
     plan = st.pool.plan(st.w.ctx_lens)
+    if wave_heads is not None:  # override the planner's choice of per-wave KV heads
+        plan.info.decode_wave_heads = wave_heads
     q, tables = st.dev[layer]
     out = torch.empty_like(q)
     st.pool.run(layer, plan, q, out, tables, st.w.scale, k_new=k_new, v_new=v_new)
@@ -360,6 +362,68 @@ def test_planned_run_appends_the_newest_token():
     st.host[0] = (q, tables, ids, k2, v2)
     compare("planned append", out, st.reference(0))
     again, _ = _planned(st)
+    assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+    st.close()
+
+
+WAVE_HEADS_LENS = [0, 1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 100, 255, 256, 257, 1000, 1024, 1025, 2000, 3001]
+
+
+@pytest.mark.parametrize("wave_heads", [0, 1])
+def test_planned_wave_heads_ragged_with_poisoned_tails(wave_heads):
+    """Each wave walking a whole piece for its own KV head gives the oracle's
+    result, for whole sequences, cut ones (merged records) and empty ones."""
+    w = workloads.custom(WAVE_HEADS_LENS, seed=34)
+    st = Staged(w)
+    _poison_tails(st)
+    out, plan = _planned(st, wave_heads=wave_heads)
+    report(f"planned wave_heads={wave_heads}", items=plan.info.num_items, merges=plan.info.num_merges,
+           longest=plan.info.max_piece_tokens)
+    assert plan.info.num_merges > 0 and plan.info.max_piece_tokens <= 1024  # the mode applies
+    compare(f"planned wave_heads={wave_heads}", out, st.reference(0))
+    st.close()
+
+
+def test_planner_picks_wave_heads_for_many_short_contexts():
+    rng = np.random.default_rng(35)
+    lens = rng.integers(1, 300, 1100)
+    lens[::97] = 0
+    w = workloads.custom([int(x) for x in lens], seed=35)
+    st = Staged(w)
+    _poison_tails(st)
+    out, plan = _planned(st)
+    report("planned many short", items=plan.info.num_items, wave_heads=plan.info.decode_wave_heads)
+    assert plan.info.decode_wave_heads == 1
+    compare("planned many short", out, st.reference(0))
+    st.close()
+
+
+def test_planned_wave_heads_appends_the_newest_token():
+    """Every wave stores the newest K/V row of its own KV head."""
+    lens = [1, 17, 300, 1000, 0, 64, 2000]
+    w = workloads.custom(lens, seed=36)
+    st = Staged(w)
+    _poison_tails(st)
+    q, tables, ids, k, v = st.host[0]
+    rng = np.random.default_rng(10)
+    k_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+    v_new = rng.standard_normal((w.batch, 8, 128)).astype(np.float16)
+    out, plan = _planned(st, k_new=torch.from_numpy(k_new).cuda(), v_new=torch.from_numpy(v_new).cuda(),
+                         wave_heads=1)
+    assert plan.info.num_merges > 0 and plan.info.max_piece_tokens <= 1024
+    k2, v2 = k.copy(), v.copy()
+    kp, vp = st.pool.k[0].cpu().numpy(), st.pool.v[0].cpu().numpy()
+    for s, c in enumerate(lens):
+        if c:
+            blk = tables[s, (c - 1) // 16]
+            r = np.searchsorted(ids, blk)
+            k2[r, (c - 1) % 16] = k_new[s]
+            v2[r, (c - 1) % 16] = v_new[s]
+            assert np.array_equal(kp[blk, :, (c - 1) % 16, :].view(np.int16), k_new[s].view(np.int16))
+            assert np.array_equal(vp[blk, :, (c - 1) % 16, :].view(np.int16), v_new[s].view(np.int16))
+    st.host[0] = (q, tables, ids, k2, v2)
+    compare("planned wave_heads append", out, st.reference(0))
+    again, _ = _planned(st, wave_heads=1)
     assert torch.equal(again.view(torch.int16), out.view(torch.int16))
     st.close()
 

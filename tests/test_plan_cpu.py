@@ -433,3 +433,24 @@ def test_mixed_launch_walks_decode_pieces_with_two_waves_when_the_tiles_dominate
     assert info.num_items > 0 and info.num_prefill_items > 0 and info.mixed_decode_waves == 4
     assert pa.pa_decode_plan(pool, [4096] * 32, 32)[0].mixed_decode_waves == 4
     assert pa.pa_prefill_plan(pool, np.array([0, 1, 2], np.int32), [50, 60], 32)[0].mixed_decode_waves == 4
+
+
+def test_wave_heads_for_many_short_pieces(pool):
+    """Per-wave KV heads only where every piece fits one wave's table register
+    (1024 tokens) and a work-group still falls to each of 256 dispatch units."""
+    def wh(lens, handle=pool):
+        info, _ = pa.pa_decode_plan(handle, lens, 32 if handle is pool else 8)
+        return info.decode_wave_heads, info.max_piece_tokens
+    assert wh([128] * 1024) == (1, 128)
+    assert wh([1024] * 128) == (1, 1024)      # 128 items x 2 work-groups
+    assert wh([1024] * 64) == (0, 1024)       # 128 work-groups: the four-wave split
+    assert wh([4096] * 32)[0] == 0            # pieces past one table register
+    assert wh([4096] * 8)[0] == 0
+    assert wh([0] * 600) == (1, 0)
+    two = pa.pa_pool_create(pa.PoolDesc(1, 64, 16, 2, 128, pa.PA_F16), FAKE, FAKE)
+    try:
+        assert wh([128] * 4096, two)[0] == 0  # two KV heads: not a multiple of the four waves
+    finally:
+        pa.pa_pool_destroy(two)
+    info, _ = pa.pa_prefill_plan(pool, [0, 1, 2], [100, 100], 32)
+    assert info.decode_wave_heads == 0
