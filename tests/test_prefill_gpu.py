@@ -35,6 +35,7 @@ class Mixed:
         self.starts = _starts(self.q_lens)
         self.q = self.w.q_rows(int(self.starts[-1]))
         self.qd = torch.from_numpy(self.q).cuda()
+        self.scale = self.w.scale
         self.poisoned = self._poison_tails()
 
     def _poison_tails(self):
@@ -58,7 +59,7 @@ class Mixed:
     def run(self):
         plan = self.st.pool.prefill_plan(self.starts, self.lens)
         out = torch.empty_like(self.qd)
-        self.st.pool.prefill_run(0, plan, self.qd, out, self.st.dev[0][1], self.w.scale)
+        self.st.pool.prefill_run(0, plan, self.qd, out, self.st.dev[0][1], self.scale)
         torch.cuda.synchronize()
         return out, plan
 
@@ -66,8 +67,8 @@ class Mixed:
         if self.st.fp8:
             ks, vs = self.st.kv_scales
             return oracle.prefill_e4m3(q, oracle.quantize_e4m3(kc, ks), oracle.quantize_e4m3(vc, vs), tables,
-                                       starts, lens, self.w.scale, 16, ks, vs)
-        return oracle.prefill(q, kc, vc, tables, starts, lens, self.w.scale, 16)
+                                       starts, lens, self.scale, 16, ks, vs)
+        return oracle.prefill(q, kc, vc, tables, starts, lens, self.scale, 16)
 
     def reference(self, rows=None):
         q, tables, ids, k, v = self.st.host[0]
@@ -236,6 +237,19 @@ def test_more_tiles_than_one_round_sampled(q_lens, hist):
     m.close()
 
 
+@pytest.mark.parametrize("scale", [0.75, 1.0, 3.0])
+def test_prompt_rows_with_softmax_scales_past_one(scale):
+    """Softmax scales past 1 (peaked weights, scores of tens in log2 units):
+    the scores stay in fp32 up to the exponential, so the error stays at the
+    F16 rounding of the output."""
+    m = Mixed([40, 100, 1, 33], [10, 300, 50, 2000], seed=140)
+    m.scale = scale
+    out, plan = m.run()
+    assert plan.info.num_prefill_items > 0
+    compare(f"prompt rows at scale {scale}", out, m.reference())
+    m.close()
+
+
 FP8 = pa.PA_FP8_E4M3
 # non-power-of-two scales: fl32(1/scale) is inexact and the codes span most
 # of the format's range
@@ -254,6 +268,15 @@ def test_fp8_mixed_step_ragged(q_lens, hist):
     report("fp8 mixed ragged", rows=len(m.q), decode_items=plan.info.num_items,
            prefill_items=plan.info.num_prefill_items, merges=plan.info.num_merges, poisoned=m.poisoned)
     compare("fp8 mixed ragged", out, m.reference())
+    m.close()
+
+
+def test_fp8_prompt_rows_with_a_score_scale_past_one():
+    """K's scale folded into the score scale takes it past 1 (10 * log2(e) * 0.1)."""
+    m = Mixed([40, 100, 1], [10, 300, 50], seed=141, dtype=FP8, kv_scales=FP8_SCALES)
+    m.scale = 10.0
+    out, _ = m.run()
+    compare("fp8 prompt rows at scale 10", out, m.reference())
     m.close()
 
 
