@@ -7,7 +7,7 @@
  * pool ("vLLM Architecture and Installation", Example 3: a block table maps a
  * request's logical positions to physical blocks; new keys and values are
  * written to slot table[p / block_size] * block_size + p % block_size, and
- * attention reads a request's history through its table).
+ * attention gathers a sequence's earlier keys and values by the same map).
  *
  * For sequence s, query head h, with g = h / (num_q_heads / num_kv_heads)
  * (query heads share KV heads in contiguous groups; "Reading Inference Engine

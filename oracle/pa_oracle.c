@@ -11,7 +11,7 @@
  *    tables): a request's block table lists the physical blocks holding its
  *    tokens in order; the slot of logical position p is
  *    table[p / block_size] * block_size + p % block_size, and the attention
- *    kernel reads a request's history through that table.
+ *    kernel gathers every earlier key and value of the request by that map.
  *  - "Reading Inference Engine Codebases", Example 2: the attention scale is
  *    1/sqrt(head dimension) unless the model overrides it, so the scale is an
  *    argument; KV heads may be shared by several query heads (grouped-query
