@@ -33,8 +33,9 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: achieved KV GB/s (% HBM peak) and decode tokens/s"
 HBM_PEAK_GBPS = 8000.0
 # the kernels and the header whose constants and argument layout they compile with
-KERNEL_SOURCES = (os.path.join(ROOT, "paged_kv_cache_64_amd", "csrc", "pa_internal.h"),
-                  os.path.join(ROOT, "paged_kv_cache_64_amd", "csrc", "pa_kernels.hip"))
+KERNEL_FILES = (os.path.join("paged_kv_cache_64_amd", "csrc", "pa_internal.h"),
+                os.path.join("paged_kv_cache_64_amd", "csrc", "pa_kernels.hip"))
+KERNEL_SOURCES = tuple(os.path.join(ROOT, f) for f in KERNEL_FILES)
 COUNTERS_FILES = {"f16": os.path.join(ROOT, "profiles", "decode_partial_c3_counters.txt"),
                   "fp8": os.path.join(ROOT, "profiles", "decode_partial_fp8_c3_counters.txt")}
 COUNTERS_CONFIG = 3          # the workload the counter files were taken on
@@ -56,11 +57,15 @@ def host_cpu_model():
     return None
 
 
-def kernel_code_hash():
+def kernel_code_hash(root=None):
     """sha256 of the kernel sources with comments and whitespace removed: it
-    changes with the code, not with its comments."""
+    changes with the code, not with its comments.  root: another checkout's
+    top directory (its files that exist are hashed), else this one."""
+    paths = KERNEL_SOURCES if root is None else [os.path.join(root, f) for f in KERNEL_FILES]
     text = ""
-    for path in KERNEL_SOURCES:
+    for path in paths:
+        if root is not None and not os.path.exists(path):
+            continue
         with open(path) as f:
             text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -124,8 +129,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3,
-                    help="workload 1..8 (default 3); 6 and 7 are mixed steps (chunked prefill); "
-                         "8 is a launch-bound 32-layer batch-1 step (see --graph)")
+                    help="workload 1..9 (default 3); 6 and 7 are mixed steps (chunked prefill); "
+                         "8 is a launch-bound 32-layer batch-1 step (see --graph); 9 is 1024 "
+                         "sequences of 128 tokens")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")

@@ -7,10 +7,12 @@ runs), in the form kept under profiles/.
         --cal-fetch DIR --cal-write DIR --cal-bytes B --bytes B --title T --workload W
         --command-fetch C --command-write C --command-cal C [--note N ...]
     python -m paged_kv_cache_64_amd.prof_summary sq DIR --kernel K [--title T --command C ... --note N ...]
+        [--code-root CHECKOUT]
 
-A counter summary records the kernel source hash of bench.py's
-kernel_code_hash(): bench.py reads the traffic figures only while the source
-is unchanged.
+Every summary records the kernel source hash of bench.py's kernel_code_hash()
+at the time it was written (right after the run, from the tree that ran), so a
+figure can be matched to the kernel source it was measured on; bench.py reads
+the traffic figures of a counter summary only while that source is unchanged.
 """
 import argparse
 import csv
@@ -99,6 +101,13 @@ def _match(means, kernel):
     return next(iter(hits.values()))
 
 
+def _code_hash(root=None):
+    sys.path.insert(0, ROOT)
+    import bench
+
+    return bench.kernel_code_hash(root)
+
+
 def _short(name, width=88):
     return name if len(name) <= width else name[:width - 3] + "..."
 
@@ -114,7 +123,7 @@ def _skips(items):
 
 
 def cmd_trace(args):
-    out = [f"# {args.title}", f"# command: {args.command}"]
+    out = [f"# {args.title}", f"# command: {args.command}", f"# kernel_code_sha256: {_code_hash()}"]
     out += [f"# {n}" for n in args.note or []]
     rows = dispatch_stats(args.dir, _skips(args.skip))
     if rows is None:
@@ -134,9 +143,6 @@ def cmd_trace(args):
 
 
 def cmd_counters(args):
-    sys.path.insert(0, ROOT)
-    import bench
-
     cal_f = _match(counter_means(args.cal_fetch, "FETCH_SIZE"), "probe_copy_kernel")[0]
     cal_w = _match(counter_means(args.cal_write, "WRITE_SIZE"), "probe_copy_kernel")[0]
     fetch_scale = args.cal_bytes / (cal_f * 1024.0)
@@ -159,7 +165,7 @@ def cmd_counters(args):
     out += [f"# {n}" for n in args.note or []]
     out += [f"kernel: {args.kernel}",
             f"workload: {args.workload}",
-            f"kernel_code_sha256: {bench.kernel_code_hash()}",
+            f"kernel_code_sha256: {_code_hash()}",
             f"fetch_scale: {fetch_scale:.6f}",
             f"write_scale: {write_scale:.6f}",
             f"fetch_bytes_per_launch: {fetch_bytes:.0f}",
@@ -178,6 +184,8 @@ def cmd_sq(args):
         out.append(f"# {args.title}")
     for cmd in args.command or []:
         out.append(f"# command: {cmd}")
+    out.append(f"# kernel_code_sha256: {_code_hash(args.code_root)}"
+               + (f" (kernel sources of {args.code_root})" if args.code_root else ""))
     out += [f"# {n}" for n in args.note or []]
     for c in sorted(names):
         v, n = _match(counter_means(args.dir, c), args.kernel)
@@ -209,6 +217,7 @@ def main(argv=None):
     q.add_argument("--title")
     q.add_argument("--command", action="append", help="one per counter pass whose output lies under DIR")
     q.add_argument("--note", action="append")
+    q.add_argument("--code-root", help="the checkout whose kernels ran (default: this one)")
     ap.add_argument("-o", "--out")
     args = ap.parse_args(argv)
     text = {"trace": cmd_trace, "counters": cmd_counters, "sq": cmd_sq}[args.cmd](args)

@@ -165,7 +165,7 @@ def test_fp8_extreme_scales_saturate_and_underflow():
     st.close()
 
 
-@pytest.mark.parametrize("k", [1, 2, 4])
+@pytest.mark.parametrize("k", [1, 2, 4, 9])
 def test_fp8_config_full_parity(k):
     w = workloads.config(k)
     st = Staged(w, dtype=FP8, kv_scales=SCALES)

@@ -320,11 +320,12 @@ def test_planned_run_ragged_with_poisoned_tails():
     st.close()
 
 
-@pytest.mark.parametrize("k", [1, 2, 4, 5])
+@pytest.mark.parametrize("k", [1, 2, 4, 5, 9])
 def test_planned_run_configs(k):
     w = workloads.config(k)
     st = Staged(w)
     out, plan = _planned(st)
+    assert plan.info.decode_wave_heads == (1 if k == 9 else 0)  # workload 9: per-wave KV heads
     report(f"planned config{k}", items=plan.info.num_items, merges=plan.info.num_merges,
            longest=plan.info.max_piece_tokens)
     compare(f"planned config{k}", out, st.reference(0))

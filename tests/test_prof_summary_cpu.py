@@ -67,6 +67,7 @@ def test_sq_lists_every_counter_of_the_kernel(tmp_path):
         (tmp_path / "sq.txt").read_text().splitlines()
     assert "k( SQ_BUSY_CYCLES: 100 per launch over 1 launches" in lines
     assert "k( SQ_WAVES: 6 per launch over 2 launches" in lines
+    assert f"# kernel_code_sha256: {bench.kernel_code_hash()}" in lines
 
 
 def test_dispatch_trace_skips_warmup_and_reports_the_median(tmp_path):
@@ -89,6 +90,7 @@ def test_dispatch_trace_skips_warmup_and_reports_the_median(tmp_path):
              "--skip", "decode_partial=3"])
     out = open(tmp_path / "out.txt").read()
     assert "first 3 dispatches" in out and "median ns" in out
+    assert f"# kernel_code_sha256: {bench.kernel_code_hash()}" in out.splitlines()
     assert ps.dispatch_stats(str(tmp_path / "none")) is None
 
 

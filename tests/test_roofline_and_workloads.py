@@ -51,10 +51,12 @@ def test_configs_are_deterministic_and_shaped():
     assert c8.layers == 32 and c8.batch == 1 and c8.max_context_len == 256 and c8.pool_blocks == 64
     assert not np.array_equal(c8.tables(0), c8.tables(1))       # a fresh table per layer
     assert all(len(np.unique(c8.tables(L)[0])) == 16 for L in (0, 31))
+    c9 = workloads.config(9)
+    assert c9.layers == 1 and c9.batch == 1024 and np.all(c9.ctx_lens == 128) and c9.max_blocks == 8
 
 
 def test_tables_are_distinct_non_contiguous_and_inside_the_pool():
-    for k in (1, 2, 4):
+    for k in (1, 2, 4, 9):
         w = workloads.config(k)
         t = w.tables(0)
         held = w.blocks_held()

@@ -37,6 +37,8 @@ every token in the cache.
 One launch-bound step (the case a captured whole-step graph is for):
   8  32 layers, batch 1, context 256; per layer the table is the first 16
      ids of a random permutation of a 64-block pool (workload 1 on every layer)
+Many short contexts (the case per-wave KV heads are for):
+  9  one layer, batch 1024, every context 128; pool of 2x the needed blocks
 """
 from __future__ import annotations
 
@@ -269,7 +271,7 @@ def _uniform_ints(seed, purpose, lo, hi, n):
 
 
 def config(k: int, seed: int | None = None) -> Workload:
-    """The workloads, numbered 1..8 as in the module docstring."""
+    """The workloads, numbered 1..9 as in the module docstring."""
     seed = k if seed is None else seed
     if k == 1:
         return Workload("paged decode, 1 layer, batch 1, ctx 256", seed, layers=1,
@@ -302,6 +304,10 @@ def config(k: int, seed: int | None = None) -> Workload:
                         ctx_lens=np.array([256], np.int32), pool_blocks=64, max_blocks=16,
                         fresh_tables_per_layer=True,
                         description="per layer: first 16 ids of a random permutation of 64 blocks")
+    if k == 9:
+        return Workload("paged decode, 1 layer, batch 1024, ctx 128", seed, layers=1,
+                        ctx_lens=np.full(1024, 128, np.int32), pool_blocks=2 * 1024 * 8,
+                        max_blocks=8)
     if k in (6, 7):
         chunk, hist, layers = (2016, 2016, 32) if k == 6 else (16352, 16352, 8)
         lens = np.array([hist + chunk] + [4096] * 32, np.int32)
