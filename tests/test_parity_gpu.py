@@ -429,6 +429,26 @@ def test_planned_wave_heads_appends_the_newest_token():
     st.close()
 
 
+@pytest.mark.parametrize("hkv", [1, 2, 4, 16])
+def test_other_kv_head_counts(hkv):
+    """Pools of 1, 2, 4 and 16 KV heads (4 query heads each): fixed split,
+    planned, and planned with per-wave KV heads where the count allows it."""
+    lens = [1, 17, 300, 1000, 0, 64, 2000, 129]
+    w = workloads.custom(lens, seed=37 + hkv, num_q_heads=4 * hkv, num_kv_heads=hkv)
+    st = Staged(w)
+    _poison_tails(st)
+    ref = st.reference(0)
+    report(f"hkv {hkv}", q_heads=4 * hkv)
+    compare(f"hkv {hkv} fixed split", st.decode(0), ref)
+    out, plan = _planned(st)
+    compare(f"hkv {hkv} planned", out, ref)
+    if hkv % 4 == 0:
+        out, plan = _planned(st, wave_heads=1)
+        assert plan.info.max_piece_tokens <= 1024
+        compare(f"hkv {hkv} planned, wave heads", out, ref)
+    st.close()
+
+
 def _cascade(st, group, plen, k_new=None, v_new=None):
     plan = st.pool.plan(st.w.ctx_lens, prefix_group=group, prefix_len=plen)
     q, tables = st.dev[0]

@@ -27,10 +27,10 @@ class Mixed:
     """A mixed step: sequences of lengths hist + q_len staged in a pool, with
     packed query rows."""
 
-    def __init__(self, q_lens, hist, seed, dtype=pa.PA_F16, kv_scales=(1.0, 1.0)):
+    def __init__(self, q_lens, hist, seed, dtype=pa.PA_F16, kv_scales=(1.0, 1.0), hkv=8):
         self.q_lens = list(q_lens)
         self.lens = [h + n for h, n in zip(hist, q_lens)]
-        self.w = workloads.custom(self.lens, seed=seed)
+        self.w = workloads.custom(self.lens, seed=seed, num_q_heads=4 * hkv, num_kv_heads=hkv)
         self.st = Staged(self.w, dtype=dtype, kv_scales=kv_scales)
         self.starts = _starts(self.q_lens)
         self.q = self.w.q_rows(int(self.starts[-1]))
@@ -247,6 +247,15 @@ def test_prompt_rows_with_softmax_scales_past_one(scale):
     out, plan = m.run()
     assert plan.info.num_prefill_items > 0
     compare(f"prompt rows at scale {scale}", out, m.reference())
+    m.close()
+
+
+@pytest.mark.parametrize("hkv", [1, 2, 16])
+def test_mixed_step_with_other_kv_head_counts(hkv):
+    m = Mixed([40, 1, 100, 1, 33], [10, 300, 50, 2000, 0], seed=150 + hkv, hkv=hkv)
+    out, plan = m.run()
+    assert plan.info.num_prefill_items > 0 and plan.info.num_items > 0
+    compare(f"mixed step, {hkv} kv heads", out, m.reference())
     m.close()
 
 
