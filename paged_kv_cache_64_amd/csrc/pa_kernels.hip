@@ -1446,7 +1446,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
     __shared__ __attribute__((aligned(16))) _Float16 k_lds[NB][kStageBlocks][kBlockSize][kHeadDim];
     __shared__ __attribute__((aligned(16))) _Float16 v_lds[NB][kStageBlocks][kBlockSize][kHeadDim];
     __shared__ float alpha_lds[kWaves][2][16];
-    __shared__ float ml_lds[kWaves][2][16][2];
+    __shared__ float m_lds[kWaves][2][16];
 
     // Plan entries are clamped so a damaged plan cannot index outside q, out,
     // the tables, the pool or the workspace.
@@ -1493,16 +1493,18 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
     }
 
     f4 oacc[2][8];
-    float m_run[2], l_run[2];  // row n of each tile, log2 units (l: this lane's share)
+    f4 lacc[2];      // running sums, in oacc's layout: rows 4r + c (every column the same)
+    float m_run[2];  // row n of each tile, log2 units
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         m_run[rt] = -INFINITY;
-        l_run[rt] = 0.0f;
+        lacc[rt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) oacc[rt][j] = f4{0.f, 0.f, 0.f, 0.f};
     }
     const float c_scale = a.scale_log2e;
-    const h2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    const _Float16 one = static_cast<_Float16>(1.0f);
+    const h8 ones8 = {one, one, one, one, one, one, one, one};
 
     // copies: wave w moves tensor w/2 (K, V) of block w%2 of the pair straight
     // into LDS, 1 KiB per load instruction: lane l fills chunk l%16 of row
@@ -1593,7 +1595,6 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
                 const float m_new = fmaxf(m_run[rt], bm);
                 // a row that has seen no key yet keeps m = -inf (and alpha 1)
                 const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run[rt] - m_new);
-                l_run[rt] *= alpha;
                 m_run[rt] = m_new;
                 if (r == 0) alpha_lds[w][rt][n] = alpha;
                 wave_lds_sync();
@@ -1605,9 +1606,14 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
                     oacc[rt][j][2] *= al.z;
                     oacc[rt][j][3] *= al.w;
                 }
+                lacc[rt][0] *= al.x;
+                lacc[rt][1] *= al.y;
+                lacc[rt][2] *= al.z;
+                lacc[rt][3] *= al.w;
             }
-            // weights exp2(s * scale - m) enter P V as F16; the running sum
-            // adds the same rounded values (masked scores give exp2(-inf) = 0)
+            // weights exp2(s * scale - m) enter P V as F16, and the running
+            // sums (one more MFMA, below) add the same rounded values (masked
+            // scores give exp2(-inf) = 0)
             const float neg_m = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
@@ -1618,7 +1624,6 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
                     const h2 pp = {static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
                     pw[rt][4 * blk + c] = pp.x;
                     pw[rt][4 * blk + c + 1] = pp.y;
-                    l_run[rt] = __builtin_amdgcn_fdot2(pp, ones, l_run[rt], false);
                 }
         }
         // P V over dims 16j .. 16j+15: lane (r, n) gets tokens 4r .. 4r+3 of
@@ -1643,6 +1648,9 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
             for (int rt = 0; rt < 2; ++rt)
                 oacc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[rt], bv, oacc[rt][j], 0, 0, 0);
         }
+        // the row sums of the same F16 weights, on the matrix cores
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[rt], ones8, lacc[rt], 0, 0, 0);
     };
 
     // the work-group walks every pair of the piece; a wave computes the pairs
@@ -1682,17 +1690,10 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
     }
     if (rows_w <= 0) return;
 
-    // (m, l) of every row to LDS; lane l then writes rows 4r + c of each tile
+    // m of every row to LDS; lane l then writes rows 4r + c of each tile
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        float l = l_run[rt];
-        l += shfl_xor(l, 16);
-        l += shfl_xor(l, 32);
-        if (r == 0) {
-            ml_lds[w][rt][n][0] = m_run[rt];
-            ml_lds[w][rt][n][1] = l;
-        }
-    }
+    for (int rt = 0; rt < 2; ++rt)
+        if (r == 0) m_lds[w][rt][n] = m_run[rt];
     wave_lds_sync();
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -1702,7 +1703,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
             const int t = 4 * r + c;  // row of the tile
             if (t >= rows_w) continue;
             const int tok = tok0 + t;
-            const float m = ml_lds[w][rt][t][0], l = ml_lds[w][rt][t][1];
+            const float m = m_lds[w][rt][t], l = lacc[rt][c];
             if (direct) {
                 const size_t qrow = static_cast<size_t>(min(row0 + tok, a.num_q_rows - 1));
                 const float inv = 1.0f / l;
