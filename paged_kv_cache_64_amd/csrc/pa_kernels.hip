@@ -1065,6 +1065,10 @@ __global__ __launch_bounds__(256, 2) void cascade_kernel(DecodeArgs a) {
 //                  B = V   (lane l: the same 8 tokens at dim 16j + l%16, two
 //                           LDS transpose reads, one per block)
 //                  D = O   (lane l: rows 4(l/16) + c, dim 16j + l%16)
+//   l  += P . 1    (F16 pools) one more such MFMA per row tile and pair with
+//                  B all ones: the row sums of the same F16 weights, in D's
+//                  row layout (FP8 pools add them with v_dot2 per lane and
+//                  reduce across lanes at the end)
 // Each wave computes only up to its last query's position, and masks only
 // the pairs that reach past its first query's position or its last key.
 // The softmax max is raised lazily as in the decode kernel (the comparison
