@@ -73,14 +73,18 @@ def kernel_code_hash(root=None):
     return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()
 
 
-def launch_kernels(info):
+def launch_kernels(info, num_kv_heads=8):
     """The kernels one pa_decode_run launch of this plan runs, as the library
-    picks them: ordinary and shared-prefix pieces share cascade_kernel, and a
-    plan that cuts sequences adds the merge."""
+    picks them: ordinary and shared-prefix pieces share cascade_kernel, a plan
+    with per-wave KV heads (pieces of at most 1024 tokens, KV heads a multiple
+    of 4) takes decode_wave_heads_kernel, and a plan that cuts sequences adds
+    the merge."""
     if info.num_items > 0 and info.num_prefix_items > 0:
         names = ["cascade_kernel"]
     else:
-        names = ["decode_partial_kernel"] if info.num_items > 0 else []
+        wave_heads = (getattr(info, "decode_wave_heads", 0) == 1 and num_kv_heads % 4 == 0
+                      and info.max_piece_tokens <= 1024)
+        names = [("decode_wave_heads_kernel" if wave_heads else "decode_partial_kernel")] if info.num_items > 0 else []
         names += ["decode_prefix_kernel"] if info.num_prefix_items > 0 else []
     if info.num_merges > 0:
         names.append("decode_merge_planned_kernel")
@@ -542,7 +546,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic if info.num_merges == 0 else None,
-                     "kernel": launch_kernels(info),
+                     "kernel": launch_kernels(info, HKV),
                      "bytes_per_launch": launch_bytes, "kv_bytes_basis": basis,
                      "mean_launch_us": round(part_mean_s * 1e6, 3)},
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,

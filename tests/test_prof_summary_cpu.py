@@ -96,11 +96,18 @@ def test_dispatch_trace_skips_warmup_and_reports_the_median(tmp_path):
 
 def test_bench_names_the_kernels_a_decode_launch_runs():
     from types import SimpleNamespace as NS
-    assert bench.launch_kernels(NS(num_items=32, num_prefix_items=0, num_merges=0)) == "decode_partial_kernel"
-    assert bench.launch_kernels(NS(num_items=40, num_prefix_items=0, num_merges=3)) == \
+    assert bench.launch_kernels(NS(num_items=32, num_prefix_items=0, num_merges=0, max_piece_tokens=4096,
+                                   decode_wave_heads=0)) == "decode_partial_kernel"
+    assert bench.launch_kernels(NS(num_items=40, num_prefix_items=0, num_merges=3, max_piece_tokens=1024,
+                                   decode_wave_heads=0)) == \
         "decode_partial_kernel + decode_merge_planned_kernel"
+    # many short pieces: each wave walks a piece for its own KV head
+    assert bench.launch_kernels(NS(num_items=1024, num_prefix_items=0, num_merges=0, max_piece_tokens=128,
+                                   decode_wave_heads=1)) == "decode_wave_heads_kernel"
+    assert bench.launch_kernels(NS(num_items=1024, num_prefix_items=0, num_merges=0, max_piece_tokens=128,
+                                   decode_wave_heads=1), num_kv_heads=2) == "decode_partial_kernel"
     # ordinary and shared-prefix pieces run in one cascade launch, then the merge
     assert bench.launch_kernels(NS(num_items=340, num_prefix_items=64, num_merges=256)) == \
         "cascade_kernel + decode_merge_planned_kernel"
-    assert bench.launch_kernels(NS(num_items=0, num_prefix_items=8, num_merges=4)) == \
+    assert bench.launch_kernels(NS(num_items=0, num_prefix_items=8, num_merges=4, max_piece_tokens=0)) == \
         "decode_prefix_kernel + decode_merge_planned_kernel"
