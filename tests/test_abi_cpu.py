@@ -218,3 +218,34 @@ def test_noalloc_decode_validation(lib, pool):
     # 1000 sequences of up to 2^20 tokens: 256 splits each, 4.3 GB of partials
     assert lib.pa_decode_workspace_bytes(pool, 1000, 32, 1 << 20) > 32 << 20
     assert f(pool, 0, FAKE, FAKE, FAKE, 1 << 16, FAKE, 1000, 32, 1 << 20, 0.1, None) == pa.PA_ERR_WORKSPACE
+
+
+def test_binding_structs_match_the_header_layout(tmp_path):
+    """Every field of pa_pool_desc and pa_plan_info sits at the same offset, and
+    each struct has the same size, in include/pa.h (compiled by the host C
+    compiler) as in the ctypes mirror the binding marshals."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"pa_pool_desc": pa.PoolDesc, "pa_plan_info": pa.PlanInfo}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "pa.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'    printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in cls._fields_:
+            lines.append(f'    printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ["    return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", "-o", str(exe), str(src)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        cname, field, value = line.split()
+        got[(cname, field)] = int(value)
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for field, _ in cls._fields_:
+            assert got[(cname, field)] == getattr(cls, field).offset, (cname, field)
