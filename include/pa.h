@@ -238,10 +238,10 @@ typedef struct {
                                    work-group that walk a decode piece (2 when the prompt
                                    tiles are the longer part, so they progress beside the
                                    decode streams; else 4); 4 in every other plan */
-    int32_t decode_wave_heads; /* pa_decode_plan: 1 when its pieces are short enough
-                                  (at most 1024 tokens) and numerous enough that each
-                                  of a work-group's four waves takes its own KV head
-                                  and walks the whole piece, else 0.  The caller may
+    int32_t decode_wave_heads; /* pa_decode_plan: 1 when its pieces are at most 1024
+                                  tokens and the plan's dispatch model rates it faster
+                                  for each of a work-group's four waves to take its own
+                                  KV head and walk the whole piece, else 0.  The caller may
                                   clear or set it before pa_decode_run; it is ignored
                                   unless num_kv_heads is a multiple of 4 and
                                   max_piece_tokens <= 1024, and in every other plan. */

@@ -207,14 +207,17 @@ constexpr int64_t kMergeBlocks = 16;
 // Per-wave KV heads (decode_wave_heads): each wave walks a whole piece for
 // its own KV head, so a work-group's fixed work (query, table, pipeline
 // start, epilogue) is spread over four times the blocks and no partial sums
-// cross waves.  Pieces are then at most one table register of blocks, and the
-// mode is chosen when it still leaves a work-group per dispatch unit.
-// Measured on one-layer cold decodes (F16 / FP8 us, four-wave split -> wave
-// heads): 1024 x 128 tokens 117.5 -> 96.7 / 81.5 -> 55.6; 512 x 256
-// 100.6 -> 90.1 / 62.4 -> 49.6; 256 x 1024 170.1 -> 161.7 / 91.9 -> 89.1;
-// 128 x 512 (256 work-groups) 46.7 -> 44.6 / 28.5 -> 26.5; but 64 x 1024
-// (128 work-groups) 45.7 -> 67.0 / 27.6 -> 39.9.
+// cross waves, at three work-groups per unit.  Pieces are then at most one
+// table register of blocks.  A work-group moves four times the blocks, so a
+// launch of few of them balances worse; the dispatch model above decides,
+// and the mode is taken when it models more than 1/64 faster.  Measured
+// (one-layer cold decodes, the newest token appended, F16 us, four-wave
+// split -> wave heads), every case as the model chose: 4096 x 32 tokens
+// 272 -> 126, 2048 x 64 178 -> 114, 128 x 1024 88.4 -> 83.3; kept split:
+// 160 x 1024 111 (wave heads 139), 150 x 512 57.6 (72.0), 40 x 4096 cut in
+// four 112 (142), 200 x 1024 146.4 (147.0), 300 x 512 115.6 (115.5).
 constexpr int kWaveHeadsMaxBlocks = 64;
+constexpr int kWaveHeadsSlots = 3;
 
 // Blocks of each piece when every context is cut into near-equal pieces of
 // at most max_piece blocks (an empty context gives an empty piece), longest
@@ -245,17 +248,20 @@ void piece_blocks(const int32_t *lens, const std::vector<int32_t> &plen, int32_t
 // `heads` consecutive work-groups, in blocks of the most loaded unit.  When
 // `heads` divides the unit count, a piece's work-groups land on `heads`
 // units whose loads stay equal, so the model tracks groups of units.
-int64_t modelled_makespan(const std::vector<int64_t> &pieces, int32_t heads) {
+// `slots` work-groups fit a unit at once, and a work-group moves `scale` times
+// its piece's blocks (scale 4 when each of its waves takes its own KV head).
+int64_t modelled_makespan(const std::vector<int64_t> &pieces, int32_t heads, int slots = kSlotsPerUnit,
+                          int64_t scale = 1) {
     const bool grouped = heads > 0 && kDispatchUnits % heads == 0;
     const int units = grouped ? kDispatchUnits / heads : kDispatchUnits;  // tracked units (or groups)
     const int per = grouped ? 1 : heads;                                  // work-groups per piece and unit
-    const int64_t first_round = static_cast<int64_t>(units) * kSlotsPerUnit;
+    const int64_t first_round = static_cast<int64_t>(units) * slots;
     std::vector<int64_t> load(units, 0);
     std::priority_queue<std::pair<int64_t, int>, std::vector<std::pair<int64_t, int>>, std::greater<>> later;
     int64_t j = 0;
     for (const int64_t p : pieces) {
         for (int h = 0; h < per; ++h, ++j) {
-            const int64_t w = p + kWgOverheadBlocks;
+            const int64_t w = p * scale + kWgOverheadBlocks;
             if (j < first_round) {
                 load[j % units] += w;
                 if (j + 1 == first_round)
@@ -462,11 +468,16 @@ pa_status build_plan(const pa_pool *pool, const int32_t *lens, int32_t batch, in
         inf.num_prefill_items = 0;
         inf.num_q_rows = batch;
         inf.mixed_decode_waves = pa::kWaves;
-        inf.decode_wave_heads = pool->desc.num_kv_heads % pa::kWaves == 0 && longest <= kWaveHeadsMaxBlocks * kBlockSize &&
-                                        static_cast<int64_t>(n_items) * (pool->desc.num_kv_heads / pa::kWaves) >=
-                                            kDispatchUnits
-                                    ? 1
-                                    : 0;
+        inf.decode_wave_heads = 0;
+        if (pool->desc.num_kv_heads % pa::kWaves == 0 && n_items > 0 && longest <= kWaveHeadsMaxBlocks * kBlockSize) {
+            std::vector<int64_t> blocks(n_items);  // in dispatch order, longest first
+            for (size_t i = 0; i < n_items; ++i)
+                blocks[i] = (static_cast<int64_t>(items[i].t_end) - items[i].t_begin + kBlockSize - 1) / kBlockSize;
+            const int64_t split = modelled_makespan(blocks, pool->desc.num_kv_heads);
+            const int64_t wave_heads =
+                modelled_makespan(blocks, pool->desc.num_kv_heads / pa::kWaves, kWaveHeadsSlots, pa::kWaves);
+            inf.decode_wave_heads = wave_heads < split - split / 64 ? 1 : 0;
+        }
         inf.plan_bytes = sizeof(int32_t) * (pa::kPlanHeader + pa::kItemInts * n_items + merges.size() +
                                             pitems.size() + mlist.size());
         size_t o_bytes = 0;

@@ -437,13 +437,18 @@ def test_mixed_launch_walks_decode_pieces_with_two_waves_when_the_tiles_dominate
 
 def test_wave_heads_for_many_short_pieces(pool):
     """Per-wave KV heads only where every piece fits one wave's table register
-    (1024 tokens) and a work-group still falls to each of 256 dispatch units."""
+    (1024 tokens) and the dispatch model rates the launch of four times fewer,
+    four times longer work-groups faster (each case below as measured)."""
     def wh(lens, handle=pool):
         info, _ = pa.pa_decode_plan(handle, lens, 32 if handle is pool else 8)
         return info.decode_wave_heads, info.max_piece_tokens
     assert wh([128] * 1024) == (1, 128)
     assert wh([1024] * 128) == (1, 1024)      # 128 items x 2 work-groups
     assert wh([1024] * 64) == (0, 1024)       # 128 work-groups: the four-wave split
+    assert wh([1024] * 160)[0] == 0           # 320 work-groups: 64 units would take two
+    assert wh([512] * 150)[0] == 0
+    assert wh([64] * 2048)[0] == 1 and wh([32] * 4096)[0] == 1
+    assert wh([4096] * 40) == (0, 1024)       # cut in four: 320 work-groups again
     assert wh([4096] * 32)[0] == 0            # pieces past one table register
     assert wh([4096] * 8)[0] == 0
     assert wh([0] * 600) == (1, 0)
