@@ -522,7 +522,7 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
         if (batch > (1 << 24)) return PA_ERR_UNSUPPORTED;
         if (query_start[0] != 0) return PA_ERR_INVALID_ARG;
         int32_t max_ctx = 0;
-        int64_t dec_blocks = 0, tile_blocks = 0;
+        int64_t dec_blocks = 0, tile_blocks = 0, n_tiles = 0, max_tile = 0;
         for (int32_t s = 0; s < batch; ++s) {
             const int64_t q_len = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
             if (q_len < 0 || lens[s] < q_len) return PA_ERR_INVALID_ARG;
@@ -533,6 +533,8 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
                 if (q_len == 1) break;
                 const int64_t kend = lens[s] - q_len + std::min<int64_t>(q_len, j0 + pa::kPrefillTile);
                 tile_blocks += (kend + kBlockSize - 1) / kBlockSize;
+                ++n_tiles;
+                max_tile = std::max<int64_t>(max_tile, (kend + kBlockSize - 1) / kBlockSize);
             }
         }
         const int32_t num_q_rows = query_start[batch];
@@ -604,8 +606,17 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
             int32_t f[pa::kPrefillItemInts];
         };
         std::vector<PrefillItem> pitems;
-        const int64_t ppiece = std::min<int64_t>(pa::kMaxPrefillPieceBlocks,
-                                                 std::max<int64_t>(8, cut(tile_blocks, items_target)));
+        int64_t ppiece = std::min<int64_t>(pa::kMaxPrefillPieceBlocks,
+                                           std::max<int64_t>(8, cut(tile_blocks, items_target)));
+        // An F16 launch of prompt tiles alone with at most one work-group per
+        // CU runs the split kernel (each tile's keys over two wave groups of
+        // one work-group), so its tiles are cut only as far as that count
+        // allows: into at most items_target / n_tiles pieces each.  The 32
+        // tiles of a 1,024-token chunk at position 3,008: whole, 96.2 us, against
+        // 121 us cut into 48 pieces for four-wave work-groups.
+        if (items.empty() && pool->elem_bytes() == 2 && n_tiles > 0 && n_tiles <= items_target)
+            ppiece = std::min<int64_t>(pa::kMaxPrefillPieceBlocks,
+                                       std::max<int64_t>(8, cut(max_tile, items_target / n_tiles)));
         for (int32_t s = 0; s < batch; ++s) {
             const int64_t q_len = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
             if (q_len < 2) continue;

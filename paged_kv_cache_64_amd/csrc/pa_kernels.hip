@@ -1445,23 +1445,35 @@ __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "me
 // the swizzle puts there, and out-of-range lanes of a zero-size resource
 // write zeros.  The arithmetic from the scores on and the epilogue are
 // prefill_body_fp8's.
-template <int NB>
+// SPLIT: 512 threads, two groups of four waves over the same 32 query rows,
+// group 0 walking the first half of the piece's stages and group 1 the rest,
+// each with its own LDS buffers; the groups pass the stage barriers together
+// and merge their (max, sum, output) through LDS at the end.  A launch of
+// few work-groups then keeps eight waves on each CU to the end of its
+// longest tile instead of leaving one four-wave work-group alone on it.
+template <int NB, bool SPLIT = false>
 __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t bx) {
     static_assert(NB == 2 || NB == 3, "two or three LDS buffers");
+    constexpr int kGroups = SPLIT ? 2 : 1;
+    constexpr int kThreads = 256 * kGroups;
     const int g = static_cast<int>(bx % a.num_kv_heads);
     const int32_t *it = a.prefill_items + kPrefillItemInts * static_cast<size_t>(bx / a.num_kv_heads);
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave of the work-group
+    const int grp = SPLIT ? w8 >> 2 : 0;                      // its group
+    const int w = SPLIT ? w8 & 3 : w8;                        // its wave within the group
     const int lane = tid & 63;
     const int n = lane & 15, r = lane >> 4;
 
     __shared__ int tbl_lds[kMaxPrefillPieceBlocks];
     // unpadded rows; 16-byte chunk c of row t sits at chunk c ^ k_swz(t) (K)
-    // or c ^ v_swz(t) (V)
-    __shared__ __attribute__((aligned(16))) _Float16 k_lds[NB][kStageBlocks][kBlockSize][kHeadDim];
-    __shared__ __attribute__((aligned(16))) _Float16 v_lds[NB][kStageBlocks][kBlockSize][kHeadDim];
-    __shared__ float alpha_lds[kWaves][2][16];
-    __shared__ float m_lds[kWaves][2][16];
+    // or c ^ v_swz(t) (V); one set per group
+    __shared__ __attribute__((aligned(16))) _Float16 k_lds_g[kGroups][NB][kStageBlocks][kBlockSize][kHeadDim];
+    __shared__ __attribute__((aligned(16))) _Float16 v_lds_g[kGroups][NB][kStageBlocks][kBlockSize][kHeadDim];
+    auto &k_lds = k_lds_g[grp];
+    auto &v_lds = v_lds_g[grp];
+    __shared__ float alpha_lds[kGroups * kWaves][2][16];
+    __shared__ float m_lds[kGroups * kWaves][2][16];
 
     // Plan entries are clamped so a damaged plan cannot index outside q, out,
     // the tables, the pool or the workspace.
@@ -1481,7 +1493,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
     const int b_hi = max(b_lo, min((t_hi + kBlockSize - 1) / kBlockSize, b_lo + kMaxPrefillPieceBlocks));
 
     const int32_t *table = a.tables + static_cast<size_t>(s) * a.max_blocks;
-    for (int i = tid; i < b_hi - b_lo; i += 256) tbl_lds[i] = table[b_lo + i];
+    for (int i = tid; i < b_hi - b_lo; i += kThreads) tbl_lds[i] = table[b_lo + i];
     __syncthreads();
 
     // this wave's query tokens and heads, and the keys its rows can see
@@ -1611,9 +1623,9 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
                 // a row that has seen no key yet keeps m = -inf (and alpha 1)
                 const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run[rt] - m_new);
                 m_run[rt] = m_new;
-                if (r == 0) alpha_lds[w][rt][n] = alpha;
+                if (r == 0) alpha_lds[w8][rt][n] = alpha;
                 wave_lds_sync();
-                const float4 al = *reinterpret_cast<const float4 *>(&alpha_lds[w][rt][4 * r]);
+                const float4 al = *reinterpret_cast<const float4 *>(&alpha_lds[w8][rt][4 * r]);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     oacc[rt][j][0] *= al.x;
@@ -1668,40 +1680,89 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
         for (int rt = 0; rt < 2; ++rt) lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[rt], ones8, lacc[rt], 0, 0, 0);
     };
 
-    // the work-group walks every pair of the piece; a wave computes the pairs
-    // below its last query's position
+    // the work-group walks every pair of the piece (SPLIT: this group its half
+    // of the stages); a wave computes the pairs below its last query's position
     const int n_stages = (b_hi - b_lo + kStageBlocks - 1) / kStageBlocks;
     const int w_blocks = w_end > t_lo ? (w_end + kBlockSize - 1) / kBlockSize - b_lo : 0;  // blocks this wave needs
-    // stage st reads LDS buffer st % NB; its loads were issued NB - 1 stages
-    // earlier.  Each stage issues kLoads * kCopyBlocks loads per wave.
+    const int half = (n_stages + 1) / 2;
+    const int my_first = SPLIT && grp ? half : 0;                            // first stage of this group
+    const int my_count = SPLIT ? (grp ? n_stages - half : half) : n_stages;  // its stages
+    const int rounds = SPLIT ? half : n_stages;  // barrier rounds, the same for both groups
+    // this group's stage st reads its LDS buffer st % NB; its loads were
+    // issued NB - 1 stages earlier.  Each stage issues kLoads * kCopyBlocks
+    // loads per wave.
     constexpr int kAhead = NB - 1;
     constexpr int kStageLoads = kLoads * kCopyBlocks;
 #pragma unroll
     for (int s0 = 0; s0 < kAhead; ++s0)
-        if (s0 < n_stages) fetch(b_lo + s0 * kStageBlocks, s0);
-    if (n_stages > 0) {
-        if (kAhead > 1 && n_stages > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (kStageLoads * (kAhead - 1)));
+        if (s0 < my_count) fetch(b_lo + (my_first + s0) * kStageBlocks, s0);
+    if (rounds > 0) {
+        if (kAhead > 1 && my_count > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (kStageLoads * (kAhead - 1)));
         else __builtin_amdgcn_s_waitcnt(0x0F70);
         raw_barrier();
     }
     auto stage = [&](int st, auto bufc) {
         constexpr int B = decltype(bufc)::value;  // == st % NB
-        const int b0 = b_lo + kStageBlocks * st;
-        const bool more = st + kAhead < n_stages;
+        const int gst = my_first + st;            // the stage within the piece
+        const int b0 = b_lo + kStageBlocks * gst;
+        const bool more = st + kAhead < my_count;
         if (more) fetch(b0 + kAhead * kStageBlocks, (B + kAhead) % NB);
+        if (!SPLIT || st < my_count) {
 #pragma unroll
-        for (int sb = 0; sb < kStageBlocks; sb += 2)
-            if (kStageBlocks * st + sb < w_blocks) compute(B, sb, b0 + sb);
+            for (int sb = 0; sb < kStageBlocks; sb += 2)
+                if (kStageBlocks * gst + sb < w_blocks) compute(B, sb, b0 + sb);
+        }
         // stage st+1's loads must have landed: all but those of later stages
         if (kAhead > 1 && more) __builtin_amdgcn_s_waitcnt(0x0F70 | (kStageLoads * (kAhead - 1)));
         else __builtin_amdgcn_s_waitcnt(0x0F70);
         raw_barrier();
     };
-    for (int st = 0; st < n_stages; st += NB) {
+    for (int st = 0; st < rounds; st += NB) {
         stage(st, std::integral_constant<int, 0>{});
-        if (st + 1 < n_stages) stage(st + 1, std::integral_constant<int, 1>{});
+        if (st + 1 < rounds) stage(st + 1, std::integral_constant<int, 1>{});
         if constexpr (NB == 3)
-            if (st + 2 < n_stages) stage(st + 2, std::integral_constant<int, 2 % NB>{});
+            if (st + 2 < rounds) stage(st + 2, std::integral_constant<int, 2 % NB>{});
+    }
+    if constexpr (SPLIT) {
+        // group 1 hands its max, sums and outputs to group 0 through LDS (the
+        // key stage buffers are free after the last barrier), one row tile at
+        // a time: per lane (r, n) 32 output values, then 4 sums
+        float *mrg = reinterpret_cast<float *>(&k_lds_g[0][0][0][0][0]);  // [wave][36][64]
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+            if (r == 0) m_lds[w8][rt][n] = m_run[rt];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            if (grp == 1) {
+                float *dst = mrg + w * 36 * 64 + lane;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dst[(j * 4 + c) * 64] = oacc[rt][j][c];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) dst[(32 + c) * 64] = lacc[rt][c];
+            }
+            __syncthreads();
+            if (grp == 0 && rows_w > 0) {
+                const float *src = mrg + w * 36 * 64 + lane;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int t = 4 * r + c;
+                    const float m0 = m_lds[w][rt][t], m1 = m_lds[4 + w][rt][t];
+                    const float M = fmaxf(m0, m1);
+                    const float a0 = m0 == -INFINITY ? 0.0f : fast_exp2(m0 - M);
+                    const float a1 = m1 == -INFINITY ? 0.0f : fast_exp2(m1 - M);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) oacc[rt][j][c] = a0 * oacc[rt][j][c] + a1 * src[(j * 4 + c) * 64];
+                    lacc[rt][c] = a0 * lacc[rt][c] + a1 * src[(32 + c) * 64];
+                }
+            }
+            __syncthreads();
+        }
+        if (grp == 1) return;
+        // the merged max of row n, which the records below carry
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) m_run[rt] = fmaxf(m_run[rt], m_lds[4 + w][rt][n]);
     }
     if (rows_w <= 0) return;
 
@@ -1753,6 +1814,13 @@ __global__ __launch_bounds__(256, WGS) void prefill_dma_kernel(DecodeArgs a) {
     prefill_body_dma<NB>(a, blockIdx.x);
 }
 
+// F16 prompt-chunk launches of at most one four-wave work-group per CU:
+// eight waves, the keys of each piece split between two groups of four, one
+// work-group per CU.
+__global__ __launch_bounds__(512, 1) void prefill_dma_split_kernel(DecodeArgs a) {
+    prefill_body_dma<3, true>(a, blockIdx.x);
+}
+
 // A mixed step's decode and prefill pieces in one launch, three work-groups
 // per CU: the decode pieces keep two blocks in flight instead of three (158
 // VGPRs on their own) and are walked by a.mixed_decode_waves of the four
@@ -1783,6 +1851,12 @@ namespace {
 //    at three per CU 7.07 ms.  Past one round the third slot keeps a CU busy
 //    while its tiles finish unevenly.
 constexpr int64_t kPrefillRoundGroups = 2 * 256;
+// Prompt-chunk launches of at most one four-wave work-group per CU run the
+// split kernel instead: the 32 tiles of a 1,024-token chunk at position 3,008
+// (256 work-groups) took 96.2 us against 116-122 us.  At two per CU the
+// four-wave work-groups are faster: two such chunks (512) 141-148 us against
+// 164 us, config 6's 2,016-token chunk (504) 137.8-142.1 against 145.5-146.5.
+constexpr int64_t kPrefillSplitGroups = 256;
 bool prefill_one_round(const DecodeArgs &a) {
     return static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads <= kPrefillRoundGroups;
 }
@@ -1851,6 +1925,8 @@ hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
     const uint32_t groups = static_cast<uint32_t>(static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads);
     if (a.elem_bytes == 1)
         hipLaunchKernelGGL((prefill_kernel<true, 3>), dim3(groups), dim3(256), 0, stream, a);
+    else if (groups <= kPrefillSplitGroups)
+        hipLaunchKernelGGL(prefill_dma_split_kernel, dim3(groups), dim3(512), 0, stream, a);
     else if (prefill_one_round(a))
         hipLaunchKernelGGL((prefill_dma_kernel<3, 2>), dim3(groups), dim3(256), 0, stream, a);
     else

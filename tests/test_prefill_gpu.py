@@ -250,6 +250,20 @@ def test_prompt_rows_with_softmax_scales_past_one(scale):
     m.close()
 
 
+@pytest.mark.parametrize("q_len,hist", [(1024, 3008), (512, 3520), (100, 4000), (32, 4000), (300, 0)])
+def test_prompt_only_launches_of_one_work_group_per_cu(q_len, hist):
+    """A prompt-only launch of at most one work-group per CU: each tile's keys
+    are split between two wave groups of one work-group and merged in LDS;
+    tiles cut into pieces (as far as that work-group count allows) write
+    records that the merge kernel combines."""
+    m = Mixed([q_len], [hist], seed=160 + q_len)
+    out, plan = m.run()
+    assert plan.info.num_items == 0 and plan.info.num_prefill_items * 8 <= 256
+    report(f"prompt only {q_len} after {hist}", items=plan.info.num_prefill_items, merges=plan.info.num_merges)
+    compare(f"prompt only {q_len} after {hist}", out, m.reference())
+    m.close()
+
+
 @pytest.mark.parametrize("hkv", [1, 2, 16])
 def test_mixed_step_with_other_kv_head_counts(hkv):
     m = Mixed([40, 1, 100, 1, 33], [10, 300, 50, 2000, 0], seed=150 + hkv, hkv=hkv)
