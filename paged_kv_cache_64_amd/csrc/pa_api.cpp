@@ -608,13 +608,13 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
         std::vector<PrefillItem> pitems;
         int64_t ppiece = std::min<int64_t>(pa::kMaxPrefillPieceBlocks,
                                            std::max<int64_t>(8, cut(tile_blocks, items_target)));
-        // An F16 launch of prompt tiles alone with at most one work-group per
-        // CU runs the split kernel (each tile's keys over two wave groups of
-        // one work-group), so its tiles are cut only as far as that count
-        // allows: into at most items_target / n_tiles pieces each.  The 32
-        // tiles of a 1,024-token chunk at position 3,008: whole, 96.2 us, against
-        // 121 us cut into 48 pieces for four-wave work-groups.
-        if (items.empty() && pool->elem_bytes() == 2 && n_tiles > 0 && n_tiles <= items_target)
+        // A launch of prompt tiles alone with at most one work-group per CU
+        // runs the split kernels (each tile's keys over two wave groups of one
+        // work-group), so its tiles are cut only as far as that count allows:
+        // into at most items_target / n_tiles pieces each.  The 32 tiles of a
+        // 1,024-token chunk at position 3,008 (F16): whole, 94.0-94.6 us,
+        // against 121 us cut into 48 pieces for four-wave work-groups.
+        if (items.empty() && n_tiles > 0 && n_tiles <= items_target)
             ppiece = std::min<int64_t>(pa::kMaxPrefillPieceBlocks,
                                        std::max<int64_t>(8, cut(max_tile, items_target / n_tiles)));
         for (int32_t s = 0; s < batch; ++s) {

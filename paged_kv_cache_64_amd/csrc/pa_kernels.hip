@@ -1135,23 +1135,34 @@ static_assert(kStageBlocks % 2 == 0 && kStageBlocks >= 2, "stages hold whole pai
 // Prompt-chunk pieces over an FP8 pool: the codes go through registers, one
 // stage ahead, and are widened to F16 on their way into LDS (F16 pools take
 // prefill_body_dma below, which copies straight into LDS).
+// SPLIT: as in prefill_body_dma, eight waves in two groups over the same
+// rows, each group half of the piece's stages in its own buffers, merged
+// through LDS at the end.
+template <bool SPLIT = false>
 __device__ __forceinline__ void prefill_body_fp8(const DecodeArgs &a, uint32_t bx) {
+    constexpr int kGroups = SPLIT ? 2 : 1;
+    constexpr int kThreads = 256 * kGroups;
     const int g = static_cast<int>(bx % a.num_kv_heads);
     const int32_t *it = a.prefill_items + kPrefillItemInts * static_cast<size_t>(bx / a.num_kv_heads);
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave of the work-group
+    const int grp = SPLIT ? w8 >> 2 : 0;                      // its group
+    const int w = SPLIT ? w8 & 3 : w8;                        // its wave within the group
     const int lane = tid & 63;
     const int n = lane & 15, r = lane >> 4;
 
     __shared__ int tbl_lds[kMaxPrefillPieceBlocks];
-    __shared__ __attribute__((aligned(16))) _Float16 k_lds[2][kStageBlocks][kBlockSize][kPadRow];  // [buffer][block][row][dim]
-    __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][kStageBlocks][kBlockSize][kPadRow];
+    // [group][buffer][block][row][dim]
+    __shared__ __attribute__((aligned(16))) _Float16 k_lds_g[kGroups][2][kStageBlocks][kBlockSize][kPadRow];
+    __shared__ __attribute__((aligned(16))) _Float16 v_lds_g[kGroups][2][kStageBlocks][kBlockSize][kPadRow];
+    auto &k_lds = k_lds_g[grp];
+    auto &v_lds = v_lds_g[grp];
     // the tile row r of tensor t (0: K, 1: V) in stage buffer buf
     auto kv_row = [&](int buf, int t, int blk, int row) -> _Float16 * {
         return t ? &v_lds[buf][blk][row][0] : &k_lds[buf][blk][row][0];
     };
-    __shared__ float alpha_lds[kWaves][2][16];
-    __shared__ float ml_lds[kWaves][2][16][2];
+    __shared__ float alpha_lds[kGroups * kWaves][2][16];
+    __shared__ float ml_lds[kGroups * kWaves][2][16][2];
 
     // Plan entries are clamped so a damaged plan cannot index outside q, out,
     // the tables, the pool or the workspace.
@@ -1171,7 +1182,7 @@ __device__ __forceinline__ void prefill_body_fp8(const DecodeArgs &a, uint32_t b
     const int b_hi = max(b_lo, min((t_hi + kBlockSize - 1) / kBlockSize, b_lo + kMaxPrefillPieceBlocks));
 
     const int32_t *table = a.tables + static_cast<size_t>(s) * a.max_blocks;
-    for (int i = tid; i < b_hi - b_lo; i += 256) tbl_lds[i] = table[b_lo + i];
+    for (int i = tid; i < b_hi - b_lo; i += kThreads) tbl_lds[i] = table[b_lo + i];
     __syncthreads();
 
     // this wave's query tokens and heads, and the keys its rows can see
@@ -1305,9 +1316,9 @@ __device__ __forceinline__ void prefill_body_fp8(const DecodeArgs &a, uint32_t b
                 const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run[rt] - m_new);
                 l_run[rt] *= alpha;
                 m_run[rt] = m_new;
-                if (r == 0) alpha_lds[w][rt][n] = alpha;
+                if (r == 0) alpha_lds[w8][rt][n] = alpha;
                 wave_lds_sync();
-                const float4 al = *reinterpret_cast<const float4 *>(&alpha_lds[w][rt][4 * r]);
+                const float4 al = *reinterpret_cast<const float4 *>(&alpha_lds[w8][rt][4 * r]);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     oacc[rt][j][0] *= al.x;
@@ -1349,42 +1360,99 @@ __device__ __forceinline__ void prefill_body_fp8(const DecodeArgs &a, uint32_t b
     // below its last query's position
     const int n_stages = (b_hi - b_lo + kStageBlocks - 1) / kStageBlocks;
     const int w_blocks = w_end > t_lo ? (w_end + kBlockSize - 1) / kBlockSize - b_lo : 0;  // blocks this wave needs
-    if (n_stages > 0) {
-        fetch(b_lo);
-        commit(0);
+    const int half = (n_stages + 1) / 2;
+    const int my_first = SPLIT && grp ? half : 0;                            // first stage of this group
+    const int my_count = SPLIT ? (grp ? n_stages - half : half) : n_stages;  // its stages
+    const int rounds = SPLIT ? half : n_stages;  // barrier rounds, the same for both groups
+    if (rounds > 0) {
+        if (!SPLIT || my_count > 0) {
+            fetch(b_lo + kStageBlocks * my_first);
+            commit(0);
+        }
         __syncthreads();
     }
-    // stage st reads LDS buffer st % 2; meanwhile stage st+1 is loaded into
-    // the staging registers and, at the end, goes into LDS buffer (st+1) % 2,
-    // which stage st-1 read before the last barrier
+    // this group's stage st reads its LDS buffer st % 2; meanwhile stage st+1
+    // is loaded into the staging registers and, at the end, goes into LDS
+    // buffer (st+1) % 2, which stage st-1 read before the last barrier
     auto stage = [&](int st, auto bufc) {
         constexpr int S = decltype(bufc)::value;  // == st % 2
-        const int b0 = b_lo + kStageBlocks * st;
-        if (st + 1 < n_stages) fetch(b0 + kStageBlocks);
+        const int gst = my_first + st;            // the stage within the piece
+        const int b0 = b_lo + kStageBlocks * gst;
+        if (st + 1 < my_count) fetch(b0 + kStageBlocks);
+        if (!SPLIT || st < my_count) {
 #pragma unroll
-        for (int sb = 0; sb < kStageBlocks; sb += 2)
-            if (kStageBlocks * st + sb < w_blocks) compute(S, sb, b0 + sb);
-        if (st + 1 < n_stages) commit(S ^ 1);
+            for (int sb = 0; sb < kStageBlocks; sb += 2)
+                if (kStageBlocks * gst + sb < w_blocks) compute(S, sb, b0 + sb);
+        }
+        if (st + 1 < my_count) commit(S ^ 1);
         __syncthreads();
     };
-    for (int st = 0; st < n_stages; st += 2) {
+    for (int st = 0; st < rounds; st += 2) {
         stage(st, std::integral_constant<int, 0>{});
-        if (st + 1 < n_stages) stage(st + 1, std::integral_constant<int, 1>{});
+        if (st + 1 < rounds) stage(st + 1, std::integral_constant<int, 1>{});
+    }
+    float mm[2][4], ll[2][4];  // SPLIT: the merged max and sum of rows 4r + c
+    if constexpr (SPLIT) {
+        // both groups' (max, sum) of every row to LDS; group 1 hands its
+        // outputs to group 0 through the free key buffers, one row tile at
+        // a time (32 values per lane), and group 0 merges
+        float *mrg = reinterpret_cast<float *>(&k_lds_g[0][0][0][0][0]);  // [wave][32][64]
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            float l = l_run[rt];
+            l += shfl_xor(l, 16);
+            l += shfl_xor(l, 32);
+            if (r == 0) {
+                ml_lds[w8][rt][n][0] = m_run[rt];
+                ml_lds[w8][rt][n][1] = l;
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            if (grp == 1) {
+                float *dst = mrg + w * 32 * 64 + lane;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dst[(j * 4 + c) * 64] = oacc[rt][j][c];
+            }
+            __syncthreads();
+            if (grp == 0 && rows_w > 0) {
+                const float *src = mrg + w * 32 * 64 + lane;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int t = 4 * r + c;
+                    const float m0 = ml_lds[w][rt][t][0], l0 = ml_lds[w][rt][t][1];
+                    const float m1 = ml_lds[4 + w][rt][t][0], l1 = ml_lds[4 + w][rt][t][1];
+                    const float M = fmaxf(m0, m1);
+                    const float a0 = m0 == -INFINITY ? 0.0f : fast_exp2(m0 - M);
+                    const float a1 = m1 == -INFINITY ? 0.0f : fast_exp2(m1 - M);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) oacc[rt][j][c] = a0 * oacc[rt][j][c] + a1 * src[(j * 4 + c) * 64];
+                    mm[rt][c] = M;
+                    ll[rt][c] = a0 * l0 + a1 * l1;
+                }
+            }
+            __syncthreads();
+        }
+        if (grp == 1) return;
     }
     if (rows_w <= 0) return;
 
-    // (m, l) of every row to LDS; lane l then writes rows 4r + c of each tile
+    if constexpr (!SPLIT) {
+        // (m, l) of every row to LDS; lane l then writes rows 4r + c of each tile
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        float l = l_run[rt];
-        l += shfl_xor(l, 16);
-        l += shfl_xor(l, 32);
-        if (r == 0) {
-            ml_lds[w][rt][n][0] = m_run[rt];
-            ml_lds[w][rt][n][1] = l;
+        for (int rt = 0; rt < 2; ++rt) {
+            float l = l_run[rt];
+            l += shfl_xor(l, 16);
+            l += shfl_xor(l, 32);
+            if (r == 0) {
+                ml_lds[w][rt][n][0] = m_run[rt];
+                ml_lds[w][rt][n][1] = l;
+            }
         }
+        wave_lds_sync();
     }
-    wave_lds_sync();
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         const int head = head0 + rt;
@@ -1393,7 +1461,7 @@ __device__ __forceinline__ void prefill_body_fp8(const DecodeArgs &a, uint32_t b
             const int t = 4 * r + c;  // row of the tile
             if (t >= rows_w) continue;
             const int tok = tok0 + t;
-            const float m = ml_lds[w][rt][t][0], l = ml_lds[w][rt][t][1];
+            const float m = SPLIT ? mm[rt][c] : ml_lds[w][rt][t][0], l = SPLIT ? ll[rt][c] : ml_lds[w][rt][t][1];
             if (direct) {
                 const size_t qrow = static_cast<size_t>(min(row0 + tok, a.num_q_rows - 1));
                 const float inv = a.v_scale / l;  // V's scale
@@ -1807,6 +1875,12 @@ __global__ __launch_bounds__(256, WGS) void prefill_kernel(DecodeArgs a) {
     prefill_body_fp8(a, blockIdx.x);
 }
 
+// FP8 prompt-chunk launches of at most one four-wave work-group per CU: the
+// split body, eight waves, one work-group per CU.
+__global__ __launch_bounds__(512, 1) void prefill_fp8_split_kernel(DecodeArgs a) {
+    prefill_body_fp8<true>(a, blockIdx.x);
+}
+
 // F16 pools: the copy goes straight to LDS, NB - 1 stages ahead; WGS
 // work-groups per CU.  launch_prefill chooses.
 template <int NB, int WGS>
@@ -1923,7 +1997,9 @@ hipError_t launch_decode_merge_planned(const DecodeArgs &a, hipStream_t stream) 
 
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
     const uint32_t groups = static_cast<uint32_t>(static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads);
-    if (a.elem_bytes == 1)
+    if (a.elem_bytes == 1 && groups <= kPrefillSplitGroups)
+        hipLaunchKernelGGL(prefill_fp8_split_kernel, dim3(groups), dim3(512), 0, stream, a);
+    else if (a.elem_bytes == 1)
         hipLaunchKernelGGL((prefill_kernel<true, 3>), dim3(groups), dim3(256), 0, stream, a);
     else if (groups <= kPrefillSplitGroups)
         hipLaunchKernelGGL(prefill_dma_split_kernel, dim3(groups), dim3(512), 0, stream, a);

@@ -303,6 +303,17 @@ def test_fp8_prompt_rows_with_a_score_scale_past_one():
     m.close()
 
 
+@pytest.mark.parametrize("q_len,hist", [(1024, 3008), (512, 3520), (32, 4000)])
+def test_fp8_prompt_only_launches_of_one_work_group_per_cu(q_len, hist):
+    """FP8 pools: each tile's keys split between two wave groups of one
+    work-group per CU, merged in LDS; cut tiles write value-domain records."""
+    m = Mixed([q_len], [hist], seed=170 + q_len, dtype=FP8, kv_scales=FP8_SCALES)
+    out, plan = m.run()
+    assert plan.info.num_items == 0 and plan.info.num_prefill_items * 8 <= 256
+    compare(f"fp8 prompt only {q_len} after {hist}", out, m.reference())
+    m.close()
+
+
 @pytest.mark.parametrize("n", [1, 17, 300])
 def test_fp8_whole_prompt_prefill(n):
     m = Mixed([n], [0], seed=120 + n, dtype=FP8, kv_scales=FP8_SCALES)
