@@ -519,3 +519,44 @@ def test_cascade_prefix_workload_full():
            merges=plan.info.num_merges)
     compare("cascade config5", out, st.reference(0))
     st.close()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_planned_decodes_against_the_oracle(case):
+    """Seeded random planned decodes over the planner's paths: ragged and
+    short contexts, cut and whole sequences, per-wave KV heads forced on and
+    off where they apply, several KV-head counts, F16 and FP8 pools, and the
+    newest token appended on odd cases."""
+    rng = np.random.default_rng(3000 + case)
+    hkv = int(rng.choice([1, 2, 4, 8, 16]))
+    top = int(rng.choice([64, 300, 2000, 6000]))
+    # about 400k (token, KV head) rows at most, so the host side stays small
+    batch = int(rng.integers(1, max(2, min(300, 800_000 // (top * hkv)))))
+    lens = [int(x) for x in rng.integers(0, top, size=batch)]
+    fp8 = case % 3 == 1
+    kw = dict(dtype=pa.PA_FP8_E4M3, kv_scales=(0.1, 0.0173)) if fp8 else {}
+    w = workloads.custom(lens, seed=4000 + case, num_q_heads=4 * hkv, num_kv_heads=hkv)
+    st = Staged(w, **kw)
+    _poison_tails(st)
+    q, tables, ids, k, v = st.host[0]
+    k_new = v_new = None
+    if case % 2 == 1:
+        k_new = rng.standard_normal((batch, hkv, 128)).astype(np.float16)
+        v_new = rng.standard_normal((batch, hkv, 128)).astype(np.float16)
+    for wave_heads in (0, 1):  # the second run appends the same rows again: same result
+        out, plan = _planned(st, k_new=None if k_new is None else torch.from_numpy(k_new).cuda(),
+                             v_new=None if v_new is None else torch.from_numpy(v_new).cuda(),
+                             wave_heads=wave_heads)
+        report(f"random decode {case}", hkv=hkv, fp8=fp8, batch=batch, top=top, wave_heads=wave_heads,
+               items=plan.info.num_items, merges=plan.info.num_merges, longest=plan.info.max_piece_tokens)
+        if k_new is not None:
+            k2, v2 = k.copy(), v.copy()
+            for s, c in enumerate(lens):
+                if c:
+                    r = np.searchsorted(ids, tables[s, (c - 1) // 16])
+                    k2[r, (c - 1) % 16] = k_new[s]
+                    v2[r, (c - 1) % 16] = v_new[s]
+            st.host[0] = (q, tables, ids, k2, v2)
+        compare(f"random decode {case} wave_heads={wave_heads}", out, st.reference(0))
+        st.host[0] = (q, tables, ids, k, v)
+    st.close()

@@ -365,3 +365,26 @@ def test_fp8_value_scale_is_linear_in_prefill_rows():
     assert torch.equal(b[normal], a2[normal])
     assert float((b - a2).abs().max()) <= 2.0 ** -24
     m.close()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_steps_against_the_oracle(case):
+    """Seeded random steps over the planner's paths: prompt-only launches
+    (split kernels, cut tiles), mixed launches with decode rows, and several
+    KV-head counts and pool types, each checked against the oracle in full."""
+    rng = np.random.default_rng(1000 + case)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    batch = int(rng.integers(1, 6))
+    q_lens = [int(x) for x in rng.choice([1, 1, 2, 17, 40, 100, 257], size=batch)]
+    if case % 2 == 0:                       # prompt-only steps on even cases
+        q_lens = [max(q, 2) for q in q_lens]
+    hist = [int(x) for x in rng.integers(0, 1500, size=batch)]
+    fp8 = case % 3 == 2
+    kw = dict(dtype=FP8, kv_scales=FP8_SCALES) if fp8 else {}
+    m = Mixed(q_lens, hist, seed=2000 + case, hkv=hkv, **kw)
+    out, plan = m.run()
+    report(f"random step {case}", hkv=hkv, fp8=fp8, q_lens=q_lens, hist=hist,
+           decode_items=plan.info.num_items, prefill_items=plan.info.num_prefill_items,
+           merges=plan.info.num_merges)
+    compare(f"random step {case}", out, m.reference())
+    m.close()
