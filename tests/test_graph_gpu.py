@@ -59,16 +59,17 @@ def test_graph_replays_equal_the_eager_step():
     st.close()
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_graph_replays_of_a_mixed_step_equal_the_eager_step(fp8):
+@pytest.mark.parametrize("fp8,prompt_only", [(False, False), (True, False), (False, True), (True, True)])
+def test_graph_replays_of_a_mixed_step_equal_the_eager_step(fp8, prompt_only):
     """A chunked-prefill / mixed step over two layers (decode rows, whole and
-    cut prompt tiles, merges) captured once and replayed: every replay gives
-    the eager bits, and the eager step matches the oracle."""
+    cut prompt tiles, merges; or prompt tiles alone, which take the split
+    kernels) captured once and replayed: every replay gives the eager bits,
+    and the eager step matches the oracle."""
     import oracle
     import paged_kv_cache_64_amd as pa
 
-    q_lens = [1, 40, 1, 300, 7]
-    hist = [700, 0, 4095, 3000, 20]
+    q_lens = [40, 300, 7] if prompt_only else [1, 40, 1, 300, 7]
+    hist = [0, 3000, 20] if prompt_only else [700, 0, 4095, 3000, 20]
     lens = [h + n for h, n in zip(hist, q_lens)]
     w = workloads.custom(lens, seed=52 + fp8, layers=2)
     scales = (0.1, 0.0173)
@@ -77,7 +78,8 @@ def test_graph_replays_of_a_mixed_step_equal_the_eager_step(fp8):
     rows = int(starts[-1])
     qs = [torch.from_numpy(w.q_rows(rows, L)).cuda() for L in range(2)]
     plan = st.pool.prefill_plan(starts, lens)
-    assert plan.info.num_merges > 0 and plan.info.num_items > 0 and plan.info.num_prefill_items > 0
+    assert plan.info.num_merges > 0 and plan.info.num_prefill_items > 0
+    assert (plan.info.num_items == 0) == prompt_only
     pinned = torch.from_numpy(plan.host.copy()).pin_memory()
     outs = [torch.zeros_like(q) for q in qs]
 
@@ -114,5 +116,5 @@ def test_graph_replays_of_a_mixed_step_equal_the_eager_step(fp8):
                                   t2, starts, lens, w.scale, 16, *scales)
     else:
         ref = oracle.prefill(qh, kc, vc, t2, starts, lens, w.scale, 16)
-    compare(f"graph mixed fp8={fp8}", eager[1], ref)
+    compare(f"graph mixed fp8={fp8} prompt_only={prompt_only}", eager[1], ref)
     st.close()
