@@ -1503,6 +1503,34 @@ __device__ __forceinline__ void lds_read_tr16_x8(u2 (&d)[8], const uint32_t (&a)
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
         : "memory");
 }
+// sixteen transpose reads in the order of two lds_read_tr16_x8 calls, two
+// per address (the second 4 KiB further on: the stage's next key block),
+// complete when the statement ends
+__device__ __forceinline__ void lds_read_tr16_x16(u2 (&d)[2][8], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %2, %17\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %4, %18\n\t"
+        "ds_read_b64_tr_b16 %5, %18 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %6, %19\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %8, %20\n\t"
+        "ds_read_b64_tr_b16 %9, %20 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %10, %21\n\t"
+        "ds_read_b64_tr_b16 %11, %21 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %12, %22\n\t"
+        "ds_read_b64_tr_b16 %13, %22 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %14, %23\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(d[0][0]), "=&v"(d[0][1]), "=&v"(d[0][2]), "=&v"(d[0][3]), "=&v"(d[0][4]), "=&v"(d[0][5]),
+          "=&v"(d[0][6]), "=&v"(d[0][7]), "=&v"(d[1][0]), "=&v"(d[1][1]), "=&v"(d[1][2]), "=&v"(d[1][3]),
+          "=&v"(d[1][4]), "=&v"(d[1][5]), "=&v"(d[1][6]), "=&v"(d[1][7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // The prompt-chunk body for F16 pools, with the copy straight into LDS
@@ -1648,6 +1676,19 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 kx[blk][kk] = *reinterpret_cast<const h8 *>(&k_lds[buf][sb + blk][n][8 * ((4 * kk + r) ^ k_swz(n))]);
+        // the value operands of P V over dims 16j .. 16j+15: lane (r, n) gets
+        // tokens 4r .. 4r+3 of each block at dim 16j + n straight from the
+        // transpose reads.  With three buffers (registers to spare) they are
+        // read here, behind the key reads, so that one wait covers both (the
+        // chunk of config 6 about 1.5 % faster); else just before P V.
+        u2 t[2][8];  // [half][4 j's x 2 blocks]
+        if constexpr (NB == 3) {
+            uint32_t ad[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                ad[j] = lds_addr(&v_lds[buf][sb][tr_row][8 * ((2 * j + (tr_col >> 3)) ^ tr_swz) + (tr_col & 7)]);
+            lds_read_tr16_x16(t, ad);
+        }
         f4 st[2][2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -1721,18 +1762,18 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
                     pw[rt][4 * blk + c + 1] = pp.y;
                 }
         }
-        // P V over dims 16j .. 16j+15: lane (r, n) gets tokens 4r .. 4r+3 of
-        // each block at dim 16j + n straight from the transpose reads
-        u2 t[2][8];  // [half][4 j's x 2 blocks]
+        if constexpr (NB != 3) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            uint32_t ad[8];
+            for (int hf = 0; hf < 2; ++hf) {
+                uint32_t ad[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int j = 4 * hf + (q >> 1), blk = q & 1;
-                ad[q] = lds_addr(&v_lds[buf][sb + blk][tr_row][8 * ((2 * j + (tr_col >> 3)) ^ tr_swz) + (tr_col & 7)]);
+                for (int q = 0; q < 8; ++q) {
+                    const int j = 4 * hf + (q >> 1), blk = q & 1;
+                    ad[q] = lds_addr(
+                        &v_lds[buf][sb + blk][tr_row][8 * ((2 * j + (tr_col >> 3)) ^ tr_swz) + (tr_col & 7)]);
+                }
+                lds_read_tr16_x8(t[hf], ad);
             }
-            lds_read_tr16_x8(t[hf], ad);
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
