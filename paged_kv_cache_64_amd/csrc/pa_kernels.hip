@@ -1944,12 +1944,17 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_split_kernel(DecodeArgs a)
 template <bool FP8>
 __global__ __launch_bounds__(256, 3) void mixed_kernel(DecodeArgs a) {
     const uint32_t nd = static_cast<uint32_t>(a.num_items) * static_cast<uint32_t>(a.num_kv_heads);
-    if (blockIdx.x < nd)
+    if (blockIdx.x < nd) {
         decode_partial_body<2, FP8, true>(a, blockIdx.x, 0, 0);
-    else if constexpr (FP8)
-        prefill_body_fp8(a, blockIdx.x - nd);
-    else
-        prefill_body_dma<2>(a, blockIdx.x - nd);
+    } else {
+        // the prompt tiles' waves issue ahead of the decode streams that
+        // share their SIMDs (wave priority 1 against 0)
+        __builtin_amdgcn_s_setprio(1);
+        if constexpr (FP8)
+            prefill_body_fp8(a, blockIdx.x - nd);
+        else
+            prefill_body_dma<2>(a, blockIdx.x - nd);
+    }
 }
 
 }  // namespace
