@@ -550,7 +550,9 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
         // 89 us, chunk alone 142-150 us, fused 228-234 us with 4 waves and
         // 190-198 us with 2 (1 wave: 188 us; 3: 220 us).  The estimate: decode
         // bytes at 6.5 TB/s against the tiles' flops at 0.85 PFLOP/s (their
-        // rates measured alone).
+        // rates measured alone).  With the tiles' waves at the higher issue
+        // priority (mixed_kernel) 2 waves still win: config 6's 32-layer step
+        // 5.13 ms against 5.28-5.30 ms with 4.
         double tile_flops = 0.0;
         for (int32_t s = 0; s < batch; ++s) {
             const int64_t q_len = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
