@@ -1618,9 +1618,16 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
     f4 oacc[2][8];
     f4 lacc[2];      // running sums, in oacc's layout: rows 4r + c (every column the same)
     float m_run[2];  // row n of each tile, log2 units
+    // m_run + kTau, and the weights' offset (-m_run, 0 while m_run = -inf),
+    // kept beside m_run where registers allow (three buffers), else derived
+    // from it at each pair: the same values either way
+    constexpr bool kKeepOffsets = NB == 3;
+    float thr[2], negm[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         m_run[rt] = -INFINITY;
+        thr[rt] = -INFINITY;
+        negm[rt] = 0.0f;
         lacc[rt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) oacc[rt][j] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1724,7 +1731,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
             const float m3 = max3_raw(st[rt][1][2], st[rt][1][3], m1);
             const float bmax = max3_raw(m2, m3, m3);
             const float mb = bmax * c_scale;
-            if (__builtin_amdgcn_ballot_w64(mb > m_run[rt] + kTau) != 0) {
+            if (__builtin_amdgcn_ballot_w64(mb > (kKeepOffsets ? thr[rt] : m_run[rt] + kTau)) != 0) {
                 float bm = mb;
                 bm = fmaxf(bm, shfl_xor(bm, 16));
                 bm = fmaxf(bm, shfl_xor(bm, 32));
@@ -1732,6 +1739,8 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
                 // a row that has seen no key yet keeps m = -inf (and alpha 1)
                 const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run[rt] - m_new);
                 m_run[rt] = m_new;
+                thr[rt] = m_new + kTau;
+                negm[rt] = m_new == -INFINITY ? 0.0f : -m_new;
                 if (r == 0) alpha_lds[w8][rt][n] = alpha;
                 wave_lds_sync();
                 const float4 al = *reinterpret_cast<const float4 *>(&alpha_lds[w8][rt][4 * r]);
@@ -1750,7 +1759,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
             // weights exp2(s * scale - m) enter P V as F16, and the running
             // sums (one more MFMA, below) add the same rounded values (masked
             // scores give exp2(-inf) = 0)
-            const float neg_m = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
+            const float neg_m = kKeepOffsets ? negm[rt] : m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
