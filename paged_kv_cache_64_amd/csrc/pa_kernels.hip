@@ -1618,10 +1618,11 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
     f4 oacc[2][8];
     f4 lacc[2];      // running sums, in oacc's layout: rows 4r + c (every column the same)
     float m_run[2];  // row n of each tile, log2 units
-    // m_run + kTau, and the weights' offset (-m_run, 0 while m_run = -inf),
-    // kept beside m_run where registers allow (three buffers), else derived
-    // from it at each pair: the same values either way
-    constexpr bool kKeepOffsets = NB == 3;
+    // the weights' offset (-m_run, 0 while m_run = -inf) and m_run + kTau,
+    // kept beside m_run instead of derived from it at each pair (the same
+    // values either way); the threshold only where registers allow (three
+    // buffers)
+    constexpr bool kKeepThreshold = NB == 3;
     float thr[2], negm[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -1731,7 +1732,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
             const float m3 = max3_raw(st[rt][1][2], st[rt][1][3], m1);
             const float bmax = max3_raw(m2, m3, m3);
             const float mb = bmax * c_scale;
-            if (__builtin_amdgcn_ballot_w64(mb > (kKeepOffsets ? thr[rt] : m_run[rt] + kTau)) != 0) {
+            if (__builtin_amdgcn_ballot_w64(mb > (kKeepThreshold ? thr[rt] : m_run[rt] + kTau)) != 0) {
                 float bm = mb;
                 bm = fmaxf(bm, shfl_xor(bm, 16));
                 bm = fmaxf(bm, shfl_xor(bm, 32));
@@ -1759,7 +1760,7 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
             // weights exp2(s * scale - m) enter P V as F16, and the running
             // sums (one more MFMA, below) add the same rounded values (masked
             // scores give exp2(-inf) = 0)
-            const float neg_m = kKeepOffsets ? negm[rt] : m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
+            const float neg_m = negm[rt];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
