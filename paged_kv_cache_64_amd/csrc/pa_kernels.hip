@@ -1635,7 +1635,8 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
     }
     const float c_scale = a.scale_log2e;
     const _Float16 one = static_cast<_Float16>(1.0f);
-    const h8 ones8 = {one, one, one, one, one, one, one, one};
+    h8 ones8 = {one, one, one, one, one, one, one, one};
+    if constexpr (NB == 3) asm volatile("" : "+v"(ones8));  // held in registers, not rebuilt per pair
 
     // copies: wave w moves tensor w/2 (K, V) of block w%2 of the pair straight
     // into LDS, 1 KiB per load instruction: lane l fills chunk l%16 of row
@@ -1661,8 +1662,10 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
             uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tbl_lds[live ? bb - b_lo : 0]));
             phys = phys > last_block ? last_block : phys;
             const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
-            const int rows = cp_tensor ? min(max(t_hi - bb * kBlockSize, 0), kBlockSize) : kBlockSize;
-            const int bytes = __builtin_amdgcn_readfirstlane(live ? rows * kHeadDim * 2 : 0);
+            // a live block holds at least one key (bb < b_hi), so only the
+            // upper clamp is needed for its value rows
+            const int rows = cp_tensor ? min(t_hi - bb * kBlockSize, kBlockSize) : kBlockSize;
+            const int bytes = live ? rows * kHeadDim * 2 : 0;
             const __amdgpu_buffer_rsrc_t rs = tile_rsrc(cp_layer + base, bytes);
             _Float16 *tile = cp_tensor ? &v_lds[buf][cp_blk0 + x][0][0] : &k_lds[buf][cp_blk0 + x][0][0];
 #pragma unroll
