@@ -1210,9 +1210,11 @@ __device__ __forceinline__ void prefill_body_fp8(const DecodeArgs &a, uint32_t b
 
     f4 oacc[2][8];
     float m_run[2], l_run[2];  // row n of each tile, log2 units (l: this lane's share)
+    float negm[2];             // the weights' offset: -m_run, 0 while m_run = -inf
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         m_run[rt] = -INFINITY;
+        negm[rt] = 0.0f;
         l_run[rt] = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) oacc[rt][j] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1316,6 +1318,7 @@ __device__ __forceinline__ void prefill_body_fp8(const DecodeArgs &a, uint32_t b
                 const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run[rt] - m_new);
                 l_run[rt] *= alpha;
                 m_run[rt] = m_new;
+                negm[rt] = m_new == -INFINITY ? 0.0f : -m_new;
                 if (r == 0) alpha_lds[w8][rt][n] = alpha;
                 wave_lds_sync();
                 const float4 al = *reinterpret_cast<const float4 *>(&alpha_lds[w8][rt][4 * r]);
@@ -1329,7 +1332,7 @@ __device__ __forceinline__ void prefill_body_fp8(const DecodeArgs &a, uint32_t b
             }
             // weights exp2(s * scale - m) enter P V as F16; the running sum
             // adds the same rounded values (masked scores give exp2(-inf) = 0)
-            const float neg_m = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
+            const float neg_m = negm[rt];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
