@@ -545,13 +545,13 @@ pa_status build_mixed_plan(const pa_pool *pool, const int32_t *query_start, cons
         // memory path, and the prompt tiles sharing the CU barely progress until
         // they end (the launch then costs the sum of its parts); with 2, both
         // kinds run side by side and the decode pieces, at about half their
-        // rate, end about when the tiles do.  Config 6's geometry (32 decodes at
-        // 4096 tokens + a 2016-token chunk at 2016), per layer: decode alone
+        // rate, end about when the tiles do.  32 decodes at 4096 tokens beside
+        // a 2016-token chunk at position 2016, per layer: decode alone
         // 89 us, chunk alone 142-150 us, fused 228-234 us with 4 waves and
         // 190-198 us with 2 (1 wave: 188 us; 3: 220 us).  The estimate: decode
         // bytes at 6.5 TB/s against the tiles' flops at 0.85 PFLOP/s (their
         // rates measured alone).  With the tiles' waves at the higher issue
-        // priority (mixed_kernel) 2 waves still win: config 6's 32-layer step
+        // priority (mixed_kernel) 2 waves still win: that step over 32 layers
         // 5.13 ms against 5.28-5.30 ms with 4.
         double tile_flops = 0.0;
         for (int32_t s = 0; s < batch; ++s) {

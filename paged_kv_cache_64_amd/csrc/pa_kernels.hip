@@ -1693,8 +1693,9 @@ __device__ __forceinline__ void prefill_body_dma(const DecodeArgs &a, uint32_t b
         // the value operands of P V over dims 16j .. 16j+15: lane (r, n) gets
         // tokens 4r .. 4r+3 of each block at dim 16j + n straight from the
         // transpose reads.  With three buffers (registers to spare) they are
-        // read here, behind the key reads, so that one wait covers both (the
-        // chunk of config 6 about 1.5 % faster); else just before P V.
+        // read here, behind the key reads, so that one wait covers both (a
+        // 2016-token chunk at position 2016 about 1.5 % faster); else just
+        // before P V.
         u2 t[2][8];  // [half][4 j's x 2 blocks]
         if constexpr (NB == 3) {
             uint32_t ad[8];
@@ -1991,7 +1992,8 @@ constexpr int64_t kPrefillRoundGroups = 2 * 256;
 // split kernel instead: the 32 tiles of a 1,024-token chunk at position 3,008
 // (256 work-groups) took 96.2 us against 116-122 us.  At two per CU the
 // four-wave work-groups are faster: two such chunks (512) 141-148 us against
-// 164 us, config 6's 2,016-token chunk (504) 137.8-142.1 against 145.5-146.5.
+// 164 us, a 2,016-token chunk at position 2,016 (504) 137.8-142.1 against
+// 145.5-146.5.
 constexpr int64_t kPrefillSplitGroups = 256;
 bool prefill_one_round(const DecodeArgs &a) {
     return static_cast<int64_t>(a.num_prefill_items) * a.num_kv_heads <= kPrefillRoundGroups;

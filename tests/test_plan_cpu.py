@@ -416,9 +416,10 @@ def test_piece_size_balances_the_compute_units(pool):
 
 def test_mixed_launch_walks_decode_pieces_with_two_waves_when_the_tiles_dominate(pool):
     """pa_plan_info.mixed_decode_waves: a mixed step whose prompt tiles take longer
-    than its decode pieces (config 6's geometry) walks the decode pieces with 2
-    of 4 waves so both kinds progress side by side; a step dominated by its
-    decode rows keeps 4, and so does every plan without both kinds."""
+    than its decode pieces (32 decodes at 4096 tokens beside a 2016-token chunk)
+    walks the decode pieces with 2 of 4 waves so both kinds progress side by
+    side; a step dominated by its decode rows keeps 4, and so does every plan
+    without both kinds."""
     cfg6_q = [2016] + [1] * 32
     cfg6_lens = [4032] + [4096] * 32
     starts = np.concatenate([[0], np.cumsum(cfg6_q)]).astype(np.int32)
