@@ -1245,9 +1245,11 @@ __device__ __forceinline__ void prefill_body_fp8(const DecodeArgs &a, uint32_t b
             uint32_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tbl_lds[live ? bb - b_lo : 0]));
             phys = phys > last_block ? last_block : phys;
             const size_t base = (static_cast<size_t>(phys) * a.num_kv_heads + g) * tile_bytes;
-            const int rows = cp_tensor ? min(max(t_hi - bb * kBlockSize, 0), kBlockSize) : kBlockSize;
-            // (wave-uniform; said so, or the compiler wraps each load in a waterfall loop)
-            const int bytes = __builtin_amdgcn_readfirstlane(live ? rows * kHeadDim : 0);
+            // a live block holds at least one key (bb < b_hi), so only the
+            // upper clamp is needed for its value rows; all of it in scalar
+            // registers (wave-uniform, so no per-lane loop around the loads)
+            const int rows = cp_tensor ? min(t_hi - bb * kBlockSize, kBlockSize) : kBlockSize;
+            const int bytes = live ? rows * kHeadDim : 0;
             const __amdgpu_buffer_rsrc_t rs = tile_rsrc(cp_layer + base, bytes);
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) stg8[x][i] = load_shared8(rs, static_cast<uint32_t>(8 * lane + 512 * i));
