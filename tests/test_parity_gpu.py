@@ -521,7 +521,7 @@ def test_cascade_prefix_workload_full():
     st.close()
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(24))
 def test_random_planned_decodes_against_the_oracle(case):
     """Seeded random planned decodes over the planner's paths: ragged and
     short contexts, cut and whole sequences, per-wave KV heads forced on and

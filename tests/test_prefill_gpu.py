@@ -367,7 +367,7 @@ def test_fp8_value_scale_is_linear_in_prefill_rows():
     m.close()
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(24))
 def test_random_steps_against_the_oracle(case):
     """Seeded random steps over the planner's paths: prompt-only launches
     (split kernels, cut tiles), mixed launches with decode rows, and several
