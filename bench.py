@@ -782,6 +782,10 @@ def bench_mixed(args, w, dev):
                      "flops_per_layer": pf_flops, "mean_layer_us": round(pf_us, 3)},
         "decode_rows_us_per_layer": round(dec_us, 3),
         "decode_rows_GBps": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),
+        # the whole step per layer (plan upload included) against the chunk
+        # and the decode rows timed alone: how much of the two parts overlaps
+        "step_us_per_layer": round(ms_per_step * 1e3 / w.layers, 3),
+        "step_over_parts": round(ms_per_step * 1e3 / w.layers / (pf_us + dec_us), 4),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
         "cpu_baseline": cpu,
         "parity_sample": parity,
