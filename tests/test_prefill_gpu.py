@@ -314,6 +314,20 @@ def test_fp8_prompt_only_launches_of_one_work_group_per_cu(q_len, hist):
     m.close()
 
 
+def test_fp8_prompt_chunk_alone_sampled():
+    """The 2016-token chunk at position 2016 on an FP8 pool: 63 tiles, one
+    round of prompt-only work-groups (more than one per CU).  Rows are
+    sampled."""
+    m = Mixed([2016], [2016], seed=133, dtype=FP8, kv_scales=FP8_SCALES)
+    out, plan = m.run()
+    assert plan.info.num_items == 0 and plan.info.num_prefill_items == 63 and plan.info.num_merges == 0
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 1000, 1983, 1984, 2015],
+                                     rng.choice(2016, 24, replace=False)])).astype(np.int64)
+    compare("fp8 chunk alone sampled", out[torch.from_numpy(rows).cuda()], m.reference(rows))
+    m.close()
+
+
 @pytest.mark.parametrize("n", [1, 17, 300])
 def test_fp8_whole_prompt_prefill(n):
     m = Mixed([n], [0], seed=120 + n, dtype=FP8, kv_scales=FP8_SCALES)
